@@ -1,0 +1,106 @@
+"""Pins for the oracle's scoring MLP and top-k keep set (CPU only).
+
+KVP promo page (arXiv 2602.10238), "Core mechanism": one small MLP per head
+over the K/V vectors gives each token a score; deployment ranks by score and
+truncates to the budget. The oracle is pinned against a naive Python
+evaluation of the MLP, against a full Python sort of (score desc, position
+asc), and against the invariants every top-k must satisfy.
+"""
+import math
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from golden.read import constants
+from oracle import policy
+
+
+def naive_mlp(k, v, w, D):
+    x = list(k) + list(v)
+    n1 = 32 * 2 * D
+    h = []
+    for j in range(32):
+        a = math.fsum(w[j * 2 * D + i] * x[i] for i in range(2 * D)) + w[n1 + j]
+        h.append(max(a, 0.0))
+    return math.fsum(w[n1 + 32 + j] * h[j] for j in range(32)) + w[n1 + 64]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_mlp_matches_naive_loops(D):
+    rng = np.random.default_rng(D)
+    w = rng.standard_normal(32 * 2 * D + 65) * 0.1
+    k = rng.standard_normal((5, D))
+    v = rng.standard_normal((5, D))
+    got = policy.mlp_scores(k, v, w)
+    for i in range(5):
+        assert abs(got[i] - naive_mlp(k[i], v[i], w.tolist(), D)) < 1e-12
+
+
+def test_mlp_relu_and_bias_terms():
+    D = 64
+    w = np.zeros(32 * 2 * D + 65)
+    w[-1] = 2.5                      # b2 only
+    assert policy.mlp_scores(np.ones((1, D)), np.ones((1, D)), w)[0] == 2.5
+    w[32 * 2 * D] = -1.0             # b1[0] negative: ReLU clips it
+    w[32 * 2 * D + 32] = 7.0         # w2[0]
+    assert policy.mlp_scores(np.zeros((1, D)), np.zeros((1, D)), w)[0] == 2.5
+    w[32 * 2 * D] = 1.0
+    assert policy.mlp_scores(np.zeros((1, D)), np.zeros((1, D)), w)[0] == 9.5
+
+
+def test_mlp_size_is_the_pages_8k():
+    c = constants()
+    n = 32 * 2 * 128 + 32 + 32 + 1
+    assert n == 8257 and abs(n - c["mlp_params_approx"][0]) < 300
+
+
+def python_topk(scores, budget):
+    n = len(scores)
+    k = budget * n // 1000
+    key = [(1, 0.0, i) if s != s else (0, -s, i) for i, s in enumerate(scores)]
+    chosen = sorted(range(n), key=lambda i: key[i])[:k]
+    out = [False] * n
+    for i in chosen:
+        out[i] = True
+    return out
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.one_of(st.floats(allow_nan=True, allow_infinity=True, width=32),
+                          st.sampled_from([0.0, 1.0, -1.0])), max_size=200),
+       st.integers(0, 1000))
+def test_topk_matches_full_python_sort(scores, budget):
+    got = policy.topk_keep(np.array(scores, np.float32), budget)
+    assert got.tolist() == python_topk(scores, budget)
+
+
+def test_topk_invariants():
+    rng = np.random.default_rng(0)
+    s = rng.standard_normal(5000)
+    for budget in (100, 300, 500, 900, 1000, 0):
+        keep = policy.topk_keep(s, budget)
+        k = budget * 5000 // 1000
+        assert keep.sum() == k
+        if 0 < k < 5000:
+            assert s[keep].min() >= s[~keep].max()
+
+
+def test_topk_ties_keep_lower_positions():
+    s = np.array([1.0, 2.0, 1.0, 1.0, 2.0, 1.0])
+    assert policy.topk_keep(s, 500).tolist() == [True, True, False, False, True, False]
+
+
+def test_topk_nan_ranks_last():
+    s = np.array([np.nan, -1e30, np.nan, -np.inf])
+    assert policy.topk_keep(s, 500).tolist() == [False, True, False, True]
+    assert policy.topk_keep(s, 750).tolist() == [True, True, False, True]
+
+
+def test_budget_k_floor():
+    assert policy.budget_k(130928, 100) == 13092
+    assert policy.budget_k(130928, 500) == 65464
+    assert policy.budget_k(32624, 300) == 9787
+    assert policy.budget_k(7, 1000) == 7 and policy.budget_k(7, 0) == 0
+    c = constants()
+    assert c["budget_min_percent"][0] == 10 and c["budget_max_percent"][0] == 90
