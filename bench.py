@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark: decode steps over a compressed KV cache on one MI355X.
+
+A step is one pass of the whole hot path over one batch: append one bf16 K/V
+token per sequence (INT4 + INT8 ring encode), score it with the per-head MLP
+and refresh the top-k keep mask, then the split INT4/INT8 decode attention
+with the log-sum-exp merge. Inputs (new tokens, queries) are generated and
+resident in HBM before the timed region.
+
+Default workload ``long128k``: batch 4, 32 query / 8 kv heads, head_dim 128,
+context 131072, keep masks from a seeded per-head MLP at 10% and at 50%
+(one cache per budget; a step runs both). To keep the 256 MB Infinity Cache
+from serving repeated reads, steps rotate over replica caches so that more
+than 1 GiB of cache is touched between two reads of the same replica.
+
+Prints one JSON line. ``value`` is KV GB/s: the attention's algorithmic bytes
+per step (kept INT4 tokens at 160 B, INT8 tokens at 264 B per kv head, plus
+queries, outputs, mask words and block table) divided by the whole step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+WORKLOAD_LAYERS = {
+    "long128k": ["long128k_b10", "long128k_b50"],
+    "uniform4k": ["uniform4k"],
+    "longtail": ["longtail"],
+    "fullstep": ["fullstep"] * 36,
+    "tiny": ["tiny"],
+}
+
+
+def algorithmic_bytes(w, lengths, keep4_counts):
+    """Bytes one attention call must move for workload ``w`` at ``lengths``."""
+    D, Hkv, Hq = w.head_dim, w.kv_heads, w.q_heads
+    per4 = D + 8 * (D // 32)          # K+V codes + K/V scale,min per group
+    per8 = 2 * D + 8                  # K+V int8 codes + two fp32 scales
+    qbytes = 2 if w.src_dtype == "bf16" else 4
+    total = 0
+    for b, L in enumerate(lengths):
+        L = int(L)
+        n8 = min(L, 16) + max(0, L - max(16, L - 128))
+        n4 = max(0, L - 144)
+        total += Hkv * n8 * per8 + int(keep4_counts[b]) * per4
+        total += Hkv * ((16 + n4 + 31) // 32) * 4     # mask words over the INT4 region
+        total += ((L + 15) // 16) * 4                 # block table entries
+        total += Hq * (D * qbytes + D * 4 + 4)        # q in, out and lse
+    return total
+
+
+def kept_counts(w, lengths):
+    """Kept INT4 positions summed over kv heads, per sequence."""
+    out = []
+    for L in lengths:
+        n4 = max(0, int(L) - 144)
+        if w.mask == "all":
+            k = n4
+        elif w.mask in ("scores", "mlp"):
+            k = (w.budget_permille * n4) // 1000
+        else:
+            k = n4 // 2
+        out.append(k * w.kv_heads)
+    return out
+
+
+# ---------------------------------------------------------------------- CPU
+def _cpu_pair(args):
+    """Oracle attention phase for one (workload, b, kvh): returns (bytes, seconds)."""
+    name, b, kvh = args
+    from threadpoolctl import threadpool_limits
+
+    import numpy as np
+
+    import workloads as W
+    from oracle import attention, policy, reference, regions
+
+    with threadpool_limits(1):
+        w = W.WORKLOADS[name]
+        L = int(w.lengths()[b])
+        k = W.bf16_bits_to_f32(W.kv_source_np(w, 0, "K", b, 0, L, kvh=kvh))
+        v = W.bf16_bits_to_f32(W.kv_source_np(w, 0, "V", b, 0, L, kvh=kvh))
+        enc = reference.encode(k, v)
+        start, n4 = regions.int4_range(L)
+        if w.mask == "mlp":
+            s = policy.mlp_scores(k, v, W.mlp_weights(w, 0)[kvh])
+            keep4 = policy.topk_keep(s[start:start + n4], w.budget_permille)
+        else:
+            keep4 = np.ones(n4, bool)
+        G = w.group_size
+        q = W.bf16_bits_to_f32(W.queries_np(w, 0, 0)[b, kvh * G:(kvh + 1) * G]).astype(np.float64)
+        t0 = time.perf_counter()
+        kh, vh = reference.decoded(enc)
+        pos = reference.kept_positions(L, keep4)
+        attention.attend(q, kh[pos], vh[pos])
+        dt = time.perf_counter() - t0
+        n8 = len(regions.int8_positions(L))
+        nbytes = int(keep4.sum()) * (w.head_dim + 8 * (w.head_dim // 32)) + n8 * (2 * w.head_dim + 8)
+        return nbytes, dt
+
+
+def cpu_baseline(layer_names, seconds: float):
+    """Time the oracle's attention phase over a bounded sample of (sequence, kv head) pairs."""
+    import multiprocessing as mp
+
+    import workloads as W
+
+    cores = len(os.sched_getaffinity(0))
+    cores = max(1, min(cores, 16))
+    pairs = []
+    i = 0
+    for name in layer_names[:2]:
+        w = W.WORKLOADS[name]
+        for b in range(w.batch):
+            for h in range(w.kv_heads):
+                pairs.append((name, b, h))
+    # bounded sample: interleave layers, take enough pairs for ~`seconds` of work
+    probe = _cpu_pair(pairs[0])
+    per_pair = max(probe[1], 1e-3)
+    n = int(min(len(pairs), max(cores, seconds * cores / per_pair)))
+    step = max(1, len(pairs) // n)
+    sample = pairs[::step][:n]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(min(cores, len(sample))) as pool:
+        res = pool.map(_cpu_pair, sample)
+    used = min(cores, len(sample))
+    nbytes = sum(r[0] for r in res)
+    busy = sum(r[1] for r in res)
+    gbs = nbytes / (busy / used) / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"{len(sample)} (sequence, kv head) pairs of {'+'.join(sorted(set(layer_names[:2])))}: "
+                      f"float64 decode + masked softmax attention, busy time summed over "
+                      f"{used} worker processes (1 thread each) and divided by {used}"}
+
+
+# ---------------------------------------------------------------------- GPU
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long128k", choices=sorted(WORKLOAD_LAYERS))
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >1 GiB between reuses")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the kernel is measured on one GPU's share; see the sharding notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import decode_attention_compressed_quantize_amd as kvc
+    from decode_attention_compressed_quantize_amd.workload_cache import LayerCache
+
+    kvc.lib()
+    dev = "cuda"
+    names = WORKLOAD_LAYERS[args.workload]
+    total_steps = args.warmup + args.steps
+    base = [W.WORKLOADS[n].replace(decode_steps=total_steps + 1) for n in names]
+    per_replica_bytes = 0
+    layers = []
+    print(f"bench: building {args.workload} ({len(base)} layer caches per replica)", file=sys.stderr, flush=True)
+    for li, w in enumerate(base):
+        lc = LayerCache(w, layer=li, device=dev, keep_sources=False)
+        layers.append(lc)
+        per_replica_bytes += lc.cache.nbytes()
+    replicas = args.replicas
+    read_per_replica = sum(algorithmic_bytes(lc.w, lc.lengths, kept_counts(lc.w, lc.lengths))
+                           for lc in layers)
+    if replicas <= 0:
+        replicas = max(1, math.ceil((1 << 30) / read_per_replica) + 1) if len(base) < 8 else 1
+    reps = [layers]
+    for r in range(1, replicas):
+        reps.append([LayerCache(w, layer=li, device=dev, keep_sources=False) for li, w in enumerate(base)])
+    print(f"bench: {replicas} replica(s), {per_replica_bytes / 2**30:.2f} GiB each", file=sys.stderr, flush=True)
+
+    # inputs for every step, resident before timing
+    inputs = []
+    for r, rep in enumerate(reps):
+        per = []
+        for li, lc in enumerate(rep):
+            w = lc.w
+            steps_here = (total_steps + replicas - 1) // replicas + 1
+            L0 = lc.lengths.copy()
+            ks, vs, qs = [], [], []
+            for s in range(steps_here):
+                ks.append(W.kv_rows_torch(w, li, "K", L0 + s, dev)[:, None])
+                vs.append(W.kv_rows_torch(w, li, "V", L0 + s, dev)[:, None])
+                qs.append(W.queries_torch(w, li, s + 1, dev))
+            out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+            lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev)
+            mlp = getattr(lc, "mlp", None)
+            per.append({"k": ks, "v": vs, "q": qs, "out": out, "lse": lse, "ws": lc.workspace(),
+                        "mlp": mlp, "one": torch.ones(w.batch, dtype=torch.int32, device=dev),
+                        "lens": lc.lengths.astype(np.int64).copy(), "n": 0})
+        inputs.append(per)
+
+    stream = torch.cuda.current_stream()
+    attn_events = []
+
+    def step(i, record):
+        r = i % replicas
+        byts = 0
+        for li, lc in enumerate(reps[r]):
+            st = inputs[r][li]
+            s = st["n"]
+            st["n"] += 1
+            st["lens"] += 1
+            lc.seq_lens.add_(1)
+            kvc.kvc_quantize_append(lc.cache, st["k"][s], st["v"][s], st["one"])
+            w = lc.w
+            budget = 1000 if w.mask == "all" else w.budget_permille
+            if w.mask == "mlp":
+                kvc.kvc_score_topk_mask(lc.cache, st["mlp"], st["k"][s], st["v"][s], st["one"], budget)
+            else:
+                kvc.kvc_score_topk_mask(lc.cache, None, None, None, None, budget)
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            kvc.kvc_decode_attention(lc.cache, st["q"][s], st["out"], st["lse"], st["ws"])
+            if record:
+                e1.record(stream)
+                attn_events.append((e0, e1, lc.w, st["lens"].copy()))
+            byts += algorithmic_bytes(w, st["lens"], kept_counts(w, st["lens"]))
+        return byts
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    step_bytes = 0
+    t0.record(stream)
+    for i in range(args.warmup, args.warmup + args.steps):
+        step_bytes += step(i, True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gbs = step_bytes / args.steps / (ms * 1e-3) / 1e9
+
+    attn_ms = [e0.elapsed_time(e1) for e0, e1, _, _ in attn_events]
+    attn_bytes = [algorithmic_bytes(w, L, kept_counts(w, L)) for _, _, w, L in attn_events]
+    a_ms = sum(attn_ms) / len(attn_ms)
+    a_gbs = (sum(attn_bytes) / len(attn_bytes)) / (a_ms * 1e-3) / 1e9
+    per_budget = {}
+    for (e0, e1, w, L), t, bb in zip(attn_events, attn_ms, attn_bytes):
+        d = per_budget.setdefault(w.name, [0.0, 0])
+        d[0] += t
+        d[1] += bb
+    detail = {n: {"attention_ms": round(v[0] / (len(attn_ms) / len(per_budget)), 4),
+                  "attention_GBs": round(v[1] / (v[0] * 1e-3) / 1e9, 1)} for n, v in per_budget.items()}
+
+    line = {
+        "metric": "compressed-KV decode attention: KV bytes GB/s (% HBM peak), decode steps/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4/int8 codes, f16 MFMA operands, f32 accumulate",
+        "data": "synthetic (seeded normal K/V/Q, seeded per-head MLP scores)",
+        "config": {
+            "workload": args.workload,
+            "layers": names if len(set(names)) > 1 else f"{len(names)} x {names[0]}",
+            "batch": base[0].batch, "q_heads": base[0].q_heads, "kv_heads": base[0].kv_heads,
+            "head_dim": base[0].head_dim, "context": int(base[0].lengths().max()),
+            "replicas": replicas,
+        },
+        "decode_steps_per_s": round(1000.0 / ms, 2),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "attention": {"ms_per_call": round(a_ms, 5), "GBs": round(a_gbs, 1), "per_layer": detail},
+        "roofline": {
+            "kernel": "kvc_decode_attention (INT4 split partials + INT8 partial + LSE merge)",
+            "bound": "hbm",
+            "achieved": round(a_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(names, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

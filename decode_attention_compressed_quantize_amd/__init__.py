@@ -1,0 +1,225 @@
+"""Python binding of libkvc: compressed-KV decode attention on MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libkvc.so`` (built in-tree by ``build.py``). PyTorch supplies device memory
+and the current stream. Importing works without a GPU; any call raises if the
+library has not been built.
+
+The functions mirror the C ABI in ``include/kvc.h``:
+``kvc_quantize_append``, ``kvc_score_topk_mask``, ``kvc_decode_attention``,
+``kvc_attention_workspace_bytes``, ``kvc_topk_workspace_bytes``,
+``kvc_status_string``, ``kvc_last_error``, ``kvc_abi_version``.
+:class:`Cache` owns the torch tensors of one layer's compressed cache and the
+``kvc_cache`` descriptor that points at them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvc.so")
+
+PAGE = 16
+N_SINK = 16
+N_RECENT = 128
+INT8_SLOTS = N_SINK + N_RECENT
+GROUP = 32
+
+KVC_BF16 = 0
+KVC_F32 = 1
+
+
+class KvcError(RuntimeError):
+    pass
+
+
+class KvcCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32),
+        ("n_sink", ctypes.c_int32),
+        ("n_recent", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("max_ctx", ctypes.c_int32),
+        ("int4_codes", ctypes.c_void_p),
+        ("int4_meta", ctypes.c_void_p),
+        ("int8_codes", ctypes.c_void_p),
+        ("int8_scales", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("keep_mask", ctypes.c_void_p),
+        ("scores", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+# exported name -> (restype, argtypes)
+_SIGNATURES = {
+    "kvc_quantize_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
+    "kvc_score_topk_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]),
+    "kvc_decode_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]),
+    "kvc_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
+    "kvc_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "kvc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kvc_last_error": (ctypes.c_char_p, []),
+    "kvc_abi_version": (ctypes.c_int32, []),
+}
+
+
+def lib():
+    """The loaded libkvc (raises KvcError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise KvcError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m decode_attention_compressed_quantize_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        L = lib()
+        raise KvcError(f"{what}: {L.kvc_status_string(status).decode()} "
+                       f"({L.kvc_last_error().decode()})")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return KVC_BF16
+    if t.dtype == torch.float32:
+        return KVC_F32
+    raise KvcError(f"unsupported dtype {t.dtype}")
+
+
+class Cache:
+    """Device tensors of one layer's compressed KV cache plus its descriptor.
+
+    ``block_table`` (int32 [B][max_pages]) and ``seq_lens`` (int32 [B]) are
+    device tensors owned by the caller; ``seq_lens`` must hold the lengths
+    after any append of the current step.
+    """
+
+    def __init__(self, batch: int, kv_heads: int, head_dim: int, max_ctx: int,
+                 num_phys_pages: int, block_table, seq_lens, device="cuda", with_scores=True):
+        import torch
+
+        self.batch, self.kv_heads, self.head_dim, self.max_ctx = batch, kv_heads, head_dim, max_ctx
+        self.num_phys_pages = num_phys_pages
+        dev = torch.device(device)
+        D = head_dim
+        self.int4_codes = torch.zeros((num_phys_pages, kv_heads, PAGE, 2, D // 2), dtype=torch.uint8, device=dev)
+        self.int4_meta = torch.zeros((num_phys_pages, kv_heads, PAGE, D // GROUP, 4), dtype=torch.int16, device=dev)
+        self.int8_codes = torch.zeros((batch, kv_heads, INT8_SLOTS, 2, D), dtype=torch.int8, device=dev)
+        self.int8_scales = torch.zeros((batch, kv_heads, INT8_SLOTS, 2), dtype=torch.float32, device=dev)
+        self.mask_words = (max_ctx + 31) // 32
+        self.keep_mask = torch.zeros((batch, kv_heads, self.mask_words), dtype=torch.int32, device=dev)
+        self.scores = (torch.zeros((batch, kv_heads, max_ctx), dtype=torch.float32, device=dev)
+                       if with_scores else None)
+        self.block_table = block_table
+        self.seq_lens = seq_lens
+        assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+        self.desc = KvcCacheStruct(
+            batch, kv_heads, head_dim, PAGE, block_table.shape[1], num_phys_pages,
+            N_SINK, N_RECENT, GROUP, max_ctx,
+            _ptr(self.int4_codes), _ptr(self.int4_meta), _ptr(self.int8_codes),
+            _ptr(self.int8_scales), _ptr(block_table), _ptr(seq_lens), _ptr(self.keep_mask),
+            _ptr(self.scores))
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+    def nbytes(self) -> int:
+        ts = [self.int4_codes, self.int4_meta, self.int8_codes, self.int8_scales, self.keep_mask]
+        if self.scores is not None:
+            ts.append(self.scores)
+        return sum(t.numel() * t.element_size() for t in ts)
+
+
+def kvc_abi_version() -> int:
+    return lib().kvc_abi_version()
+
+
+def kvc_status_string(status: int) -> str:
+    return lib().kvc_status_string(status).decode()
+
+
+def kvc_last_error() -> str:
+    return lib().kvc_last_error().decode()
+
+
+def kvc_attention_workspace_bytes(cache: Cache, num_q_heads: int) -> int:
+    return lib().kvc_attention_workspace_bytes(cache.ref(), num_q_heads)
+
+
+def kvc_topk_workspace_bytes(cache: Cache) -> int:
+    return lib().kvc_topk_workspace_bytes(cache.ref())
+
+
+def kvc_quantize_append(cache: Cache, k_new, v_new, n_new, stream=None):
+    """Encode k_new/v_new ([B][n_new_max][Hkv][D], bf16 or fp32) at the tail of each sequence."""
+    n_max = k_new.shape[1]
+    _check(lib().kvc_quantize_append(cache.ref(), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                     n_max, _ptr(n_new), _stream(stream)), "kvc_quantize_append")
+
+
+def kvc_score_topk_mask(cache: Cache, mlp, k_new, v_new, n_new, budget_permille: int,
+                        ws=None, stream=None):
+    """Score appended tokens with the per-head MLP (if ``mlp`` is given) and refresh the keep mask."""
+    n_max = 0 if k_new is None else k_new.shape[1]
+    src = KVC_BF16 if k_new is None else _dtype_code(k_new)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_score_topk_mask(cache.ref(), _ptr(mlp), _ptr(k_new), _ptr(v_new), src, n_max,
+                                     _ptr(n_new), int(budget_permille), _ptr(ws), nbytes,
+                                     _stream(stream)), "kvc_score_topk_mask")
+
+
+def kvc_decode_attention(cache: Cache, q, out, lse, ws, softmax_scale: float = 0.0, stream=None):
+    """Decode attention of q ([B][Hq][D]) into out (fp32 [B][Hq][D]) and lse (fp32 [B][Hq] or None)."""
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().kvc_decode_attention(cache.ref(), _ptr(q), _dtype_code(q), q.shape[1],
+                                      float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), nbytes,
+                                      _stream(stream)), "kvc_decode_attention")
+
+
+def attention_workspace(cache: Cache, num_q_heads: int, device="cuda"):
+    """Allocate a workspace tensor of the size kvc_decode_attention needs."""
+    import torch
+
+    n = kvc_attention_workspace_bytes(cache, num_q_heads)
+    return torch.empty(max(n // 4, 1), dtype=torch.float32, device=device)

@@ -1,0 +1,168 @@
+// libkvc host layer: argument validation, split planning, workspace sizing
+// and kernel launches behind the C ABI declared in include/kvc.h.
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "kvc_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvc_status fail(kvc_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+
+// Validates the host fields of a cache descriptor and the pointers a call needs.
+enum Need : unsigned {
+  kNeedInt4 = 1u,
+  kNeedInt8 = 2u,
+  kNeedMask = 4u,
+  kNeedScores = 8u,
+};
+
+kvc_status check_cache(const kvc_cache* c, unsigned need) {
+  if (!c) return fail(KVC_E_NULL, "cache descriptor is NULL");
+  if (c->batch < 1 || c->num_kv_heads < 1 || c->max_ctx < 1 || c->num_phys_pages < 1)
+    return fail(KVC_E_SHAPE, "batch, num_kv_heads, max_ctx and num_phys_pages must be >= 1");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(KVC_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->page_size != kvc::kPage) return fail(KVC_E_UNSUPPORTED, "page_size must be 16");
+  if (c->n_sink != kvc::kSink || c->n_recent != kvc::kRecent)
+    return fail(KVC_E_UNSUPPORTED, "n_sink must be 16 and n_recent 128");
+  if (c->group != kvc::kGroup) return fail(KVC_E_UNSUPPORTED, "group must be 32");
+  if ((long long)c->max_pages_per_seq * kvc::kPage < c->max_ctx)
+    return fail(KVC_E_SHAPE, "max_pages_per_seq * 16 must cover max_ctx");
+  if (!c->block_table || !c->seq_lens) return fail(KVC_E_NULL, "block_table or seq_lens is NULL");
+  if ((need & kNeedInt4) && (!c->int4_codes || !c->int4_meta))
+    return fail(KVC_E_NULL, "int4_codes or int4_meta is NULL");
+  if ((need & kNeedInt8) && (!c->int8_codes || !c->int8_scales))
+    return fail(KVC_E_NULL, "int8_codes or int8_scales is NULL");
+  if ((need & kNeedMask) && !c->keep_mask) return fail(KVC_E_NULL, "keep_mask is NULL");
+  if ((need & kNeedScores) && !c->scores) return fail(KVC_E_NULL, "scores is NULL");
+  return KVC_OK;
+}
+
+kvc_status check_append(const void* k_new, const void* v_new, kvc_dtype src, int n_new_max,
+                        const int32_t* n_new) {
+  if (n_new_max < 0) return fail(KVC_E_SHAPE, "n_new_max must be >= 0");
+  if (src != KVC_BF16 && src != KVC_F32) return fail(KVC_E_UNSUPPORTED, "src must be BF16 or F32");
+  if (n_new_max > 0 && (!k_new || !v_new || !n_new))
+    return fail(KVC_E_NULL, "k_new, v_new or n_new is NULL");
+  return KVC_OK;
+}
+
+kvc_status launched(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_error = std::string("kernel launch failed: ") + hipGetErrorString(e);
+    return KVC_E_LAUNCH;
+  }
+  return KVC_OK;
+}
+
+}  // namespace
+
+namespace kvc {
+
+AttnPlan plan_attention(const kvc_cache& c, int num_q_heads) {
+  (void)num_q_heads;
+  const long long n4max = c.max_ctx > kInt8Slots ? (long long)c.max_ctx - kInt8Slots : 0;
+  const long long pairs = (long long)c.batch * c.num_kv_heads;
+  // Aim for about 4096 INT4 work items over the whole batch, at least 256
+  // positions each, in whole 32-position mask words.
+  long long chunk = (pairs * n4max + 4095) / 4096;
+  if (chunk < 256) chunk = 256;
+  chunk = (chunk + 31) / 32 * 32;
+  AttnPlan p;
+  p.chunk = (int)chunk;
+  p.nsplit = n4max > 0 ? (int)((n4max + chunk - 1) / chunk) : 1;
+  return p;
+}
+
+}  // namespace kvc
+
+extern "C" {
+
+KVC_API int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+KVC_API const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+KVC_API const char* kvc_status_string(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_E_NULL: return "null pointer";
+    case KVC_E_SHAPE: return "bad shape";
+    case KVC_E_UNSUPPORTED: return "unsupported configuration";
+    case KVC_E_WORKSPACE: return "workspace too small";
+    case KVC_E_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+KVC_API size_t kvc_attention_workspace_bytes(const kvc_cache* c, int32_t num_q_heads) {
+  if (check_cache(c, 0) != KVC_OK || num_q_heads < 1 || num_q_heads % c->num_kv_heads) return 0;
+  const kvc::AttnPlan p = kvc::plan_attention(*c, num_q_heads);
+  return kvc::attention_ws_floats(*c, num_q_heads, p) * sizeof(float);
+}
+
+KVC_API size_t kvc_topk_workspace_bytes(const kvc_cache* c) {
+  (void)c;
+  return 0;
+}
+
+KVC_API kvc_status kvc_quantize_append(const kvc_cache* c, const void* k_new, const void* v_new,
+                                       kvc_dtype src, int32_t n_new_max, const int32_t* n_new,
+                                       hipStream_t stream) {
+  kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8);
+  if (st != KVC_OK) return st;
+  st = check_append(k_new, v_new, src, n_new_max, n_new);
+  if (st != KVC_OK) return st;
+  if (n_new_max == 0) return KVC_OK;
+  return launched(kvc::launch_quantize_append(*c, k_new, v_new, src, n_new_max, n_new, stream));
+}
+
+KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, const void* k_new,
+                                       const void* v_new, kvc_dtype src, int32_t n_new_max,
+                                       const int32_t* n_new, int32_t budget_permille, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  kvc_status st = check_cache(c, kNeedMask | kNeedScores);
+  if (st != KVC_OK) return st;
+  if (budget_permille < 0 || budget_permille > 1000)
+    return fail(KVC_E_SHAPE, "budget_permille must be in [0, 1000]");
+  if (mlp) {
+    st = check_append(k_new, v_new, src, n_new_max, n_new);
+    if (st != KVC_OK) return st;
+    if (n_new_max > 0) {
+      st = launched(kvc::launch_score(*c, mlp, k_new, v_new, src, n_new_max, n_new, stream));
+      if (st != KVC_OK) return st;
+    }
+  }
+  return launched(kvc::launch_topk(*c, budget_permille, stream));
+}
+
+KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_dtype q_dtype,
+                                        int32_t num_q_heads, float softmax_scale, float* out,
+                                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8 | kNeedMask);
+  if (st != KVC_OK) return st;
+  if (!q || !out) return fail(KVC_E_NULL, "q or out is NULL");
+  if (q_dtype != KVC_BF16 && q_dtype != KVC_F32)
+    return fail(KVC_E_UNSUPPORTED, "q_dtype must be BF16 or F32");
+  if (num_q_heads < 1 || num_q_heads % c->num_kv_heads)
+    return fail(KVC_E_SHAPE, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int G = num_q_heads / c->num_kv_heads;
+  if (G * (c->head_dim / kvc::kGroup) > 16 || (G & (G - 1)))
+    return fail(KVC_E_UNSUPPORTED, "need (num_q_heads/num_kv_heads) a power of two with G*D/32 <= 16");
+  const kvc::AttnPlan plan = kvc::plan_attention(*c, num_q_heads);
+  const size_t need = kvc::attention_ws_floats(*c, num_q_heads, plan) * sizeof(float);
+  if (!ws || ws_bytes < need) return fail(KVC_E_WORKSPACE, "attention workspace too small");
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
+  return launched(kvc::launch_attention(*c, q, q_dtype, num_q_heads, scale, out, lse,
+                                        static_cast<float*>(ws), plan, stream));
+}
+
+}  // extern "C"

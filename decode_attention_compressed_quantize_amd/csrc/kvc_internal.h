@@ -1,0 +1,49 @@
+// Internal declarations shared by the libkvc host layer and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int kPage = 16;
+constexpr int kSink = 16;
+constexpr int kRecent = 128;
+constexpr int kInt8Slots = kSink + kRecent;  // 144
+constexpr int kGroup = 32;
+constexpr int kHidden = 32;
+
+__host__ __device__ inline int mlp_floats(int head_dim) { return kHidden * 2 * head_dim + 2 * kHidden + 1; }
+__host__ __device__ inline int mask_words(int max_ctx) { return (max_ctx + 31) / 32; }
+
+// How the INT4 region is cut into split-KV chunks for one attention call.
+struct AttnPlan {
+  int chunk;   // positions per INT4 chunk (multiple of 32)
+  int nsplit;  // INT4 chunks per (sequence, kv head); partial index nsplit is the INT8 region
+};
+
+AttnPlan plan_attention(const kvc_cache& c, int num_q_heads);
+
+// Partials: float [B][Hq][nsplit + 1][2 + D] as (m, l, o[0..D-1]); m is in log2 units.
+inline size_t attention_ws_floats(const kvc_cache& c, int num_q_heads, const AttnPlan& p) {
+  return (size_t)c.batch * num_q_heads * (size_t)(p.nsplit + 1) * (size_t)(2 + c.head_dim);
+}
+
+hipError_t launch_quantize_append(const kvc_cache& c, const void* k_new, const void* v_new,
+                                  kvc_dtype src, int n_new_max, const int32_t* n_new,
+                                  hipStream_t s);
+
+hipError_t launch_score(const kvc_cache& c, const float* mlp, const void* k_new, const void* v_new,
+                        kvc_dtype src, int n_new_max, const int32_t* n_new, hipStream_t s);
+
+hipError_t launch_topk(const kvc_cache& c, int budget_permille, hipStream_t s);
+
+hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype, int num_q_heads,
+                            float softmax_scale, float* out, float* lse, float* ws,
+                            const AttnPlan& plan, hipStream_t s);
+
+}  // namespace kvc

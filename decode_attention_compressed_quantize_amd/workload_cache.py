@@ -1,0 +1,139 @@
+"""Build one layer's compressed cache for a synthetic workload on the GPU.
+
+Plumbing for tests and the benchmark: inputs come from the seeded generators
+in ``workloads``; all encoding, scoring, masking and attention run in libkvc
+through the binding. Nothing here computes any part of the method.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+import workloads as W
+
+from . import (Cache, attention_workspace, kvc_quantize_append, kvc_score_topk_mask)
+
+
+def pack_bits(flags: np.ndarray, words: int) -> np.ndarray:
+    """Pack bool flags [n] into uint32 words (bit t%32 of word t/32) as int32."""
+    out = np.zeros(words * 32, dtype=np.uint64)
+    out[: flags.shape[0]] = flags.astype(np.uint64)
+    w = out.reshape(words, 32)
+    packed = (w << np.arange(32, dtype=np.uint64)).sum(axis=1).astype(np.uint32)
+    return packed.view(np.int32)
+
+
+class LayerCache:
+    """A prefilled cache of one layer of workload ``w`` plus its source tensors."""
+
+    def __init__(self, w: W.Workload, layer: int = 0, device="cuda", batch_rows=None,
+                 table: Optional[np.ndarray] = None, keep_sources: bool = True):
+        import torch
+
+        self.w, self.layer, self.device = w, layer, device
+        self.lengths = w.lengths()
+        if table is None:
+            table, num_pages = W.page_table(w, layer)
+        else:
+            num_pages = int(table.max()) + 1
+        self.table_np = table
+        self.max_ctx = w.max_ctx()
+        self.table = torch.from_numpy(table).to(device)
+        self.seq_lens = torch.from_numpy(self.lengths.astype(np.int32)).to(device)
+        self.cache = Cache(w.batch, w.kv_heads, w.head_dim, self.max_ctx, num_pages,
+                           self.table, self.seq_lens, device=device)
+        self.k_src = {}
+        self.v_src = {}
+        self._prefill(keep_sources)
+
+    # -------------------------------------------------------------- prefill
+    def _prefill(self, keep_sources: bool):
+        import torch
+
+        w = self.w
+        dt = torch.bfloat16 if w.src_dtype == "bf16" else torch.float32
+        # prefill in sequence batches so the staging tensor stays small
+        lmax = int(self.lengths.max())
+        per = max(1, int(2 ** 31 // max(1, lmax * w.kv_heads * w.head_dim * 2)))
+        for b0 in range(0, w.batch, per):
+            b1 = min(w.batch, b0 + per)
+            k_new = torch.zeros((b1 - b0, lmax, w.kv_heads, w.head_dim), dtype=dt, device=self.device)
+            v_new = torch.zeros_like(k_new)
+            n_new = torch.zeros(b1 - b0, dtype=torch.int32, device=self.device)
+            for b in range(b0, b1):
+                L = int(self.lengths[b])
+                k = W.kv_source_torch(w, self.layer, "K", b, 0, L, self.device)
+                v = W.kv_source_torch(w, self.layer, "V", b, 0, L, self.device)
+                k_new[b - b0, :L] = k
+                v_new[b - b0, :L] = v
+                n_new[b - b0] = L
+                if keep_sources:
+                    self.k_src[b] = k
+                    self.v_src[b] = v
+            sub = self._sub_cache(b0, b1)
+            kvc_quantize_append(sub, k_new, v_new, n_new)
+            if w.mask == "mlp":
+                self._mlp_subset(sub, k_new, v_new, n_new)
+            del k_new, v_new
+        self._mask()
+
+    def _sub_cache(self, b0: int, b1: int) -> Cache:
+        """A descriptor view of sequences [b0, b1) sharing this cache's memory."""
+        if b0 == 0 and b1 == self.w.batch:
+            return self.cache
+        import copy
+
+        c = self.cache
+        sub = copy.copy(c)
+        sub.desc = type(c.desc).from_buffer_copy(c.desc)
+        D = self.w.head_dim
+        sub.desc.batch = b1 - b0
+        sub.desc.int8_codes = c.int8_codes[b0:b1].data_ptr()
+        sub.desc.int8_scales = c.int8_scales[b0:b1].data_ptr()
+        sub.desc.block_table = self.table[b0:b1].data_ptr()
+        sub.desc.seq_lens = self.seq_lens[b0:b1].data_ptr()
+        sub.desc.keep_mask = c.keep_mask[b0:b1].data_ptr()
+        sub.desc.scores = c.scores[b0:b1].data_ptr()
+        return sub
+
+    def _mlp_subset(self, sub, k_new, v_new, n_new):
+        import torch
+
+        if not hasattr(self, "mlp"):
+            self.mlp_np = W.mlp_weights(self.w, self.layer)
+            self.mlp = torch.from_numpy(self.mlp_np).to(self.device)
+        # scores only; the mask is refreshed once for the whole batch afterwards
+        kvc_score_topk_mask(sub, self.mlp, k_new, v_new, n_new, 0)
+
+    def _mask(self):
+        import torch
+
+        w = self.w
+        c = self.cache
+        if w.mask == "bernoulli":
+            rows = np.zeros((w.batch, w.kv_heads, c.mask_words), dtype=np.int32)
+            for b in range(w.batch):
+                for h in range(w.kv_heads):
+                    L = int(self.lengths[b])
+                    rows[b, h] = pack_bits(W.bernoulli_keep_np(w, self.layer, b, h, L), c.mask_words)
+            c.keep_mask.copy_(torch.from_numpy(rows))
+        elif w.mask == "all":
+            kvc_score_topk_mask(c, None, None, None, None, 1000)
+        elif w.mask == "scores":
+            for b in range(w.batch):
+                L = int(self.lengths[b])
+                c.scores[b, :, :L] = W.given_scores_torch(w, self.layer, b, L, self.device)
+            kvc_score_topk_mask(c, None, None, None, None, w.budget_permille)
+        elif w.mask == "mlp":
+            kvc_score_topk_mask(c, None, None, None, None, w.budget_permille)
+        else:
+            raise ValueError(w.mask)
+
+    # -------------------------------------------------------------- decode
+    def queries(self, step: int = 0):
+        return W.queries_torch(self.w, self.layer, step, self.device)
+
+    def workspace(self):
+        return attention_workspace(self.cache, self.w.q_heads, self.device)

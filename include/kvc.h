@@ -1,0 +1,181 @@
+/*
+ * kvc.h - C ABI of libkvc: decode-step attention over a compressed KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method: the KV4-RL review ("KV4-RL: Unlocking Faster Asynchronous
+ * Rollouts for RLVR with INT4 KV Cache Quantization"), section 3, stores the
+ * whole context in paged, calibration-free INT4 and protects the first 16
+ * positions (attention sinks) and the 128 most recent positions in an INT8
+ * side cache; attention processes the two regions independently and joins
+ * them with an exact softmax merge, never rebuilding the full cache.
+ * Evicted INT4 positions are excluded by a binary keep mask of retained
+ * indices (Shadow Mask Distillation page, arXiv 2605.06850, Figure 1
+ * caption) chosen per head by score -> sort -> truncate to a budget with a
+ * small per-head MLP over the K/V vectors (KVP promo page, arXiv
+ * 2602.10238, section "Core mechanism").
+ *
+ * Numeric rules the pages leave open (fixed by this library):
+ *   INT4: per (token, kv head, K or V, group of 32 head_dim entries):
+ *         scale = fp16((max-min)/15), min = fp16(min) (RNE, saturated),
+ *         code = clamp(rint((x - min) * (1/scale)), 0, 15), scale 0 -> code 0;
+ *         value = code*scale + min.
+ *   INT8: per (token, kv head, K or V): s = max|x|/127 (fp32),
+ *         code = clamp(rint(x * (1/s)), -127, 127), s < FLT_MIN -> code 0;
+ *         value = code*s.
+ *   All of it in float32 round-to-nearest-even, no fused multiply-add.
+ *   Logits are (q . k)*softmax_scale; query head h reads kv head h/(Hq/Hkv).
+ *
+ * Memory layout (all device memory, owned by the caller; D = head_dim,
+ * Hkv = num_kv_heads, P = num_phys_pages, B = batch, page = 16 tokens):
+ *   int4_codes  uint8  [P][Hkv][16][2][D/2]   per token: K codes then V codes;
+ *               byte j of a K (or V) row holds code 2j in its low nibble and
+ *               code 2j+1 in its high nibble.
+ *   int4_meta   uint16 [P][Hkv][16][D/32][4]  IEEE fp16 bits, per group:
+ *               (K scale, K min, V scale, V min).
+ *   int8_codes  int8   [B][Hkv][144][2][D]    per slot: K codes then V codes.
+ *   int8_scales float  [B][Hkv][144][2]       per slot: (K scale, V scale).
+ *               Position t lives in slot t (t < 16) or 16 + (t-16) mod 128.
+ *   block_table int32  [B][max_pages_per_seq] logical page -> physical page.
+ *   seq_lens    int32  [B]                    current length L_b (after any
+ *               append made in the same step); never written by the library.
+ *   keep_mask   uint32 [B][Hkv][ceil(max_ctx/32)]  bit t%32 of word t/32 is 1
+ *               when position t is retained. Only INT4-region bits
+ *               ([16, L-128)) are read by attention; the refresh writes 1 for
+ *               the protected positions and 0 at and beyond L.
+ *   scores      float  [B][Hkv][max_ctx]      per-position utility score.
+ *
+ * Regions for a sequence of length L: INT8 = [0, min(L,16)) and
+ * [max(16, L-128), L); INT4 = [16, L-128) (empty when L <= 144). INT4 codes
+ * are written for every appended position, so a position leaving the
+ * 128-window needs no re-encoding: the INT4 region simply grows by one.
+ *
+ * Conventions: every call is enqueued on the caller's stream and never
+ * synchronises; argument errors are returned synchronously; kernels never
+ * allocate; the library keeps no state besides a thread-local error string.
+ * Device contents (lengths, table entries) are trusted: out-of-range page ids
+ * or lengths are skipped by the kernels rather than dereferenced, which leaves
+ * the affected outputs unspecified.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_API __attribute__((visibility("default")))
+#define KVC_ABI_VERSION 1
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_E_NULL = -1,        /* a required pointer is NULL */
+  KVC_E_SHAPE = -2,       /* a size is out of range or inconsistent */
+  KVC_E_UNSUPPORTED = -3, /* a valid but unsupported configuration */
+  KVC_E_WORKSPACE = -4,   /* workspace missing or too small */
+  KVC_E_LAUNCH = -5       /* a kernel launch failed */
+} kvc_status;
+
+typedef enum { KVC_BF16 = 0, KVC_F32 = 1 } kvc_dtype;
+
+/* One compressed KV cache (one layer). Sizes are host values; pointers are
+ * device pointers laid out as described above. */
+typedef struct kvc_cache {
+  int32_t batch;             /* B >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1 */
+  int32_t head_dim;          /* D: 64 or 128 */
+  int32_t page_size;         /* must be 16 */
+  int32_t max_pages_per_seq; /* >= ceil(max_ctx/16) */
+  int32_t num_phys_pages;    /* P >= 1 */
+  int32_t n_sink;            /* must be 16 */
+  int32_t n_recent;          /* must be 128 */
+  int32_t group;             /* must be 32 */
+  int32_t max_ctx;           /* capacity in positions, >= 1 */
+  uint8_t* int4_codes;
+  uint16_t* int4_meta;
+  int8_t* int8_codes;
+  float* int8_scales;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  uint32_t* keep_mask;
+  float* scores;
+} kvc_cache;
+
+/*
+ * kvc_quantize_append - encode appended tokens into the cache.
+ * Source: KV4-RL review, section 3 (INT4 for the full context, INT8 side
+ * cache for the 16 sink and 128 recent positions).
+ *   k_new, v_new : device [B][n_new_max][Hkv][D] of type src (BF16 or F32).
+ *   n_new        : device int32 [B]; sequence b appends n_new[b] <= n_new_max
+ *                  tokens at positions seq_lens[b]-n_new[b] ... seq_lens[b]-1
+ *                  (row j of k_new holds position seq_lens[b]-n_new[b]+j).
+ *   Writes INT4 codes and meta for every appended position, and INT8 codes
+ *   and scales for appended positions that are sinks (< 16) or lie in the
+ *   128-position recent window of the new length; a decode append (n_new=1)
+ *   overwrites the ring slot of the position that leaves the window.
+ *   n_new_max = 0 is a no-op. Needs int4_codes, int4_meta, int8_codes,
+ *   int8_scales, block_table, seq_lens.
+ */
+KVC_API kvc_status kvc_quantize_append(const kvc_cache* c, const void* k_new, const void* v_new,
+                                       kvc_dtype src, int32_t n_new_max, const int32_t* n_new,
+                                       hipStream_t stream);
+
+/*
+ * kvc_score_topk_mask - score appended tokens and refresh the keep mask.
+ * Source: KVP promo page (arXiv 2602.10238), section "Core mechanism" (one MLP
+ * per head over K/V, scores ranked and truncated to a budget); Shadow Mask
+ * Distillation page, Figure 1 caption (binary mask of retained indices).
+ *   mlp          : device float [Hkv][32*2D + 32 + 32 + 1] per head:
+ *                  W1 [32][2D] row-major (input = K || V), b1 [32], w2 [32], b2;
+ *                  or NULL when the caller already wrote `scores`.
+ *   k_new, v_new, src, n_new_max, n_new : as for kvc_quantize_append; used
+ *                  only when mlp != NULL (scores for the appended positions
+ *                  are w2 . relu(W1 [k||v] + b1) + b2 in float32).
+ *   budget_permille : 0..1000. For each (sequence, kv head), with
+ *                  n4 = max(0, L-144) and k = floor(budget*n4/1000), keeps the k
+ *                  INT4-region positions with the highest score; ties keep the
+ *                  lower position; NaN ranks below every number.
+ *   ws, ws_bytes : device scratch of at least kvc_topk_workspace_bytes(c)
+ *                  bytes (may be NULL when that is 0).
+ */
+KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, const void* k_new,
+                                       const void* v_new, kvc_dtype src, int32_t n_new_max,
+                                       const int32_t* n_new, int32_t budget_permille, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
+
+/*
+ * kvc_decode_attention - one decode query per sequence over the compressed cache.
+ * Source: KV4-RL review, section 3 (INT4 and INT8 regions processed
+ * independently, outputs combined by an exact softmax merge).
+ *   q            : device [B][num_q_heads][D] of type q_dtype (BF16 or F32).
+ *   num_q_heads  : multiple of Hkv with (num_q_heads/Hkv) * (D/32) <= 16.
+ *   softmax_scale: logit scale; <= 0 selects 1/sqrt(D).
+ *   out          : device float [B][num_q_heads][D], softmax-weighted values.
+ *   lse          : device float [B][num_q_heads] natural-log log-sum-exp of the
+ *                  scaled logits over the attended positions, or NULL.
+ *   ws, ws_bytes : device scratch of at least
+ *                  kvc_attention_workspace_bytes(c, num_q_heads) bytes; its
+ *                  contents on entry do not matter.
+ *   Attends to the INT8 positions and to the INT4-region positions whose
+ *   keep_mask bit is set. A sequence with L = 0 yields out = 0, lse = -inf.
+ */
+KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_dtype q_dtype,
+                                        int32_t num_q_heads, float softmax_scale, float* out,
+                                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace sizes (host-only, no device work). Return 0 for an invalid cache. */
+KVC_API size_t kvc_attention_workspace_bytes(const kvc_cache* c, int32_t num_q_heads);
+KVC_API size_t kvc_topk_workspace_bytes(const kvc_cache* c);
+
+/* Host-only helpers. */
+KVC_API const char* kvc_status_string(kvc_status s);
+KVC_API const char* kvc_last_error(void);
+KVC_API int32_t kvc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H */

@@ -1,0 +1,97 @@
+"""Test-side helpers: read GPU cache buffers through the documented layout and
+compute the oracle's expectation for one (sequence, kv head).
+
+The layout readers follow the memory-layout section of include/kvc.h; they
+share no code with the library.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import workloads as W
+from oracle import policy, quant, reference, regions
+
+D_GROUP = 32
+
+
+def to_f32(src):
+    """Source values (bf16 bits uint16 or float32) as float32."""
+    if src.dtype == np.uint16:
+        return W.bf16_bits_to_f32(src)
+    return np.asarray(src, np.float32)
+
+
+def source_np(w, layer, which, b, L, kvh):
+    return to_f32(W.kv_source_np(w, layer, which, b, 0, L, kvh=kvh))
+
+
+def unpage_int4(codes, meta, table, b, kvh, L):
+    """GPU INT4 buffers -> (K codes [L][D/2], V codes [L][D/2], meta [L][D/32][4] uint16)."""
+    npg = (L + 15) // 16
+    pages = table[b, :npg]
+    c = codes[pages, kvh].reshape(npg * 16, 2, codes.shape[-1])[:L]
+    m = meta[pages, kvh].reshape(npg * 16, meta.shape[-2], 4)[:L]
+    return c[:, 0], c[:, 1], m.view(np.uint16)
+
+
+def int8_slot_rows(codes8, scales8, b, kvh, L):
+    """GPU INT8 buffers in position order of the protected positions."""
+    pos = regions.int8_positions(L)
+    slots = np.array([regions.ring_slot(int(t)) for t in pos], dtype=np.int64)
+    c = codes8[b, kvh, slots]           # [n8][2][D]
+    s = scales8[b, kvh, slots]          # [n8][2]
+    return pos, c[:, 0], c[:, 1], s[:, 0], s[:, 1]
+
+
+def mask_bits(words_row, L):
+    w = np.asarray(words_row).view(np.uint32).astype(np.uint64)
+    bits = ((w[:, None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)).reshape(-1)
+    return bits[:L].astype(bool)
+
+
+def keep4_from_mask(words_row, L):
+    start, n4 = regions.int4_range(L)
+    return mask_bits(words_row, L)[start:start + n4]
+
+
+def check_codes(w, layer, b, kvh, L, cpu):
+    """Bit-exact comparison of one (sequence, kv head) of GPU buffers with the oracle."""
+    k = source_np(w, layer, "K", b, L, kvh)
+    v = source_np(w, layer, "V", b, L, kvh)
+    enc = reference.encode(k, v)
+    kc, vc, meta = unpage_int4(cpu["int4_codes"], cpu["int4_meta"], cpu["table"], b, kvh, L)
+    np.testing.assert_array_equal(kc, quant.pack_nibbles(enc["k4"]), err_msg=f"K INT4 codes b={b} h={kvh}")
+    np.testing.assert_array_equal(vc, quant.pack_nibbles(enc["v4"]), err_msg=f"V INT4 codes b={b} h={kvh}")
+    np.testing.assert_array_equal(meta[..., 0], enc["k4_scale"].view(np.uint16), err_msg="K scale")
+    np.testing.assert_array_equal(meta[..., 1], enc["k4_min"].view(np.uint16), err_msg="K min")
+    np.testing.assert_array_equal(meta[..., 2], enc["v4_scale"].view(np.uint16), err_msg="V scale")
+    np.testing.assert_array_equal(meta[..., 3], enc["v4_min"].view(np.uint16), err_msg="V min")
+    pos, k8, v8, ks8, vs8 = int8_slot_rows(cpu["int8_codes"], cpu["int8_scales"], b, kvh, L)
+    np.testing.assert_array_equal(k8, enc["k8"], err_msg="K INT8 codes")
+    np.testing.assert_array_equal(v8, enc["v8"], err_msg="V INT8 codes")
+    np.testing.assert_array_equal(ks8.view(np.uint32), enc["k8_scale"].view(np.uint32), err_msg="K INT8 scale")
+    np.testing.assert_array_equal(vs8.view(np.uint32), enc["v8_scale"].view(np.uint32), err_msg="V INT8 scale")
+    return enc
+
+
+def oracle_heads(w, layer, b, kvh, L, keep4, q_heads, scale=None):
+    """Oracle (out [G][D], lse [G]) for the query heads of kv head ``kvh``."""
+    k = source_np(w, layer, "K", b, L, kvh)
+    v = source_np(w, layer, "V", b, L, kvh)
+    q = to_f32(q_heads).astype(np.float64)
+    return reference.decode_group(q, k, v, keep4, scale)
+
+
+def assert_attention_close(out, lse, ref_out, ref_lse, what=""):
+    """max-abs 2e-3 and rel-L2 1e-3 on the output, max-abs 2e-3 on the LSE."""
+    out = np.asarray(out, np.float64)
+    ref_out = np.asarray(ref_out, np.float64)
+    err = np.abs(out - ref_out).max()
+    rel = np.linalg.norm(out - ref_out) / max(np.linalg.norm(ref_out), 1e-30)
+    lerr = np.abs(np.asarray(lse, np.float64) - np.asarray(ref_lse, np.float64)).max()
+    assert err <= 2e-3, f"{what} max-abs {err:.3e}"
+    assert rel <= 1e-3, f"{what} rel-L2 {rel:.3e}"
+    assert lerr <= 2e-3, f"{what} lse max-abs {lerr:.3e}"
+    return err, rel, lerr

@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI (no GPU needed, no device work).
+
+The library must load, export every function include/kvc.h declares, and
+reject bad arguments with the documented status codes before touching the
+device. These calls never launch a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_compressed_quantize_amd as kvc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvc.LIB_PATH):
+        from decode_attention_compressed_quantize_amd import build
+
+        build.build()
+    return kvc.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvc.h")).read()
+    return re.findall(r"KVC_API\s+[\w\s\*]+?\b(kvc_\w+)\s*\(", src)
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("kvc_quantize_append", "kvc_score_topk_mask", "kvc_decode_attention"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in kvc._SIGNATURES, f"binding lacks {name}"
+
+
+def test_abi_version_and_strings(lib):
+    assert kvc.kvc_abi_version() == 1
+    assert kvc.kvc_status_string(0) == "ok"
+    assert kvc.kvc_status_string(-4) == "workspace too small"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def desc(**kw):
+    d = dict(batch=2, num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=64,
+             num_phys_pages=128, n_sink=16, n_recent=128, group=32, max_ctx=1024,
+             int4_codes=FAKE, int4_meta=FAKE, int8_codes=FAKE, int8_scales=FAKE,
+             block_table=FAKE, seq_lens=FAKE, keep_mask=FAKE, scores=FAKE)
+    d.update(kw)
+    return kvc.KvcCacheStruct(**d)
+
+
+def attn(lib, c, q=FAKE, hq=32, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.kvc_decode_attention(ctypes.byref(c) if c is not None else None, q, 0, hq, 0.0,
+                                    out, None, ws, ws_bytes, None)
+
+
+def test_attention_argument_errors(lib):
+    assert attn(lib, None) == -1
+    assert attn(lib, desc(), q=None) == -1
+    assert attn(lib, desc(int4_codes=None)) == -1
+    assert attn(lib, desc(keep_mask=None)) == -1
+    assert attn(lib, desc(head_dim=96)) == -3
+    assert attn(lib, desc(page_size=32)) == -3
+    assert attn(lib, desc(n_recent=64)) == -3
+    assert attn(lib, desc(group=64)) == -3
+    assert attn(lib, desc(max_pages_per_seq=10)) == -2
+    assert attn(lib, desc(batch=0)) == -2
+    assert attn(lib, desc(), hq=12) == -2          # not a multiple of Hkv
+    assert attn(lib, desc(), hq=64) == -3          # G = 8 at D = 128 exceeds 16 columns
+    assert attn(lib, desc(), hq=24) == -3          # G = 3 is not a power of two
+    assert attn(lib, desc(), ws=None) == -4
+    assert attn(lib, desc(), ws_bytes=16) == -4
+    assert "workspace" in kvc.kvc_last_error()
+
+
+def test_append_and_topk_argument_errors(lib):
+    c = desc()
+    r = lib.kvc_quantize_append(ctypes.byref(c), FAKE, FAKE, 0, -1, FAKE, None)
+    assert r == -2
+    r = lib.kvc_quantize_append(ctypes.byref(c), None, FAKE, 0, 4, FAKE, None)
+    assert r == -1
+    r = lib.kvc_quantize_append(ctypes.byref(c), FAKE, FAKE, 7, 4, FAKE, None)
+    assert r == -3
+    assert lib.kvc_quantize_append(ctypes.byref(c), FAKE, FAKE, 0, 0, FAKE, None) == 0  # no-op
+    r = lib.kvc_score_topk_mask(ctypes.byref(c), None, None, None, 0, 0, None, 1001, None, 0, None)
+    assert r == -2
+    r = lib.kvc_score_topk_mask(ctypes.byref(desc(scores=None)), None, None, None, 0, 0, None, 500,
+                                None, 0, None)
+    assert r == -1
+    r = lib.kvc_score_topk_mask(ctypes.byref(c), FAKE, None, FAKE, 0, 4, FAKE, 500, None, 0, None)
+    assert r == -1
+
+
+def test_workspace_size_covers_every_split(lib):
+    # (m, l, o[D]) per query head for every INT4 chunk plus the INT8 partial
+    for max_ctx in (1, 144, 145, 4096, 131072):
+        c = desc(max_ctx=max_ctx, max_pages_per_seq=(max_ctx + 15) // 16)
+        n = lib.kvc_attention_workspace_bytes(ctypes.byref(c), 32)
+        per_split = 2 * 32 * (128 + 2) * 4
+        assert n % per_split == 0
+        assert n // per_split >= 2   # at least one INT4 chunk plus the INT8 partial
+    assert lib.kvc_attention_workspace_bytes(ctypes.byref(desc(head_dim=96)), 32) == 0
+    assert lib.kvc_topk_workspace_bytes(ctypes.byref(desc())) == 0

@@ -1,0 +1,234 @@
+"""GPU parity: libkvc against the CPU oracle on the same seeded inputs.
+
+Codes, scales and mask bits must match bit for bit; scores within 1e-4;
+attention output within max-abs 2e-3 and rel-L2 1e-3 and LSE within 2e-3 of
+the float64 oracle. Small cases check every (sequence, kv head); full-size
+workloads (the launch configuration the benchmark times) check sampled
+sequences.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from kvc_testlib import (assert_attention_close, check_codes, keep4_from_mask, mask_bits,
+                         oracle_heads, source_np, to_f32)
+from oracle import policy, regions
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def kvc():
+    import decode_attention_compressed_quantize_amd as m
+
+    return m
+
+
+def LayerCache(*a, **k):
+    from decode_attention_compressed_quantize_amd.workload_cache import LayerCache as LC
+
+    return LC(*a, **k)
+
+
+def cpu_buffers(lc):
+    c = lc.cache
+    torch.cuda.synchronize()
+    return {
+        "int4_codes": c.int4_codes.cpu().numpy(),
+        "int4_meta": c.int4_meta.cpu().numpy(),
+        "int8_codes": c.int8_codes.cpu().numpy(),
+        "int8_scales": c.int8_scales.cpu().numpy(),
+        "keep_mask": c.keep_mask.cpu().numpy(),
+        "scores": c.scores.cpu().numpy(),
+        "table": lc.table_np,
+    }
+
+
+def run_attention(lc, step=0, q=None):
+    w = lc.w
+    if q is None:
+        q = lc.queries(step)
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device="cuda")
+    kvc().kvc_decode_attention(lc.cache, q, out, lse, lc.workspace())
+    torch.cuda.synchronize()
+    qn = q.cpu()
+    qn = qn.view(torch.int16).numpy().view(np.uint16) if q.dtype == torch.bfloat16 else qn.numpy()
+    return qn, out.cpu().numpy(), lse.cpu().numpy()
+
+
+def expected_keep4(w, lc, cpu, b, kvh, L):
+    """Keep flags the oracle expects for one (sequence, kv head)."""
+    start, n4 = regions.int4_range(L)
+    if w.mask == "all":
+        return np.ones(n4, bool)
+    if w.mask == "bernoulli":
+        return W.bernoulli_keep_np(w, lc.layer, b, kvh, L)[start:start + n4]
+    if w.mask == "scores":
+        s = W.given_scores_np(w, lc.layer, b, L)[kvh]
+        return policy.topk_keep(s[start:start + n4], w.budget_permille)
+    # mlp: exact against the GPU's own float32 scores; scores checked separately
+    s = cpu["scores"][b, kvh, :L].astype(np.float64)
+    return policy.topk_keep(s[start:start + n4], w.budget_permille)
+
+
+def check_pair(w, lc, cpu, qn, out, lse, b, kvh):
+    L = int(lc.lengths[b])
+    G = w.group_size
+    if L > 0:
+        check_codes(w, lc.layer, b, kvh, L, cpu)
+    if w.mask != "bernoulli":  # masks written by the refresh kernel
+        bits = mask_bits(cpu["keep_mask"][b, kvh], cpu["keep_mask"].shape[-1] * 32)
+        assert bits[regions.int8_positions(L)].all(), "protected positions must be kept"
+        assert not bits[L:].any(), "positions at or beyond L must be clear"
+    keep4 = keep4_from_mask(cpu["keep_mask"][b, kvh], L)
+    np.testing.assert_array_equal(keep4, expected_keep4(w, lc, cpu, b, kvh, L),
+                                  err_msg=f"keep mask b={b} h={kvh}")
+    if w.mask == "mlp" and L > 0:
+        k = source_np(w, lc.layer, "K", b, L, kvh)
+        v = source_np(w, lc.layer, "V", b, L, kvh)
+        ref = policy.mlp_scores(k, v, lc.mlp_np[kvh])
+        got = cpu["scores"][b, kvh, :L].astype(np.float64)
+        assert np.abs(got - ref).max() <= 1e-4, f"scores b={b} h={kvh}"
+    hs = slice(kvh * G, (kvh + 1) * G)
+    if L == 0:
+        assert (out[b, hs] == 0).all() and np.isneginf(lse[b, hs]).all()
+        return
+    ro, rl = oracle_heads(w, lc.layer, b, kvh, L, keep4, qn[b, hs])
+    assert_attention_close(out[b, hs], lse[b, hs], ro, rl, what=f"{w.name} b={b} h={kvh}")
+
+
+def check_workload(w, pairs=None):
+    lc = LayerCache(w)
+    cpu = cpu_buffers(lc)
+    qn, out, lse = run_attention(lc)
+    if pairs is None:
+        pairs = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+    for b, h in pairs:
+        print(f"  check {w.name} b={b} kvh={h} L={int(lc.lengths[b])}", flush=True)
+        check_pair(w, lc, cpu, qn, out, lse, b, h)
+    return lc
+
+
+# ---------------------------------------------------------------- small cases
+def test_tiny_full_config():
+    check_workload(W.WORKLOADS["tiny"])
+
+
+def test_uniform_small_ragged():
+    w = W.WORKLOADS["uniform4k"].replace(name="uniform_small", batch=3, ctx=1000)
+    check_workload(w)
+
+
+def test_edge_lengths_with_given_scores():
+    lens = (1, 16, 17, 100, 144, 145, 161, 1000, 2049, 0)
+    w = W.WORKLOADS["longtail"].replace(name="edges", batch=len(lens), ctx_range=None,
+                                        ctx_list=lens)
+    check_workload(w)
+
+
+@pytest.mark.parametrize("budget", [0, 100, 500, 1000])
+def test_mlp_scores_and_topk(budget):
+    w = W.WORKLOADS["long128k_b10"].replace(name="mlp_small", batch=2, ctx=3000,
+                                            budget_permille=budget)
+    check_workload(w)
+
+
+def test_mha_and_fp32_queries():
+    w = W.Workload("mha", 2, 8, 8, 128, ctx=700, src_dtype="f32", mask="bernoulli")
+    check_workload(w)
+
+
+def test_gqa8_head_dim_64():
+    w = W.Workload("gqa8", 2, 16, 2, 64, ctx=1500, mask="scores", budget_permille=300)
+    check_workload(w)
+
+
+def test_identity_vs_shuffled_pages_and_rerun_are_bit_identical():
+    w = W.WORKLOADS["uniform4k"].replace(name="paging", batch=2, ctx=2000)
+    a = LayerCache(w)
+    b = LayerCache(w.replace(shuffled_pages=False))
+    _, oa, la = run_attention(a)
+    _, oa2, la2 = run_attention(a)
+    _, ob, lb = run_attention(b)
+    assert np.array_equal(oa, oa2) and np.array_equal(la, la2)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+# ---------------------------------------------------------------- decode steps
+def test_decode_steps_cross_window_and_budget():
+    """Append one token per step (ring overwrite, INT4 region growth, score,
+    top-k refresh) and check every step against the oracle at the new length."""
+    m = kvc()
+    w = W.WORKLOADS["fullstep"].replace(name="steps", batch=3, layers=1, ctx=130,
+                                        decode_steps=40, ctx_list=(130, 150, 300))
+    lc = LayerCache(w)
+    lens = lc.lengths.copy()
+    one = torch.ones(w.batch, dtype=torch.int32, device="cuda")
+    for step in range(1, 41):
+        k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+        v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+        lens += 1
+        lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        lc.lengths = lens.copy()
+        m.kvc_quantize_append(lc.cache, k_new, v_new, one)
+        m.kvc_score_topk_mask(lc.cache, lc.mlp, k_new, v_new, one, w.budget_permille)
+        if step % 5 == 0 or step in (14, 15, 16):
+            cpu = cpu_buffers(lc)
+            qn, out, lse = run_attention(lc, step=step)
+            for b in range(w.batch):
+                for h in (0, w.kv_heads - 1):
+                    check_pair(w, lc, cpu, qn, out, lse, b, h)
+
+
+# ---------------------------------------------------------------- full sizes
+def sample_pairs(w, n, seed):
+    rng = np.random.default_rng(seed)
+    bs = rng.choice(w.batch, size=min(n, w.batch), replace=False)
+    return [(int(b), int(rng.integers(w.kv_heads))) for b in bs]
+
+
+def test_full_uniform4k_sampled():
+    w = W.WORKLOADS["uniform4k"]
+    check_workload(w, sample_pairs(w, 4, 1))
+
+
+def test_full_longtail_sampled():
+    w = W.WORKLOADS["longtail"]
+    lens = w.lengths()
+    pairs = sample_pairs(w, 3, 2) + [(int(np.argmax(lens)), 7), (int(np.argmin(lens)), 0)]
+    check_workload(w, pairs)
+
+
+@pytest.mark.parametrize("name", ["long128k_b10", "long128k_b50"])
+def test_full_long128k_sampled(name):
+    w = W.WORKLOADS[name]
+    check_workload(w, [(0, 0), (3, 7), (1, 4)])
+
+
+def test_full_decode_step_layer_sampled():
+    """One layer of the full decode-step workload: prefill, then one decode step."""
+    m = kvc()
+    w = W.WORKLOADS["fullstep"]
+    lc = LayerCache(w, keep_sources=False)
+    lens = lc.lengths.copy()
+    k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+    v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+    lens += 1
+    lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    lc.lengths = lens.copy()
+    one = torch.ones(w.batch, dtype=torch.int32, device="cuda")
+    m.kvc_quantize_append(lc.cache, k_new, v_new, one)
+    m.kvc_score_topk_mask(lc.cache, lc.mlp, k_new, v_new, one, w.budget_permille)
+    cpu = cpu_buffers(lc)
+    qn, out, lse = run_attention(lc, step=1)
+    for b, h in [(0, 0), (77, 5), (127, 7)]:
+        print(f"  check fullstep b={b} kvh={h}", flush=True)
+        check_pair(w, lc, cpu, qn, out, lse, b, h)

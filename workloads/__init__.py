@@ -165,6 +165,7 @@ class Workload:
     layers: int = 1
     ctx: Optional[int] = None                  # uniform context length
     ctx_range: Optional[Tuple[int, int]] = None  # log-uniform per-sequence lengths
+    ctx_list: Optional[Tuple[int, ...]] = None   # explicit per-sequence lengths
     src_dtype: str = "bf16"                    # K/V/Q source type: "bf16" or "f32"
     mask: str = "all"                          # "all" | "bernoulli" | "scores" | "mlp"
     budget_permille: Optional[int] = None
@@ -179,6 +180,8 @@ class Workload:
 
     def lengths(self) -> np.ndarray:
         """Per-sequence context lengths (int32 [B])."""
+        if self.ctx_list is not None:
+            return np.array(self.ctx_list, dtype=np.int32)
         if self.ctx is not None:
             return np.full(self.batch, self.ctx, dtype=np.int32)
         lo, hi = self.ctx_range
@@ -274,6 +277,34 @@ def kv_source_torch(w: Workload, layer: int, which: str, b: int, t0: int, t1: in
     return x
 
 
+def kv_rows_torch(w: Workload, layer: int, which: str, positions, device):
+    """One source row per sequence: position ``positions[b]`` of sequence b, [B][Hkv][D].
+
+    Identical values to :func:`kv_source_torch` / :func:`kv_source_np` at those
+    positions (the per-sequence stream key enters as a tensor).
+    """
+    import torch
+
+    H, D = w.kv_heads, w.head_dim
+    keys = torch.tensor([_s64(_kv_key(w, layer, which, b)) for b in range(len(positions))],
+                        dtype=torch.int64, device=device)
+    pos = torch.as_tensor(np.asarray(positions, dtype=np.int64), device=device)
+    hd = torch.arange(H * D, dtype=torch.int64, device=device)
+    idx = pos[:, None] * (H * D) + hd[None, :]
+    z = (idx + 1) * _s64(GAMMA) + keys[:, None]
+    z = (z ^ _srl(z, 30)) * _s64(M1)
+    z = (z ^ _srl(z, 27)) * _s64(M2)
+    z = z ^ _srl(z, 31)
+    t32, t16 = _torch_tables(device)
+    top = _srl(z, 48)
+    x = (t16[top].view(torch.bfloat16) if w.src_dtype == "bf16" else t32[top])
+    out = outlier_set(w, which)
+    if out.size:
+        sel = torch.from_numpy(out).to(device)
+        x[:, sel] = x[:, sel] * 8
+    return x.view(len(positions), H, D)
+
+
 def queries_np(w: Workload, layer: int, step: int) -> np.ndarray:
     """Decode queries [B][Hq][D] (bf16 bits or float32)."""
     idx = np.arange(w.batch * w.q_heads * w.head_dim, dtype=np.int64)
@@ -336,7 +367,7 @@ def page_table(w: Workload, layer: int = 0):
     are handed out in order.
     """
     cap = w.capacity()
-    npages = (cap + PAGE - 1) // PAGE
+    npages = np.maximum((cap + PAGE - 1) // PAGE, 1)
     total = int(npages.sum())
     max_pages = int(npages.max())
     if w.shuffled_pages:
