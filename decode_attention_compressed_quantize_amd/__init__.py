@@ -218,8 +218,8 @@ def kvc_decode_attention(cache: Cache, q, out, lse, ws, softmax_scale: float = 0
 
 
 def attention_workspace(cache: Cache, num_q_heads: int, device="cuda"):
-    """Allocate a workspace tensor of the size kvc_decode_attention needs."""
+    """Allocate a zero-filled workspace of the size kvc_decode_attention needs."""
     import torch
 
     n = kvc_attention_workspace_bytes(cache, num_q_heads)
-    return torch.empty(max(n // 4, 1), dtype=torch.float32, device=device)
+    return torch.zeros(max(n // 4, 1), dtype=torch.float32, device=device)

@@ -68,16 +68,18 @@ namespace kvc {
 
 AttnPlan plan_attention(const kvc_cache& c, int num_q_heads) {
   (void)num_q_heads;
-  const long long n4max = c.max_ctx > kInt8Slots ? (long long)c.max_ctx - kInt8Slots : 0;
+  // INT4 chunk j covers positions [j*chunk, (j+1)*chunk) of the INT4 region
+  // [16, max_ctx - 128). Aim for about 1536 chunk workgroups (4 waves each)
+  // over the batch, with chunks of 1024..2048 positions.
+  const long long end4 = c.max_ctx > kInt8Slots ? (long long)c.max_ctx - kRecent : 0;
   const long long pairs = (long long)c.batch * c.num_kv_heads;
-  // Aim for about 4096 INT4 work items over the whole batch, at least 256
-  // positions each, in whole 32-position mask words.
-  long long chunk = (pairs * n4max + 4095) / 4096;
-  if (chunk < 256) chunk = 256;
-  chunk = (chunk + 31) / 32 * 32;
+  long long chunk = (pairs * end4 + 1535) / 1536;
+  chunk = (chunk + 255) / 256 * 256;
+  if (chunk < 1024) chunk = 1024;
+  if (chunk > 2048) chunk = 2048;
   AttnPlan p;
   p.chunk = (int)chunk;
-  p.nsplit = n4max > 0 ? (int)((n4max + chunk - 1) / chunk) : 1;
+  p.nsplit = end4 > 0 ? (int)((end4 + chunk - 1) / chunk) : 1;
   return p;
 }
 
@@ -155,8 +157,10 @@ KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_d
   if (num_q_heads < 1 || num_q_heads % c->num_kv_heads)
     return fail(KVC_E_SHAPE, "num_q_heads must be a positive multiple of num_kv_heads");
   const int G = num_q_heads / c->num_kv_heads;
-  if (G * (c->head_dim / kvc::kGroup) > 16 || (G & (G - 1)))
-    return fail(KVC_E_UNSUPPORTED, "need (num_q_heads/num_kv_heads) a power of two with G*D/32 <= 16");
+  if (G > 4 || (G & (G - 1)))
+    return fail(KVC_E_UNSUPPORTED, "num_q_heads/num_kv_heads must be 1, 2 or 4");
+  if ((long long)c->max_ctx > 255LL * 2048 + kvc::kRecent)
+    return fail(KVC_E_UNSUPPORTED, "max_ctx above 522368 positions is not supported");
   const kvc::AttnPlan plan = kvc::plan_attention(*c, num_q_heads);
   const size_t need = kvc::attention_ws_floats(*c, num_q_heads, plan) * sizeof(float);
   if (!ws || ws_bytes < need) return fail(KVC_E_WORKSPACE, "attention workspace too small");

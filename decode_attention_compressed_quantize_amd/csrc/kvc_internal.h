@@ -22,13 +22,14 @@ __host__ __device__ inline int mask_words(int max_ctx) { return (max_ctx + 31) /
 
 // How the INT4 region is cut into split-KV chunks for one attention call.
 struct AttnPlan {
-  int chunk;   // positions per INT4 chunk (multiple of 32)
+  int chunk;   // positions per INT4 chunk (multiple of 256, at most 2048)
   int nsplit;  // INT4 chunks per (sequence, kv head); partial index nsplit is the INT8 region
 };
 
 AttnPlan plan_attention(const kvc_cache& c, int num_q_heads);
 
-// Partials: float [B][Hq][nsplit + 1][2 + D] as (m, l, o[0..D-1]); m is in log2 units.
+// Attention workspace: partials float [B][Hkv][nsplit + 1][G][2 + D] as
+// (m, l, o[0..D-1]) with m in log2 units. No initialisation needed.
 inline size_t attention_ws_floats(const kvc_cache& c, int num_q_heads, const AttnPlan& p) {
   return (size_t)c.batch * num_q_heads * (size_t)(p.nsplit + 1) * (size_t)(2 + c.head_dim);
 }

@@ -93,7 +93,7 @@ typedef struct kvc_cache {
   int32_t n_sink;            /* must be 16 */
   int32_t n_recent;          /* must be 128 */
   int32_t group;             /* must be 32 */
-  int32_t max_ctx;           /* capacity in positions, >= 1 */
+  int32_t max_ctx;           /* capacity in positions, >= 1 (attention: <= 522368) */
   uint8_t* int4_codes;
   uint16_t* int4_meta;
   int8_t* int8_codes;
@@ -151,14 +151,15 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
  * Source: KV4-RL review, section 3 (INT4 and INT8 regions processed
  * independently, outputs combined by an exact softmax merge).
  *   q            : device [B][num_q_heads][D] of type q_dtype (BF16 or F32).
- *   num_q_heads  : multiple of Hkv with (num_q_heads/Hkv) * (D/32) <= 16.
+ *   num_q_heads  : Hkv, 2*Hkv or 4*Hkv (query heads per kv head G = 1, 2, 4).
  *   softmax_scale: logit scale; <= 0 selects 1/sqrt(D).
  *   out          : device float [B][num_q_heads][D], softmax-weighted values.
  *   lse          : device float [B][num_q_heads] natural-log log-sum-exp of the
  *                  scaled logits over the attended positions, or NULL.
  *   ws, ws_bytes : device scratch of at least
- *                  kvc_attention_workspace_bytes(c, num_q_heads) bytes; its
- *                  contents on entry do not matter.
+ *                  kvc_attention_workspace_bytes(c, num_q_heads) bytes for the
+ *                  per-chunk partials; its contents on entry do not matter.
+ *                  Calls sharing one workspace must not overlap.
  *   Attends to the INT8 positions and to the INT4-region positions whose
  *   keep_mask bit is set. A sequence with L = 0 yields out = 0, lse = -inf.
  */

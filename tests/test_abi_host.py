@@ -76,8 +76,9 @@ def test_attention_argument_errors(lib):
     assert attn(lib, desc(max_pages_per_seq=10)) == -2
     assert attn(lib, desc(batch=0)) == -2
     assert attn(lib, desc(), hq=12) == -2          # not a multiple of Hkv
-    assert attn(lib, desc(), hq=64) == -3          # G = 8 at D = 128 exceeds 16 columns
-    assert attn(lib, desc(), hq=24) == -3          # G = 3 is not a power of two
+    assert attn(lib, desc(), hq=64) == -3          # G = 8 is not supported
+    assert attn(lib, desc(), hq=24) == -3          # G = 3 is not supported
+    assert attn(lib, desc(head_dim=64), hq=64) == -3
     assert attn(lib, desc(), ws=None) == -4
     assert attn(lib, desc(), ws_bytes=16) == -4
     assert "workspace" in kvc.kvc_last_error()
@@ -102,12 +103,17 @@ def test_append_and_topk_argument_errors(lib):
 
 
 def test_workspace_size_covers_every_split(lib):
-    # (m, l, o[D]) per query head for every INT4 chunk plus the INT8 partial
+    # (m, l, o[D]) per query head for every INT4 chunk of at most 2048
+    # positions plus the INT8 partial
     for max_ctx in (1, 144, 145, 4096, 131072):
         c = desc(max_ctx=max_ctx, max_pages_per_seq=(max_ctx + 15) // 16)
         n = lib.kvc_attention_workspace_bytes(ctypes.byref(c), 32)
+        counters = 0
         per_split = 2 * 32 * (128 + 2) * 4
-        assert n % per_split == 0
-        assert n // per_split >= 2   # at least one INT4 chunk plus the INT8 partial
+        assert (n - counters) % per_split == 0
+        nparts = (n - counters) // per_split
+        assert nparts >= 2
+        end4 = max(0, max_ctx - 128) if max_ctx > 144 else 0
+        assert (nparts - 1) * 2048 >= end4
     assert lib.kvc_attention_workspace_bytes(ctypes.byref(desc(head_dim=96)), 32) == 0
     assert lib.kvc_topk_workspace_bytes(ctypes.byref(desc())) == 0

@@ -102,7 +102,8 @@ def check_pair(w, lc, cpu, qn, out, lse, b, kvh):
         assert (out[b, hs] == 0).all() and np.isneginf(lse[b, hs]).all()
         return
     ro, rl = oracle_heads(w, lc.layer, b, kvh, L, keep4, qn[b, hs])
-    assert_attention_close(out[b, hs], lse[b, hs], ro, rl, what=f"{w.name} b={b} h={kvh}")
+    err, rel, lerr = assert_attention_close(out[b, hs], lse[b, hs], ro, rl, what=f"{w.name} b={b} h={kvh}")
+    print(f"    {w.name} b={b} kvh={kvh} L={L}: max-abs {err:.2e} rel-L2 {rel:.2e} lse {lerr:.2e}", flush=True)
 
 
 def check_workload(w, pairs=None):
@@ -146,9 +147,14 @@ def test_mha_and_fp32_queries():
     check_workload(w)
 
 
-def test_gqa8_head_dim_64():
-    w = W.Workload("gqa8", 2, 16, 2, 64, ctx=1500, mask="scores", budget_permille=300)
+def test_gqa2_head_dim_64():
+    w = W.Workload("gqa2", 2, 4, 2, 64, ctx=1500, mask="scores", budget_permille=300)
     check_workload(w)
+
+
+def test_gqa2_head_dim_128_long_chunks():
+    w = W.Workload("gqa2_128", 3, 16, 8, 128, ctx=9000, mask="scores", budget_permille=700)
+    check_workload(w, [(0, 0), (1, 5), (2, 7)])
 
 
 def test_identity_vs_shuffled_pages_and_rerun_are_bit_identical():
