@@ -151,9 +151,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
       const int shift = 24 - 8 * pass;
       for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < n4; i += kTopkThreads) {
-        const uint32_t key = order_key(sc[i]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      // 16 scores per thread per step, all loads issued before any is used
+      for (int base = tid; base < n4; base += kTopkThreads * 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int i = base + u * kTopkThreads;
+          v[u] = i < n4 ? sc[i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (base + u * kTopkThreads < n4) {
+            const uint32_t key = order_key(v[u]);
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+          }
+        }
       }
       __syncthreads();
       if (wid == 0) {
@@ -197,10 +209,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
     const int w = w0 + tid;
     uint32_t gt = 0, eq = 0;  // bit masks over the word's INT4 positions
     if (w < p.words && k > 0 && !all) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int t = w * 32 + i;
+        v[i] = (t >= kSink && t < kSink + n4) ? sc[t - kSink] : 0.0f;
+      }
+#pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int t = w * 32 + i;
         if (t >= kSink && t < kSink + n4) {
-          const uint32_t key = order_key(sc[t - kSink]);
+          const uint32_t key = order_key(v[i]);
           if (key > T) gt |= 1u << i;
           else if (key == T) eq |= 1u << i;
         }
