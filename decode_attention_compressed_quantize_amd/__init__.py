@@ -144,7 +144,7 @@ class Cache:
         dev = torch.device(device)
         D = head_dim
         self.int4_codes = torch.zeros((num_phys_pages, kv_heads, PAGE, 2, D // 2), dtype=torch.uint8, device=dev)
-        self.int4_meta = torch.zeros((num_phys_pages, kv_heads, PAGE, D // GROUP, 4), dtype=torch.int16, device=dev)
+        self.int4_meta = torch.zeros((num_phys_pages, kv_heads, PAGE, 2, D // GROUP, 2), dtype=torch.int16, device=dev)
         self.int8_codes = torch.zeros((batch, kv_heads, INT8_SLOTS, 2, D), dtype=torch.int8, device=dev)
         self.int8_scales = torch.zeros((batch, kv_heads, INT8_SLOTS, 2), dtype=torch.float32, device=dev)
         self.mask_words = (max_ctx + 31) // 32

@@ -1,5 +1,5 @@
 // Split-region decode attention over the compressed cache, with the exact
-// log-sum-exp merge, in one kernel launch.
+// log-sum-exp merge of the per-chunk partials in a second, small launch.
 //
 // Source: KV4-RL review, section 3 - the INT4 region and the protected INT8
 // region are processed independently and their outputs are combined by an
@@ -11,32 +11,40 @@
 // chunk of `chunk` positions), plus one workgroup per (sequence, kv head) for
 // the INT8 region. Every workgroup writes one unnormalised partial
 // (m, l, o[D]) per query head: m is the max logit in log2 units
-// (logit * log2 e), l = sum 2^(s - m), o = sum 2^(s - m) * v. A second,
-// small kernel merges the nsplit + 1 partials of each (sequence, kv head) in
+// (logit * log2 e), l = sum 2^(s - m), o = sum 2^(s - m) * v. The merge
+// kernel combines the nsplit + 1 partials of each (sequence, kv head) in
 // index order, so results do not depend on scheduling.
 //
 // INT4 chunk, per wave (a quarter of the chunk):
 //  * The kept positions (keep-mask bits) are compacted with ballot/mbcnt into
-//    an LDS list of token-record indices, so evicted tokens cost no HBM reads
-//    and every read is a whole token record (K||V codes, 128 B at D = 128).
+//    an LDS list of token-record indices, so evicted tokens cost no HBM reads.
 //    The mask words and block-table entries of the wave's range are fetched
-//    with one load each, and the main loop fetches the next 32 tokens while
-//    it computes the current ones.
+//    with one load each.
+//  * The list is walked in 32-token tiles, each as two steps: a K step (K
+//    codes and K meta) that writes the tile's logits to LDS, raises the
+//    running max per head and rescales the accumulators once, and a V step
+//    (V codes and V meta, whose line the K step has just brought into L2)
+//    that accumulates P.V with p = 2^(s - max). The steps form one stream
+//    behind a ring of kRing register tiles, so the loads of the next steps
+//    are in flight during each step's arithmetic.
 //  * Logits use v_mfma_f32_16x16x32_f16 with the raw codes: a nibble n becomes
 //    the fp16 value 1024 + n (or 1024 + 16n) by OR-ing it into 0x6400, which is
 //    exact; one MFMA row is one token, one column one (group, head) pair, and
-//    the query operand is zero outside the column's own group, so each column
-//    accumulates exactly one group's dot product q_g . c_g. The per-group
-//    scale and min are then applied in float32:
+//    the query operand (q, zero outside the column's own group) makes
+//    each column accumulate exactly one group's dot product. The accumulators
+//    start at -sum(q) * 1024, so the offset cancels inside the MFMA; the
+//    per-group scale and min are then applied in float32:
 //      s = sum_g scale_g (q_g . c_g) + min_g sum(q_g)   (rows = tokens).
+//    The exponentials 2^(s - max) are taken once per (token, head) and left
+//    in LDS for the V step.
 //  * P.V uses the same MFMA with rows = (group, head) pairs, whose P operand
 //    is p * V_scale[token][group] in fp16, and columns = channels 8n + m read
-//    from V-code dword n; the codes enter as 1024 + 16c and the 1024 offset
-//    plus 16 * 8 (centring the codes) is removed by one extra MFMA against a
-//    constant 1152 operand. Only rows whose group matches the column's channel
-//    group are kept. The remaining term sum_t p_t (V_min + 8 V_scale)[t][g] is
-//    accumulated in float32 on the side.
-//  * Softmax: exact running max per head with a wave-uniform rescale branch.
+//    from V-code dword n; the codes enter as the exact fp16 subnormals
+//    c * 2^-24 or c * 2^-20 (one AND each, no offset). One more MFMA against
+//    a constant 1.0 operand sums the fp16 P operand per row, which centres the
+//    codes at 8: the fp16 rounding of P then weighs (c - 8) instead of c. Only
+//    rows whose group matches the column's channel group are kept. The side
+//    term sum_t p_t V_min + 8 p_t V_scale is accumulated in float32.
 #include "kvc_internal.h"
 
 #include <type_traits>
@@ -47,9 +55,11 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in both halves
-constexpr uint32_t kCentre = 0x64806480u;  // fp16 1152.0 = 1024 + 16 * 8 in both halves
+constexpr uint32_t kOne = 0x3C003C00u;     // fp16 1.0 in both halves
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 4;  // INT4 steps in flight per wave (the one in use plus three prefetched)
+static_assert(kRing % 2 == 0, "ring slots alternate between K and V steps");
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -155,34 +165,45 @@ struct Shape {
   static constexpr int NC = NG * G;   // distinct (group, head) columns, <= 16
 };
 
-// LDS shared by the INT4 and INT8 paths of one workgroup.
+// LDS of one workgroup. The INT4 path gives each wave its own region (kept
+// list, pass-1 logits - later reused for the wave's output -, and staging for
+// one tile of V codes and meta); the INT8 path overlays its own buffers.
 template <int D, int G>
 struct Smem {
-  static constexpr int kListCap = 512;  // positions per wave (chunk <= 4 * 512)
+  static constexpr int kListCap = 512;  // positions per wave: chunk <= 4 * 512
+  // Row strides padded so that the 16-lane row groups of a wave fall into
+  // different LDS banks on the P.V operand reads.
+  static constexpr int kLgStride = 48;    // 32 logits + 16
+  static constexpr int kVStride = D / 8 + 4;
+  struct Wave4 {
+    uint32_t rec[kListCap + 32];          // token-record indices, padded with copies
+    union {
+      float logit[G][kLgStride];          // the current tile's logits / alpha, then p
+      float o[G][D];                      // the wave's unnormalised output
+    } lo;
+    uint32_t vbuf[32][kVStride];          // V codes of the current 32 tokens
+    uint32_t mbuf[32][D / 32];            // K or V (scale | min << 16) of the current 32 tokens
+  };
+  struct Int8 {
+    float q[G][D];
+    int8_t vcode[kWaves][36][D];
+    float vscale[kWaves][36];
+    float p[kWaves][G][36];
+    float o[kWaves][G][D];
+  };
   union {
-    struct {
-      uint64_t code[kWaves][kListCap + 64];  // byte offset of the token's K codes
-      uint32_t meta[kWaves][kListCap + 64];  // byte offset of the token's meta row
-    } list;
-    struct {
-      float q[G][D];
-      int8_t vcode[kWaves][36][D];
-      float vscale[kWaves][36];
-      float p[kWaves][G][36];
-    } i8;
+    Wave4 w4[kWaves];
+    Int8 i8;
   } u;
-  float o[kWaves][G][D];
   float m[kWaves][G];
   float l[kWaves][G];
   float vm[kWaves][16];
   int32_t pages[kWaves][64];
-  uint32_t vbuf[kWaves][32][D / 8];  // V codes of the current 32 tokens
-  uint32_t mbuf[kWaves][32][D / 16]; // meta rows of the current 32 tokens
 };
 
 // Combine the four waves' (m, l, o) held in LDS into one partial and store it.
-template <int D, int G>
-__device__ inline void store_partial(const AttnParams& p, Smem<D, G>& sm, float* dst) {
+template <int D, int G, typename OF>
+__device__ inline void store_partial(Smem<D, G>& sm, OF o_of, float* dst) {
   const int tid = threadIdx.x;
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, ch = i % D;
@@ -196,7 +217,7 @@ __device__ inline void store_partial(const AttnParams& p, Smem<D, G>& sm, float*
         const float mw = sm.m[w][h];
         if (mw == -INFINITY) continue;
         const float a = __builtin_amdgcn_exp2f(mw - M);
-        o += a * sm.o[w][h][ch];
+        o += a * o_of(w)[h * D + ch];
         l += a * sm.l[w][h];
       }
     }
@@ -207,15 +228,23 @@ __device__ inline void store_partial(const AttnParams& p, Smem<D, G>& sm, float*
 }
 
 // ------------------------------------------------------------------ INT4 chunk
+// Per wave: compact the kept positions of its quarter of the chunk, then walk
+// them in 32-token tiles, each a K step (logits, running max, one rescale)
+// followed by a V step (P.V), with the next steps' loads in flight.
 template <int D, int G, bool QBF16>
 __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, int split) {
   using S = Shape<D, G>;
+  constexpr int NG = S::NG, VD = S::VD, NC = S::NC;
+  constexpr int MH = NG / 2;  // meta words per half row (K or V part)
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int s = lane >> 4;          // row slot
-  const int n = lane & 15;          // column
-  const int gc = (n / G) % S::NG;   // column's group
-  const int hc = n % G;             // column's head
+  const int s = lane >> 4;         // row slot
+  const int n = lane & 15;         // column
+  const int gc = (n / G) % NG;     // column's group
+  const int hc = n % G;            // column's head
+  const int tl = lane >> 1;        // token this lane stages (compact loads)
+  const int hf = lane & 1;         // which half of that token's row
+  auto& wv = sm.u.w4[wave];
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
   const int n4 = L > kInt8Slots ? L - kInt8Slots : 0;
@@ -225,14 +254,25 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
   const int lo = w0 > r0 ? w0 : r0;
   const int hi = w0 + q4 < r1 ? w0 + q4 : r1;
 
-  // ---- compact the kept positions of this wave's range into an LDS list
-  uint64_t* lcode = sm.u.list.code[wave];
-  uint32_t* lmeta = sm.u.list.meta[wave];
-  int cnt = 0;
-  const uint32_t* mrow = p.mask + ((size_t)b * p.hkv + kvh) * p.words;
-  const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+  // The query entries this lane feeds to the QK product (code s*D/4 + 8m + perm[r]
+  // of its column's head), loaded first so their latency overlaps the compaction.
+  float qraw[NG][8];
   {
-    // one load for the range's mask words (<= 32) and one for its pages (<= 64)
+    const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + hc) * D;
+    const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+    for (int m = 0; m < NG; ++m)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) qraw[m][r] = load_q<QBF16>(p.q, qoff + s * (D / 4) + 8 * m + perm[r]);
+  }
+
+  // ---- compact the kept positions of this wave's range into an LDS list
+  uint32_t* list = wv.rec;
+  int cnt = 0;
+  {
+    const uint32_t* mrow = p.mask + ((size_t)b * p.hkv + kvh) * p.words;
+    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+    // one load for the range's mask words (<= 12) and one for its pages (<= 24)
     uint32_t myword = 0;
     int32_t mypage = -1;
     if (lane < q4 / 32 && w0 + 32 * lane < hi) myword = mrow[(w0 >> 5) + lane];
@@ -251,252 +291,303 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       if (kept) {
         const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        const uint32_t rec = ((uint32_t)page * p.hkv + kvh) * kPage + (pos & (kPage - 1));
-        lcode[cnt + rank] = (uint64_t)rec * D;
-        lmeta[cnt + rank] = rec * (uint32_t)(S::NG * 8);
+        list[cnt + rank] = ((uint32_t)page * p.hkv + kvh) * kPage + (pos & (kPage - 1));
       }
       cnt += __popcll(bal);
     }
   }
   if (cnt > 0) {
     // pad to a whole tile plus one more, so the prefetch never needs a branch
-    const uint64_t fc = lcode[0];
-    const uint32_t fm = lmeta[0];
-    const int padded = ((cnt + 31) & ~31) + 32;
-    if (cnt + lane < padded) { lcode[cnt + lane] = fc; lmeta[cnt + lane] = fm; }
+    const uint32_t fill = list[0];
+    const int padded = (cnt + 31) & ~31;
+    if (cnt + lane < padded) list[cnt + lane] = fill;
   }
 
-  float m_col = -INFINITY, l_col = 0.0f, vm_col = 0.0f;
-  float4v acc[8], acc_off = {0.0f, 0.0f, 0.0f, 0.0f};
+  // Per lane: m_col and l_col belong to head hc (the lane's column head),
+  // vm1/vm2 to accumulator row (gc, hc) of the P operand; acc holds P.V with
+  // rows (group, head) and columns channels, acc_one = sum of the fp16 P
+  // operand per row.
+  float m_col = -INFINITY, l_col = 0.0f, vm1 = 0.0f, vm2 = 0.0f;
+  float4v acc[8], acc_one = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = acc_off;
+  for (int m = 0; m < 8; ++m) acc[m] = acc_one;
 
   if (cnt > 0) {
-    // ---- query operands: column (gc, hc) holds q for group gc only
-    const int hq = kvh * G + hc;
-    const size_t qoff = ((size_t)b * p.hkv * G + hq) * D;
+    // ---- query operands: column (gc, hc) holds q for group gc only, divided
+    // by 16 in the k slots whose codes enter as 1024 + 16c (exact in fp16 for
+    // a bf16 query)
     const int slot_group = (s * D / 4) / 32;
     const bool active = slot_group == gc;
-    half8 bq[S::NG];
-    float off = 0.0f, qsum = 0.0f;
-    const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    const float alpha = p.alpha;
+    half8 bq[NG];
+    float off = 0.0f, qs = 0.0f;
 #pragma unroll
-    for (int m = 0; m < S::NG; ++m) {
+    for (int m = 0; m < NG; ++m) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const int code = s * (D / 4) + 8 * m + perm[r];
         const bool x16 = (r == 2 || r == 3 || r == 6 || r == 7);
-        float qv = load_q<QBF16>(p.q, qoff + code);
-        qv = active ? qv : 0.0f;
-        qsum += qv;
+        const float qv = active ? qraw[m][r] : 0.0f;
+        qs += qv;
         const _Float16 qh = (_Float16)(x16 ? qv * 0.0625f : qv);
         bq[m][r] = qh;
         off += (float)qh * 1024.0f;
       }
     }
     // every code of the column's group sits in exactly one active slot
-    qsum = rows_sum(qsum);
-    // the column's offset sums over all four k-slots (rows of the B operand)
     off = rows_sum(off);
-    const float alpha = p.alpha;
-    const float a_off = alpha * off;
-    const float a_qs = alpha * qsum;
-
-    // ---- main loop over 32 kept tokens per iteration, next tokens prefetched
-    // A tile in flight: K codes in MFMA operand order (token n and 16 + n,
-    // slot s), and for token lane/2 one half of its V codes and of its meta row.
-    struct Tile {
-      uint32_t kd0[S::NG], kd1[S::NG];
-      uint32_t vh[S::VD / 2];
-      uint32_t mh[S::NG];
-    };
-    const int vdw = n % S::VD;
-    const int tl = lane >> 1, hf = lane & 1;
+    qs = rows_sum(qs);
+    // QK accumulators start at -off, which removes the 1024 of every code
+    const float4v offv = {-off, -off, -off, -off};
     const uint8_t* kbase = p.codes + s * S::SB;
     const uint8_t* vbase = p.codes + D / 2 + hf * (D / 4);
-    const uint8_t* mbase = reinterpret_cast<const uint8_t*>(p.meta) + hf * (D / 8);
-    uint32_t* vrow = sm.vbuf[wave][tl] + hf * (S::VD / 2);
-    uint32_t* mrow_l = sm.mbuf[wave][tl] + hf * (S::NG);
-    auto fetch = [&](int it, Tile& t) {
-      const uint64_t o0 = lcode[it + n], o1 = lcode[it + 16 + n];
-      const uint64_t ov = lcode[it + tl];
-      const uint32_t om = lmeta[it + tl];
-      if constexpr (D == 128) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kbase + o0);
-        const u32x4 c = *reinterpret_cast<const u32x4*>(kbase + o1);
-        const u32x4 v0 = *reinterpret_cast<const u32x4*>(vbase + ov);
-        const u32x4 v1 = *reinterpret_cast<const u32x4*>(vbase + ov + 16);
-        const u32x4 mm = *reinterpret_cast<const u32x4*>(mbase + om);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          t.kd0[m] = a[m]; t.kd1[m] = c[m]; t.vh[m] = v0[m]; t.vh[4 + m] = v1[m]; t.mh[m] = mm[m];
-        }
+    const uint8_t* mbase = reinterpret_cast<const uint8_t*>(p.meta) + hf * (MH * 4);
+    const int ntile = (cnt + 31) >> 5;  // 32-token tiles
+    const int nstep = 2 * ntile;        // K step, then V step, per tile
+
+    // One stream of steps: step 2j brings K codes and K meta of tile j, step
+    // 2j + 1 the V codes and V meta of the same tokens. The V half of a token
+    // record shares the 128-byte line of its K half, so it is read from L2
+    // right after the K step brought the line in. Both kinds load the same
+    // registers with the same instructions (two loads of NG code dwords, one
+    // of MH meta dwords), so the ring never drains between them.
+    struct Tile {
+      uint32_t c[2 * NG];
+      uint32_t mh[MH];
+    };
+    // kind: true for a K step, false for a V step; steps past the end reload
+    // the last tile (L2 hits, results unused)
+    auto fetch = [&](auto kind, int step, Tile& t) {
+      constexpr bool isk = decltype(kind)::value;
+      const int tile = step >> 1;
+      const int it = 32 * (tile < ntile ? tile : ntile - 1);
+      const uint32_t rt = list[it + tl];
+      const uint8_t* a0;
+      const uint8_t* a1;
+      if constexpr (isk) {
+        a0 = kbase + (uint64_t)list[it + n] * D;
+        a1 = kbase + (uint64_t)list[it + 16 + n] * D;
       } else {
-        const u32x2 a = *reinterpret_cast<const u32x2*>(kbase + o0);
-        const u32x2 c = *reinterpret_cast<const u32x2*>(kbase + o1);
-        const u32x4 v0 = *reinterpret_cast<const u32x4*>(vbase + ov);
-        const u32x2 mm = *reinterpret_cast<const u32x2*>(mbase + om);
+        a0 = vbase + (uint64_t)rt * D;
+        a1 = a0 + 4 * NG;
+      }
+      const uint8_t* am = mbase + (uint64_t)rt * (D / 4) + (isk ? 0 : D / 8);
+      if constexpr (D == 128) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(a0);
+        const u32x4 y = *reinterpret_cast<const u32x4*>(a1);
+        const u32x2 mm = *reinterpret_cast<const u32x2*>(am);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) { t.kd0[m] = a[m]; t.kd1[m] = c[m]; t.mh[m] = mm[m]; }
+        for (int m = 0; m < 4; ++m) { t.c[m] = x[m]; t.c[4 + m] = y[m]; }
+        t.mh[0] = mm[0];
+        t.mh[1] = mm[1];
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(a0);
+        const u32x2 y = *reinterpret_cast<const u32x2*>(a1);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) t.vh[m] = v0[m];
+        for (int m = 0; m < 2; ++m) { t.c[m] = x[m]; t.c[2 + m] = y[m]; }
+        t.mh[0] = *reinterpret_cast<const uint32_t*>(am);
       }
     };
-    auto compute = [&](const Tile& cur, int it, auto tail) {
-      const uint32_t* kd0 = cur.kd0;
-      const uint32_t* kd1 = cur.kd1;
-#pragma unroll
-      for (int m = 0; m < S::VD / 2; ++m) vrow[m] = cur.vh[m];
-#pragma unroll
-      for (int m = 0; m < S::NG; ++m) mrow_l[m] = cur.mh[m];
-      __builtin_amdgcn_wave_barrier();
-      uint32_t vd[8];
-      u32x2 md[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = i < 4 ? 4 * s + i : 16 + 4 * s + (i - 4);
-        vd[i] = sm.vbuf[wave][tok][vdw];
-        md[i] = *reinterpret_cast<const u32x2*>(&sm.mbuf[wave][tok][2 * gc]);
-      }
 
-      // QK: C[token][(g,h)] = q_g . c_g
-      float4v c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = c0;
+    // ---- K step: logits of 32 tokens, running max, rescale when it rises,
+    // then p = 2^(s - max) of every (token, head) once, into LDS
+    auto compute1 = [&](const Tile& t, int it) {
 #pragma unroll
-      for (int m = 0; m < S::NG; ++m) {
-        uint32_t x = kd0[m];
+      for (int m = 0; m < MH; ++m) wv.mbuf[tl][hf * MH + m] = t.mh[m];
+      __builtin_amdgcn_wave_barrier();
+      // QK: C[token][(g,h)] = q_g . c_g (codes taken as 1024 + c)
+      float4v c0 = offv, c1 = offv;
+#pragma unroll
+      for (int m = 0; m < NG; ++m) {
+        uint32_t x = t.c[m];
         uint32_t y = x >> 8;
         half8 a = as_half8(and_or(x, 0x000F000Fu, kMagic), and_or(x, 0x00F000F0u, kMagic),
                            and_or(y, 0x000F000Fu, kMagic), and_or(y, 0x00F000F0u, kMagic));
         c0 = mfma16x16x32(a, bq[m], c0);
-        x = kd1[m];
+        x = t.c[NG + m];
         y = x >> 8;
         a = as_half8(and_or(x, 0x000F000Fu, kMagic), and_or(x, 0x00F000F0u, kMagic),
                      and_or(y, 0x000F000Fu, kMagic), and_or(y, 0x00F000F0u, kMagic));
         c1 = mfma16x16x32(a, bq[m], c1);
       }
+      // u_g = scale_g (q_g . c_g) + min_g sum(q_g); the logit in log2 units is
+      // alpha * sum_g u_g, with alpha applied in the exponent below
       float sv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        const int tok = i < 4 ? 4 * s + i : 16 + 4 * s + (i - 4);
+        const uint32_t km = wv.mbuf[tok][gc];
         const float d = i < 4 ? c0[i] : c1[i - 4];
-        const float ks = h2f(md[i][0] & 0xFFFFu), km = h2f(md[i][0] >> 16);
-        const float e = fmaf(d, alpha, -a_off);
-        sv[i] = fmaf(ks, e, km * a_qs);
+        sv[i] = fmaf(h2f(km & 0xFFFFu), d, fmaf(h2f(km >> 16), qs, 0.0f));
       }
       // sum the group columns of each head (columns h, h+G, h+2G, ... within a row)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if constexpr (S::NC >= 2 * G) sv[i] += row_ror<G>(sv[i]);
-        if constexpr (S::NC >= 4 * G) sv[i] += row_ror<2 * G>(sv[i]);
-        if constexpr (S::NC >= 8 * G) sv[i] += row_ror<4 * G>(sv[i]);
-        if constexpr (S::NC >= 16 * G) sv[i] += row_ror<8 * G>(sv[i]);
+        if constexpr (NC >= 2 * G) sv[i] += row_ror<G>(sv[i]);
+        if constexpr (NC >= 4 * G) sv[i] += row_ror<2 * G>(sv[i]);
+        if constexpr (NC >= 8 * G) sv[i] += row_ror<4 * G>(sv[i]);
+        if constexpr (NC >= 16 * G) sv[i] += row_ror<8 * G>(sv[i]);
       }
-      if constexpr (decltype(tail)::value) {
+      // Padding tokens past cnt repeat list[0], whose logit tile 0 has already
+      // folded into the max, so they cannot raise it; they get p = 0 below.
+      float tmax = sv[0];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tok = i < 4 ? 4 * s + i : 16 + 4 * s + (i - 4);
-          if (it + tok >= cnt) sv[i] = -INFINITY;
-        }
+      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
+      if (n < G) {
+        const float4v lo4 = {sv[0], sv[1], sv[2], sv[3]};
+        const float4v hi4 = {sv[4], sv[5], sv[6], sv[7]};
+        *reinterpret_cast<float4v*>(&wv.lo.logit[n][4 * s]) = lo4;
+        *reinterpret_cast<float4v*>(&wv.lo.logit[n][16 + 4 * s]) = hi4;
       }
-      // running max per head, rescale only when it grows
-      float bm = sv[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) bm = fmaxf(bm, sv[i]);
-      bm = rows_max(bm);
-      if (__ballot(bm > m_col)) {
-        const float mn = fmaxf(m_col, bm);
-        const float a = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_col - mn);
-        m_col = mn;
-        l_col *= a;
-        vm_col *= a;
-        float ah[G];
+      // every tile holds at least one kept token, so the new max is finite
+      // (m_col is in log2 units, alpha > 0)
+      const float mnew = fmaxf(m_col, alpha * rows_max(tmax));
+      if (__ballot(mnew > m_col) != 0) {
+        const float f = __builtin_amdgcn_exp2f(m_col - mnew);  // 0 on the first tile
+        l_col *= f;
+        vm1 *= f;
+        vm2 *= f;
+        // accumulator row 4s + j belongs to head j % G (G divides 4); lane
+        // h < G has column (0, h), so it holds head h's factor
+        float fh[G];
 #pragma unroll
         for (int h = 0; h < G; ++h)
-          ah[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), h));
+          fh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), h));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float f = ah[j % G];
+          const float fj = fh[j % G];
 #pragma unroll
-          for (int m = 0; m < 8; ++m) acc[m][j] *= f;
-          acc_off[j] *= f;
+          for (int m = 0; m < 8; ++m) acc[m][j] *= fj;
+          acc_one[j] *= fj;
         }
       }
+      m_col = mnew;
+      __builtin_amdgcn_wave_barrier();
+      // p for (head hc, tokens of this lane): 2 per lane at G = 4, 1 at G = 2,
+      // 1 on half the lanes at G = 1
+      const int lim = cnt - it;  // tokens of this tile below lim are real
+      if constexpr (G == 4) {
+        const int k2 = 2 * (4 * s + n / 4);
+        float2v lg = *reinterpret_cast<const float2v*>(&wv.lo.logit[hc][k2]);
+        lg[0] = k2 < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, lg[0], -m_col)) : 0.0f;
+        lg[1] = k2 + 1 < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, lg[1], -m_col)) : 0.0f;
+        l_col += lg[0] + lg[1];
+        *reinterpret_cast<float2v*>(&wv.lo.logit[hc][k2]) = lg;
+      } else {
+        const int k = G == 2 ? 8 * s + n / 2 : 16 * s + n;
+        if (k < 32) {
+          const float pr = k < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, wv.lo.logit[hc][k], -m_col)) : 0.0f;
+          l_col += pr;
+          wv.lo.logit[hc][k] = pr;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    // ---- V step: P.V of the same 32 tokens. V codes enter the MFMA as the
+    // exact fp16 subnormals c * 2^-24 (low nibble of a half) and c * 2^-20
+    // (second nibble), so no offset has to be removed afterwards.
+    const int vdw = n % VD;
+    auto compute2 = [&](const Tile& t) {
+#pragma unroll
+      for (int m = 0; m < VD / 2; ++m) wv.vbuf[tl][hf * (VD / 2) + m] = t.c[m];
+#pragma unroll
+      for (int m = 0; m < MH; ++m) wv.mbuf[tl][hf * MH + m] = t.mh[m];
+      __builtin_amdgcn_wave_barrier();
+      const float4v pv0 = *reinterpret_cast<const float4v*>(&wv.lo.logit[hc][4 * s]);
+      const float4v pv1 = *reinterpret_cast<const float4v*>(&wv.lo.logit[hc][16 + 4 * s]);
+      uint32_t vd[8];
       float pp[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float pr = __builtin_amdgcn_exp2f(sv[i] - m_col);
-        l_col += pr;
-        const float vsc = h2f(md[i][1] & 0xFFFFu);
-        vm_col = fmaf(pr, fmaf(8.0f, vsc, h2f(md[i][1] >> 16)), vm_col);
-        pp[i] = pr * vsc;
+        const int tok = i < 4 ? 4 * s + i : 16 + 4 * s + (i - 4);
+        vd[i] = wv.vbuf[tok][vdw];
+        const uint32_t vmeta = wv.mbuf[tok][gc];
+        const float pr = i < 4 ? pv0[i] : pv1[i - 4];
+        const float ps = fmaf(pr, h2f(vmeta & 0xFFFFu), 0.0f);
+        vm1 = fmaf(pr, h2f(vmeta >> 16), vm1);
+        vm2 += ps;
+        pp[i] = ps;
       }
       const half8 A = as_half8(pack_f16x2(pp[0], pp[1]), pack_f16x2(pp[2], pp[3]),
                                pack_f16x2(pp[4], pp[5]), pack_f16x2(pp[6], pp[7]));
-      // P.V: V codes of tokens (2q, 2q+1) paired into fp16 halves 1024 + 16c
-      uint32_t xlo[4], xhi[4];
+      // V codes of tokens (2q, 2q+1) paired into the halves of one dword
+      uint32_t xv[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        xlo[q] = __builtin_amdgcn_perm(vd[2 * q + 1], vd[2 * q], 0x05040100u);
-        xhi[q] = __builtin_amdgcn_perm(vd[2 * q + 1], vd[2 * q], 0x07060302u);
+        xv[q] = __builtin_amdgcn_perm(vd[2 * q + 1], vd[2 * q], 0x05040100u);      // channels 0..3
+        xv[4 + q] = __builtin_amdgcn_perm(vd[2 * q + 1], vd[2 * q], 0x07060302u);  // channels 4..7
       }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         uint32_t bw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t x = m < 4 ? xlo[q] : xhi[q];
-          const int mm = m & 3;
-          const uint32_t y = mm == 0 ? (x << 4) : mm == 1 ? x : mm == 2 ? (x >> 4) : (x >> 8);
-          bw[q] = and_or(y, 0x00F000F0u, kMagic);
+          const uint32_t x = xv[(m / 4) * 4 + q];
+          const uint32_t y = (m & 2) ? x >> 8 : x;
+          bw[q] = y & ((m & 1) ? 0x00F000F0u : 0x000F000Fu);
         }
         acc[m] = mfma16x16x32(A, as_half8(bw[0], bw[1], bw[2], bw[3]), acc[m]);
       }
-      acc_off = mfma16x16x32(A, as_half8(kCentre, kCentre, kCentre, kCentre), acc_off);
+      acc_one = mfma16x16x32(A, as_half8(kOne, kOne, kOne, kOne), acc_one);
       __builtin_amdgcn_wave_barrier();
     };
-    // whole tiles ping-pong between two register sets; the last tile (which
-    // may hold padding) masks its invalid tokens
-    using Full = std::integral_constant<bool, false>;
-    using Tail = std::integral_constant<bool, true>;
-    const int last = (cnt - 1) & ~31;
-    Tile t0, t1;
-    fetch(0, t0);
-    int it = 0;
-    for (;;) {
-      fetch(it + 32, t1);
-      if (it == last) { compute(t0, it, Tail{}); break; }
-      compute(t0, it, Full{});
-      it += 32;
-      fetch(it + 32, t0);
-      if (it == last) { compute(t1, it, Tail{}); break; }
-      compute(t1, it, Full{});
-      it += 32;
+
+    // slot j of the ring always holds a step of parity j, so every unrolled
+    // slot knows its kind at compile time
+    using KStep = std::integral_constant<bool, true>;
+    using VStep = std::integral_constant<bool, false>;
+    Tile ring[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing - 1; ++j) {
+      if (j % 2 == 0) fetch(KStep{}, j, ring[j]);
+      else fetch(VStep{}, j, ring[j]);
     }
+    for (int step = 0; step < nstep; step += kRing) {
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) {
+        if (step + j < nstep) {
+          if ((j + kRing - 1) % 2 == 0) fetch(KStep{}, step + j + kRing - 1, ring[(j + kRing - 1) % kRing]);
+          else fetch(VStep{}, step + j + kRing - 1, ring[(j + kRing - 1) % kRing]);
+          if (j % 2 == 0) compute1(ring[j], 16 * (step + j));
+          else compute2(ring[j]);
+        }
+      }
+    }
+    // l: sum over the lanes of each head (all rows, columns h, h+G, ...)
     l_col = rows_sum(l_col);
-    vm_col = rows_sum(vm_col);
+    if constexpr (G < 16) l_col += row_ror<G>(l_col);
+    if constexpr (2 * G < 16) l_col += row_ror<2 * G>(l_col);
+    if constexpr (4 * G < 16) l_col += row_ror<4 * G>(l_col);
+    if constexpr (8 * G < 16) l_col += row_ror<8 * G>(l_col);
+    vm1 = rows_sum(vm1);
+    vm2 = rows_sum(vm2);
   }
 
-  // ---- this wave's (m, l, o) into LDS
+  // ---- this wave's (m, l, o) into LDS (o reuses the logit area)
   if (lane < G) {
     sm.m[wave][lane] = m_col;  // lane h < G has column (0, h)
     sm.l[wave][lane] = l_col;
   }
-  if (lane < 16) sm.vm[wave][lane] = vm_col;
+  // side term of row (g, h): sum_t p (V_min + 8 V_scale)
+  if (lane < 16) sm.vm[wave][lane] = fmaf(8.0f, vm2, vm1);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 4 * s + j;
-    const int g = (row / G) % S::NG, h = row % G;
-    const bool ok = row < S::NC && g == n / 4 && n < S::VD && cnt > 0;
+    const int g = (row / G) % NG, h = row % G;
+    const bool ok = row < NC && g == n / 4 && n < VD && cnt > 0;
     if (ok) {
-      const float vmin = sm.vm[wave][g * G + h];
+      // channel 8n + m: sum p V_scale c, with c entering as c * 2^-24 (m even)
+      // or c * 2^-20 (m odd); minus 8 sum p V_scale re-centres the codes
+      const float side = sm.vm[wave][g * G + h] - 8.0f * acc_one[j];
 #pragma unroll
       for (int m = 0; m < 8; ++m)
-        sm.o[wave][h][8 * n + m] = (acc[m][j] - acc_off[j]) * 0.0625f + vmin;
+        wv.lo.o[h][8 * n + m] = fmaf(acc[m][j], (m & 1) ? 1048576.0f : 16777216.0f, side);
     }
   }
   if (cnt == 0) {
-    for (int i = lane; i < G * D; i += 64) sm.o[wave][i / D][i % D] = 0.0f;
+    for (int i = lane; i < G * D; i += 64) wv.lo.o[i / D][i % D] = 0.0f;
   }
 }
 
@@ -585,7 +676,7 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) sm.o[wave][h][lane * CPL + c] = o[h][c];
+    for (int c = 0; c < CPL; ++c) sm.u.i8.o[wave][h][lane * CPL + c] = o[h][c];
 }
 
 // ------------------------------------------------------------------ merge
@@ -607,6 +698,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   const int np = p.nsplit + 1;
   const float* parts = p.parts + ((size_t)b * p.hkv + kvh) * np * G * (2 + D) + (size_t)h * (2 + D);
   const size_t pstride = (size_t)G * (2 + D);
+  // this thread's first kPre float4 slices of the partial outputs, issued
+  // together with the (m, l) loads
+  constexpr int kPre = 128 / R;
+  float4v pre[kPre];
+  {
+    const int c4 = tid % NF, r = tid / NF;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      const int j = r + i * R;
+      const int jj = j < np ? j : np - 1;
+      pre[i] = *reinterpret_cast<const float4v*>(parts + jj * pstride + 2 + 4 * c4);
+    }
+  }
   float mj = -INFINITY, lj = 0.0f;
   if (tid < np) {
     const float2v ml = *reinterpret_cast<const float2v*>(parts + tid * pstride);
@@ -634,11 +738,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   for (int w = 0; w < kThreads / 64; ++w) den += red[w][1];
   const int c4 = tid % NF, r = tid / NF;
   float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-  for (int j = r; j < np; j += R) {
-    const float w = wts[j];
-    if (w != 0.0f) acc += w * *reinterpret_cast<const float4v*>(parts + j * pstride + 2 + 4 * c4);
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int j = r + i * R;
+    if (j < np) acc += wts[j] * pre[i];
   }
+  // every partial is written by the attention kernel, so no load is skipped
+  for (int j = r + kPre * R; j < np; j += R)
+    acc += wts[j] * *reinterpret_cast<const float4v*>(parts + j * pstride + 2 + 4 * c4);
   part_acc[tid] = acc;
   __syncthreads();
   if (r == 0) {
@@ -652,16 +759,21 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
 }
 
 template <int D, int G, bool QBF16>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void attention_kernel(AttnParams p) {
   __shared__ Smem<D, G> sm;
   // blockIdx.x: split (nsplit = INT8 region), blockIdx.y: kv head, blockIdx.z: sequence
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  if (split < p.nsplit) int4_chunk<D, G, QBF16>(p, sm, b, kvh, split);
-  else int8_region<D, G, QBF16>(p, sm, b, kvh);
-  __syncthreads();
   const int np = p.nsplit + 1;
   float* dst = p.parts + (((size_t)b * p.hkv + kvh) * np + split) * G * (2 + D);
-  store_partial<D, G>(p, sm, dst);
+  if (split < p.nsplit) {
+    int4_chunk<D, G, QBF16>(p, sm, b, kvh, split);
+    __syncthreads();
+    store_partial<D, G>(sm, [&](int w) { return &sm.u.w4[w].lo.o[0][0]; }, dst);
+  } else {
+    int8_region<D, G, QBF16>(p, sm, b, kvh);
+    __syncthreads();
+    store_partial<D, G>(sm, [&](int w) { return &sm.u.i8.o[w][0][0]; }, dst);
+  }
 }
 
 template <int D, int G>

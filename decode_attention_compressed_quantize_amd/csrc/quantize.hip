@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantParams p) {
   }
   if ((hl % LPG) == 0) {
     const int g = hl / LPG;
-    uint32_t* m = reinterpret_cast<uint32_t*>(p.meta + (rec * (D / 32) + g) * 4 + (is_v ? 2 : 0));
+    uint32_t* m = reinterpret_cast<uint32_t*>(p.meta + ((rec * 2 + (is_v ? 1 : 0)) * (D / 32) + g) * 2);
     *m = (uint32_t)sh | ((uint32_t)mh << 16);
   }
 

@@ -30,8 +30,8 @@
  *   int4_codes  uint8  [P][Hkv][16][2][D/2]   per token: K codes then V codes;
  *               byte j of a K (or V) row holds code 2j in its low nibble and
  *               code 2j+1 in its high nibble.
- *   int4_meta   uint16 [P][Hkv][16][D/32][4]  IEEE fp16 bits, per group:
- *               (K scale, K min, V scale, V min).
+ *   int4_meta   uint16 [P][Hkv][16][2][D/32][2]  IEEE fp16 bits: per token, the K
+ *               groups then the V groups, each as (scale, min).
  *   int8_codes  int8   [B][Hkv][144][2][D]    per slot: K codes then V codes.
  *   int8_scales float  [B][Hkv][144][2]       per slot: (K scale, V scale).
  *               Position t lives in slot t (t < 16) or 16 + (t-16) mod 128.

@@ -28,11 +28,15 @@ def source_np(w, layer, which, b, L, kvh):
 
 
 def unpage_int4(codes, meta, table, b, kvh, L):
-    """GPU INT4 buffers -> (K codes [L][D/2], V codes [L][D/2], meta [L][D/32][4] uint16)."""
+    """GPU INT4 buffers -> (K codes [L][D/2], V codes [L][D/2], meta [L][2][D/32][2] uint16).
+
+    meta[..., 0, g, 0] is the K scale of group g, [..., 0, g, 1] the K min,
+    [..., 1, g, 0] the V scale and [..., 1, g, 1] the V min.
+    """
     npg = (L + 15) // 16
     pages = table[b, :npg]
     c = codes[pages, kvh].reshape(npg * 16, 2, codes.shape[-1])[:L]
-    m = meta[pages, kvh].reshape(npg * 16, meta.shape[-2], 4)[:L]
+    m = meta[pages, kvh].reshape(npg * 16, 2, meta.shape[-2], 2)[:L]
     return c[:, 0], c[:, 1], m.view(np.uint16)
 
 
@@ -64,10 +68,10 @@ def check_codes(w, layer, b, kvh, L, cpu):
     kc, vc, meta = unpage_int4(cpu["int4_codes"], cpu["int4_meta"], cpu["table"], b, kvh, L)
     np.testing.assert_array_equal(kc, quant.pack_nibbles(enc["k4"]), err_msg=f"K INT4 codes b={b} h={kvh}")
     np.testing.assert_array_equal(vc, quant.pack_nibbles(enc["v4"]), err_msg=f"V INT4 codes b={b} h={kvh}")
-    np.testing.assert_array_equal(meta[..., 0], enc["k4_scale"].view(np.uint16), err_msg="K scale")
-    np.testing.assert_array_equal(meta[..., 1], enc["k4_min"].view(np.uint16), err_msg="K min")
-    np.testing.assert_array_equal(meta[..., 2], enc["v4_scale"].view(np.uint16), err_msg="V scale")
-    np.testing.assert_array_equal(meta[..., 3], enc["v4_min"].view(np.uint16), err_msg="V min")
+    np.testing.assert_array_equal(meta[:, 0, :, 0], enc["k4_scale"].view(np.uint16), err_msg="K scale")
+    np.testing.assert_array_equal(meta[:, 0, :, 1], enc["k4_min"].view(np.uint16), err_msg="K min")
+    np.testing.assert_array_equal(meta[:, 1, :, 0], enc["v4_scale"].view(np.uint16), err_msg="V scale")
+    np.testing.assert_array_equal(meta[:, 1, :, 1], enc["v4_min"].view(np.uint16), err_msg="V min")
     pos, k8, v8, ks8, vs8 = int8_slot_rows(cpu["int8_codes"], cpu["int8_scales"], b, kvh, L)
     np.testing.assert_array_equal(k8, enc["k8"], err_msg="K INT8 codes")
     np.testing.assert_array_equal(v8, enc["v8"], err_msg="V INT8 codes")
