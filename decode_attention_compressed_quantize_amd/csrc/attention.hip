@@ -81,6 +81,8 @@ struct AttnParams {
   float* out;
   float* lse;
   float alpha;  // softmax scale * log2(e)
+  int batch;
+  int int8_first;  // dispatch the INT8-region workgroups before the INT4 chunks
   int hkv;
   int max_pages;
   int num_pages;
@@ -151,6 +153,22 @@ __device__ inline float rows_sum(float v) {
   return a + b;
 }
 
+// Reductions over all 64 lanes: DPP rotations within each row, then the rows.
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, row_ror<1>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<8>(v));
+  return rows_max(v);
+}
+__device__ inline float wave_sum(float v) {
+  v += row_ror<1>(v);
+  v += row_ror<2>(v);
+  v += row_ror<4>(v);
+  v += row_ror<8>(v);
+  return rows_sum(v);
+}
+
 template <bool QBF16>
 __device__ inline float load_q(const void* q, size_t off) {
   if constexpr (QBF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(q)[off] << 16);
@@ -170,17 +188,17 @@ struct Shape {
 // one tile of V codes and meta); the INT8 path overlays its own buffers.
 template <int D, int G>
 struct Smem {
-  static constexpr int kListCap = 512;  // positions per wave: chunk <= 4 * 512
+  static constexpr int kListCap = kMaxChunk / kWaves;  // positions per wave
   // Row strides padded so that the 16-lane row groups of a wave fall into
   // different LDS banks on the P.V operand reads.
   static constexpr int kLgStride = 48;    // 32 logits + 16
   static constexpr int kVStride = D / 8 + 4;
   struct Wave4 {
-    uint32_t rec[kListCap + 32];          // token-record indices, padded with copies
     union {
-      float logit[G][kLgStride];          // the current tile's logits / alpha, then p
-      float o[G][D];                      // the wave's unnormalised output
-    } lo;
+      uint32_t rec[kListCap + 32];        // token-record indices, padded with copies
+      float o[G][D];                      // the wave's unnormalised output (after the list)
+    } ro;
+    float logit[G][kLgStride];            // the current tile's logits / alpha, then p
     uint32_t vbuf[32][kVStride];          // V codes of the current 32 tokens
     uint32_t mbuf[32][D / 32];            // K or V (scale | min << 16) of the current 32 tokens
   };
@@ -198,7 +216,7 @@ struct Smem {
   float m[kWaves][G];
   float l[kWaves][G];
   float vm[kWaves][16];
-  int32_t pages[kWaves][64];
+  int32_t pages[kWaves][kListCap / kPage];
 };
 
 // Combine the four waves' (m, l, o) held in LDS into one partial and store it.
@@ -258,26 +276,53 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
   // of its column's head), loaded first so their latency overlaps the compaction.
   float qraw[NG][8];
   {
-    const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + hc) * D;
+    // the lane's D/4 query entries are contiguous: a few 16-byte loads
+    constexpr int NE = D / 4;
+    const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + hc) * D + s * NE;
+    float qe[NE];
+    if constexpr (QBF16) {
+      const u32x4* qp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + qoff);
+#pragma unroll
+      for (int i = 0; i < NE / 8; ++i) {
+        const u32x4 x = qp[i];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          qe[8 * i + 2 * k] = __uint_as_float(x[k] << 16);
+          qe[8 * i + 2 * k + 1] = __uint_as_float(x[k] & 0xFFFF0000u);
+        }
+      }
+    } else {
+      const float4v* qp = reinterpret_cast<const float4v*>(reinterpret_cast<const float*>(p.q) + qoff);
+#pragma unroll
+      for (int i = 0; i < NE / 4; ++i) {
+        const float4v x = qp[i];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qe[4 * i + k] = x[k];
+      }
+    }
     const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 #pragma unroll
     for (int m = 0; m < NG; ++m)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) qraw[m][r] = load_q<QBF16>(p.q, qoff + s * (D / 4) + 8 * m + perm[r]);
+      for (int r = 0; r < 8; ++r) qraw[m][r] = qe[8 * m + perm[r]];
   }
 
   // ---- compact the kept positions of this wave's range into an LDS list
-  uint32_t* list = wv.rec;
+  uint32_t* list = wv.ro.rec;
   int cnt = 0;
   {
     const uint32_t* mrow = p.mask + ((size_t)b * p.hkv + kvh) * p.words;
     const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-    // one load for the range's mask words (<= 12) and one for its pages (<= 24)
+    // one load for the range's mask words (<= 64) and two for its pages (<= 128)
     uint32_t myword = 0;
-    int32_t mypage = -1;
     if (lane < q4 / 32 && w0 + 32 * lane < hi) myword = mrow[(w0 >> 5) + lane];
-    if (lane < q4 / 16 && w0 + 16 * lane < hi) mypage = bt[(w0 >> 4) + lane];
-    sm.pages[wave][lane] = mypage;
+#pragma unroll
+    for (int i = 0; i < Smem<D, G>::kListCap / kPage / 64; ++i) {
+      const int j = lane + 64 * i;
+      int32_t pg = -1;
+      if (j < q4 / 16 && w0 + 16 * j < hi) pg = bt[(w0 >> 4) + j];
+      sm.pages[wave][j] = pg;
+    }
     __builtin_amdgcn_wave_barrier();
     for (int r = 0; w0 + 64 * r < hi; ++r) {
       const uint32_t wlo = __builtin_amdgcn_readlane(myword, 2 * r);
@@ -435,8 +480,8 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       if (n < G) {
         const float4v lo4 = {sv[0], sv[1], sv[2], sv[3]};
         const float4v hi4 = {sv[4], sv[5], sv[6], sv[7]};
-        *reinterpret_cast<float4v*>(&wv.lo.logit[n][4 * s]) = lo4;
-        *reinterpret_cast<float4v*>(&wv.lo.logit[n][16 + 4 * s]) = hi4;
+        *reinterpret_cast<float4v*>(&wv.logit[n][4 * s]) = lo4;
+        *reinterpret_cast<float4v*>(&wv.logit[n][16 + 4 * s]) = hi4;
       }
       // every tile holds at least one kept token, so the new max is finite
       // (m_col is in log2 units, alpha > 0)
@@ -467,17 +512,17 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       const int lim = cnt - it;  // tokens of this tile below lim are real
       if constexpr (G == 4) {
         const int k2 = 2 * (4 * s + n / 4);
-        float2v lg = *reinterpret_cast<const float2v*>(&wv.lo.logit[hc][k2]);
+        float2v lg = *reinterpret_cast<const float2v*>(&wv.logit[hc][k2]);
         lg[0] = k2 < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, lg[0], -m_col)) : 0.0f;
         lg[1] = k2 + 1 < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, lg[1], -m_col)) : 0.0f;
         l_col += lg[0] + lg[1];
-        *reinterpret_cast<float2v*>(&wv.lo.logit[hc][k2]) = lg;
+        *reinterpret_cast<float2v*>(&wv.logit[hc][k2]) = lg;
       } else {
         const int k = G == 2 ? 8 * s + n / 2 : 16 * s + n;
         if (k < 32) {
-          const float pr = k < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, wv.lo.logit[hc][k], -m_col)) : 0.0f;
+          const float pr = k < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, wv.logit[hc][k], -m_col)) : 0.0f;
           l_col += pr;
-          wv.lo.logit[hc][k] = pr;
+          wv.logit[hc][k] = pr;
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -493,8 +538,8 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
 #pragma unroll
       for (int m = 0; m < MH; ++m) wv.mbuf[tl][hf * MH + m] = t.mh[m];
       __builtin_amdgcn_wave_barrier();
-      const float4v pv0 = *reinterpret_cast<const float4v*>(&wv.lo.logit[hc][4 * s]);
-      const float4v pv1 = *reinterpret_cast<const float4v*>(&wv.lo.logit[hc][16 + 4 * s]);
+      const float4v pv0 = *reinterpret_cast<const float4v*>(&wv.logit[hc][4 * s]);
+      const float4v pv1 = *reinterpret_cast<const float4v*>(&wv.logit[hc][16 + 4 * s]);
       uint32_t vd[8];
       float pp[8];
 #pragma unroll
@@ -563,7 +608,7 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
     vm2 = rows_sum(vm2);
   }
 
-  // ---- this wave's (m, l, o) into LDS (o reuses the logit area)
+  // ---- this wave's (m, l, o) into LDS (o reuses the list area)
   if (lane < G) {
     sm.m[wave][lane] = m_col;  // lane h < G has column (0, h)
     sm.l[wave][lane] = l_col;
@@ -583,78 +628,80 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       const float side = sm.vm[wave][g * G + h] - 8.0f * acc_one[j];
 #pragma unroll
       for (int m = 0; m < 8; ++m)
-        wv.lo.o[h][8 * n + m] = fmaf(acc[m][j], (m & 1) ? 1048576.0f : 16777216.0f, side);
+        wv.ro.o[h][8 * n + m] = fmaf(acc[m][j], (m & 1) ? 1048576.0f : 16777216.0f, side);
     }
   }
   if (cnt == 0) {
-    for (int i = lane; i < G * D; i += 64) wv.lo.o[i / D][i % D] = 0.0f;
+    for (int i = lane; i < G * D; i += 64) wv.ro.o[i / D][i % D] = 0.0f;
   }
 }
 
 // ------------------------------------------------------------------ INT8 region
 // The <= 144 protected positions of one (sequence, kv head) in float32: each
-// wave takes 36 positions, lane = token for the logits, lane = channels for P.V.
+// wave takes 36 slots, lane = slot for the logits, lane = channels for P.V.
+// Which slots hold attended positions follows from L alone: all 144 when
+// L >= 144, else exactly slots [0, L) (slot = position below 144). So every
+// slot's codes and scales are loaded at once, together with the query and the
+// length, and masked afterwards; the region's sums do not depend on order.
 template <int D, int G, bool QBF16>
 __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh) {
   constexpr int CPL = D / 64;
+  constexpr int NW = D / 16;  // 16-byte words per K (or V) row
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
-  const int ns = L < kSink ? L : kSink;
-  const int rr0 = L - kRecent > kSink ? L - kRecent : kSink;
-  const int nr = L > rr0 ? L - rr0 : 0;
-  const int n8 = ns + nr;
+  const int slot = wave * 36 + lane;
+  const bool inr = lane < 36;
+  const size_t base = ((size_t)b * p.hkv + kvh) * kInt8Slots;
+  u32x4 kw[NW];
+  float2v sc = {0.0f, 0.0f};
+  if (inr) {
+    const u32x4* row = reinterpret_cast<const u32x4*>(p.codes8 + (base + slot) * 2 * D);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) kw[i] = row[i];
+    u32x4 vw[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) vw[i] = row[NW + i];
+    sc = *reinterpret_cast<const float2v*>(p.scales8 + (base + slot) * 2);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) *reinterpret_cast<u32x4*>(&sm.u.i8.vcode[wave][lane][16 * i]) = vw[i];
+  }
   for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int h = i / D, d = i % D;
     sm.u.i8.q[h][d] = load_q<QBF16>(p.q, ((size_t)b * p.hkv * G + kvh * G + h) * D + d) * p.alpha;
   }
+  int L = p.seq_lens[b];
+  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+  const int nvalid = L < kInt8Slots ? L : kInt8Slots;
+  const int cntw = nvalid - wave * 36 < 0 ? 0 : (nvalid - wave * 36 > 36 ? 36 : nvalid - wave * 36);
+  const bool valid = lane < cntw;
   __syncthreads();
-  const int i0 = wave * 36;
-  const int cntw = n8 - i0 < 0 ? 0 : (n8 - i0 > 36 ? 36 : n8 - i0);
-  const size_t base = ((size_t)b * p.hkv + kvh) * kInt8Slots;
   float s[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) s[h] = -INFINITY;
-  const bool valid = lane < cntw;
   if (valid) {
-    const int idx = i0 + lane;
-    const int pos = idx < ns ? idx : rr0 + (idx - ns);
-    const int slot = pos < kSink ? pos : kSink + (pos - kSink) % kRecent;
-    const int8_t* kc = p.codes8 + (base + slot) * 2 * D;
-    const float ks = p.scales8[(base + slot) * 2 + 0];
-    const float vs = p.scales8[(base + slot) * 2 + 1];
     float dot[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) dot[h] = 0.0f;
-    for (int d0 = 0; d0 < D; d0 += 16) {
-      const u32x4 w4 = *reinterpret_cast<const u32x4*>(kc + d0);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const float c = (float)(int8_t)(w4[k / 4] >> (8 * (k % 4)));
+        const float c = (float)(int8_t)(kw[i][k / 4] >> (8 * (k % 4)));
 #pragma unroll
-        for (int h = 0; h < G; ++h) dot[h] = fmaf(sm.u.i8.q[h][d0 + k], c, dot[h]);
+        for (int h = 0; h < G; ++h) dot[h] = fmaf(sm.u.i8.q[h][16 * i + k], c, dot[h]);
       }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = ks * dot[h];
-    for (int d0 = 0; d0 < D; d0 += 16)
-      *reinterpret_cast<u32x4*>(&sm.u.i8.vcode[wave][lane][d0]) = *reinterpret_cast<const u32x4*>(kc + D + d0);
-    sm.u.i8.vscale[wave][lane] = vs;
+    for (int h = 0; h < G; ++h) s[h] = sc[0] * dot[h];
   }
   float m[G], l[G], o[G][CPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float mx = s[h];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mx = wave_max(s[h]);
     m[h] = mx;
     const float pr = valid ? __builtin_amdgcn_exp2f(s[h] - mx) : 0.0f;
-    float sum = pr;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    l[h] = sum;
-    if (lane < 36) sm.u.i8.p[wave][h][lane] = pr * (valid ? sm.u.i8.vscale[wave][lane] : 0.0f);
+    l[h] = wave_sum(pr);
+    if (lane < 36) sm.u.i8.p[wave][h][lane] = pr * sc[1];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
   }
@@ -687,7 +734,6 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
 // one (m, l) pair per thread, then D/4 float4 columns x 8 partial sums.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
-  constexpr int kMaxParts = 256;  // the host plan keeps nsplit + 1 <= 256
   constexpr int NF = D / 4;       // float4 columns
   constexpr int R = kThreads / NF;  // threads per column
   __shared__ float wts[kMaxParts];
@@ -761,14 +807,33 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
 template <int D, int G, bool QBF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void attention_kernel(AttnParams p) {
   __shared__ Smem<D, G> sm;
-  // blockIdx.x: split (nsplit = INT8 region), blockIdx.y: kv head, blockIdx.z: sequence
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // One-dimensional grid, dispatched in index order and spread round-robin
+  // over the 8 XCDs. The INT8 regions take `pairs` consecutive items, before
+  // (int8_first) or after the INT4 chunks; INT4 item j is chunk j / pairs of
+  // pair j % pairs (chunk-major: the first, fullest chunks of every sequence
+  // go first, and each XCD gets every 8th pair of every chunk index, i.e. the
+  // same mix of sequence lengths). Pair = b * Hkv + kvh. Partial index: INT4
+  // chunk j at j, the INT8 region at nsplit.
+  const int pairs = p.hkv * p.batch;
+  const int n4 = pairs * p.nsplit;
+  const int item = blockIdx.x;
+  const int i8 = p.int8_first ? item : item - n4;         // INT8 item index if >= 0
+  const int i4 = p.int8_first ? item - pairs : item;      // INT4 item index
+  int pair, split;
+  if (i8 >= 0 && i8 < pairs) {
+    pair = i8;
+    split = p.nsplit;
+  } else {
+    pair = i4 % pairs;
+    split = i4 / pairs;
+  }
+  const int kvh = pair % p.hkv, b = pair / p.hkv;
   const int np = p.nsplit + 1;
   float* dst = p.parts + (((size_t)b * p.hkv + kvh) * np + split) * G * (2 + D);
   if (split < p.nsplit) {
     int4_chunk<D, G, QBF16>(p, sm, b, kvh, split);
     __syncthreads();
-    store_partial<D, G>(sm, [&](int w) { return &sm.u.w4[w].lo.o[0][0]; }, dst);
+    store_partial<D, G>(sm, [&](int w) { return &sm.u.w4[w].ro.o[0][0]; }, dst);
   } else {
     int8_region<D, G, QBF16>(p, sm, b, kvh);
     __syncthreads();
@@ -778,7 +843,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
 template <int D, int G>
 hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, hipStream_t s) {
-  const dim3 grid(p.nsplit + 1, c.num_kv_heads, c.batch);
+  const dim3 grid((unsigned)(p.nsplit + 1) * c.num_kv_heads * c.batch);
   if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true>), grid, dim3(kThreads), 0, s, p);
   else hipLaunchKernelGGL((attention_kernel<D, G, false>), grid, dim3(kThreads), 0, s, p);
   hipLaunchKernelGGL((merge_kernel<D, G>), dim3(G, c.num_kv_heads, c.batch), dim3(kThreads), 0, s, p);
@@ -804,12 +869,14 @@ hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype
   p.lse = lse;
   p.alpha = softmax_scale * kLog2e;
   p.hkv = c.num_kv_heads;
+  p.batch = c.batch;
   p.max_pages = c.max_pages_per_seq;
   p.num_pages = c.num_phys_pages;
   p.max_ctx = c.max_ctx;
   p.words = mask_words(c.max_ctx);
   p.chunk = plan.chunk;
   p.nsplit = plan.nsplit;
+  p.int8_first = plan.int8_first;
   const int G = num_q_heads / c.num_kv_heads;
   const bool bf = q_dtype == KVC_BF16;
   if (c.head_dim == 128) {

@@ -1,6 +1,7 @@
 // libkvc host layer: argument validation, split planning, workspace sizing
 // and kernel launches behind the C ABI declared in include/kvc.h.
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 
@@ -23,6 +24,8 @@ enum Need : unsigned {
   kNeedScores = 8u,
 };
 
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
 kvc_status check_cache(const kvc_cache* c, unsigned need) {
   if (!c) return fail(KVC_E_NULL, "cache descriptor is NULL");
   if (c->batch < 1 || c->num_kv_heads < 1 || c->max_ctx < 1 || c->num_phys_pages < 1)
@@ -42,6 +45,10 @@ kvc_status check_cache(const kvc_cache* c, unsigned need) {
     return fail(KVC_E_NULL, "int8_codes or int8_scales is NULL");
   if ((need & kNeedMask) && !c->keep_mask) return fail(KVC_E_NULL, "keep_mask is NULL");
   if ((need & kNeedScores) && !c->scores) return fail(KVC_E_NULL, "scores is NULL");
+  const void* ptrs[] = {c->int4_codes, c->int4_meta, c->int8_codes, c->int8_scales, c->keep_mask,
+                        c->scores};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return fail(KVC_E_UNSUPPORTED, "cache arrays must be 16-byte aligned");
   return KVC_OK;
 }
 
@@ -69,17 +76,26 @@ namespace kvc {
 AttnPlan plan_attention(const kvc_cache& c, int num_q_heads) {
   (void)num_q_heads;
   // INT4 chunk j covers positions [j*chunk, (j+1)*chunk) of the INT4 region
-  // [16, max_ctx - 128). Aim for about 1536 chunk workgroups (4 waves each)
-  // over the batch, with chunks of 1024..2048 positions.
+  // [16, max_ctx - 128). Aim for about two resident rounds of chunk
+  // workgroups (three 4-wave workgroups per CU on 256 CUs): long lists keep
+  // each workgroup's load pipeline full and pay its set-up (mask and
+  // block-table loads, compaction) rarely, while the second round evens out
+  // the finish times. The short INT8-region workgroups go first when they
+  // fit in one round, else after the chunks.
+  constexpr long long kResident = 768;
   const long long end4 = c.max_ctx > kInt8Slots ? (long long)c.max_ctx - kRecent : 0;
   const long long pairs = (long long)c.batch * c.num_kv_heads;
-  long long chunk = (pairs * end4 + 1535) / 1536;
+  const long long target = 2 * kResident;
+  long long chunk = (pairs * end4 + target - 1) / target;
+  const long long fit = (end4 + kMaxParts - 2) / (kMaxParts - 1);  // nsplit + 1 <= kMaxParts
+  if (chunk < fit) chunk = fit;
   chunk = (chunk + 255) / 256 * 256;
   if (chunk < 1024) chunk = 1024;
-  if (chunk > 2048) chunk = 2048;
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
   AttnPlan p;
   p.chunk = (int)chunk;
   p.nsplit = end4 > 0 ? (int)((end4 + chunk - 1) / chunk) : 1;
+  p.int8_first = pairs <= kResident ? 1 : 0;
   return p;
 }
 
@@ -152,6 +168,8 @@ KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_d
   kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8 | kNeedMask);
   if (st != KVC_OK) return st;
   if (!q || !out) return fail(KVC_E_NULL, "q or out is NULL");
+  if (misaligned(q) || misaligned(out) || misaligned(ws))
+    return fail(KVC_E_UNSUPPORTED, "q, out and ws must be 16-byte aligned");
   if (q_dtype != KVC_BF16 && q_dtype != KVC_F32)
     return fail(KVC_E_UNSUPPORTED, "q_dtype must be BF16 or F32");
   if (num_q_heads < 1 || num_q_heads % c->num_kv_heads)
@@ -159,8 +177,8 @@ KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_d
   const int G = num_q_heads / c->num_kv_heads;
   if (G > 4 || (G & (G - 1)))
     return fail(KVC_E_UNSUPPORTED, "num_q_heads/num_kv_heads must be 1, 2 or 4");
-  if ((long long)c->max_ctx > 255LL * 2048 + kvc::kRecent)
-    return fail(KVC_E_UNSUPPORTED, "max_ctx above 522368 positions is not supported");
+  if ((long long)c->max_ctx > (long long)(kvc::kMaxParts - 1) * kvc::kMaxChunk + kvc::kRecent)
+    return fail(KVC_E_UNSUPPORTED, "max_ctx above 2089088 positions is not supported");
   const kvc::AttnPlan plan = kvc::plan_attention(*c, num_q_heads);
   const size_t need = kvc::attention_ws_floats(*c, num_q_heads, plan) * sizeof(float);
   if (!ws || ws_bytes < need) return fail(KVC_E_WORKSPACE, "attention workspace too small");

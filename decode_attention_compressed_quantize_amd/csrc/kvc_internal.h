@@ -21,9 +21,12 @@ __host__ __device__ inline int mlp_floats(int head_dim) { return kHidden * 2 * h
 __host__ __device__ inline int mask_words(int max_ctx) { return (max_ctx + 31) / 32; }
 
 // How the INT4 region is cut into split-KV chunks for one attention call.
+constexpr int kMaxChunk = 8192;  // positions per chunk workgroup (4 waves x 2048)
+constexpr int kMaxParts = 256;   // partials per (sequence, kv head) the merge accepts
 struct AttnPlan {
-  int chunk;   // positions per INT4 chunk (multiple of 256, at most 2048)
+  int chunk;   // positions per INT4 chunk (multiple of 256, 1024 .. kMaxChunk)
   int nsplit;  // INT4 chunks per (sequence, kv head); partial index nsplit is the INT8 region
+  int int8_first;  // dispatch order: INT8-region workgroups before (1) or after (0) the chunks
 };
 
 AttnPlan plan_attention(const kvc_cache& c, int num_q_heads);

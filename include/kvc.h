@@ -52,6 +52,8 @@
  * Conventions: every call is enqueued on the caller's stream and never
  * synchronises; argument errors are returned synchronously; kernels never
  * allocate; the library keeps no state besides a thread-local error string.
+ * The cache arrays and the q, out and ws buffers of attention must be 16-byte
+ * aligned (device allocations are); a misaligned one gives KVC_E_UNSUPPORTED.
  * Device contents (lengths, table entries) are trusted: out-of-range page ids
  * or lengths are skipped by the kernels rather than dereferenced, which leaves
  * the affected outputs unspecified.
@@ -93,7 +95,7 @@ typedef struct kvc_cache {
   int32_t n_sink;            /* must be 16 */
   int32_t n_recent;          /* must be 128 */
   int32_t group;             /* must be 32 */
-  int32_t max_ctx;           /* capacity in positions, >= 1 (attention: <= 522368) */
+  int32_t max_ctx;           /* capacity in positions, >= 1 (attention: <= 2089088) */
   uint8_t* int4_codes;
   uint16_t* int4_meta;
   int8_t* int8_codes;

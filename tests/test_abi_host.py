@@ -79,6 +79,10 @@ def test_attention_argument_errors(lib):
     assert attn(lib, desc(), hq=64) == -3          # G = 8 is not supported
     assert attn(lib, desc(), hq=24) == -3          # G = 3 is not supported
     assert attn(lib, desc(head_dim=64), hq=64) == -3
+    assert attn(lib, desc(), q=FAKE + 2) == -3     # 16-byte alignment is required
+    assert attn(lib, desc(), out=FAKE + 4) == -3
+    assert attn(lib, desc(int4_codes=FAKE + 8)) == -3
+    assert "aligned" in kvc.kvc_last_error()
     assert attn(lib, desc(), ws=None) == -4
     assert attn(lib, desc(), ws_bytes=16) == -4
     assert "workspace" in kvc.kvc_last_error()
@@ -103,9 +107,9 @@ def test_append_and_topk_argument_errors(lib):
 
 
 def test_workspace_size_covers_every_split(lib):
-    # (m, l, o[D]) per query head for every INT4 chunk of at most 2048
-    # positions plus the INT8 partial
-    for max_ctx in (1, 144, 145, 4096, 131072):
+    # (m, l, o[D]) per query head for every INT4 chunk of at most 8192
+    # positions plus the INT8 partial, and at most 256 partials
+    for max_ctx in (1, 144, 145, 4096, 131072, 2089088):
         c = desc(max_ctx=max_ctx, max_pages_per_seq=(max_ctx + 15) // 16)
         n = lib.kvc_attention_workspace_bytes(ctypes.byref(c), 32)
         counters = 0
@@ -114,6 +118,7 @@ def test_workspace_size_covers_every_split(lib):
         nparts = (n - counters) // per_split
         assert nparts >= 2
         end4 = max(0, max_ctx - 128) if max_ctx > 144 else 0
-        assert (nparts - 1) * 2048 >= end4
+        assert (nparts - 1) * 8192 >= end4
+        assert nparts <= 256
     assert lib.kvc_attention_workspace_bytes(ctypes.byref(desc(head_dim=96)), 32) == 0
     assert lib.kvc_topk_workspace_bytes(ctypes.byref(desc())) == 0
