@@ -234,6 +234,7 @@ def main():
             lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev)
             mlp = getattr(lc, "mlp", None)
             per.append({"k": ks, "v": vs, "q": qs, "out": out, "lse": lse, "ws": lc.workspace(),
+                        "topk": kvc.topk_workspace(lc.cache),
                         "mlp": mlp, "one": torch.ones(w.batch, dtype=torch.int32, device=dev),
                         "lens": lc.lengths.astype(np.int64).copy(), "n": 0})
         inputs.append(per)
@@ -254,9 +255,10 @@ def main():
             w = lc.w
             budget = 1000 if w.mask == "all" else w.budget_permille
             if w.mask == "mlp":
-                kvc.kvc_score_topk_mask(lc.cache, st["mlp"], st["k"][s], st["v"][s], st["one"], budget)
+                kvc.kvc_score_topk_mask(lc.cache, st["mlp"], st["k"][s], st["v"][s], st["one"], budget,
+                                        ws=st["topk"])
             else:
-                kvc.kvc_score_topk_mask(lc.cache, None, None, None, None, budget)
+                kvc.kvc_score_topk_mask(lc.cache, None, None, None, None, budget, ws=st["topk"])
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)

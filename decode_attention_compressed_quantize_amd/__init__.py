@@ -200,7 +200,10 @@ def kvc_quantize_append(cache: Cache, k_new, v_new, n_new, stream=None):
 
 def kvc_score_topk_mask(cache: Cache, mlp, k_new, v_new, n_new, budget_permille: int,
                         ws=None, stream=None):
-    """Score appended tokens with the per-head MLP (if ``mlp`` is given) and refresh the keep mask."""
+    """Score appended tokens with the per-head MLP (if ``mlp`` is given) and refresh the keep mask.
+
+    ``ws`` is None or a refresh state from :func:`topk_workspace`, kept by the
+    caller for this cache from call to call."""
     n_max = 0 if k_new is None else k_new.shape[1]
     src = KVC_BF16 if k_new is None else _dtype_code(k_new)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -215,6 +218,14 @@ def kvc_decode_attention(cache: Cache, q, out, lse, ws, softmax_scale: float = 0
     _check(lib().kvc_decode_attention(cache.ref(), _ptr(q), _dtype_code(q), q.shape[1],
                                       float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), nbytes,
                                       _stream(stream)), "kvc_decode_attention")
+
+
+def topk_workspace(cache: Cache, device="cuda"):
+    """Allocate a zero-filled top-k refresh state for ``cache`` (see kvc_score_topk_mask)."""
+    import torch
+
+    n = kvc_topk_workspace_bytes(cache)
+    return torch.zeros(max(n // 4, 1), dtype=torch.int32, device=device)
 
 
 def attention_workspace(cache: Cache, num_q_heads: int, device="cuda"):

@@ -126,8 +126,8 @@ KVC_API size_t kvc_attention_workspace_bytes(const kvc_cache* c, int32_t num_q_h
 }
 
 KVC_API size_t kvc_topk_workspace_bytes(const kvc_cache* c) {
-  (void)c;
-  return 0;
+  if (check_cache(c, 0) != KVC_OK) return 0;
+  return (size_t)c->batch * c->num_kv_heads * sizeof(kvc::TopkState);
 }
 
 KVC_API kvc_status kvc_quantize_append(const kvc_cache* c, const void* k_new, const void* v_new,
@@ -145,12 +145,15 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
                                        const void* v_new, kvc_dtype src, int32_t n_new_max,
                                        const int32_t* n_new, int32_t budget_permille, void* ws,
                                        size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   kvc_status st = check_cache(c, kNeedMask | kNeedScores);
   if (st != KVC_OK) return st;
   if (budget_permille < 0 || budget_permille > 1000)
     return fail(KVC_E_SHAPE, "budget_permille must be in [0, 1000]");
+  if (ws) {
+    if (ws_bytes < (size_t)c->batch * c->num_kv_heads * sizeof(kvc::TopkState))
+      return fail(KVC_E_WORKSPACE, "top-k workspace too small");
+    if (misaligned(ws)) return fail(KVC_E_UNSUPPORTED, "ws must be 16-byte aligned");
+  }
   if (mlp) {
     st = check_append(k_new, v_new, src, n_new_max, n_new);
     if (st != KVC_OK) return st;
@@ -159,7 +162,10 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
       if (st != KVC_OK) return st;
     }
   }
-  return launched(kvc::launch_topk(*c, budget_permille, stream));
+  // The incremental update relies on every score below the previous length
+  // being unchanged, which holds when this call writes the new scores itself.
+  return launched(kvc::launch_topk(*c, budget_permille, static_cast<kvc::TopkState*>(ws),
+                                   mlp != nullptr, stream));
 }
 
 KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_dtype q_dtype,

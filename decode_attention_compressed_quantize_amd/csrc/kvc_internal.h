@@ -44,7 +44,26 @@ hipError_t launch_quantize_append(const kvc_cache& c, const void* k_new, const v
 hipError_t launch_score(const kvc_cache& c, const float* mlp, const void* k_new, const void* v_new,
                         kvc_dtype src, int n_new_max, const int32_t* n_new, hipStream_t s);
 
-hipError_t launch_topk(const kvc_cache& c, int budget_permille, hipStream_t s);
+// Keep-mask refresh state of one (sequence, kv head), kept in the caller's
+// top-k workspace between calls. Keys are composite: (order key of the score
+// << 32) | (0xFFFFFFFF - position), so larger means kept first and no two
+// keys are equal. a holds the na smallest kept keys (ascending), b the nb
+// largest keys not kept (descending); each list is exact for what it holds.
+constexpr int kTopkBuf = 64;
+constexpr uint32_t kTopkMagic = 0x4B565431u;
+struct TopkState {
+  uint32_t magic;  // kTopkMagic when valid
+  int32_t len;     // sequence length the mask and lists describe
+  int32_t k;       // kept INT4-region positions
+  int32_t budget;  // budget_permille used
+  int32_t na, nb;
+  int32_t pad[2];
+  uint64_t a[kTopkBuf];
+  uint64_t b[kTopkBuf];
+};
+
+hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state, bool incremental,
+                       hipStream_t s);
 
 hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype, int num_q_heads,
                             float softmax_scale, float* out, float* lse, float* ws,

@@ -17,8 +17,12 @@
 // k-th key T and how many keys equal to T must be kept; a final in-order pass
 // keeps every key > T and the lowest-position keys == T, which is the unique
 // answer under "score descending, then position ascending". Scores are
-// static once written, so refreshing from scratch equals any incremental
-// update.
+// static once written, so a decode step (one position joins the INT4 region,
+// k grows by at most one) changes at most two candidate bits: with a state in
+// the workspace, one wave applies the step exactly from short sorted lists of
+// the keys on either side of the threshold, and the full refresh above runs
+// only when the state does not apply (first call, new budget, several new
+// positions, caller-written scores, a list run dry).
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -107,6 +111,8 @@ struct TopkParams {
   const float* scores;
   const int32_t* seq_lens;
   uint32_t* mask;
+  TopkState* state;  // per (sequence, kv head), or null
+  int incremental;   // the caller wrote no score below the previous length
   int hkv;
   int max_ctx;
   int words;
@@ -121,12 +127,134 @@ __device__ inline uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kTopkThreads = 1024;
+// Composite key: score first, then the lower position.
+__device__ inline uint64_t comp_key(uint32_t key, int pos) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
+}
+__device__ inline int comp_pos(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
 
+constexpr int kTopkThreads = 1024;
+constexpr int kCandCap = 512;  // keys around the threshold a refresh can sort into the lists
+
+// ---- one decode step on the lists, one wave, lane i holding a[i] and b[i]
+__device__ inline uint64_t wave_at(uint64_t v, int i) {
+  return ((uint64_t)__builtin_amdgcn_readlane((int)(v >> 32), i) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)v, i);
+}
+__device__ inline uint64_t from_lane_below(uint64_t v) { return __shfl_up(v, 1); }
+__device__ inline uint64_t from_lane_above(uint64_t v) { return __shfl_down(v, 1); }
+
+// Insert x into the ascending list (a) or descending list (b) when it belongs
+// to the part the list must hold: always if the list holds its whole side,
+// else only if x falls before the list's last entry. A full list drops its
+// last entry.
+template <bool Ascending>
+__device__ inline uint64_t list_insert(uint64_t v, int& n, uint64_t x, bool whole, int lane) {
+  if (!whole) {
+    if (n == 0) return v;
+    const uint64_t last = wave_at(v, n - 1);
+    if (Ascending ? !(x < last) : !(x > last)) return v;
+  }
+  const int at = (int)__popcll(__ballot(lane < n && (Ascending ? v < x : v > x)));
+  const uint64_t below = from_lane_below(v);
+  n = n < kTopkBuf ? n + 1 : kTopkBuf;
+  return lane < at ? v : (lane == at ? x : below);
+}
+__device__ inline uint64_t list_push_front(uint64_t v, int& n, uint64_t x, int lane) {
+  const uint64_t below = from_lane_below(v);
+  n = n < kTopkBuf ? n + 1 : kTopkBuf;
+  return lane == 0 ? x : below;
+}
+__device__ inline uint64_t list_pop_front(uint64_t v, int& n) {
+  --n;
+  return from_lane_above(v);
+}
+
+// Applies one appended position (length L - 1 -> L) to the mask and the lists.
+// Returns false, having written nothing, when the state does not describe
+// length L - 1 under this budget or a list it needs has run out.
+__device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, long long k,
+                          const float* sc, uint32_t* mrow, int lane) {
+  if (L < 1 || st->magic != kTopkMagic || st->budget != p.budget || st->len != L - 1) return false;
+  const int n4p = L - 1 > kInt8Slots ? L - 1 - kInt8Slots : 0;
+  const long long kp = ((long long)p.budget * n4p) / 1000;
+  if (st->k != kp) return false;
+  int na = st->na, nb = st->nb;
+  if (na < 0 || na > kTopkBuf || nb < 0 || nb > kTopkBuf) return false;
+  uint64_t A = lane < na ? st->a[lane] : 0, B = lane < nb ? st->b[lane] : 0;
+  int clear_pos = -1, set_pos = -1;
+  if (n4 != n4p) {
+    // position kSink + n4p leaves the recent window and becomes a candidate
+    const int xpos = kSink + n4p;
+    const uint64_t x = comp_key(order_key(sc[n4p]), xpos);
+    const long long out_before = n4p - kp;  // candidates not kept
+    if (k == kp) {
+      if (k == 0) {
+        clear_pos = xpos;
+        B = list_insert<false>(B, nb, x, nb == out_before, lane);
+      } else {
+        if (na == 0) return false;
+        const uint64_t a0 = wave_at(A, 0);
+        if (x > a0) {  // x displaces the smallest kept key
+          clear_pos = comp_pos(a0);
+          const bool whole = na == k;
+          A = list_pop_front(A, na);
+          B = list_push_front(B, nb, a0, lane);
+          A = list_insert<true>(A, na, x, whole, lane);
+        } else {
+          clear_pos = xpos;
+          B = list_insert<false>(B, nb, x, nb == out_before, lane);
+        }
+      }
+    } else {  // one more kept: x or the best key not kept
+      if (out_before == 0 || (nb > 0 && x > wave_at(B, 0))) {
+        A = list_insert<true>(A, na, x, na == kp, lane);
+      } else {
+        if (nb == 0) return false;
+        const uint64_t z = wave_at(B, 0);
+        set_pos = comp_pos(z);
+        B = list_pop_front(B, nb);
+        A = list_push_front(A, na, z, lane);
+        clear_pos = xpos;
+        B = list_insert<false>(B, nb, x, nb == out_before - 1, lane);
+      }
+    }
+  }
+  if (lane == 0) {
+    // the new position is protected; then the candidate changes
+    __hip_atomic_fetch_or(&mrow[(L - 1) >> 5], 1u << ((L - 1) & 31), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+    if (set_pos >= 0)
+      __hip_atomic_fetch_or(&mrow[set_pos >> 5], 1u << (set_pos & 31), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+    if (clear_pos >= 0)
+      __hip_atomic_fetch_and(&mrow[clear_pos >> 5], ~(1u << (clear_pos & 31)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    st->len = L;
+    st->k = (int32_t)k;
+    st->na = na;
+    st->nb = nb;
+  }
+  if (lane < na) st->a[lane] = A;
+  if (lane < nb) st->b[lane] = B;
+  return true;
+}
+
+// ---- full refresh. An exact radix select over the 32-bit score keys (4
+// passes of 8 bits, MSB first) finds, for up to three ranks at once, the key
+// at that rank and how many keys equal to it lie within the rank: rank k
+// (the threshold), and with a state to fill, ranks k - 63 and k + 64, which
+// bound the keys the two lists must hold. The in-order mask pass keeps every
+// key above the threshold and the lowest positions equal to it (the unique
+// answer under "score descending, then position ascending"), and collects the
+// keys between the two outer ranks; sorted, they give the lists.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[3][256];
   __shared__ uint32_t scan[kTopkThreads / 64];
-  __shared__ uint32_t sel_digit, sel_above;
+  __shared__ uint32_t sel_digit[3], sel_above[3];
+  __shared__ uint64_t cand[kCandCap];
+  __shared__ uint32_t ncand;
+  __shared__ int done;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -139,17 +267,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   const long long k = ((long long)p.budget * n4) / 1000;
   const float* sc = p.scores + ((size_t)b * p.hkv + h) * p.max_ctx + kSink;
   uint32_t* mrow = p.mask + ((size_t)b * p.hkv + h) * p.words;
+  TopkState* st = p.state ? p.state + (size_t)b * p.hkv + h : nullptr;
 
-  // ---- radix select of the k-th largest key (only when 0 < k < n4)
-  uint32_t T = 0xFFFFFFFFu;  // threshold key; with need = 0 nothing at T is kept
-  long long need = 0;         // how many keys == T to keep (lowest positions first)
+  if (wid == 0) {
+    const bool ok = st && p.incremental && topk_step(p, st, L, n4, k, sc, mrow, lane);
+    if (lane == 0) done = ok ? 1 : 0;
+    if (lane == 0) ncand = 0;
+  }
+  __syncthreads();
+  if (done) return;
+
+  // ---- radix select: target 0 = rank k, 1 = rank k - 63, 2 = rank k + 64
   const bool all = k >= n4;
-  if (k > 0 && !all) {
-    uint32_t prefix = 0, pmask = 0;
-    long long remaining = k;
+  long long rank[3];
+  rank[0] = (k > 0 && !all) ? k : 0;
+  rank[1] = (st && k > 0) ? (k - kTopkBuf + 1 > 1 ? k - kTopkBuf + 1 : 1) : 0;
+  rank[2] = (st && k < n4) ? (k + kTopkBuf < n4 ? k + kTopkBuf : n4) : 0;
+  uint32_t prefix[3] = {0, 0, 0};
+  long long remaining[3] = {rank[0], rank[1], rank[2]};
+  if (rank[0] > 0 || rank[1] > 0 || rank[2] > 0) {
+    uint32_t pmask = 0;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+      // targets sharing a prefix share one histogram
+      int src[3];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        src[t] = t;
+        for (int u = 0; u < t; ++u)
+          if (src[t] == t && rank[u] > 0 && prefix[u] == prefix[t]) src[t] = u;
+      }
+      for (int i = tid; i < 3 * 256; i += kTopkThreads) hist[i >> 8][i & 255] = 0;
       __syncthreads();
       // 16 scores per thread per step, all loads issued before any is used
       for (int base = tid; base < n4; base += kTopkThreads * 16) {
@@ -163,52 +311,65 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
         for (int u = 0; u < 16; ++u) {
           if (base + u * kTopkThreads < n4) {
             const uint32_t key = order_key(v[u]);
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            const uint32_t dg = (key >> shift) & 255u;
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+              if (rank[t] > 0 && src[t] == t && (key & pmask) == prefix[t]) atomicAdd(&hist[t][dg], 1u);
           }
         }
       }
       __syncthreads();
-      if (wid == 0) {
-        // lane l owns bins 4l..4l+3; suffix sums from the top bin down
-        uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
-                 c3 = hist[4 * lane + 3];
-        const uint32_t s = c0 + c1 + c2 + c3;
-        uint32_t suf = s;  // inclusive suffix over lanes >= lane
+      if (wid < 3 && rank[wid] > 0) {
+        // lane l owns bins 4l..4l+3 of the target's histogram; suffix sums from the top bin down
+        const uint32_t* hh = hist[src[wid]];
+        const long long want = remaining[wid];
+        uint32_t c0 = hh[4 * lane], c1 = hh[4 * lane + 1], c2 = hh[4 * lane + 2], c3 = hh[4 * lane + 3];
+        const uint32_t s4 = c0 + c1 + c2 + c3;
+        uint32_t suf = s4;  // inclusive suffix over lanes >= lane
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const uint32_t t = __shfl_down(suf, o);
           if (lane + o < 64) suf += t;
         }
-        const uint32_t above = suf - s;  // keys in bins of higher lanes
-        if ((long long)above < remaining && remaining <= (long long)suf) {
+        const uint32_t above = suf - s4;  // keys in bins of higher lanes
+        if ((long long)above < want && want <= (long long)suf) {
           uint32_t acc = above;
           int d = 4 * lane + 3;
           const uint32_t cs[4] = {c0, c1, c2, c3};
           for (int q = 3; q >= 0; --q) {
-            if ((long long)(acc + cs[q]) >= remaining) { d = 4 * lane + q; break; }
+            if ((long long)(acc + cs[q]) >= want) { d = 4 * lane + q; break; }
             acc += cs[q];
           }
-          sel_digit = (uint32_t)d;
-          sel_above = acc;
+          sel_digit[wid] = (uint32_t)d;
+          sel_above[wid] = acc;
         }
       }
       __syncthreads();
-      const uint32_t d = sel_digit;
-      remaining -= sel_above;
-      prefix |= d << shift;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        if (rank[t] > 0) {
+          remaining[t] -= sel_above[t];
+          prefix[t] |= sel_digit[t] << shift;
+        }
+      }
       pmask |= 255u << shift;
       __syncthreads();
     }
-    T = prefix;
-    need = remaining;
   }
+  // threshold: keys > T kept, and the first `need` keys == T (in position order)
+  const uint32_t T = rank[0] > 0 ? prefix[0] : 0xFFFFFFFFu;
+  const long long need = rank[0] > 0 ? remaining[0] : 0;
+  // window of keys the lists need, and how many keys lie above it
+  const uint32_t hi = rank[1] > 0 ? prefix[1] : 0xFFFFFFFFu;
+  const uint32_t lo = rank[2] > 0 ? prefix[2] : 0u;
+  const long long above_hi = rank[1] > 0 ? rank[1] - remaining[1] : 0;
 
   // ---- in-order pass: one mask word per thread, block-wide running count of keys == T
   long long carry = 0;
   for (int w0 = 0; w0 < p.words; w0 += kTopkThreads) {
     const int w = w0 + tid;
     uint32_t gt = 0, eq = 0;  // bit masks over the word's INT4 positions
-    if (w < p.words && k > 0 && !all) {
+    if (w < p.words && n4 > 0 && (st || (k > 0 && !all))) {
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
@@ -222,6 +383,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
           const uint32_t key = order_key(v[i]);
           if (key > T) gt |= 1u << i;
           else if (key == T) eq |= 1u << i;
+          if (st && key >= lo && key <= hi) {
+            const uint32_t slot = atomicAdd(&ncand, 1u);
+            if (slot < kCandCap) cand[slot] = comp_key(key, t);
+          }
         }
       }
     }
@@ -243,8 +408,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
     }
     const long long before = carry + wave_base + (incl - cnt);
     if (w < p.words) {
-      uint32_t bits = gt;
-      if (eq) {
+      uint32_t bits = (k > 0 && !all) ? gt : 0u;
+      if (eq && k > 0 && !all) {
         long long r = before;
         for (int i = 0; i < 32; ++i) {
           if (eq & (1u << i)) {
@@ -264,6 +429,56 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
     }
     carry += tile_total;
     __syncthreads();
+  }
+  if (!st) return;
+
+  // ---- lists: sort the window (descending composite keys) and cut at rank k
+  const uint32_t nc = ncand;
+  const bool fits = nc <= kCandCap;
+  if (fits) {
+    int n2 = 1;
+    while (n2 < (int)nc) n2 <<= 1;
+    for (int i = tid; i < n2; i += kTopkThreads)
+      if (i >= (int)nc) cand[i] = 0;  // below every real key (positions < 2^32 - 1)
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < n2; i += kTopkThreads) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const bool desc = (i & size) == 0;
+            const uint64_t x = cand[i], y = cand[j];
+            if (desc ? x < y : x > y) { cand[i] = y; cand[j] = x; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  // global rank (1-based) of cand[i] is above_hi + i + 1
+  const int na = (int)(k < kTopkBuf ? k : kTopkBuf);
+  const int nb = (int)(n4 - k < kTopkBuf ? n4 - k : kTopkBuf);
+  if (wid == 0) {
+    bool ok = fits;
+    if (ok && lane < na) {
+      const long long i = k - lane - above_hi - 1;
+      if (i >= 0 && i < nc) st->a[lane] = cand[i];
+      else ok = false;
+    }
+    if (ok && lane < nb) {
+      const long long i = k + lane - above_hi;
+      if (i >= 0 && i < nc) st->b[lane] = cand[i];
+      else ok = false;
+    }
+    ok = __ballot(!ok) == 0;
+    if (lane == 0) {
+      st->len = L;
+      st->k = (int32_t)k;
+      st->budget = p.budget;
+      st->na = na;
+      st->nb = nb;
+      st->magic = ok ? kTopkMagic : 0u;
+    }
   }
 }
 
@@ -299,8 +514,11 @@ hipError_t launch_score(const kvc_cache& c, const float* mlp, const void* k_new,
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const kvc_cache& c, int budget_permille, hipStream_t s) {
+hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state, bool incremental,
+                       hipStream_t s) {
   TopkParams p;
+  p.state = state;
+  p.incremental = incremental ? 1 : 0;
   p.scores = c.scores;
   p.seq_lens = c.seq_lens;
   p.mask = c.keep_mask;

@@ -140,8 +140,16 @@ KVC_API kvc_status kvc_quantize_append(const kvc_cache* c, const void* k_new, co
  *                  n4 = max(0, L-144) and k = floor(budget*n4/1000), keeps the k
  *                  INT4-region positions with the highest score; ties keep the
  *                  lower position; NaN ranks below every number.
- *   ws, ws_bytes : device scratch of at least kvc_topk_workspace_bytes(c)
- *                  bytes (may be NULL when that is 0).
+ *   ws, ws_bytes : NULL, or refresh state of at least kvc_topk_workspace_bytes(c)
+ *                  bytes that the caller keeps for this cache from call to call
+ *                  (zero-filled before the first call). With NULL every call
+ *                  refreshes the mask from all scores. With a state, a call that
+ *                  computes the scores itself (mlp != NULL) after exactly one
+ *                  appended position since the previous call with the same
+ *                  budget updates the mask in place; otherwise it refreshes
+ *                  fully and rebuilds the state. Either way the mask is the one
+ *                  defined above. The state assumes the mask and the scores
+ *                  below the previous length were not changed by anyone else.
  */
 KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, const void* k_new,
                                        const void* v_new, kvc_dtype src, int32_t n_new_max,
@@ -169,7 +177,9 @@ KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_d
                                         int32_t num_q_heads, float softmax_scale, float* out,
                                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace sizes (host-only, no device work). Return 0 for an invalid cache. */
+/* Workspace sizes (host-only, no device work). Return 0 for an invalid cache.
+ * kvc_topk_workspace_bytes is the size of the optional refresh state of
+ * kvc_score_topk_mask: 1056 bytes per (sequence, kv head). */
 KVC_API size_t kvc_attention_workspace_bytes(const kvc_cache* c, int32_t num_q_heads);
 KVC_API size_t kvc_topk_workspace_bytes(const kvc_cache* c);
 

@@ -104,6 +104,8 @@ def test_append_and_topk_argument_errors(lib):
     assert r == -1
     r = lib.kvc_score_topk_mask(ctypes.byref(c), FAKE, None, FAKE, 0, 4, FAKE, 500, None, 0, None)
     assert r == -1
+    r = lib.kvc_score_topk_mask(ctypes.byref(c), None, None, None, 0, 0, None, 500, FAKE, 1024, None)
+    assert r == -4  # state smaller than kvc_topk_workspace_bytes
 
 
 def test_workspace_size_covers_every_split(lib):
@@ -121,4 +123,5 @@ def test_workspace_size_covers_every_split(lib):
         assert (nparts - 1) * 8192 >= end4
         assert nparts <= 256
     assert lib.kvc_attention_workspace_bytes(ctypes.byref(desc(head_dim=96)), 32) == 0
-    assert lib.kvc_topk_workspace_bytes(ctypes.byref(desc())) == 0
+    assert lib.kvc_topk_workspace_bytes(ctypes.byref(desc())) == 2 * 8 * 1056
+    assert lib.kvc_topk_workspace_bytes(ctypes.byref(desc(head_dim=96))) == 0

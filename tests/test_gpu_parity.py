@@ -194,6 +194,65 @@ def test_decode_steps_cross_window_and_budget():
                     check_pair(w, lc, cpu, qn, out, lse, b, h)
 
 
+def _decode_topk_run(w, steps, budgets, stall=None, mlp=None):
+    """Decode steps with a top-k refresh state; the keep mask is checked
+    against the oracle's top-k of the GPU's own scores after every step.
+    ``budgets[step]`` may change mid-run and ``stall`` names (step, sequence)
+    pairs that append nothing at that step; both force full refreshes."""
+    m = kvc()
+    lc = LayerCache(w)
+    if mlp is not None:  # a replacement scorer; existing scores are set to its output
+        lc.mlp.copy_(torch.from_numpy(mlp))
+        lc.cache.scores.fill_(float(mlp[0, -1]))
+    state = m.topk_workspace(lc.cache)
+    lens = lc.lengths.copy()
+    for step in range(steps):
+        budget = budgets(step)
+        n_new = np.ones(w.batch, np.int32)
+        for (s, b) in (stall or ()):
+            if s == step:
+                n_new[b] = 0
+        k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+        v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+        lens += n_new
+        lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        nn = torch.from_numpy(n_new).cuda()
+        m.kvc_quantize_append(lc.cache, k_new, v_new, nn)
+        m.kvc_score_topk_mask(lc.cache, lc.mlp, k_new, v_new, nn, budget, ws=state)
+        torch.cuda.synchronize()
+        maskw = lc.cache.keep_mask.cpu().numpy()
+        scores = lc.cache.scores.cpu().numpy()
+        for b in range(w.batch):
+            L = int(lens[b])
+            start, n4 = regions.int4_range(L)
+            for h in range(w.kv_heads):
+                bits = mask_bits(maskw[b, h], maskw.shape[-1] * 32)
+                want = policy.topk_keep(scores[b, h, start:start + n4].astype(np.float64), budget)
+                assert np.array_equal(bits[start:start + n4], want), f"step {step} b={b} h={h}"
+                assert bits[regions.int8_positions(L)].all(), f"step {step} b={b} h={h} protected"
+                assert not bits[L:].any(), f"step {step} b={b} h={h} beyond L"
+    return lc
+
+
+def test_incremental_topk_every_step():
+    """Hundreds of decode steps on the refresh state: lists drain and rebuild,
+    the budget changes once, some sequences skip steps; the mask must equal the
+    oracle's top-k after every step."""
+    w = W.WORKLOADS["fullstep"].replace(name="inc", batch=3, kv_heads=2, q_heads=8, layers=1,
+                                        ctx=2000, ctx_list=(140, 700, 2000), decode_steps=400)
+    _decode_topk_run(w, 400, lambda s: 500 if s < 300 else 200,
+                     stall=[(50, 1), (51, 1), (120, 2)])
+
+
+def test_incremental_topk_all_scores_tied():
+    """A zero scorer makes every score equal: the window around the threshold
+    overflows, so every call refreshes fully; ties keep the lowest positions."""
+    w = W.WORKLOADS["fullstep"].replace(name="ties", batch=2, kv_heads=2, q_heads=8, layers=1,
+                                        ctx=900, ctx_list=(300, 900), decode_steps=30)
+    zero = np.zeros_like(W.mlp_weights(w, 0))
+    _decode_topk_run(w, 30, lambda s: 300, mlp=zero)
+
+
 # ---------------------------------------------------------------- full sizes
 def sample_pairs(w, n, seed):
     rng = np.random.default_rng(seed)
