@@ -215,6 +215,14 @@ def main():
     reps = [layers]
     for r in range(1, replicas):
         reps.append([LayerCache(w, layer=li, device=dev, keep_sources=False) for li, w in enumerate(base)])
+    # As in a model, the layers of one batch share one lengths tensor, which the
+    # caller advances once per step.
+    for rep in reps:
+        for lc in rep[1:]:
+            assert np.array_equal(lc.lengths, rep[0].lengths)
+            lc.seq_lens = rep[0].seq_lens
+            lc.cache.seq_lens = rep[0].seq_lens
+            lc.cache.desc.seq_lens = rep[0].seq_lens.data_ptr()
     print(f"bench: {replicas} replica(s), {per_replica_bytes / 2**30:.2f} GiB each", file=sys.stderr, flush=True)
 
     # inputs for every step, resident before timing
@@ -245,12 +253,12 @@ def main():
     def step(i, record):
         r = i % replicas
         byts = 0
+        reps[r][0].seq_lens.add_(1)
         for li, lc in enumerate(reps[r]):
             st = inputs[r][li]
             s = st["n"]
             st["n"] += 1
             st["lens"] += 1
-            lc.seq_lens.add_(1)
             kvc.kvc_quantize_append(lc.cache, st["k"][s], st["v"][s], st["one"])
             w = lc.w
             budget = 1000 if w.mask == "all" else w.budget_permille
@@ -260,8 +268,7 @@ def main():
             else:
                 kvc.kvc_score_topk_mask(lc.cache, None, None, None, None, budget, ws=st["topk"])
             if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0, e1 = events.pop()
                 e0.record(stream)
             kvc.kvc_decode_attention(lc.cache, st["q"][s], st["out"], st["lse"], st["ws"])
             if record:
@@ -270,6 +277,12 @@ def main():
             byts += algorithmic_bytes(w, st["lens"], kept_counts(w, st["lens"]))
         return byts
 
+    # The attention calls of every TIME_EVERY-th timed step are bracketed by
+    # HIP events on the launch stream (an event record costs a few us of GPU
+    # time, so recording on every step would inflate the step time).
+    TIME_EVERY = 4
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps * len(names))]
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
@@ -278,7 +291,7 @@ def main():
     step_bytes = 0
     t0.record(stream)
     for i in range(args.warmup, args.warmup + args.steps):
-        step_bytes += step(i, True)
+        step_bytes += step(i, (i - args.warmup) % TIME_EVERY == 0)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
@@ -318,7 +331,8 @@ def main():
         },
         "decode_steps_per_s": round(1000.0 / ms, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "attention": {"ms_per_call": round(a_ms, 5), "GBs": round(a_gbs, 1), "per_layer": detail},
+        "attention": {"ms_per_call": round(a_ms, 5), "GBs": round(a_gbs, 1), "per_layer": detail,
+                      "timed_calls": len(attn_ms), "timed_every_nth_step": TIME_EVERY},
         "roofline": {
             "kernel": "kvc_decode_attention call: attention_kernel (INT4 chunks + INT8 region) "
                       "then merge_kernel, timed together with HIP events on the launch stream",

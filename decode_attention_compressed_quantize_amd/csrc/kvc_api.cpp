@@ -157,6 +157,10 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
   if (mlp) {
     st = check_append(k_new, v_new, src, n_new_max, n_new);
     if (st != KVC_OK) return st;
+    if (n_new_max > 0 && n_new_max <= kvc::kRecent)
+      return launched(kvc::launch_score_topk(*c, mlp, k_new, v_new, src, n_new_max, n_new,
+                                             budget_permille, static_cast<kvc::TopkState*>(ws),
+                                             stream));
     if (n_new_max > 0) {
       st = launched(kvc::launch_score(*c, mlp, k_new, v_new, src, n_new_max, n_new, stream));
       if (st != KVC_OK) return st;

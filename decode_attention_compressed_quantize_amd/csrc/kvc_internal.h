@@ -64,6 +64,10 @@ struct TopkState {
 
 hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state, bool incremental,
                        hipStream_t s);
+// Scoring and refresh in one launch; only for n_new_max <= kRecent.
+hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k_new,
+                             const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
+                             int budget_permille, TopkState* state, hipStream_t s);
 
 hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype, int num_q_heads,
                             float softmax_scale, float* out, float* lse, float* ws,

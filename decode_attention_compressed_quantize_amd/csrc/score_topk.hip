@@ -6,11 +6,9 @@
 // Shadow Mask Distillation page (arXiv 2605.06850), Figure 1 caption - the
 // eviction records the retained indices in a binary mask.
 //
-// Scoring: one wave per (kv head, run of tokens). Lane (u, half) holds row u
-// of W1 restricted to K (half 0) or V (half 1) in registers, so W1 is read
-// once per wave; each token's K||V is staged in LDS as float32 and every lane
-// takes a broadcast dot product, then the two halves and the 32 hidden units
-// are combined with shuffles.
+// Scoring: one 256-thread workgroup per (kv head, run of appended rows); each
+// thread holds an eighth of one W1 row in registers, so a decode step (one row
+// per sequence) scores every row in parallel.
 //
 // Top-k: one workgroup per (sequence, kv head). An exact radix select over
 // order-preserving 32-bit keys (4 passes of 8 bits, MSB first) finds the
@@ -40,70 +38,113 @@ struct ScoreParams {
   int hkv;
   int n_new_max;
   int max_ctx;
-  int tokens_per_wave;
-  int waves_per_head;
+  int tokens_per_group;  // appended rows (b, j) handled by one workgroup
+  int groups_per_head;
+};
+
+constexpr int kScoreThreads = 256;
+
+// Scores appended row f = b * n_new_max + j of kv head h with the 256 threads
+// gtid = 0..255 of one group. Every thread of the workgroup must call it the
+// same number of times (it holds workgroup barriers); `valid` is false for
+// rows past the end. Thread gtid owns hidden unit u = gtid / 8 and the input
+// slice part = gtid % 8 (2D/8 entries of K||V); the 8 parts of a unit are
+// summed with lane shuffles, then relu, w2 and the sum over the 32 units
+// (within each wave, then across the group's 4 waves through LDS).
+// The thread's slice of head h's scorer: W1 row u restricted to its part, b1[u], w2[u].
+template <int D>
+struct ScorerSlice {
+  float w1[2 * D / 8];
+  float b1, w2, b2;
+  __device__ void load(const ScoreParams& p, int h, int gtid) {
+    constexpr int IN = 2 * D;
+    constexpr int PART = IN / 8;
+    const int u = gtid >> 3, part = gtid & 7;
+    const float* wh = p.mlp + (size_t)h * mlp_floats(D);
+#pragma unroll
+    for (int i = 0; i < PART; i += 4) {
+      const float4 f4 = *reinterpret_cast<const float4*>(wh + (size_t)u * IN + part * PART + i);
+      w1[i] = f4.x; w1[i + 1] = f4.y; w1[i + 2] = f4.z; w1[i + 3] = f4.w;
+    }
+    b1 = wh[kHidden * IN + u];
+    w2 = wh[kHidden * IN + kHidden + u];
+    b2 = wh[kHidden * IN + 2 * kHidden];
+  }
 };
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(64) void score_kernel(ScoreParams p) {
-  __shared__ float xs[2 * D];
-  const int lane = threadIdx.x;
-  const int h = blockIdx.x / p.waves_per_head;
-  const int w = blockIdx.x % p.waves_per_head;
-  const int u = lane & 31;
-  const int half = lane >> 5;
-  const float* wh = p.mlp + (size_t)h * mlp_floats(D);
-  float w1[D];
-#pragma unroll
-  for (int i = 0; i < D; i += 4) {
-    const float4 f = *reinterpret_cast<const float4*>(wh + (size_t)u * 2 * D + half * D + i);
-    w1[i] = f.x; w1[i + 1] = f.y; w1[i + 2] = f.z; w1[i + 3] = f.w;
-  }
-  const float b1 = wh[kHidden * 2 * D + u];
-  const float w2 = wh[kHidden * 2 * D + kHidden + u];
-  const float b2 = wh[kHidden * 2 * D + 2 * kHidden];
-
+__device__ void score_row(const ScoreParams& p, const ScorerSlice<D>& m, int h, long long f, int gtid,
+                          float* xs, float* wsum) {
+  constexpr int IN = 2 * D;
+  constexpr int PART = IN / 8;
+  const int lane = gtid & 63;
+  const int part = gtid & 7;
   const long long total = (long long)p.batch * p.n_new_max;
-  const long long f0 = (long long)w * p.tokens_per_wave;
-  const long long f1 = f0 + p.tokens_per_wave < total ? f0 + p.tokens_per_wave : total;
-  for (long long f = f0; f < f1; ++f) {
-    const int b = (int)(f / p.n_new_max);
+  int b = 0, pos = -1;
+  size_t src = 0;
+  if (f < total) {
+    b = (int)(f / p.n_new_max);
     const int j = (int)(f % p.n_new_max);
     const int nn = p.n_new[b];
-    if (j >= nn) continue;
-    const int L = p.seq_lens[b];
-    const int pos = L - nn + j;
-    if (pos < 0 || pos >= p.max_ctx) continue;
-    const size_t src = (((size_t)b * p.n_new_max + j) * p.hkv + h) * D;
-    __syncthreads();
-    // stage K||V as float32: 2D values, 2D/64 per lane
-#pragma unroll
-    for (int i = lane; i < 2 * D; i += 64) {
-      const int which = i / D;
-      const int d = i % D;
-      const void* base = which ? p.v_new : p.k_new;
+    if (j < nn) {
+      pos = p.seq_lens[b] - nn + j;
+      if (pos >= p.max_ctx) pos = -1;
+      src = (((size_t)b * p.n_new_max + j) * p.hkv + h) * D;
+    }
+  }
+  const bool valid = pos >= 0;
+  __syncthreads();  // xs and wsum of the previous row are consumed
+  if (valid) {
+    for (int i = gtid; i < IN; i += kScoreThreads) {
+      const void* base = i < D ? p.k_new : p.v_new;
+      const int d = i < D ? i : i - D;
       float v;
       if constexpr (BF16) v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[src + d] << 16);
       else v = reinterpret_cast<const float*>(base)[src + d];
       xs[i] = v;
     }
-    __syncthreads();
-    float acc = 0.0f;
-    const float* xh = xs + half * D;
-#pragma unroll
-    for (int i = 0; i < D; i += 4) {
-      const float4 x4 = *reinterpret_cast<const float4*>(xh + i);
-      acc = fmaf(w1[i], x4.x, acc);
-      acc = fmaf(w1[i + 1], x4.y, acc);
-      acc = fmaf(w1[i + 2], x4.z, acc);
-      acc = fmaf(w1[i + 3], x4.w, acc);
-    }
-    acc += __shfl_xor(acc, 32);
-    float hv = fmaxf(acc + b1, 0.0f) * w2;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) hv += __shfl_xor(hv, o);
-    if (lane == 0) p.scores[((size_t)b * p.hkv + h) * p.max_ctx + pos] = hv + b2;
   }
+  __syncthreads();
+  float acc = 0.0f;
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < PART; i += 4) {
+      const float4 x4 = *reinterpret_cast<const float4*>(xs + part * PART + i);
+      acc = fmaf(m.w1[i], x4.x, acc);
+      acc = fmaf(m.w1[i + 1], x4.y, acc);
+      acc = fmaf(m.w1[i + 2], x4.z, acc);
+      acc = fmaf(m.w1[i + 3], x4.w, acc);
+    }
+  }
+  // the 8 parts of unit u sit in 8 consecutive lanes
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  float hv = part == 0 ? fmaxf(acc + m.b1, 0.0f) * m.w2 : 0.0f;
+  // 8 units per wave, then the 4 waves
+#pragma unroll
+  for (int o = 8; o < 64; o <<= 1) hv += __shfl_xor(hv, o);
+  if (lane == 0) wsum[gtid >> 6] = hv;
+  __syncthreads();
+  if (valid && gtid == 0) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kScoreThreads / 64; ++w) sum += wsum[w];
+    p.scores[((size_t)b * p.hkv + h) * p.max_ctx + pos] = sum + m.b2;
+  }
+}
+
+// One 256-thread workgroup per (kv head, run of appended rows).
+template <int D, bool BF16>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
+  __shared__ float xs[2 * D];
+  __shared__ float wsum[kScoreThreads / 64];
+  const int h = blockIdx.x / p.groups_per_head;
+  const int g = blockIdx.x % p.groups_per_head;
+  const long long f0 = (long long)g * p.tokens_per_group;
+  ScorerSlice<D> m;
+  m.load(p, h, threadIdx.x);
+  for (int i = 0; i < p.tokens_per_group; ++i) score_row<D, BF16>(p, m, h, f0 + i, threadIdx.x, xs, wsum);
 }
 
 // ----------------------------------------------------------------- top-k
@@ -248,15 +289,13 @@ __device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, lon
 // key above the threshold and the lowest positions equal to it (the unique
 // answer under "score descending, then position ascending"), and collects the
 // keys between the two outer ranks; sorted, they give the lists.
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+__device__ void topk_pair(const TopkParams& p, int h, int b) {
   __shared__ uint32_t hist[3][256];
   __shared__ uint32_t scan[kTopkThreads / 64];
   __shared__ uint32_t sel_digit[3], sel_above[3];
   __shared__ uint64_t cand[kCandCap];
   __shared__ uint32_t ncand;
   __shared__ int done;
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -482,10 +521,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   }
 }
 
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+  topk_pair(p, blockIdx.x, blockIdx.y);
+}
+
+// Scoring and the keep-mask refresh in one launch, for calls that append at
+// most 128 positions: the refresh only reads scores of INT4-region positions,
+// which lie below L - 128 and so were written by earlier calls. Workgroups
+// [0, pairs) refresh one (sequence, kv head) each; the rest score 4 appended
+// rows each (one per 256-thread quarter) for one kv head.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(ScoreParams sp, TopkParams tp) {
+  __shared__ float xs[kTopkThreads / kScoreThreads][2 * D];
+  __shared__ float wsum[kTopkThreads / kScoreThreads][kScoreThreads / 64];
+  const int pairs = tp.hkv * sp.batch;
+  if ((int)blockIdx.x < pairs) {
+    topk_pair(tp, blockIdx.x % tp.hkv, blockIdx.x / tp.hkv);
+    return;
+  }
+  const int g = blockIdx.x - pairs;
+  const int h = g % sp.hkv;
+  const int q = threadIdx.x / kScoreThreads;
+  const long long f = (long long)(g / sp.hkv) * (kTopkThreads / kScoreThreads) + q;
+  ScorerSlice<D> m;
+  m.load(sp, h, threadIdx.x % kScoreThreads);
+  score_row<D, BF16>(sp, m, h, f, threadIdx.x % kScoreThreads, xs[q], wsum[q]);
+}
+
 }  // namespace
 
-hipError_t launch_score(const kvc_cache& c, const float* mlp, const void* k_new, const void* v_new,
-                        kvc_dtype src, int n_new_max, const int32_t* n_new, hipStream_t s) {
+namespace {
+
+ScoreParams score_params(const kvc_cache& c, const float* mlp, const void* k_new, const void* v_new,
+                         int n_new_max, const int32_t* n_new) {
   ScoreParams p;
   p.mlp = mlp;
   p.k_new = k_new;
@@ -498,24 +566,15 @@ hipError_t launch_score(const kvc_cache& c, const float* mlp, const void* k_new,
   p.n_new_max = n_new_max;
   p.max_ctx = c.max_ctx;
   const long long total = (long long)c.batch * n_new_max;
-  long long tpw = (total + 511) / 512;
-  if (tpw < 16) tpw = 16;
-  p.tokens_per_wave = (int)tpw;
-  p.waves_per_head = (int)((total + tpw - 1) / tpw);
-  const dim3 grid((unsigned)(p.waves_per_head * c.num_kv_heads));
-  const bool bf = src == KVC_BF16;
-  if (c.head_dim == 128) {
-    if (bf) hipLaunchKernelGGL((score_kernel<128, true>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((score_kernel<128, false>), grid, dim3(64), 0, s, p);
-  } else {
-    if (bf) hipLaunchKernelGGL((score_kernel<64, true>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((score_kernel<64, false>), grid, dim3(64), 0, s, p);
-  }
-  return hipGetLastError();
+  // up to 4096 workgroups per head; one row per workgroup at decode
+  long long tpg = (total + 4095) / 4096;
+  if (tpg < 1) tpg = 1;
+  p.tokens_per_group = (int)tpg;
+  p.groups_per_head = (int)((total + tpg - 1) / tpg);
+  return p;
 }
 
-hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state, bool incremental,
-                       hipStream_t s) {
+TopkParams topk_params(const kvc_cache& c, int budget_permille, TopkState* state, bool incremental) {
   TopkParams p;
   p.state = state;
   p.incremental = incremental ? 1 : 0;
@@ -526,7 +585,49 @@ hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state
   p.max_ctx = c.max_ctx;
   p.words = mask_words(c.max_ctx);
   p.budget = budget_permille;
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_score(const kvc_cache& c, const float* mlp, const void* k_new, const void* v_new,
+                        kvc_dtype src, int n_new_max, const int32_t* n_new, hipStream_t s) {
+  const ScoreParams p = score_params(c, mlp, k_new, v_new, n_new_max, n_new);
+  const dim3 grid((unsigned)(p.groups_per_head * c.num_kv_heads));
+  const bool bf = src == KVC_BF16;
+  if (c.head_dim == 128) {
+    if (bf) hipLaunchKernelGGL((score_kernel<128, true>), grid, dim3(kScoreThreads), 0, s, p);
+    else hipLaunchKernelGGL((score_kernel<128, false>), grid, dim3(kScoreThreads), 0, s, p);
+  } else {
+    if (bf) hipLaunchKernelGGL((score_kernel<64, true>), grid, dim3(kScoreThreads), 0, s, p);
+    else hipLaunchKernelGGL((score_kernel<64, false>), grid, dim3(kScoreThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state, bool incremental,
+                       hipStream_t s) {
+  const TopkParams p = topk_params(c, budget_permille, state, incremental);
   hipLaunchKernelGGL(topk_kernel, dim3(c.num_kv_heads, c.batch), dim3(kTopkThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k_new,
+                             const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
+                             int budget_permille, TopkState* state, hipStream_t s) {
+  const ScoreParams sp = score_params(c, mlp, k_new, v_new, n_new_max, n_new);
+  const TopkParams tp = topk_params(c, budget_permille, state, true);
+  const long long rows = (long long)c.batch * n_new_max;
+  const long long quads = (rows + 3) / 4;
+  const dim3 grid((unsigned)((long long)c.batch * c.num_kv_heads + quads * c.num_kv_heads));
+  const bool bf = src == KVC_BF16;
+  if (c.head_dim == 128) {
+    if (bf) hipLaunchKernelGGL((score_topk_kernel<128, true>), grid, dim3(kTopkThreads), 0, s, sp, tp);
+    else hipLaunchKernelGGL((score_topk_kernel<128, false>), grid, dim3(kTopkThreads), 0, s, sp, tp);
+  } else {
+    if (bf) hipLaunchKernelGGL((score_topk_kernel<64, true>), grid, dim3(kTopkThreads), 0, s, sp, tp);
+    else hipLaunchKernelGGL((score_topk_kernel<64, false>), grid, dim3(kTopkThreads), 0, s, sp, tp);
+  }
   return hipGetLastError();
 }
 
