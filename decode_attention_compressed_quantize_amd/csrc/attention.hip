@@ -384,7 +384,8 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
     // QK accumulators start at -off, which removes the 1024 of every code
     const float4v offv = {-off, -off, -off, -off};
     const uint8_t* kbase = p.codes + s * S::SB;
-    const uint8_t* vbase = p.codes + D / 2 + hf * (D / 4);
+    // V pieces: 4 lanes per token at D = 128, 2 at D = 64, 16 bytes each
+    const uint8_t* vbase = p.codes + D / 2 + (D == 128 ? 16 * (lane & 3) : 16 * (lane & 1));
     const uint8_t* mbase = reinterpret_cast<const uint8_t*>(p.meta) + hf * (MH * 4);
     const int ntile = (cnt + 31) >> 5;  // 32-token tiles
     const int nstep = 2 * ntile;        // K step, then V step, per tile
@@ -409,11 +410,17 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       const uint8_t* a0;
       const uint8_t* a1;
       if constexpr (isk) {
+        // lane (s, n): K slot s of tokens n and 16 + n (4 lanes per token row)
         a0 = kbase + (uint64_t)list[it + n] * D;
         a1 = kbase + (uint64_t)list[it + 16 + n] * D;
+      } else if constexpr (D == 128) {
+        // lane (t, j): 16-byte piece j of the V codes of tokens t and 16 + t
+        a0 = vbase + (uint64_t)list[it + (lane >> 2)] * D;
+        a1 = vbase + (uint64_t)list[it + 16 + (lane >> 2)] * D;
       } else {
-        a0 = vbase + (uint64_t)rt * D;
-        a1 = a0 + 4 * NG;
+        // lane (t, j): 16-byte piece j of the V codes of token t
+        a0 = vbase + (uint64_t)list[it + (lane >> 1)] * D;
+        a1 = a0;
       }
       const uint8_t* am = mbase + (uint64_t)rt * (D / 4) + (isk ? 0 : D / 8);
       if constexpr (D == 128) {
@@ -424,11 +431,16 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
         for (int m = 0; m < 4; ++m) { t.c[m] = x[m]; t.c[4 + m] = y[m]; }
         t.mh[0] = mm[0];
         t.mh[1] = mm[1];
-      } else {
+      } else if constexpr (isk) {
         const u32x2 x = *reinterpret_cast<const u32x2*>(a0);
         const u32x2 y = *reinterpret_cast<const u32x2*>(a1);
 #pragma unroll
         for (int m = 0; m < 2; ++m) { t.c[m] = x[m]; t.c[2 + m] = y[m]; }
+        t.mh[0] = *reinterpret_cast<const uint32_t*>(am);
+      } else {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(a0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) t.c[m] = x[m];
         t.mh[0] = *reinterpret_cast<const uint32_t*>(am);
       }
     };
@@ -534,7 +546,14 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
     const int vdw = n % VD;
     auto compute2 = [&](const Tile& t) {
 #pragma unroll
-      for (int m = 0; m < VD / 2; ++m) wv.vbuf[tl][hf * (VD / 2) + m] = t.c[m];
+      for (int m = 0; m < 4; ++m) {
+        if constexpr (D == 128) {
+          wv.vbuf[lane >> 2][4 * (lane & 3) + m] = t.c[m];
+          wv.vbuf[16 + (lane >> 2)][4 * (lane & 3) + m] = t.c[4 + m];
+        } else {
+          wv.vbuf[lane >> 1][4 * (lane & 1) + m] = t.c[m];
+        }
+      }
 #pragma unroll
       for (int m = 0; m < MH; ++m) wv.mbuf[tl][hf * MH + m] = t.mh[m];
       __builtin_amdgcn_wave_barrier();
