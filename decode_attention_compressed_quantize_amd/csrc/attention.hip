@@ -216,7 +216,6 @@ struct Smem {
   float m[kWaves][G];
   float l[kWaves][G];
   float vm[kWaves][16];
-  int32_t pages[kWaves][kListCap / kPage];
 };
 
 // Combine the four waves' (m, l, o) held in LDS into one partial and store it.
@@ -313,23 +312,34 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
   {
     const uint32_t* mrow = p.mask + ((size_t)b * p.hkv + kvh) * p.words;
     const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-    // one load for the range's mask words (<= 64) and two for its pages (<= 128)
+    // one load for the range's mask words (<= 64) and two for its pages (<= 128),
+    // all kept in registers and broadcast with readlane while compacting
     uint32_t myword = 0;
     if (lane < q4 / 32 && w0 + 32 * lane < hi) myword = mrow[(w0 >> 5) + lane];
-#pragma unroll
-    for (int i = 0; i < Smem<D, G>::kListCap / kPage / 64; ++i) {
-      const int j = lane + 64 * i;
-      int32_t pg = -1;
-      if (j < q4 / 16 && w0 + 16 * j < hi) pg = bt[(w0 >> 4) + j];
-      sm.pages[wave][j] = pg;
-    }
-    __builtin_amdgcn_wave_barrier();
+    int32_t pg0 = -1, pg1 = -1;
+    if (lane < q4 / 16 && w0 + 16 * lane < hi) pg0 = bt[(w0 >> 4) + lane];
+    if (64 + lane < q4 / 16 && w0 + 16 * (64 + lane) < hi) pg1 = bt[(w0 >> 4) + 64 + lane];
     for (int r = 0; w0 + 64 * r < hi; ++r) {
       const uint32_t wlo = __builtin_amdgcn_readlane(myword, 2 * r);
       const uint32_t whi = __builtin_amdgcn_readlane(myword, 2 * r + 1);
       const uint64_t bits = (uint64_t)wlo | ((uint64_t)whi << 32);
       const int pos = w0 + 64 * r + lane;
-      const int page = sm.pages[wave][(64 * r + lane) >> 4];
+      // pages 4r .. 4r+3 cover this round; lane takes page 4r + lane / 16
+      const int src = 4 * r;
+      int32_t pa, pb, pc, pd;
+      if (src < 64) {
+        pa = __builtin_amdgcn_readlane(pg0, src);
+        pb = __builtin_amdgcn_readlane(pg0, src + 1);
+        pc = __builtin_amdgcn_readlane(pg0, src + 2);
+        pd = __builtin_amdgcn_readlane(pg0, src + 3);
+      } else {
+        pa = __builtin_amdgcn_readlane(pg1, src - 64);
+        pb = __builtin_amdgcn_readlane(pg1, src - 63);
+        pc = __builtin_amdgcn_readlane(pg1, src - 62);
+        pd = __builtin_amdgcn_readlane(pg1, src - 61);
+      }
+      const int q16 = lane >> 4;
+      const int page = q16 == 0 ? pa : (q16 == 1 ? pb : (q16 == 2 ? pc : pd));
       const bool kept = ((bits >> lane) & 1u) && pos >= lo && pos < hi && page >= 0 &&
                         page < p.num_pages;
       const uint64_t bal = __ballot(kept);

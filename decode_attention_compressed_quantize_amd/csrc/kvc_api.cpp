@@ -76,16 +76,19 @@ namespace kvc {
 AttnPlan plan_attention(const kvc_cache& c, int num_q_heads) {
   (void)num_q_heads;
   // INT4 chunk j covers positions [j*chunk, (j+1)*chunk) of the INT4 region
-  // [16, max_ctx - 128). Aim for about two resident rounds of chunk
-  // workgroups (three 4-wave workgroups per CU on 256 CUs): long lists keep
-  // each workgroup's load pipeline full and pay its set-up (mask and
-  // block-table loads, compaction) rarely, while the second round evens out
-  // the finish times. The short INT8-region workgroups go first when they
-  // fit in one round, else after the chunks.
-  constexpr long long kResident = 768;
+  // [16, max_ctx - 128). Chunks are made as long as the per-wave list allows
+  // while leaving at least about kTarget chunk workgroups: a long list keeps
+  // a workgroup's load pipeline full and pays its set-up (mask and
+  // block-table loads, compaction) and epilogue rarely. Measured on 256 CUs,
+  // ~512 long chunk workgroups beat one or two full resident rounds (768 or
+  // 1536 workgroups at three per CU) at 10% and 50% kept. The short
+  // INT8-region workgroups go first when they fit in one round, else after
+  // the chunks.
+  constexpr long long kResident = 768;  // 3 workgroups per CU x 256 CUs
+  constexpr long long kTarget = 384;
   const long long end4 = c.max_ctx > kInt8Slots ? (long long)c.max_ctx - kRecent : 0;
   const long long pairs = (long long)c.batch * c.num_kv_heads;
-  const long long target = 2 * kResident;
+  const long long target = kTarget;
   long long chunk = (pairs * end4 + target - 1) / target;
   const long long fit = (end4 + kMaxParts - 2) / (kMaxParts - 1);  // nsplit + 1 <= kMaxParts
   if (chunk < fit) chunk = fit;
