@@ -351,11 +351,16 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       cnt += __popcll(bal);
     }
   }
+  cnt = __builtin_amdgcn_readfirstlane(cnt);  // wave-uniform: keeps the main loop scalar
+  // Pad the list with copies of its first entry to a whole number of ring
+  // turns (kRing steps = kRing / 2 tiles), so the unrolled main loop needs no
+  // per-step guard: a guard there turns into divergent branches, across which
+  // the compiler can only drain every outstanding load. Padded tokens get p = 0.
+  constexpr int kTurn = 16 * kRing;  // tokens per ring turn
+  const int padded = (cnt + kTurn - 1) / kTurn * kTurn;
   if (cnt > 0) {
-    // pad to a whole tile plus one more, so the prefetch never needs a branch
     const uint32_t fill = list[0];
-    const int padded = (cnt + 31) & ~31;
-    if (cnt + lane < padded) list[cnt + lane] = fill;
+    for (int i = cnt + lane; i < padded; i += 64) list[i] = fill;
   }
 
   // Per lane: m_col and l_col belong to head hc (the lane's column head),
@@ -397,8 +402,8 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
     // V pieces: 4 lanes per token at D = 128, 2 at D = 64, 16 bytes each
     const uint8_t* vbase = p.codes + D / 2 + (D == 128 ? 16 * (lane & 3) : 16 * (lane & 1));
     const uint8_t* mbase = reinterpret_cast<const uint8_t*>(p.meta) + hf * (MH * 4);
-    const int ntile = (cnt + 31) >> 5;  // 32-token tiles
-    const int nstep = 2 * ntile;        // K step, then V step, per tile
+    const int ntile = padded >> 5;  // 32-token tiles
+    const int nstep = 2 * ntile;    // K step, then V step, per tile; a multiple of kRing
 
     // One stream of steps: step 2j brings K codes and K meta of tile j, step
     // 2j + 1 the V codes and V meta of the same tokens. The V half of a token
@@ -619,12 +624,10 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
     for (int step = 0; step < nstep; step += kRing) {
 #pragma unroll
       for (int j = 0; j < kRing; ++j) {
-        if (step + j < nstep) {
-          if ((j + kRing - 1) % 2 == 0) fetch(KStep{}, step + j + kRing - 1, ring[(j + kRing - 1) % kRing]);
-          else fetch(VStep{}, step + j + kRing - 1, ring[(j + kRing - 1) % kRing]);
-          if (j % 2 == 0) compute1(ring[j], 16 * (step + j));
-          else compute2(ring[j]);
-        }
+        if ((j + kRing - 1) % 2 == 0) fetch(KStep{}, step + j + kRing - 1, ring[(j + kRing - 1) % kRing]);
+        else fetch(VStep{}, step + j + kRing - 1, ring[(j + kRing - 1) % kRing]);
+        if (j % 2 == 0) compute1(ring[j], 16 * (step + j));
+        else compute2(ring[j]);
       }
     }
     // l: sum over the lanes of each head (all rows, columns h, h+G, ...)
@@ -834,7 +837,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
 }
 
 template <int D, int G, bool QBF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void attention_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
   __shared__ Smem<D, G> sm;
   // One-dimensional grid, dispatched in index order and spread round-robin
   // over the 8 XCDs. The INT8 regions take `pairs` consecutive items, before
