@@ -14,6 +14,17 @@ unchanged). The budget applies per (sequence, kv head) to the INT4 region:
 k = floor(budget_permille * n4 / 1000); order by score descending, then
 position ascending; NaN ranks below every number, -inf included (so the
 order is total and the kept set unique).
+
+Block policy (KVP promo page, section "Engineering limits": a paged cache
+evicts whole blocks, so token scores are averaged per block before ranking,
+and a coarse recency cut to the most recent positions comes before the
+learned selection). Readings: blocks are the 16-token pages [16j, 16j+16);
+the candidates are the INT4-region positions, or with a window W > 0 only
+the last W of them; a block's score is the float32 mean of its candidate
+positions' scores (summed in position order, then divided by their count);
+k = floor(budget_permille * nb / 1000) of the nb candidate blocks are kept,
+ordered like tokens (score descending, then block index ascending, NaN
+last); every candidate position of a kept block is kept.
 """
 from __future__ import annotations
 
@@ -61,4 +72,35 @@ def topk_keep(scores_int4, budget_permille: int):
     order = np.lexsort((pos, -s, nan))
     keep = np.zeros(n4, dtype=bool)
     keep[order[:k]] = True
+    return keep
+
+
+def block_keep(scores_int4, budget_permille: int, block: int = 16, window: int = 0):
+    """Keep flags (bool [n4]) under the block policy for INT4-region scores given in
+    position order from position 16 (a block boundary)."""
+    s = np.asarray(scores_int4, np.float32)
+    n4 = s.shape[0]
+    keep = np.zeros(n4, dtype=bool)
+    c0 = max(0, n4 - window) if window > 0 else 0  # first candidate (region offset)
+    if n4 == 0 or c0 >= n4:
+        return keep
+    j0 = c0 // block
+    j1 = (n4 + block - 1) // block
+    means = np.zeros(j1 - j0, dtype=np.float32)
+    for j in range(j0, j1):
+        a, b = max(block * j, c0), min(block * j + block, n4)
+        acc = np.float32(0.0)
+        for t in range(a, b):          # position order, float32
+            acc = np.float32(acc + s[t])
+        means[j - j0] = np.float32(acc / np.float32(b - a))
+    nb = j1 - j0
+    k = (int(budget_permille) * nb) // 1000
+    m = means.astype(np.float64)
+    nan = np.isnan(m)
+    m[nan] = -np.inf
+    idx = np.arange(nb)
+    order = np.lexsort((idx, -m, nan))
+    for jj in order[:k]:
+        j = j0 + int(jj)
+        keep[max(block * j, c0):min(block * j + block, n4)] = True
     return keep

@@ -104,3 +104,83 @@ def test_budget_k_floor():
     assert policy.budget_k(7, 1000) == 7 and policy.budget_k(7, 0) == 0
     c = constants()
     assert c["budget_min_percent"][0] == 10 and c["budget_max_percent"][0] == 90
+
+
+# ------------------------------------------------------------- block policy
+def fraction_block_keep(scores, budget, block, window):
+    """Independent pin: exact rational block means, Python sort."""
+    from fractions import Fraction
+
+    n4 = len(scores)
+    c0 = max(0, n4 - window) if window > 0 else 0
+    keep = [False] * n4
+    if c0 >= n4:
+        return np.array(keep)
+    blocks = []
+    j = c0 // block
+    while block * j < n4:
+        a, b = max(block * j, c0), min(block * j + block, n4)
+        mean = Fraction(sum(int(x) for x in scores[a:b]), b - a)
+        blocks.append((-mean, j, a, b))
+        j += 1
+    k = budget * len(blocks) // 1000
+    for _, _, a, b in sorted(blocks)[:k]:
+        for t in range(a, b):
+            keep[t] = True
+    return np.array(keep)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.integers(-50, 50), min_size=0, max_size=200), st.integers(0, 1000),
+       st.sampled_from([0, 1, 7, 16, 33, 100, 1000]))
+def test_block_policy_matches_exact_rational_ranking(ints, budget, window):
+    # integer scores: float32 sums are exact and distinct means stay distinct
+    scores = np.array(ints, np.float32)
+    got = policy.block_keep(scores, budget, 16, window)
+    np.testing.assert_array_equal(got, fraction_block_keep(ints, budget, 16, window))
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.floats(-1e3, 1e3, width=32), min_size=0, max_size=120), st.integers(0, 1000))
+def test_block_policy_with_one_token_blocks_is_token_topk(vals, budget):
+    s = np.array(vals, np.float32)
+    np.testing.assert_array_equal(policy.block_keep(s, budget, block=1), policy.topk_keep(s, budget))
+
+
+def test_block_policy_hand_cases():
+    # three full blocks with means 1, 3, 2; 66.7% of 3 blocks -> 2 blocks: the 3s and the 2s
+    s = np.repeat(np.array([1.0, 3.0, 2.0], np.float32), 16)
+    keep = policy.block_keep(s, 667)
+    assert not keep[:16].any() and keep[16:].all()
+    # 40 positions scored by index, window 20: candidates 20..39 in blocks
+    # [20, 32) (mean 25.5) and [32, 40) (mean 35.5); half of 2 blocks keeps the second
+    s = np.arange(40, dtype=np.float32)
+    keep = policy.block_keep(s, 500, window=20)
+    assert keep[32:].all() and not keep[:32].any()
+    # budget 1000 keeps every candidate, none before the window
+    keep = policy.block_keep(s, 1000, window=20)
+    assert keep[20:].all() and not keep[:20].any()
+    # ties keep the lower block; a NaN block ranks below -inf
+    s = np.concatenate([np.full(16, 5.0), np.full(16, 5.0), np.full(16, -np.inf), np.full(16, np.nan)]).astype(np.float32)
+    assert policy.block_keep(s, 250)[:16].all() and not policy.block_keep(s, 250)[16:].any()
+    keep = policy.block_keep(s, 750)
+    assert keep[:48].all() and not keep[48:].any()
+
+
+def test_block_policy_invariants():
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        n4 = int(rng.integers(0, 400))
+        s = rng.standard_normal(n4).astype(np.float32)
+        budget = int(rng.integers(0, 1001))
+        window = int(rng.choice([0, 10, 64, 200]))
+        keep = policy.block_keep(s, budget, 16, window)
+        c0 = max(0, n4 - window) if window > 0 else 0
+        assert not keep[:c0].any()
+        # whole candidate blocks only
+        for j in range(c0 // 16, (n4 + 15) // 16):
+            a, b = max(16 * j, c0), min(16 * j + 16, n4)
+            assert keep[a:b].all() or not keep[a:b].any()
+        nb = (n4 + 15) // 16 - c0 // 16 if n4 > c0 else 0
+        kept_blocks = sum(1 for j in range(c0 // 16, (n4 + 15) // 16) if keep[max(16 * j, c0)])
+        assert kept_blocks == budget * nb // 1000
