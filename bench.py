@@ -35,6 +35,8 @@ KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_compressed_quantize_amd", "
 
 WORKLOAD_LAYERS = {
     "long128k": ["long128k_b10", "long128k_b50"],
+    "long128k_blocks": ["long128k_blk_b10", "long128k_blk_b50"],
+    "long128k_recent16k": ["long128k_r16k_b10", "long128k_r16k_b50"],
     "uniform4k": ["uniform4k"],
     "longtail": ["longtail"],
     "fullstep": ["fullstep"] * 36,
@@ -61,12 +63,22 @@ def algorithmic_bytes(w, lengths, keep4_counts):
 
 
 def kept_counts(w, lengths):
-    """Kept INT4 positions summed over kv heads, per sequence."""
+    """Kept INT4 positions summed over kv heads, per sequence.
+
+    Under the block policy only the first and the last candidate block can
+    hold fewer than ``block_tokens`` positions (at least one each), so the
+    count used is the lower bound (kb - 2) * B + 2, never an overstatement."""
     out = []
     for L in lengths:
         n4 = max(0, int(L) - 144)
         if w.mask == "all":
             k = n4
+        elif w.mask in ("scores", "mlp") and w.policy == "block":
+            B = w.block_tokens
+            c0 = max(0, n4 - w.recency_window) if w.recency_window > 0 else 0
+            nb = (n4 + B - 1) // B - c0 // B if n4 > c0 else 0
+            kb = (w.budget_permille * nb) // 1000
+            k = n4 - c0 if kb >= nb else max(kb, kb * B - 2 * (B - 1))
         elif w.mask in ("scores", "mlp"):
             k = (w.budget_permille * n4) // 1000
         else:
@@ -122,7 +134,11 @@ def _cpu_pair(args):
         start, n4 = regions.int4_range(L)
         if w.mask == "mlp":
             s = policy.mlp_scores(k, v, W.mlp_weights(w, 0)[kvh])
-            keep4 = policy.topk_keep(s[start:start + n4], w.budget_permille)
+            if w.policy == "block":
+                keep4 = policy.block_keep(s[start:start + n4], w.budget_permille, w.block_tokens,
+                                          w.recency_window)
+            else:
+                keep4 = policy.topk_keep(s[start:start + n4], w.budget_permille)
         else:
             keep4 = np.ones(n4, bool)
         G = w.group_size
@@ -212,9 +228,11 @@ def main():
                            for lc in layers)
     if replicas <= 0:
         replicas = max(1, math.ceil((1 << 30) / read_per_replica) + 1) if len(base) < 8 else 1
+    # replicas are device copies of the prefilled caches, within 96 GiB in all
+    replicas = max(1, min(replicas, int((96 << 30) // max(1, per_replica_bytes))))
     reps = [layers]
     for r in range(1, replicas):
-        reps.append([LayerCache(w, layer=li, device=dev, keep_sources=False) for li, w in enumerate(base)])
+        reps.append([lc.replica() for lc in layers])
     # As in a model, the layers of one batch share one lengths tensor, which the
     # caller advances once per step.
     for rep in reps:
@@ -242,7 +260,7 @@ def main():
             lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev)
             mlp = getattr(lc, "mlp", None)
             per.append({"k": ks, "v": vs, "q": qs, "out": out, "lse": lse, "ws": lc.workspace(),
-                        "topk": kvc.topk_workspace(lc.cache),
+                        "state": lc.refresh_state(),
                         "mlp": mlp, "one": torch.ones(w.batch, dtype=torch.int32, device=dev),
                         "lens": lc.lengths.astype(np.int64).copy(), "n": 0})
         inputs.append(per)
@@ -261,12 +279,7 @@ def main():
             st["lens"] += 1
             kvc.kvc_quantize_append(lc.cache, st["k"][s], st["v"][s], st["one"])
             w = lc.w
-            budget = 1000 if w.mask == "all" else w.budget_permille
-            if w.mask == "mlp":
-                kvc.kvc_score_topk_mask(lc.cache, st["mlp"], st["k"][s], st["v"][s], st["one"], budget,
-                                        ws=st["topk"])
-            else:
-                kvc.kvc_score_topk_mask(lc.cache, None, None, None, None, budget, ws=st["topk"])
+            lc.refresh(st["k"][s], st["v"][s], st["one"], ws=st["state"])
             if record:
                 e0, e1 = events.pop()
                 e0.record(stream)
@@ -328,6 +341,10 @@ def main():
             "batch": base[0].batch, "q_heads": base[0].q_heads, "kv_heads": base[0].kv_heads,
             "head_dim": base[0].head_dim, "context": int(base[0].lengths().max()),
             "replicas": replicas,
+            "keep_policy": [(f"{w.policy}" + (f"{w.block_tokens}" if w.policy == "block" else "")
+                             + (f", recency window {w.recency_window}" if w.recency_window else "")
+                             + (f", budget {w.budget_permille / 10:g}%" if w.budget_permille else ""))
+                            for w in base[:2]],
         },
         "decode_steps_per_s": round(1000.0 / ms, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),

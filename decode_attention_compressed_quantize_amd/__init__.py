@@ -6,7 +6,8 @@ and the current stream. Importing works without a GPU; any call raises if the
 library has not been built.
 
 The functions mirror the C ABI in ``include/kvc.h``:
-``kvc_quantize_append``, ``kvc_score_topk_mask``, ``kvc_decode_attention``,
+``kvc_quantize_append``, ``kvc_score_topk_mask``, ``kvc_score_block_mask``,
+``kvc_decode_attention``,
 ``kvc_attention_workspace_bytes``, ``kvc_topk_workspace_bytes``,
 ``kvc_status_string``, ``kvc_last_error``, ``kvc_abi_version``.
 :class:`Cache` owns the torch tensors of one layer's compressed cache and the
@@ -70,6 +71,12 @@ _SIGNATURES = {
                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_size_t, ctypes.c_void_p]),
+    "kvc_score_block_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]),
+    "kvc_block_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
     "kvc_decode_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -212,6 +219,25 @@ def kvc_score_topk_mask(cache: Cache, mlp, k_new, v_new, n_new, budget_permille:
                                      _stream(stream)), "kvc_score_topk_mask")
 
 
+def kvc_score_block_mask(cache: Cache, mlp, k_new, v_new, n_new, budget_permille: int,
+                         recency_window: int = 0, block_tokens: int = PAGE, ws=None, stream=None):
+    """Score appended tokens (if ``mlp`` is given) and refresh the keep mask by whole blocks.
+
+    ``ws`` is None or a refresh state from :func:`block_workspace` for the same
+    block size, kept by the caller for this cache from call to call."""
+    n_max = 0 if k_new is None else k_new.shape[1]
+    src = KVC_BF16 if k_new is None else _dtype_code(k_new)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_score_block_mask(cache.ref(), _ptr(mlp), _ptr(k_new), _ptr(v_new), src, n_max,
+                                      _ptr(n_new), int(budget_permille), int(block_tokens),
+                                      int(recency_window), _ptr(ws), nbytes, _stream(stream)),
+           "kvc_score_block_mask")
+
+
+def kvc_block_workspace_bytes(cache: Cache, block_tokens: int = PAGE) -> int:
+    return int(lib().kvc_block_workspace_bytes(cache.ref(), int(block_tokens)))
+
+
 def kvc_decode_attention(cache: Cache, q, out, lse, ws, softmax_scale: float = 0.0, stream=None):
     """Decode attention of q ([B][Hq][D]) into out (fp32 [B][Hq][D]) and lse (fp32 [B][Hq] or None)."""
     nbytes = ws.numel() * ws.element_size()
@@ -225,6 +251,14 @@ def topk_workspace(cache: Cache, device="cuda"):
     import torch
 
     n = kvc_topk_workspace_bytes(cache)
+    return torch.zeros(max(n // 4, 1), dtype=torch.int32, device=device)
+
+
+def block_workspace(cache: Cache, block_tokens: int = PAGE, device="cuda"):
+    """Allocate a zero-filled block refresh state for ``cache`` (see kvc_score_block_mask)."""
+    import torch
+
+    n = kvc_block_workspace_bytes(cache, block_tokens)
     return torch.zeros(max(n // 4, 1), dtype=torch.int32, device=device)
 
 

@@ -64,6 +64,39 @@ struct TopkState {
 
 hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state, bool incremental,
                        hipStream_t s);
+// Block-granular keep-mask refresh from the scores (whole blocks of 16, 32 or
+// 64 tokens, up to kMaxBlocks candidate blocks per sequence).
+constexpr int kMaxBlocks = 131072;
+// Optional refresh state of one (sequence, kv head): this header, then one
+// key per INT4-region block by absolute block index (order key of the block's
+// mean score over its candidates when the header was written).
+constexpr uint32_t kBlockMagic = 0x4B564231u;
+struct BlockStateHeader {
+  uint32_t magic;   // kBlockMagic when valid
+  int32_t len;      // sequence length the keys and threshold describe
+  int32_t block;    // block size
+  int32_t window;   // recency window
+  int32_t budget;   // budget_permille of thr
+  uint32_t thr;     // key of the k-th largest block (when has_thr)
+  int32_t has_thr;
+  int32_t pad[9];
+};
+static_assert(sizeof(BlockStateHeader) == 64, "header size");
+// Sized for the smallest block (16 tokens), so that every block size finds
+// the headers at the same offsets.
+inline size_t block_state_stride(const kvc_cache& c) {
+  const int n4 = c.max_ctx > kInt8Slots ? c.max_ctx - kInt8Slots : 0;
+  const size_t keys = (size_t)(n4 + kPage - 1) / kPage;
+  return sizeof(BlockStateHeader) + (keys + 3) / 4 * 16;
+}
+hipError_t launch_block_topk(const kvc_cache& c, int budget_permille, int block_tokens, int window,
+                             void* state, hipStream_t s);
+// Scoring and block refresh in one launch; only for n_new_max <= kRecent.
+hipError_t launch_score_block(const kvc_cache& c, const float* mlp, const void* k_new,
+                              const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
+                              int budget_permille, int block_tokens, int window, void* state,
+                              hipStream_t s);
+
 // Scoring and refresh in one launch; only for n_new_max <= kRecent.
 hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k_new,
                              const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,

@@ -521,6 +521,510 @@ __device__ void topk_pair(const TopkParams& p, int h, int b) {
   }
 }
 
+// ---- block-granular refresh (KVP promo page, "Engineering limits": a paged
+// cache evicts whole blocks, ranked by the mean score of their tokens, after an
+// optional coarse recency cut). Region offsets o = position - 16; block j of
+// B tokens covers offsets [Bj, Bj + B); offsets below c0 (the recency cut) are
+// not candidates. A block's key is the order key of the float32 mean of its
+// candidate scores, summed in position order. One workgroup per (sequence,
+// kv head).
+struct BlockTopkParams {
+  const float* scores;
+  const int32_t* seq_lens;
+  uint32_t* mask;
+  unsigned char* state;  // per-pair BlockStateHeader + keys, or NULL
+  size_t state_stride;   // bytes per (sequence, kv head)
+  int hkv;
+  int max_ctx;
+  int words;
+  int budget;
+  int window;
+};
+
+constexpr int kBlockWaves = kTopkThreads / 64;
+constexpr int kBlockKeysLds = 32768;  // block keys cached in LDS up to this many blocks
+constexpr int kBlockBitWords = kMaxBlocks / 32;  // kept-block bitmap
+constexpr int kChunkPos = 256;        // offsets one wave loads per 16-byte load (4 per lane)
+constexpr int kRoundChunks = 8;       // loads a wave keeps in flight per round
+
+struct BlockLds {
+  uint32_t keys[kBlockKeysLds];
+  uint32_t kept_bits[kBlockBitWords];
+  uint32_t seg[kMaxBlocks / 64];  // per 64-block segment: keys equal to T, then their prefix
+  uint32_t hist[256];
+  uint32_t red[2][kBlockWaves];
+  uint32_t sel_digit, sel_above, sel_count;
+};
+
+// Four consecutive scores; p is 16-byte aligned when vec is set.
+__device__ inline float4 load_scores4(const float* p, bool vec) {
+  if (vec) return *reinterpret_cast<const float4*>(p);
+  return make_float4(p[0], p[1], p[2], p[3]);
+}
+
+// Histogram add of one digit per active lane; lanes of a wave sharing a digit
+// are added together (a few rounds), the rest one by one.
+__device__ inline void hist_add(uint32_t* hist, uint32_t d, bool active, int lane) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const uint64_t am = __ballot(active);
+    if (am == 0) return;
+    const int first = __ffsll((long long)am) - 1;
+    const uint32_t d0 = __shfl(d, first);
+    const uint64_t same = __ballot(active && d == d0);
+    if (lane == first) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+    if (d == d0) active = false;
+  }
+  if (active) atomicAdd(&hist[d], 1u);
+}
+
+// Workgroup sums of two counters (every thread gets both totals).
+__device__ inline void block_sum2(BlockLds& sm, uint32_t& x, uint32_t& y, int lane, int wid) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    x += __shfl_xor(x, o);
+    y += __shfl_xor(y, o);
+  }
+  if (lane == 0) {
+    sm.red[0][wid] = x;
+    sm.red[1][wid] = y;
+  }
+  __syncthreads();
+  x = 0;
+  y = 0;
+  for (int q = 0; q < kBlockWaves; ++q) {
+    x += sm.red[0][q];
+    y += sm.red[1][q];
+  }
+  __syncthreads();
+}
+
+// The smallest key above t (up) or the largest key below t (!up) among n
+// keys, with its multiplicity (cnt = 0 when there is none); workgroup-wide.
+template <typename KeyOf>
+__device__ inline void block_next_key(BlockLds& sm, KeyOf key_of, int n, uint32_t t, bool up,
+                                      uint32_t& best, uint32_t& cnt, int tid, int lane, int wid) {
+  best = 0;
+  cnt = 0;
+  auto merge = [&](uint32_t k, uint32_t c) {
+    if (c == 0) return;
+    if (cnt == 0 || (up ? k < best : k > best)) {
+      best = k;
+      cnt = c;
+    } else if (k == best) {
+      cnt += c;
+    }
+  };
+#pragma unroll 4
+  for (int i = tid; i < n; i += kTopkThreads) {
+    const uint32_t k = key_of(i);
+    if (up ? k > t : k < t) merge(k, 1);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t ob = __shfl_xor(best, o);
+    const uint32_t oc = __shfl_xor(cnt, o);
+    merge(ob, oc);
+  }
+  if (lane == 0) {
+    sm.red[0][wid] = best;
+    sm.red[1][wid] = cnt;
+  }
+  __syncthreads();
+  best = 0;
+  cnt = 0;
+  for (int q = 0; q < kBlockWaves; ++q) merge(sm.red[0][q], sm.red[1][q]);
+  __syncthreads();
+}
+
+// Bits of positions [lo, hi) that fall in the mask word starting at position base.
+__device__ inline uint32_t range_bits(int lo, int hi, int base) {
+  lo -= base;
+  hi -= base;
+  if (lo < 0) lo = 0;
+  if (hi > 32) hi = 32;
+  if (hi <= lo) return 0u;
+  const uint32_t upto_hi = hi == 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u);
+  return upto_hi & ~((1u << lo) - 1u);
+}
+
+// Key of block j from its candidate scores, one load at a time (for the rare
+// stateless refresh of more blocks than LDS caches).
+template <int B>
+__device__ inline uint32_t block_key_serial(const float* sc, int j, int c0, int n4) {
+  const int a = B * j > c0 ? B * j : c0;
+  const int e = B * j + B < n4 ? B * j + B : n4;
+  float sum = 0.0f;
+  for (int t = a; t < e; ++t) sum += sc[t];
+  return order_key(sum / (float)(e - a));
+}
+
+// Key of block j from its candidate scores, loaded up to 32 at a time.
+template <int B>
+__device__ inline uint32_t block_key_direct(const float* sc, int j, int c0, int n4) {
+  constexpr int kPart = B < 32 ? B : 32;
+  const int a = B * j > c0 ? B * j : c0;
+  const int e = B * j + B < n4 ? B * j + B : n4;
+  float sum = 0.0f;
+#pragma unroll
+  for (int c = 0; c < B; c += kPart) {
+    float v[kPart];
+#pragma unroll
+    for (int i = 0; i < kPart; ++i) v[i] = a + c + i < e ? sc[a + c + i] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPart; ++i)
+      if (a + c + i < e) sum += v[i];
+  }
+  return order_key(sum / (float)(e - a));
+}
+
+template <int B>
+__device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, int b) {
+  static_assert(B == 16 || B == 32 || B == 64, "block size");
+  constexpr int kOldWords = 5;  // previous mask words held per thread (the rest re-read)
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int L = p.seq_lens[b];
+  if (L < 0) L = 0;
+  if (L > p.max_ctx) L = p.max_ctx;
+  const int n4 = L > kInt8Slots ? L - kInt8Slots : 0;
+  const int c0 = p.window > 0 ? (n4 - p.window > 0 ? n4 - p.window : 0) : 0;
+  const int j0 = c0 / B;
+  const int nb = n4 > c0 ? (n4 + B - 1) / B - j0 : 0;
+  const long long k = ((long long)p.budget * nb) / 1000;
+  const bool all = k >= nb;
+  const bool select = k > 0 && !all;
+  const float* sc = p.scores + ((size_t)b * p.hkv + h) * p.max_ctx + kSink;
+  uint32_t* mrow = p.mask + ((size_t)b * p.hkv + h) * p.words;
+  const bool cached = nb <= kBlockKeysLds;
+  BlockStateHeader* st = p.state ? reinterpret_cast<BlockStateHeader*>(
+                                       p.state + ((size_t)b * p.hkv + h) * p.state_stride)
+                                 : nullptr;
+  uint32_t* skeys = st ? reinterpret_cast<uint32_t*>(st + 1) : nullptr;
+  // keys are stored (LDS cache, state) only where something keeps them
+  const bool need_keys = (select && cached) || st != nullptr;
+
+  // ---- everything that does not depend on the state is loaded up front: the
+  // previous mask words, the state's keys (into LDS), and the keys of the first
+  // and the last candidate block (the ones a one-token step changes)
+  uint32_t old_w[kOldWords];
+#pragma unroll
+  for (int m = 0; m < kOldWords; ++m) {
+    const int w = tid + m * kTopkThreads;
+    old_w[m] = w < p.words ? mrow[w] : 0u;
+  }
+  bool valid = false, thr_ok = false;
+  int len0 = 0;
+  uint32_t thr0 = 0;
+  if (st) {
+    const uint32_t magic = st->magic;
+    len0 = st->len;
+    valid = magic == kBlockMagic && st->block == B && st->window == p.window && len0 >= 0 &&
+            len0 <= L;
+    thr_ok = valid && st->has_thr != 0 && st->budget == p.budget;
+    thr0 = st->thr;
+  }
+  int spec_r = -1;
+  uint32_t spec_key = 0;
+  if (need_keys && nb > 0) {
+    if (tid == kTopkThreads - 1) spec_r = nb - 1;
+    if (tid == kTopkThreads - 2 && nb > 1) spec_r = 0;
+    if (spec_r >= 0) spec_key = block_key_direct<B>(sc, j0 + spec_r, c0, n4);
+  }
+  if (st && cached) {
+#pragma unroll 8
+    for (int i = tid; i < nb; i += kTopkThreads) sm.keys[i] = skeys[j0 + i];
+  }
+  // the previous mask words are needed only at the end; keep them here, with
+  // this round of loads, instead of a round trip of their own later
+#pragma unroll
+  for (int m = 0; m < kOldWords; ++m) asm volatile("" ::"v"(old_w[m]));
+
+  // keys recomputed from the scores: relative blocks [ra, nb), and block 0
+  // when the recency cut moved (blocks in between are full and unchanged)
+  int ra = 0;
+  bool first_too = false;
+  if (valid) {
+    const int n4o = len0 > kInt8Slots ? len0 - kInt8Slots : 0;
+    const int c0o = p.window > 0 ? (n4o - p.window > 0 ? n4o - p.window : 0) : 0;
+    ra = n4o / B - j0;
+    if (ra < 0) ra = 0;
+    if (ra > nb) ra = nb;
+    first_too = c0o != c0 && ra > 0;
+  }
+  __syncthreads();  // header read and state keys in LDS before anything is rewritten
+
+  auto store_key = [&](int r, uint32_t key) {
+    if (cached) sm.keys[r] = key;
+    if (st) skeys[j0 + r] = key;
+  };
+  if (need_keys && nb - ra >= kTopkThreads) {
+    // many keys: a wave round covers kRoundChunks * 256 consecutive offsets,
+    // lane l holding offsets 4l..4l+3 of each 256; the B/4 lanes of one block
+    // pass the running sum along in position order
+    constexpr int kLanesPerBlock = B / 4;
+    constexpr int kChunks = B == 64 ? kRoundChunks / 2 : kRoundChunks;  // longer chains, fewer loads
+    constexpr int kBlocksPerChunk = kChunkPos / B;
+    constexpr int kBlocksPerRound = kChunks * kBlocksPerChunk;
+    const bool vec = (reinterpret_cast<uintptr_t>(sc) & 15) == 0;
+    const int sub = lane % kLanesPerBlock;
+    for (int g = wid; ra + g * kBlocksPerRound < nb; g += kBlockWaves) {
+      const int ob = B * (j0 + ra + g * kBlocksPerRound) + 4 * lane;
+      float4 v[kChunks];
+#pragma unroll
+      for (int u = 0; u < kChunks; ++u) {
+        const int o = ob + u * kChunkPos;
+        v[u] = o < n4 ? load_scores4(sc + o, vec) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < kChunks; ++u) {
+        const int r = ra + g * kBlocksPerRound + u * kBlocksPerChunk + lane / kLanesPerBlock;
+        const int j = j0 + r;
+        const int a = B * j > c0 ? B * j : c0;
+        const int e = B * j + B < n4 ? B * j + B : n4;
+        const int o = ob + u * kChunkPos;
+        float run = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kLanesPerBlock; ++t) {
+          const float prev = __shfl_up(run, 1, kLanesPerBlock);
+          if (sub == t) {
+            float x = t == 0 ? 0.0f : prev;
+            if (o >= a && o < e) x += v[u].x;
+            if (o + 1 >= a && o + 1 < e) x += v[u].y;
+            if (o + 2 >= a && o + 2 < e) x += v[u].z;
+            if (o + 3 >= a && o + 3 < e) x += v[u].w;
+            run = x;
+          }
+        }
+        if (sub == kLanesPerBlock - 1 && r < nb) store_key(r, order_key(run / (float)(e - a)));
+      }
+    }
+    if (first_too && spec_r == 0) store_key(0, spec_key);
+  } else if (need_keys) {
+    // few keys: one block per thread; the first and the last block come from
+    // the threads that computed them up front
+    if (spec_r >= 0 && (spec_r >= ra || (spec_r == 0 && first_too))) store_key(spec_r, spec_key);
+    const int r = ra + tid;
+    if (r < nb && r != nb - 1 && !(r == 0 && nb > 1)) store_key(r, block_key_direct<B>(sc, j0 + r, c0, n4));
+  }
+  __syncthreads();
+  auto key_of = [&](int i) -> uint32_t {
+    if (cached) return sm.keys[i];
+    if (st) return skeys[j0 + i];
+    return block_key_serial<B>(sc, j0 + i, c0, n4);
+  };
+
+  // ---- threshold T = key of the k-th largest block; need = blocks with key T
+  // kept (lowest block first) out of eqT with that key
+  uint32_t T = 0u;
+  long long need = 0, eqT = 0;
+  if (select) {
+    bool found = false;
+    if (thr_ok) {
+      // start from the previous threshold: count the keys above and equal to
+      // it, then move it to the next distinct key up or down while it selects
+      // more or fewer than k blocks (a few keys change from call to call)
+      uint32_t gt = 0, eq = 0;
+#pragma unroll 8
+      for (int i = tid; i < nb; i += kTopkThreads) {
+        const uint32_t key = key_of(i);
+        gt += key > thr0;
+        eq += key == thr0;
+      }
+      block_sum2(sm, gt, eq, lane, wid);
+      uint32_t t = thr0;
+      for (int step = 0; step < 4; ++step) {
+        if ((long long)gt < k && k <= (long long)gt + eq) {
+          T = t;
+          need = k - gt;
+          eqT = eq;
+          found = true;
+          break;
+        }
+        if (step == 3) break;
+        const bool up = (long long)gt >= k;
+        uint32_t nt, nc;
+        block_next_key(sm, key_of, nb, t, up, nt, nc, tid, lane, wid);
+        if (nc == 0) break;
+        if (up) {
+          gt -= nc;
+        } else {
+          gt += eq;
+        }
+        t = nt;
+        eq = nc;
+      }
+    }
+    if (!found) {  // radix select, 8 bits per pass
+      uint32_t prefix = 0, pmask = 0;
+      long long remaining = k;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < 256; i += kTopkThreads) sm.hist[i] = 0;
+        __syncthreads();
+        for (int i0 = 0; i0 < nb; i0 += kTopkThreads) {
+          const int i = i0 + tid;
+          const uint32_t key = i < nb ? key_of(i) : 0u;
+          hist_add(sm.hist, (key >> shift) & 255u, i < nb && (key & pmask) == prefix, lane);
+        }
+        __syncthreads();
+        if (wid == 0) {
+          uint32_t c4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) c4[q] = sm.hist[4 * lane + q];
+          const uint32_t s4 = c4[0] + c4[1] + c4[2] + c4[3];
+          uint32_t suf = s4;  // keys whose digit is >= 4 * lane
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t t = __shfl_down(suf, o);
+            if (lane + o < 64) suf += t;
+          }
+          const uint32_t above = suf - s4;
+          if ((long long)above < remaining && remaining <= (long long)suf) {
+            uint32_t acc = above;
+            int d = 4 * lane, cd = c4[0];
+            for (int q = 3; q >= 0; --q) {
+              if ((long long)(acc + c4[q]) >= remaining) {
+                d = 4 * lane + q;
+                cd = c4[q];
+                break;
+              }
+              acc += c4[q];
+            }
+            sm.sel_digit = (uint32_t)d;
+            sm.sel_above = acc;
+            sm.sel_count = (uint32_t)cd;
+          }
+        }
+        __syncthreads();
+        remaining -= sm.sel_above;
+        prefix |= sm.sel_digit << shift;
+        pmask |= 255u << shift;
+        eqT = sm.sel_count;  // after the last pass: keys equal to the threshold
+        __syncthreads();
+      }
+      T = prefix;
+      need = remaining;
+    }
+  }
+  // with every tie at T kept (always so for distinct keys), kept = key >= T
+  const bool by_key = select && need == eqT;
+
+  // ---- otherwise a kept flag per candidate block, by 64-block segments (wave
+  // ballots): ties at T are kept in block order, ranked by a segment prefix
+  if (select && !by_key) {
+    const int nseg = (nb + 63) / 64;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int sg = wid; sg < nseg; sg += kBlockWaves) {
+      const int i = 64 * sg + lane;
+      const uint64_t eqs = __ballot(i < nb && key_of(i) == T);
+      if (lane == 0) sm.seg[sg] = (uint32_t)__popcll(eqs);
+    }
+    __syncthreads();
+    if (wid == 0) {  // exclusive prefix of the segment counts
+      const int per = (nseg + 63) / 64;
+      const int lo = lane * per < nseg ? lane * per : nseg;
+      const int hi = lo + per < nseg ? lo + per : nseg;
+      uint32_t sum = 0;
+      for (int q = lo; q < hi; ++q) sum += sm.seg[q];
+      uint32_t incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      uint32_t run = incl - sum;
+      for (int q = lo; q < hi; ++q) {
+        const uint32_t c = sm.seg[q];
+        sm.seg[q] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+    for (int sg = wid; sg < nseg; sg += kBlockWaves) {
+      const int i = 64 * sg + lane;
+      bool kept = false, eq = false;
+      if (i < nb) {
+        const uint32_t key = key_of(i);
+        kept = key > T;
+        eq = key == T;
+      }
+      const uint64_t eqs = __ballot(eq);
+      if (eq) kept = (long long)sm.seg[sg] + __popcll(eqs & below) < need;
+      const uint64_t ks = __ballot(kept);
+      if (lane == 0) sm.kept_bits[2 * sg] = (uint32_t)ks;
+      if (lane == 32) sm.kept_bits[2 * sg + 1] = (uint32_t)(ks >> 32);
+    }
+    __syncthreads();
+  }
+
+  // ---- kept-block bitmap when kept means key >= T (or every block): one
+  // ballot per 64-block segment (the tie case filled it above)
+  if (all || by_key) {
+    const int nseg = (nb + 63) / 64;
+    for (int sg = wid; sg < nseg; sg += kBlockWaves) {
+      const int i = 64 * sg + lane;
+      const uint64_t ks = __ballot(i < nb && (all || key_of(i) >= T));
+      if (lane == 0) sm.kept_bits[2 * sg] = (uint32_t)ks;
+      if (lane == 32) sm.kept_bits[2 * sg + 1] = (uint32_t)(ks >> 32);
+    }
+    __syncthreads();
+  }
+
+  // ---- mask words: protected positions kept, kept blocks' candidates kept,
+  // everything else (evicted, cut, positions >= L) clear; a word is stored only
+  // where it differs from what the mask holds. Word w (positions 32w..32w+31)
+  // meets at most two blocks, jA and jB, jB starting at position split.
+  const int rec0 = L - kRecent > kSink ? L - kRecent : kSink;
+  const int lo4 = kSink + c0, hi4 = kSink + n4;
+  const bool any_kept = all || select;
+  auto kept_block = [&](int j) -> bool {
+    const int r = j - j0;
+    return any_kept && r >= 0 && r < nb && ((sm.kept_bits[r >> 5] >> (r & 31)) & 1u);
+  };
+  auto word_bits = [&](int w) -> uint32_t {
+    const int base = 32 * w;
+    uint32_t bits = range_bits(0, L < kSink ? L : kSink, base) | range_bits(rec0, L, base);
+    const uint32_t cand = range_bits(lo4, hi4, base);
+    if (cand) {
+      const int jA = (base - kSink + B) / B - 1;  // floor((base - 16) / B), base - 16 >= -B
+      const int jB = (base + 31 - kSink) / B;
+      const int split = kSink + B * jB;
+      uint32_t kb = 0;
+      if (kept_block(jA)) kb |= range_bits(kSink + B * jA, split, base);
+      if (kept_block(jB)) kb |= range_bits(split, split + B, base);
+      bits |= cand & kb;
+    }
+    return bits;
+  };
+#pragma unroll
+  for (int m = 0; m < kOldWords; ++m) {
+    const int w = tid + m * kTopkThreads;
+    if (w < p.words) {
+      const uint32_t bits = word_bits(w);
+      if (bits != old_w[m]) mrow[w] = bits;
+    }
+  }
+  for (int w = tid + kOldWords * kTopkThreads; w < p.words; w += kTopkThreads) {
+    const uint32_t bits = word_bits(w);
+    if (bits != mrow[w]) mrow[w] = bits;
+  }
+  if (st && tid == 0) {
+    st->magic = kBlockMagic;
+    st->len = L;
+    st->block = B;
+    st->window = p.window;
+    st->budget = p.budget;
+    st->thr = T;
+    st->has_thr = select ? 1 : 0;
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(kTopkThreads) void block_topk_kernel(BlockTopkParams p) {
+  __shared__ BlockLds sm;
+  block_topk_pair<B>(p, sm, blockIdx.x % p.hkv, blockIdx.x / p.hkv);
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   topk_pair(p, blockIdx.x, blockIdx.y);
 }
@@ -609,6 +1113,84 @@ hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state
                        hipStream_t s) {
   const TopkParams p = topk_params(c, budget_permille, state, incremental);
   hipLaunchKernelGGL(topk_kernel, dim3(c.num_kv_heads, c.batch), dim3(kTopkThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16, int B>
+__global__ __launch_bounds__(kTopkThreads) void score_block_kernel(ScoreParams sp, BlockTopkParams bp) {
+  __shared__ BlockLds sm;
+  __shared__ float xs[kTopkThreads / kScoreThreads][2 * D];
+  __shared__ float wsum[kTopkThreads / kScoreThreads][kScoreThreads / 64];
+  const int pairs = bp.hkv * sp.batch;
+  if ((int)blockIdx.x < pairs) {  // the refresh never reads this call's rows: they are protected
+    block_topk_pair<B>(bp, sm, blockIdx.x % bp.hkv, blockIdx.x / bp.hkv);
+    return;
+  }
+  const int g = blockIdx.x - pairs;
+  const int h = g % sp.hkv;
+  const int q = threadIdx.x / kScoreThreads;
+  const long long f = (long long)(g / sp.hkv) * (kTopkThreads / kScoreThreads) + q;
+  ScorerSlice<D> m;
+  m.load(sp, h, threadIdx.x % kScoreThreads);
+  score_row<D, BF16>(sp, m, h, f, threadIdx.x % kScoreThreads, xs[q], wsum[q]);
+}
+
+static BlockTopkParams block_params(const kvc_cache& c, int budget_permille, int block_tokens,
+                                    int window, void* state) {
+  BlockTopkParams p;
+  p.scores = c.scores;
+  p.seq_lens = c.seq_lens;
+  p.mask = c.keep_mask;
+  p.state = static_cast<unsigned char*>(state);
+  p.state_stride = block_state_stride(c);
+  p.hkv = c.num_kv_heads;
+  p.max_ctx = c.max_ctx;
+  p.words = mask_words(c.max_ctx);
+  p.budget = budget_permille;
+  p.window = window;
+  return p;
+}
+
+hipError_t launch_block_topk(const kvc_cache& c, int budget_permille, int block_tokens, int window,
+                             void* state, hipStream_t s) {
+  const BlockTopkParams p = block_params(c, budget_permille, block_tokens, window, state);
+  const dim3 grid(c.batch * c.num_kv_heads), block(kTopkThreads);
+  switch (block_tokens) {
+    case 16: hipLaunchKernelGGL(block_topk_kernel<16>, grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL(block_topk_kernel<32>, grid, block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL(block_topk_kernel<64>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+static void launch_score_block_d(const dim3& grid, int block_tokens, const ScoreParams& sp,
+                                 const BlockTopkParams& bp, hipStream_t s) {
+  const dim3 block(kTopkThreads);
+  if (block_tokens == 16) hipLaunchKernelGGL((score_block_kernel<D, BF16, 16>), grid, block, 0, s, sp, bp);
+  else if (block_tokens == 32) hipLaunchKernelGGL((score_block_kernel<D, BF16, 32>), grid, block, 0, s, sp, bp);
+  else hipLaunchKernelGGL((score_block_kernel<D, BF16, 64>), grid, block, 0, s, sp, bp);
+}
+
+hipError_t launch_score_block(const kvc_cache& c, const float* mlp, const void* k_new,
+                              const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
+                              int budget_permille, int block_tokens, int window, void* state,
+                              hipStream_t s) {
+  if (block_tokens != 16 && block_tokens != 32 && block_tokens != 64) return hipErrorInvalidValue;
+  const ScoreParams sp = score_params(c, mlp, k_new, v_new, n_new_max, n_new);
+  const BlockTopkParams bp = block_params(c, budget_permille, block_tokens, window, state);
+  const long long rows = (long long)c.batch * n_new_max;
+  const long long quads = (rows + 3) / 4;
+  const dim3 grid((unsigned)((long long)c.batch * c.num_kv_heads + quads * c.num_kv_heads));
+  const bool bf = src == KVC_BF16;
+  if (c.head_dim == 128) {
+    if (bf) launch_score_block_d<128, true>(grid, block_tokens, sp, bp, s);
+    else launch_score_block_d<128, false>(grid, block_tokens, sp, bp, s);
+  } else {
+    if (bf) launch_score_block_d<64, true>(grid, block_tokens, sp, bp, s);
+    else launch_score_block_d<64, false>(grid, block_tokens, sp, bp, s);
+  }
   return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ import numpy as np
 
 import workloads as W
 
-from . import (Cache, attention_workspace, kvc_quantize_append, kvc_score_topk_mask)
+from . import (Cache, attention_workspace, block_workspace, kvc_quantize_append,
+               kvc_score_block_mask, kvc_score_topk_mask, topk_workspace)
 
 
 def pack_bits(flags: np.ndarray, words: int) -> np.ndarray:
@@ -121,15 +122,55 @@ class LayerCache:
             c.keep_mask.copy_(torch.from_numpy(rows))
         elif w.mask == "all":
             kvc_score_topk_mask(c, None, None, None, None, 1000)
-        elif w.mask == "scores":
-            for b in range(w.batch):
-                L = int(self.lengths[b])
-                c.scores[b, :, :L] = W.given_scores_torch(w, self.layer, b, L, self.device)
-            kvc_score_topk_mask(c, None, None, None, None, w.budget_permille)
-        elif w.mask == "mlp":
-            kvc_score_topk_mask(c, None, None, None, None, w.budget_permille)
+        elif w.mask in ("scores", "mlp"):
+            if w.mask == "scores":
+                for b in range(w.batch):
+                    L = int(self.lengths[b])
+                    c.scores[b, :, :L] = W.given_scores_torch(w, self.layer, b, L, self.device)
+            self.refresh(None, None, None, None)
         else:
             raise ValueError(w.mask)
+
+    def refresh(self, k_new, v_new, n_new, ws=None, stream=None):
+        """Score appended tokens (``mlp`` workloads) and refresh the keep mask
+        with the workload's policy; ``ws`` is that policy's refresh state or None."""
+        w = self.w
+        if w.mask == "bernoulli":  # a host-drawn mask; nothing to refresh
+            return
+        mlp = getattr(self, "mlp", None) if k_new is not None and w.mask == "mlp" else None
+        if mlp is None:
+            k_new = v_new = n_new = None
+        budget = 1000 if w.mask == "all" else w.budget_permille
+        if self.block_policy:
+            kvc_score_block_mask(self.cache, mlp, k_new, v_new, n_new, budget, w.recency_window,
+                                 w.block_tokens, ws=ws, stream=stream)
+        else:
+            kvc_score_topk_mask(self.cache, mlp, k_new, v_new, n_new, budget, ws=ws, stream=stream)
+
+    @property
+    def block_policy(self) -> bool:
+        return self.w.policy == "block" and self.w.mask in ("scores", "mlp")
+
+    def refresh_state(self):
+        """A zero-filled refresh state for this cache's keep policy."""
+        if self.block_policy:
+            return block_workspace(self.cache, self.w.block_tokens, self.device)
+        return topk_workspace(self.cache, self.device)
+
+    def replica(self) -> "LayerCache":
+        """An independent copy on the device (same contents, own memory)."""
+        import copy
+
+        c = self.cache
+        r = copy.copy(self)
+        r.table = self.table.clone()
+        r.seq_lens = self.seq_lens.clone()
+        r.cache = Cache(c.batch, c.kv_heads, c.head_dim, c.max_ctx, c.num_phys_pages, r.table,
+                        r.seq_lens, device=self.device)
+        for name in ("int4_codes", "int4_meta", "int8_codes", "int8_scales", "keep_mask", "scores"):
+            getattr(r.cache, name).copy_(getattr(c, name))
+        r.k_src, r.v_src = {}, {}
+        return r
 
     # -------------------------------------------------------------- decode
     def queries(self, step: int = 0):

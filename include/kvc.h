@@ -157,6 +157,47 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
                                        size_t ws_bytes, hipStream_t stream);
 
 /*
+ * kvc_score_block_mask - score appended tokens and refresh the keep mask at
+ * block granularity, after an optional recency cut.
+ * Source: KVP promo page (arXiv 2602.10238), section "Engineering limits": a
+ * paged cache evicts whole blocks, so token scores are averaged per block
+ * before ranking, and a coarse recency cut narrows the candidates first.
+ *   mlp, k_new, v_new, src, n_new_max, n_new : as for kvc_score_topk_mask.
+ *   block_tokens : 16, 32 or 64 (one, two or four pages). Block j covers
+ *                  INT4-region offsets [B*j, B*j+B), offset = position - 16.
+ *   recency_window : 0, or W > 0: only the last W positions of the INT4 region
+ *                  (positions >= max(16, L-128-W)) are candidates; older INT4
+ *                  positions are evicted.
+ *   budget_permille : with nb blocks holding candidates, keeps
+ *                  floor(budget*nb/1000) blocks by the float32 mean of their
+ *                  candidate positions' scores (summed in position order),
+ *                  highest first; ties keep the lower block; NaN ranks below
+ *                  every number. Every candidate position of a kept block is
+ *                  kept; protected positions are kept, positions >= L cleared.
+ *   Returns KVC_E_UNSUPPORTED for another block size, KVC_E_SHAPE for a budget
+ *   outside [0, 1000] or a negative window.
+ *   ws, ws_bytes : NULL, or refresh state of at least
+ *                  kvc_block_workspace_bytes(c, block_tokens) bytes, 16-byte
+ *                  aligned, that the caller keeps for this cache from call to
+ *                  call (zero-filled before the first call). It holds each
+ *                  block's key and the last threshold per (sequence, kv head);
+ *                  a call recomputes only the keys of blocks whose candidates
+ *                  changed since the length it recorded, and tries the previous
+ *                  threshold before a full selection. A different block size or
+ *                  window, or a shorter sequence, rebuilds the state. With NULL
+ *                  every call works from all scores. The mask is the one defined
+ *                  above either way. The state assumes the scores below the
+ *                  previous length minus 128 were not changed by anyone else.
+ *   The mask it writes is a valid input for kvc_decode_attention like any other.
+ *   Returns KVC_E_WORKSPACE for a state smaller than required.
+ */
+KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, const void* k_new,
+                                        const void* v_new, kvc_dtype src, int32_t n_new_max,
+                                        const int32_t* n_new, int32_t budget_permille,
+                                        int32_t block_tokens, int32_t recency_window, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+
+/*
  * kvc_decode_attention - one decode query per sequence over the compressed cache.
  * Source: KV4-RL review, section 3 (INT4 and INT8 regions processed
  * independently, outputs combined by an exact softmax merge).
@@ -179,9 +220,15 @@ KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_d
 
 /* Workspace sizes (host-only, no device work). Return 0 for an invalid cache.
  * kvc_topk_workspace_bytes is the size of the optional refresh state of
- * kvc_score_topk_mask: 1056 bytes per (sequence, kv head). */
+ * kvc_score_topk_mask: 1056 bytes per (sequence, kv head).
+ * kvc_block_workspace_bytes is the size of the optional refresh state of
+ * kvc_score_block_mask (the same for block sizes 16, 32 and 64; 0 for any
+ * other): per (sequence, kv head) a 64-byte header plus 4 bytes per 16
+ * INT4-region positions of a max_ctx-long sequence, rounded up to 16 bytes.
+ * One state may serve calls with different block sizes. */
 KVC_API size_t kvc_attention_workspace_bytes(const kvc_cache* c, int32_t num_q_heads);
 KVC_API size_t kvc_topk_workspace_bytes(const kvc_cache* c);
+KVC_API size_t kvc_block_workspace_bytes(const kvc_cache* c, int32_t block_tokens);
 
 /* Host-only helpers. */
 KVC_API const char* kvc_status_string(kvc_status s);

@@ -18,7 +18,9 @@ order is total and the kept set unique).
 Block policy (KVP promo page, section "Engineering limits": a paged cache
 evicts whole blocks, so token scores are averaged per block before ranking,
 and a coarse recency cut to the most recent positions comes before the
-learned selection). Readings: blocks are the 16-token pages [16j, 16j+16);
+learned selection). Readings: block j of B tokens covers the INT4-region
+offsets [Bj, Bj+B), offset = position - 16, so with B = 16 the blocks are
+whole pages (the section names 16, 32 and 64 as sizes to try);
 the candidates are the INT4-region positions, or with a window W > 0 only
 the last W of them; a block's score is the float32 mean of its candidate
 positions' scores (summed in position order, then divided by their count);

@@ -125,3 +125,40 @@ def test_workspace_size_covers_every_split(lib):
     assert lib.kvc_attention_workspace_bytes(ctypes.byref(desc(head_dim=96)), 32) == 0
     assert lib.kvc_topk_workspace_bytes(ctypes.byref(desc())) == 2 * 8 * 1056
     assert lib.kvc_topk_workspace_bytes(ctypes.byref(desc(head_dim=96))) == 0
+
+
+def test_block_mask_argument_errors(lib):
+    def call(c, budget=500, block=16, window=0, mlp=None, n_max=0, ws=None, ws_bytes=0):
+        return lib.kvc_score_block_mask(ctypes.byref(c), mlp, None, None, 0, n_max, None, budget,
+                                        block, window, ws, ws_bytes, None)
+
+    assert call(desc(), block=8) == -3
+    assert call(desc(), block=48) == -3
+    assert "16, 32 or 64" in kvc.kvc_last_error()
+    assert call(desc(), budget=1001) == -2
+    assert call(desc(), budget=-1) == -2
+    assert call(desc(), window=-1) == -2
+    assert call(desc(scores=None)) == -1
+    assert call(desc(keep_mask=None)) == -1
+    assert call(desc(), mlp=FAKE, n_max=4) == -1   # MLP without K/V rows
+    need = lib.kvc_block_workspace_bytes(ctypes.byref(desc()), 16)
+    assert call(desc(), ws=FAKE, ws_bytes=need - 16) == -4
+    assert "state" in kvc.kvc_last_error()
+    assert call(desc(), ws=FAKE + 4, ws_bytes=need) == -3
+    # more than 131072 blocks per sequence
+    big = 131072 * 16 + 1
+    assert call(desc(max_ctx=big, max_pages_per_seq=(big + 15) // 16)) == -3
+
+
+def test_block_workspace_size(lib):
+    # 64-byte header + one 4-byte key per 16 INT4-region positions, rounded up
+    # to 16 bytes; the same for every block size
+    for max_ctx in (1, 144, 145, 1024, 131072 + 26):
+        c = desc(max_ctx=max_ctx, max_pages_per_seq=(max_ctx + 15) // 16)
+        n4 = max(0, max_ctx - 144)
+        keys = (n4 + 15) // 16
+        stride = 64 + (keys + 3) // 4 * 16
+        for B in (16, 32, 64):
+            assert lib.kvc_block_workspace_bytes(ctypes.byref(c), B) == 2 * 8 * stride
+    assert lib.kvc_block_workspace_bytes(ctypes.byref(desc()), 8) == 0
+    assert lib.kvc_block_workspace_bytes(ctypes.byref(desc(head_dim=96)), 16) == 0

@@ -64,6 +64,14 @@ def run_attention(lc, step=0, q=None):
     return qn, out.cpu().numpy(), lse.cpu().numpy()
 
 
+def policy_keep(w, s4, budget=None):
+    """The oracle's keep flags for INT4-region scores under the workload's policy."""
+    budget = w.budget_permille if budget is None else budget
+    if w.policy == "block":
+        return policy.block_keep(s4, budget, w.block_tokens, w.recency_window)
+    return policy.topk_keep(s4, budget)
+
+
 def expected_keep4(w, lc, cpu, b, kvh, L):
     """Keep flags the oracle expects for one (sequence, kv head)."""
     start, n4 = regions.int4_range(L)
@@ -73,10 +81,10 @@ def expected_keep4(w, lc, cpu, b, kvh, L):
         return W.bernoulli_keep_np(w, lc.layer, b, kvh, L)[start:start + n4]
     if w.mask == "scores":
         s = W.given_scores_np(w, lc.layer, b, L)[kvh]
-        return policy.topk_keep(s[start:start + n4], w.budget_permille)
+        return policy_keep(w, s[start:start + n4])
     # mlp: exact against the GPU's own float32 scores; scores checked separately
     s = cpu["scores"][b, kvh, :L].astype(np.float64)
-    return policy.topk_keep(s[start:start + n4], w.budget_permille)
+    return policy_keep(w, s[start:start + n4])
 
 
 def check_pair(w, lc, cpu, qn, out, lse, b, kvh):
@@ -253,6 +261,216 @@ def test_incremental_topk_all_scores_tied():
     _decode_topk_run(w, 30, lambda s: 300, mlp=zero)
 
 
+# ---------------------------------------------------------------- block policy
+@pytest.mark.parametrize("block,window,budget", [(16, 0, 100), (16, 0, 500), (32, 0, 300),
+                                                 (64, 0, 700), (16, 1000, 500), (64, 777, 250),
+                                                 (16, 0, 0), (32, 5000, 1000)])
+def test_block_policy_mlp_small(block, window, budget):
+    w = W.WORKLOADS["long128k_blk_b10"].replace(name="blk_small", batch=2, ctx_list=(3000, 2345),
+                                                budget_permille=budget, block_tokens=block,
+                                                recency_window=window)
+    check_workload(w)
+
+
+def test_block_policy_edge_lengths_given_scores():
+    lens = (1, 16, 17, 100, 144, 145, 161, 175, 176, 177, 1000, 2049, 0)
+    w = W.WORKLOADS["longtail"].replace(name="blk_edges", batch=len(lens), ctx_range=None,
+                                        ctx_list=lens, policy="block", block_tokens=32,
+                                        recency_window=40)
+    check_workload(w)
+
+
+def _block_mask_only(lengths, kv_heads, scores, budget, block, window):
+    """Refresh a bare cache's mask from given scores; compare every bit."""
+    m = kvc()
+    nseq = len(lengths)
+    max_ctx = scores.shape[-1]
+    pages = (max_ctx + 15) // 16
+    table = torch.arange(nseq * pages, dtype=torch.int32, device="cuda").view(nseq, pages)
+    seq = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    c = m.Cache(nseq, kv_heads, 64, max_ctx, nseq * pages, table, seq)
+    c.keep_mask.fill_(-1)
+    c.scores.copy_(torch.from_numpy(scores))
+    m.kvc_score_block_mask(c, None, None, None, None, budget, window, block)
+    torch.cuda.synchronize()
+    words = c.keep_mask.cpu().numpy()
+    nbits = words.shape[-1] * 32
+    for b, L in enumerate(lengths):
+        start, n4 = regions.int4_range(L)
+        for h in range(kv_heads):
+            want = np.zeros(nbits, bool)
+            want[regions.int8_positions(L)] = True
+            want[start:start + n4] = policy.block_keep(scores[b, h, start:start + n4], budget,
+                                                       block, window)
+            got = mask_bits(words[b, h], nbits)
+            bad = np.flatnonzero(got != want)
+            assert bad.size == 0, f"b={b} h={h} L={L}: {bad.size} bits differ, first {bad[:8]}"
+
+
+def _special_scores(kind, shape, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "ties":  # small integers: exact block means, many equal keys
+        return rng.integers(0, 3, size=shape).astype(np.float32)
+    s = rng.standard_normal(shape).astype(np.float32)
+    flat = s.reshape(-1)
+    n = flat.size
+    for value, count in ((np.nan, 40), (np.inf, 20), (-np.inf, 20), (-0.0, 200), (0.0, 200)):
+        flat[rng.integers(0, n, count)] = value
+    # some whole blocks of one value (equal means across blocks, -0 and +0 alike)
+    for v in (-0.0, 0.0, 1.5, 1.5, -np.inf):
+        b0 = int(rng.integers(0, n // 16)) * 16
+        flat[b0:b0 + 16] = v
+    return s
+
+
+@pytest.mark.parametrize("kind", ["ties", "special"])
+@pytest.mark.parametrize("block,window,budget", [(16, 0, 300), (16, 0, 0), (16, 0, 1000),
+                                                 (32, 1234, 500), (64, 0, 123), (16, 200000, 999),
+                                                 (64, 100, 500)])
+def test_block_mask_special_scores(kind, block, window, budget):
+    """Ties, NaN, infinities and signed zeros; one sequence has more than 8192
+    16-token blocks (block keys recomputed per radix pass instead of cached)."""
+    lengths = [0, 100, 144, 145, 160, 161, 5000, 140000]
+    scores = _special_scores(kind, (len(lengths), 2, 140000), seed=block + window + budget)
+    _block_mask_only(lengths, 2, scores, budget, block, window)
+
+
+def test_block_mask_max_context():
+    """The longest context the cache accepts, 16-token blocks (130559 of them)."""
+    L = 2089088
+    scores = _special_scores("ties", (1, 1, L), seed=7)
+    _block_mask_only([L], 1, scores, 400, 16, 0)
+    _block_mask_only([L], 1, scores, 400, 64, 1_000_000)
+
+
+def test_block_policy_decode_steps():
+    """Append, score and block refresh every step across the recent window's
+    edge; mask checked every step, attention at a few."""
+    m = kvc()
+    w = W.WORKLOADS["fullstep"].replace(name="blk_steps", batch=3, layers=1, ctx=130,
+                                        decode_steps=60, ctx_list=(130, 170, 1000), policy="block",
+                                        block_tokens=16, recency_window=300)
+    lc = LayerCache(w)
+    lens = lc.lengths.copy()
+    one = torch.ones(w.batch, dtype=torch.int32, device="cuda")
+    for step in range(1, 61):
+        k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+        v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+        lens += 1
+        lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        lc.lengths = lens.copy()
+        m.kvc_quantize_append(lc.cache, k_new, v_new, one)
+        lc.refresh(k_new, v_new, one)
+        cpu = cpu_buffers(lc)
+        for b in range(w.batch):
+            L = int(lens[b])
+            for h in range(w.kv_heads):
+                keep4 = keep4_from_mask(cpu["keep_mask"][b, h], L)
+                want = expected_keep4(w, lc, cpu, b, h, L)
+                assert np.array_equal(keep4, want), f"step {step} b={b} h={h}"
+        if step % 15 == 0:
+            qn, out, lse = run_attention(lc, step=step)
+            for b in range(w.batch):
+                for h in (0, w.kv_heads - 1):
+                    check_pair(w, lc, cpu, qn, out, lse, b, h)
+
+
+def test_block_policy_append_longer_than_recent_window():
+    """More than 128 rows appended in one call: they are scored in a launch of
+    their own before the block refresh (a shorter append runs both in one)."""
+    m = kvc()
+    w = W.WORKLOADS["fullstep"].replace(name="blk_bigappend", batch=2, layers=1, ctx=300,
+                                        ctx_list=(300, 1000), decode_steps=200, policy="block",
+                                        block_tokens=32, recency_window=500)
+    lc = LayerCache(w)
+    lens0 = lc.lengths.copy()
+    n = np.array([200, 150], np.int32)
+    k_new = torch.zeros((w.batch, 200, w.kv_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    v_new = torch.zeros_like(k_new)
+    for b in range(w.batch):
+        t0, t1 = int(lens0[b]), int(lens0[b] + n[b])
+        k_new[b, :n[b]] = W.kv_source_torch(w, 0, "K", b, t0, t1, "cuda")
+        v_new[b, :n[b]] = W.kv_source_torch(w, 0, "V", b, t0, t1, "cuda")
+    lens = lens0 + n
+    lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+    lc.lengths = lens.copy()
+    nn = torch.from_numpy(n).cuda()
+    m.kvc_quantize_append(lc.cache, k_new, v_new, nn)
+    lc.refresh(k_new, v_new, nn)
+    cpu = cpu_buffers(lc)
+    qn, out, lse = run_attention(lc, step=1)
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            check_pair(w, lc, cpu, qn, out, lse, b, h)
+
+
+def _block_state_run(w, steps, plan, shrink=None, stall=None):
+    """Decode steps refreshing through one block refresh state; after every
+    step the mask must equal the oracle's block policy on the GPU's scores.
+    ``plan(step)`` gives (budget, window, block) and may change them mid-run;
+    ``shrink`` names (step, sequence, positions) rollbacks of a sequence."""
+    m = kvc()
+    lc = LayerCache(w)
+    state = m.block_workspace(lc.cache, 16)  # the largest of the three sizes
+    lens = lc.lengths.copy()
+    for step in range(steps):
+        budget, window, block = plan(step)
+        n_new = np.ones(w.batch, np.int32)
+        for (s_, b) in (stall or ()):
+            if s_ == step:
+                n_new[b] = 0
+        for (s_, b, d) in (shrink or ()):
+            if s_ == step:
+                lens[b] -= d
+        k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+        v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+        lens += n_new
+        lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        nn = torch.from_numpy(n_new).cuda()
+        m.kvc_quantize_append(lc.cache, k_new, v_new, nn)
+        m.kvc_score_block_mask(lc.cache, lc.mlp, k_new, v_new, nn, budget, window, block, ws=state)
+        torch.cuda.synchronize()
+        maskw = lc.cache.keep_mask.cpu().numpy()
+        scores = lc.cache.scores.cpu().numpy()
+        for b in range(w.batch):
+            L = int(lens[b])
+            start, n4 = regions.int4_range(L)
+            for h in range(w.kv_heads):
+                bits = mask_bits(maskw[b, h], maskw.shape[-1] * 32)
+                want = policy.block_keep(scores[b, h, start:start + n4], budget, block, window)
+                assert np.array_equal(bits[start:start + n4], want), f"step {step} b={b} h={h}"
+                assert bits[regions.int8_positions(L)].all(), f"step {step} b={b} h={h} protected"
+                assert not bits[L:].any(), f"step {step} b={b} h={h} beyond L"
+    return lc
+
+
+def test_block_state_every_step():
+    """Hundreds of steps on one state: the budget changes (threshold retried,
+    then reselected), sequences stall and one is rolled back (state rebuilt),
+    then the window and the block size change (state rebuilt)."""
+    w = W.WORKLOADS["fullstep"].replace(name="blk_state", batch=3, kv_heads=2, q_heads=8, layers=1,
+                                        ctx=2500, ctx_list=(140, 700, 2500), decode_steps=400,
+                                        policy="block")
+
+    def plan(step):
+        budget = 300 if step < 100 else 120
+        window = 0 if step < 200 else 600
+        block = 16 if step < 260 else (32 if step < 330 else 64)
+        return budget, window, block
+
+    _block_state_run(w, 400, plan, shrink=[(150, 1, 50)], stall=[(40, 0), (41, 0), (120, 2)])
+
+
+def test_block_state_many_blocks_per_step():
+    """A state over 2500 blocks (the key pass that spans many waves) with a
+    recency window; a stall and a long rollback rebuild it."""
+    w = W.WORKLOADS["fullstep"].replace(name="blk_state_big", batch=2, kv_heads=2, q_heads=8,
+                                        layers=1, ctx=40000, ctx_list=(40000, 23000), decode_steps=40,
+                                        policy="block")
+    _block_state_run(w, 40, lambda s: (250 if s < 20 else 700, 0 if s < 30 else 20000, 16),
+                     shrink=[(10, 1, 5000)], stall=[(5, 0)])
+
+
 # ---------------------------------------------------------------- full sizes
 def sample_pairs(w, n, seed):
     rng = np.random.default_rng(seed)
@@ -272,7 +490,8 @@ def test_full_longtail_sampled():
     check_workload(w, pairs)
 
 
-@pytest.mark.parametrize("name", ["long128k_b10", "long128k_b50"])
+@pytest.mark.parametrize("name", ["long128k_b10", "long128k_b50", "long128k_blk_b10",
+                                  "long128k_r16k_b50"])
 def test_full_long128k_sampled(name):
     w = W.WORKLOADS[name]
     check_workload(w, [(0, 0), (3, 7), (1, 4)])

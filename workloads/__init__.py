@@ -169,6 +169,9 @@ class Workload:
     src_dtype: str = "bf16"                    # K/V/Q source type: "bf16" or "f32"
     mask: str = "all"                          # "all" | "bernoulli" | "scores" | "mlp"
     budget_permille: Optional[int] = None
+    policy: str = "token"                      # keep policy: "token" top-k or "block" (whole blocks)
+    block_tokens: int = 16                     # block size of the "block" policy
+    recency_window: int = 0                    # "block" policy: candidates = last W INT4 positions (0 = all)
     outlier_channels: int = 0                  # (kv head, dim) channels scaled x8
     shuffled_pages: bool = True
     decode_steps: int = 0                      # extra capacity for appended tokens
@@ -214,6 +217,16 @@ WORKLOADS = {
                              budget_permille=100),
     "long128k_b50": Workload("long128k_b50", 4, 32, 8, 128, ctx=131072, mask="mlp",
                              budget_permille=500),
+    # Long context, whole 16-token blocks ranked by mean MLP score, at 10% and 50%.
+    "long128k_blk_b10": Workload("long128k_blk_b10", 4, 32, 8, 128, ctx=131072, mask="mlp",
+                                 budget_permille=100, policy="block"),
+    "long128k_blk_b50": Workload("long128k_blk_b50", 4, 32, 8, 128, ctx=131072, mask="mlp",
+                                 budget_permille=500, policy="block"),
+    # Long context, coarse recency cut to the last 16K positions, then blocks at 10% / 50%.
+    "long128k_r16k_b10": Workload("long128k_r16k_b10", 4, 32, 8, 128, ctx=131072, mask="mlp",
+                                  budget_permille=100, policy="block", recency_window=16384),
+    "long128k_r16k_b50": Workload("long128k_r16k_b50", 4, 32, 8, 128, ctx=131072, mask="mlp",
+                                  budget_permille=500, policy="block", recency_window=16384),
     # Full decode step: 36 layers, append + score + top-k refresh (30%) + attention.
     "fullstep": Workload("fullstep", 128, 32, 8, 128, layers=36, ctx=32768, mask="mlp",
                          budget_permille=300, decode_steps=64),
