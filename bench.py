@@ -56,8 +56,13 @@ def algorithmic_bytes(w, lengths, keep4_counts):
         n8 = min(L, 16) + max(0, L - max(16, L - 128))
         n4 = max(0, L - 144)
         total += Hkv * n8 * per8 + int(keep4_counts[b]) * per4
-        total += Hkv * ((16 + n4 + 31) // 32) * 4     # mask words over the INT4 region
-        total += ((L + 15) // 16) * 4                 # block table entries
+        if w.recency_window > 0:  # the windowed call reads only the window's words and pages
+            nw = min(n4, w.recency_window)
+            total += Hkv * ((nw + 31) // 32) * 4
+            total += ((nw + 15) // 16) * 4
+        else:
+            total += Hkv * ((16 + n4 + 31) // 32) * 4     # mask words over the INT4 region
+            total += ((L + 15) // 16) * 4                 # block table entries
         total += Hq * (D * qbytes + D * 4 + 4)        # q in, out and lse
     return total
 
@@ -283,7 +288,11 @@ def main():
             if record:
                 e0, e1 = events.pop()
                 e0.record(stream)
-            kvc.kvc_decode_attention(lc.cache, st["q"][s], st["out"], st["lse"], st["ws"])
+            if w.recency_window > 0:
+                kvc.kvc_decode_attention_windowed(lc.cache, w.recency_window, st["q"][s], st["out"],
+                                                  st["lse"], st["ws"])
+            else:
+                kvc.kvc_decode_attention(lc.cache, st["q"][s], st["out"], st["lse"], st["ws"])
             if record:
                 e1.record(stream)
                 attn_events.append((e0, e1, lc.w, st["lens"].copy()))

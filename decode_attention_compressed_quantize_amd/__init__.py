@@ -81,6 +81,10 @@ _SIGNATURES = {
                                             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                             ctypes.c_void_p]),
+    "kvc_decode_attention_windowed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                                     ctypes.c_int, ctypes.c_int32, ctypes.c_float,
+                                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_size_t, ctypes.c_void_p]),
     "kvc_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
     "kvc_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "kvc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -244,6 +248,16 @@ def kvc_decode_attention(cache: Cache, q, out, lse, ws, softmax_scale: float = 0
     _check(lib().kvc_decode_attention(cache.ref(), _ptr(q), _dtype_code(q), q.shape[1],
                                       float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), nbytes,
                                       _stream(stream)), "kvc_decode_attention")
+
+
+def kvc_decode_attention_windowed(cache: Cache, int4_window: int, q, out, lse, ws,
+                                  softmax_scale: float = 0.0, stream=None):
+    """Decode attention reading only the last ``int4_window`` INT4-region positions (0: all)."""
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().kvc_decode_attention_windowed(cache.ref(), int(int4_window), _ptr(q), _dtype_code(q),
+                                               q.shape[1], float(softmax_scale), _ptr(out), _ptr(lse),
+                                               _ptr(ws), nbytes, _stream(stream)),
+           "kvc_decode_attention_windowed")
 
 
 def topk_workspace(cache: Cache, device="cuda"):

@@ -90,6 +90,7 @@ struct AttnParams {
   int words;
   int chunk;
   int nsplit;
+  int window;  // > 0: only the last `window` INT4-region positions are read
 };
 
 __device__ inline float h2f(uint32_t bits16) {
@@ -265,9 +266,16 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
   const int n4 = L > kInt8Slots ? L - kInt8Slots : 0;
-  const int r0 = kSink, r1 = kSink + n4;  // INT4 region [r0, r1)
+  // INT4 region [r0, r1), or its last `window` positions; chunks start at
+  // base (0, or the window's start rounded down to 64 positions)
+  int r0 = kSink, base = 0;
+  const int r1 = kSink + n4;
+  if (p.window > 0 && r1 - p.window > r0) {
+    r0 = r1 - p.window;
+    base = r0 & ~63;
+  }
   const int q4 = p.chunk / kWaves;
-  const int w0 = split * p.chunk + wave * q4;
+  const int w0 = base + split * p.chunk + wave * q4;
   const int lo = w0 > r0 ? w0 : r0;
   const int hi = w0 + q4 < r1 ? w0 + q4 : r1;
 
@@ -886,8 +894,9 @@ hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, hipStr
 
 hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype, int num_q_heads,
                             float softmax_scale, float* out, float* lse, float* ws,
-                            const AttnPlan& plan, hipStream_t s) {
+                            const AttnPlan& plan, int window, hipStream_t s) {
   AttnParams p;
+  p.window = window;
   p.q = q;
   p.codes = c.int4_codes;
   p.meta = c.int4_meta;

@@ -73,32 +73,44 @@ kvc_status launched(hipError_t e) {
 
 namespace kvc {
 
-AttnPlan plan_attention(const kvc_cache& c, int num_q_heads) {
-  (void)num_q_heads;
-  // INT4 chunk j covers positions [j*chunk, (j+1)*chunk) of the INT4 region
-  // [16, max_ctx - 128). Chunks are made as long as the per-wave list allows
-  // while leaving at least about kTarget chunk workgroups: a long list keeps
-  // a workgroup's load pipeline full and pays its set-up (mask and
-  // block-table loads, compaction) and epilogue rarely. Measured on 256 CUs,
-  // ~512 long chunk workgroups beat one or two full resident rounds (768 or
-  // 1536 workgroups at three per CU) at 10% and 50% kept. The short
-  // INT8-region workgroups go first when they fit in one round, else after
-  // the chunks.
+AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window) {
+  // INT4 chunk j covers positions [base + j*chunk, base + (j+1)*chunk) of the
+  // INT4 region [16, max_ctx - 128), base = 0 (with a window: the window's
+  // first position rounded down to 64). Chunks are made as long as the
+  // per-wave list allows while leaving at least about kTarget chunk
+  // workgroups: a long list keeps a workgroup's load pipeline full and pays
+  // its set-up (mask and block-table loads, compaction) and epilogue rarely.
+  // Measured on 256 CUs, ~512 long chunk workgroups beat one or two full
+  // resident rounds (768 or 1536 workgroups at three per CU) at 10% and 50%
+  // kept. The short INT8-region workgroups go first when they fit in one
+  // round, else after the chunks.
   constexpr long long kResident = 768;  // 3 workgroups per CU x 256 CUs
   constexpr long long kTarget = 384;
   const long long end4 = c.max_ctx > kInt8Slots ? (long long)c.max_ctx - kRecent : 0;
+  long long span = end4;  // positions a sequence's chunks must cover
+  if (window > 0 && (long long)window + 64 < span) span = (long long)window + 64;
   const long long pairs = (long long)c.batch * c.num_kv_heads;
-  const long long target = kTarget;
-  long long chunk = (pairs * end4 + target - 1) / target;
-  const long long fit = (end4 + kMaxParts - 2) / (kMaxParts - 1);  // nsplit + 1 <= kMaxParts
+  long long chunk = (pairs * span + kTarget - 1) / kTarget;
+  const long long fit = (span + kMaxParts - 2) / (kMaxParts - 1);  // nsplit + 1 <= kMaxParts
   if (chunk < fit) chunk = fit;
   chunk = (chunk + 255) / 256 * 256;
   if (chunk < 1024) chunk = 1024;
   if (chunk > kMaxChunk) chunk = kMaxChunk;
   AttnPlan p;
   p.chunk = (int)chunk;
-  p.nsplit = end4 > 0 ? (int)((end4 + chunk - 1) / chunk) : 1;
+  p.nsplit = span > 0 ? (int)((span + chunk - 1) / chunk) : 1;
   p.int8_first = pairs <= kResident ? 1 : 0;
+  if (window > 0) {
+    // never more partials than the whole-region plan, whose count sizes the workspace
+    const AttnPlan full = plan_attention(c, num_q_heads, 0);
+    if (p.nsplit > full.nsplit) {
+      long long c2 = (span + full.nsplit - 1) / full.nsplit;
+      c2 = (c2 + 255) / 256 * 256;
+      if (c2 < 1024) c2 = 1024;
+      p.chunk = (int)c2;
+      p.nsplit = (int)((span + c2 - 1) / c2);
+    }
+  }
   return p;
 }
 
@@ -124,7 +136,7 @@ KVC_API const char* kvc_status_string(kvc_status s) {
 
 KVC_API size_t kvc_attention_workspace_bytes(const kvc_cache* c, int32_t num_q_heads) {
   if (check_cache(c, 0) != KVC_OK || num_q_heads < 1 || num_q_heads % c->num_kv_heads) return 0;
-  const kvc::AttnPlan p = kvc::plan_attention(*c, num_q_heads);
+  const kvc::AttnPlan p = kvc::plan_attention(*c, num_q_heads, 0);
   return kvc::attention_ws_floats(*c, num_q_heads, p) * sizeof(float);
 }
 
@@ -218,9 +230,10 @@ KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, co
       kvc::launch_block_topk(*c, budget_permille, block_tokens, recency_window, ws, stream));
 }
 
-KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_dtype q_dtype,
-                                        int32_t num_q_heads, float softmax_scale, float* out,
-                                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+static kvc_status decode_attention(const kvc_cache* c, int32_t window, const void* q,
+                                   kvc_dtype q_dtype, int32_t num_q_heads, float softmax_scale,
+                                   float* out, float* lse, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
   kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8 | kNeedMask);
   if (st != KVC_OK) return st;
   if (!q || !out) return fail(KVC_E_NULL, "q or out is NULL");
@@ -235,12 +248,30 @@ KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_d
     return fail(KVC_E_UNSUPPORTED, "num_q_heads/num_kv_heads must be 1, 2 or 4");
   if ((long long)c->max_ctx > (long long)(kvc::kMaxParts - 1) * kvc::kMaxChunk + kvc::kRecent)
     return fail(KVC_E_UNSUPPORTED, "max_ctx above 2089088 positions is not supported");
-  const kvc::AttnPlan plan = kvc::plan_attention(*c, num_q_heads);
-  const size_t need = kvc::attention_ws_floats(*c, num_q_heads, plan) * sizeof(float);
+  if (window < 0) return fail(KVC_E_SHAPE, "int4_window must be >= 0");
+  const kvc::AttnPlan full = kvc::plan_attention(*c, num_q_heads, 0);
+  const size_t need = kvc::attention_ws_floats(*c, num_q_heads, full) * sizeof(float);
   if (!ws || ws_bytes < need) return fail(KVC_E_WORKSPACE, "attention workspace too small");
+  const kvc::AttnPlan plan = window > 0 ? kvc::plan_attention(*c, num_q_heads, window) : full;
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
   return launched(kvc::launch_attention(*c, q, q_dtype, num_q_heads, scale, out, lse,
-                                        static_cast<float*>(ws), plan, stream));
+                                        static_cast<float*>(ws), plan, window, stream));
+}
+
+KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_dtype q_dtype,
+                                        int32_t num_q_heads, float softmax_scale, float* out,
+                                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_attention(c, 0, q, q_dtype, num_q_heads, softmax_scale, out, lse, ws, ws_bytes,
+                          stream);
+}
+
+KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int4_window,
+                                                 const void* q, kvc_dtype q_dtype,
+                                                 int32_t num_q_heads, float softmax_scale,
+                                                 float* out, float* lse, void* ws, size_t ws_bytes,
+                                                 hipStream_t stream) {
+  return decode_attention(c, int4_window, q, q_dtype, num_q_heads, softmax_scale, out, lse, ws,
+                          ws_bytes, stream);
 }
 
 }  // extern "C"

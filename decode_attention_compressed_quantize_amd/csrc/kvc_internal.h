@@ -29,7 +29,8 @@ struct AttnPlan {
   int int8_first;  // dispatch order: INT8-region workgroups before (1) or after (0) the chunks
 };
 
-AttnPlan plan_attention(const kvc_cache& c, int num_q_heads);
+// window > 0: chunks cover only the last `window` INT4-region positions.
+AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window);
 
 // Attention workspace: partials float [B][Hkv][nsplit + 1][G][2 + D] as
 // (m, l, o[0..D-1]) with m in log2 units. No initialisation needed.
@@ -104,6 +105,6 @@ hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k
 
 hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype, int num_q_heads,
                             float softmax_scale, float* out, float* lse, float* ws,
-                            const AttnPlan& plan, hipStream_t s);
+                            const AttnPlan& plan, int window, hipStream_t s);
 
 }  // namespace kvc

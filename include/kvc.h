@@ -218,6 +218,26 @@ KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_d
                                         int32_t num_q_heads, float softmax_scale, float* out,
                                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * kvc_decode_attention_windowed - kvc_decode_attention restricted to a
+ * recency window of the INT4 region.
+ * Source: KVP promo page (arXiv 2602.10238), section "Engineering limits": a
+ * coarse recency cut (e.g. to the last 16K positions) before the learned
+ * selection; what the cut removes is never read.
+ *   int4_window : 0 (the whole region: same as kvc_decode_attention), or W > 0:
+ *                 only INT4-region positions in [max(16, L-128-W), L-128) whose
+ *                 keep_mask bit is set are attended, plus every INT8 position;
+ *                 mask bits of older INT4 positions are not read. Work is
+ *                 planned over W positions per sequence instead of max_ctx.
+ *   Other arguments, the workspace size and errors as kvc_decode_attention;
+ *   KVC_E_SHAPE for a negative window.
+ */
+KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int4_window,
+                                                 const void* q, kvc_dtype q_dtype,
+                                                 int32_t num_q_heads, float softmax_scale,
+                                                 float* out, float* lse, void* ws, size_t ws_bytes,
+                                                 hipStream_t stream);
+
 /* Workspace sizes (host-only, no device work). Return 0 for an invalid cache.
  * kvc_topk_workspace_bytes is the size of the optional refresh state of
  * kvc_score_topk_mask: 1056 bytes per (sequence, kv head).

@@ -86,6 +86,11 @@ def test_attention_argument_errors(lib):
     assert attn(lib, desc(), ws=None) == -4
     assert attn(lib, desc(), ws_bytes=16) == -4
     assert "workspace" in kvc.kvc_last_error()
+    c = desc()
+    assert lib.kvc_decode_attention_windowed(ctypes.byref(c), -1, FAKE, 0, 32, 0.0, FAKE, None,
+                                             FAKE, 1 << 40, None) == -2
+    assert lib.kvc_decode_attention_windowed(ctypes.byref(c), 100, FAKE, 0, 32, 0.0, FAKE, None,
+                                             FAKE, 16, None) == -4
 
 
 def test_append_and_topk_argument_errors(lib):

@@ -51,13 +51,18 @@ def cpu_buffers(lc):
     }
 
 
-def run_attention(lc, step=0, q=None):
+def run_attention(lc, step=0, q=None, window=None):
     w = lc.w
     if q is None:
         q = lc.queries(step)
     out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device="cuda")
-    kvc().kvc_decode_attention(lc.cache, q, out, lse, lc.workspace())
+    if window is None:
+        window = w.recency_window  # a recency-cut workload reads only its window
+    if window > 0:
+        kvc().kvc_decode_attention_windowed(lc.cache, window, q, out, lse, lc.workspace())
+    else:
+        kvc().kvc_decode_attention(lc.cache, q, out, lse, lc.workspace())
     torch.cuda.synchronize()
     qn = q.cpu()
     qn = qn.view(torch.int16).numpy().view(np.uint16) if q.dtype == torch.bfloat16 else qn.numpy()
@@ -469,6 +474,27 @@ def test_block_state_many_blocks_per_step():
                                         policy="block")
     _block_state_run(w, 40, lambda s: (250 if s < 20 else 700, 0 if s < 30 else 20000, 16),
                      shrink=[(10, 1, 5000)], stall=[(5, 0)])
+
+
+@pytest.mark.parametrize("window", [1, 63, 64, 100, 1000, 2700, 5000])
+def test_windowed_attention_ignores_older_positions(window):
+    """A token-level mask keeps positions all over the INT4 region; the
+    windowed call must attend to exactly those in the last `window` of it."""
+    w = W.WORKLOADS["long128k_b10"].replace(name="win", batch=3, ctx_list=(3000, 700, 145),
+                                            budget_permille=500)
+    lc = LayerCache(w)
+    cpu = cpu_buffers(lc)
+    qn, out, lse = run_attention(lc, window=window)
+    G = w.group_size
+    for b in range(w.batch):
+        L = int(lc.lengths[b])
+        _, n4 = regions.int4_range(L)
+        for h in range(w.kv_heads):
+            keep4 = keep4_from_mask(cpu["keep_mask"][b, h], L).copy()
+            keep4[: max(0, n4 - window)] = False
+            hs = slice(h * G, (h + 1) * G)
+            ro, rl = oracle_heads(w, lc.layer, b, h, L, keep4, qn[b, hs])
+            assert_attention_close(out[b, hs], lse[b, hs], ro, rl, what=f"window {window} b={b} h={h}")
 
 
 # ---------------------------------------------------------------- full sizes
