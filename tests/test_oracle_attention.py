@@ -183,3 +183,61 @@ def test_int4_region_reads_int4_and_protected_reads_int8():
     mask4[pos8] = False
     np.testing.assert_array_equal(kh[mask4], k4[mask4])
     assert not np.array_equal(k8, k4[pos8])
+
+
+# ------------------------------------------------------------- pure KV4
+# The KV4-RL review (section 3) compares INT8 protection against pure KV4: no
+# protected positions, so every cached position is INT4 and subject to the
+# keep mask. In the oracle that is n_sink = n_recent = 0.
+def int4_exact_sources(L, D, seed):
+    """K/V rows that the INT4 group encoding represents exactly (codes 0..15 plus an offset)."""
+    rng = np.random.default_rng(seed)
+    x = np.empty((L, D), np.float32)
+    for t in range(L):
+        for g in range(D // 32):
+            codes = rng.integers(0, 16, 32)
+            codes[0], codes[1] = 0, 15
+            x[t, g * 32:(g + 1) * 32] = codes + rng.integers(-20, 20)
+    return x
+
+
+@pytest.mark.parametrize("L,keep_frac", [(1, 1.0), (40, 0.5), (300, 1.0), (300, 0.2)])
+def test_pure_kv4_composition_equals_plain_attention_on_exact_data(L, keep_frac):
+    D, G = 64, 2
+    k, v = int4_exact_sources(L, D, 21), int4_exact_sources(L, D, 22)
+    q = rand((G, D), 23) * 0.05
+    keep = np.random.default_rng(24).random(L) < keep_frac
+    keep[L // 2] = True  # never empty
+    out, lse = reference.decode_group(q, k, v, keep, n_sink=0, n_recent=0)
+    pos = np.nonzero(keep)[0]
+    s = (q @ k[pos].astype(np.float64).T) / math.sqrt(D)
+    mx = s.max(axis=1, keepdims=True)
+    e = np.exp(s - mx)
+    ref = (e @ v[pos].astype(np.float64)) / e.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(lse, (mx[:, 0] + np.log(e.sum(axis=1))), rtol=1e-12)
+
+
+def test_pure_kv4_reads_every_position_from_int4():
+    L, D = 200, 32
+    rng = np.random.default_rng(25)
+    k = rng.standard_normal((L, D)).astype(np.float32)
+    v = rng.standard_normal((L, D)).astype(np.float32)
+    assert regions.int8_positions(L, 0, 0).shape == (0,)
+    assert regions.int4_range(L, 0, 0) == (0, L)
+    enc = reference.encode(k, v, 0, 0)
+    kh, vh = reference.decoded(enc)
+    np.testing.assert_array_equal(kh, quant.int4_decode(*quant.int4_encode(k)))
+    np.testing.assert_array_equal(vh, quant.int4_decode(*quant.int4_encode(v)))
+    keep = rng.random(L) < 0.3
+    np.testing.assert_array_equal(reference.kept_positions(L, keep, 0, 0), np.nonzero(keep)[0])
+    # the protected configuration attends the window whatever the mask says
+    assert len(reference.kept_positions(L, np.zeros(L - 144, bool))) == 144
+
+
+def test_pure_kv4_all_evicted_gives_empty_attention():
+    L, D = 50, 32
+    k = rand((L, D), 26).astype(np.float32)
+    out, lse = reference.decode_group(rand((2, D), 27), k, k, np.zeros(L, bool), n_sink=0,
+                                      n_recent=0)
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse))
