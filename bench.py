@@ -37,6 +37,7 @@ WORKLOAD_LAYERS = {
     "long128k": ["long128k_b10", "long128k_b50"],
     "long128k_blocks": ["long128k_blk_b10", "long128k_blk_b50"],
     "long128k_recent16k": ["long128k_r16k_b10", "long128k_r16k_b50"],
+    "long128k_kv4": ["long128k_kv4_b10", "long128k_kv4_b50"],
     "uniform4k": ["uniform4k"],
     "longtail": ["longtail"],
     "fullstep": ["fullstep"] * 36,
@@ -51,17 +52,18 @@ def algorithmic_bytes(w, lengths, keep4_counts):
     per8 = 2 * D + 8                  # K+V int8 codes + two fp32 scales
     qbytes = 2 if w.src_dtype == "bf16" else 4
     total = 0
+    sink, recent = (16, 128) if w.protect else (0, 0)
     for b, L in enumerate(lengths):
         L = int(L)
-        n8 = min(L, 16) + max(0, L - max(16, L - 128))
-        n4 = max(0, L - 144)
+        n8 = min(L, sink) + max(0, L - max(sink, L - recent)) if w.protect else 0
+        n4 = max(0, L - sink - recent)
         total += Hkv * n8 * per8 + int(keep4_counts[b]) * per4
         if w.recency_window > 0:  # the windowed call reads only the window's words and pages
             nw = min(n4, w.recency_window)
             total += Hkv * ((nw + 31) // 32) * 4
             total += ((nw + 15) // 16) * 4
         else:
-            total += Hkv * ((16 + n4 + 31) // 32) * 4     # mask words over the INT4 region
+            total += Hkv * ((sink + n4 + 31) // 32) * 4   # mask words over the INT4 region
             total += ((L + 15) // 16) * 4                 # block table entries
         total += Hq * (D * qbytes + D * 4 + 4)        # q in, out and lse
     return total
@@ -74,8 +76,9 @@ def kept_counts(w, lengths):
     hold fewer than ``block_tokens`` positions (at least one each), so the
     count used is the lower bound (kb - 2) * B + 2, never an overstatement."""
     out = []
+    slots = 144 if w.protect else 0
     for L in lengths:
-        n4 = max(0, int(L) - 144)
+        n4 = max(0, int(L) - slots)
         if w.mask == "all":
             k = n4
         elif w.mask in ("scores", "mlp") and w.policy == "block":
@@ -135,8 +138,9 @@ def _cpu_pair(args):
         L = int(w.lengths()[b])
         k = W.bf16_bits_to_f32(W.kv_source_np(w, 0, "K", b, 0, L, kvh=kvh))
         v = W.bf16_bits_to_f32(W.kv_source_np(w, 0, "V", b, 0, L, kvh=kvh))
-        enc = reference.encode(k, v)
-        start, n4 = regions.int4_range(L)
+        ns, nr = (regions.N_SINK, regions.N_RECENT) if w.protect else (0, 0)
+        enc = reference.encode(k, v, ns, nr)
+        start, n4 = regions.int4_range(L, ns, nr)
         if w.mask == "mlp":
             s = policy.mlp_scores(k, v, W.mlp_weights(w, 0)[kvh])
             if w.policy == "block":
@@ -150,10 +154,10 @@ def _cpu_pair(args):
         q = W.bf16_bits_to_f32(W.queries_np(w, 0, 0)[b, kvh * G:(kvh + 1) * G]).astype(np.float64)
         t0 = time.perf_counter()
         kh, vh = reference.decoded(enc)
-        pos = reference.kept_positions(L, keep4)
+        pos = reference.kept_positions(L, keep4, ns, nr)
         attention.attend(q, kh[pos], vh[pos])
         dt = time.perf_counter() - t0
-        n8 = len(regions.int8_positions(L))
+        n8 = len(regions.int8_positions(L, ns, nr))
         nbytes = int(keep4.sum()) * (w.head_dim + 8 * (w.head_dim // 32)) + n8 * (2 * w.head_dim + 8)
         return nbytes, dt
 

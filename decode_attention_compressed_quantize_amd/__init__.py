@@ -143,11 +143,13 @@ class Cache:
 
     ``block_table`` (int32 [B][max_pages]) and ``seq_lens`` (int32 [B]) are
     device tensors owned by the caller; ``seq_lens`` must hold the lengths
-    after any append of the current step.
+    after any append of the current step. ``protect=False`` builds the
+    unprotected (pure KV4) cache: no INT8 side cache, n_sink = n_recent = 0.
     """
 
     def __init__(self, batch: int, kv_heads: int, head_dim: int, max_ctx: int,
-                 num_phys_pages: int, block_table, seq_lens, device="cuda", with_scores=True):
+                 num_phys_pages: int, block_table, seq_lens, device="cuda", with_scores=True,
+                 protect: bool = True):
         import torch
 
         self.batch, self.kv_heads, self.head_dim, self.max_ctx = batch, kv_heads, head_dim, max_ctx
@@ -156,8 +158,13 @@ class Cache:
         D = head_dim
         self.int4_codes = torch.zeros((num_phys_pages, kv_heads, PAGE, 2, D // 2), dtype=torch.uint8, device=dev)
         self.int4_meta = torch.zeros((num_phys_pages, kv_heads, PAGE, 2, D // GROUP, 2), dtype=torch.int16, device=dev)
-        self.int8_codes = torch.zeros((batch, kv_heads, INT8_SLOTS, 2, D), dtype=torch.int8, device=dev)
-        self.int8_scales = torch.zeros((batch, kv_heads, INT8_SLOTS, 2), dtype=torch.float32, device=dev)
+        self.protect = protect
+        self.n_sink, self.n_recent = (N_SINK, N_RECENT) if protect else (0, 0)
+        if protect:
+            self.int8_codes = torch.zeros((batch, kv_heads, INT8_SLOTS, 2, D), dtype=torch.int8, device=dev)
+            self.int8_scales = torch.zeros((batch, kv_heads, INT8_SLOTS, 2), dtype=torch.float32, device=dev)
+        else:
+            self.int8_codes = self.int8_scales = None
         self.mask_words = (max_ctx + 31) // 32
         self.keep_mask = torch.zeros((batch, kv_heads, self.mask_words), dtype=torch.int32, device=dev)
         self.scores = (torch.zeros((batch, kv_heads, max_ctx), dtype=torch.float32, device=dev)
@@ -167,7 +174,7 @@ class Cache:
         assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
         self.desc = KvcCacheStruct(
             batch, kv_heads, head_dim, PAGE, block_table.shape[1], num_phys_pages,
-            N_SINK, N_RECENT, GROUP, max_ctx,
+            self.n_sink, self.n_recent, GROUP, max_ctx,
             _ptr(self.int4_codes), _ptr(self.int4_meta), _ptr(self.int8_codes),
             _ptr(self.int8_scales), _ptr(block_table), _ptr(seq_lens), _ptr(self.keep_mask),
             _ptr(self.scores))
@@ -176,9 +183,9 @@ class Cache:
         return ctypes.byref(self.desc)
 
     def nbytes(self) -> int:
-        ts = [self.int4_codes, self.int4_meta, self.int8_codes, self.int8_scales, self.keep_mask]
-        if self.scores is not None:
-            ts.append(self.scores)
+        ts = [self.int4_codes, self.int4_meta, self.int8_codes, self.int8_scales, self.keep_mask,
+              self.scores]
+        ts = [t for t in ts if t is not None]
         return sum(t.numel() * t.element_size() for t in ts)
 
 

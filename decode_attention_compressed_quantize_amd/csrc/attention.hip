@@ -91,6 +91,7 @@ struct AttnParams {
   int chunk;
   int nsplit;
   int window;  // > 0: only the last `window` INT4-region positions are read
+  int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
 };
 
 __device__ inline float h2f(uint32_t bits16) {
@@ -265,11 +266,12 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
   auto& wv = sm.u.w4[wave];
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
-  const int n4 = L > kInt8Slots ? L - kInt8Slots : 0;
+  const int slots = p.sink + p.recent;
+  const int n4 = L > slots ? L - slots : 0;
   // INT4 region [r0, r1), or its last `window` positions; chunks start at
   // base (0, or the window's start rounded down to 64 positions)
-  int r0 = kSink, base = 0;
-  const int r1 = kSink + n4;
+  int r0 = p.sink, base = 0;
+  const int r1 = p.sink + n4;
   if (p.window > 0 && r1 - p.window > r0) {
     r0 = r1 - p.window;
     base = r0 & ~63;
@@ -690,8 +692,9 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int slot = wave * 36 + lane;
-  const bool inr = lane < 36;
-  const size_t base = ((size_t)b * p.hkv + kvh) * kInt8Slots;
+  const int slots = p.sink + p.recent;  // 144, or 0 without INT8 protection
+  const bool inr = lane < 36 && slot < slots;
+  const size_t base = ((size_t)b * p.hkv + kvh) * slots;
   u32x4 kw[NW];
   float2v sc = {0.0f, 0.0f};
   if (inr) {
@@ -711,7 +714,7 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
   }
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
-  const int nvalid = L < kInt8Slots ? L : kInt8Slots;
+  const int nvalid = L < slots ? L : slots;
   const int cntw = nvalid - wave * 36 < 0 ? 0 : (nvalid - wave * 36 > 36 ? 36 : nvalid - wave * 36);
   const bool valid = lane < cntw;
   __syncthreads();
@@ -897,6 +900,8 @@ hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype
                             const AttnPlan& plan, int window, hipStream_t s) {
   AttnParams p;
   p.window = window;
+  p.sink = c.n_sink;
+  p.recent = c.n_recent;
   p.q = q;
   p.codes = c.int4_codes;
   p.meta = c.int4_meta;

@@ -33,15 +33,16 @@ kvc_status check_cache(const kvc_cache* c, unsigned need) {
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(KVC_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c->page_size != kvc::kPage) return fail(KVC_E_UNSUPPORTED, "page_size must be 16");
-  if (c->n_sink != kvc::kSink || c->n_recent != kvc::kRecent)
-    return fail(KVC_E_UNSUPPORTED, "n_sink must be 16 and n_recent 128");
+  const bool protect = c->n_sink == kvc::kSink && c->n_recent == kvc::kRecent;
+  if (!protect && (c->n_sink != 0 || c->n_recent != 0))
+    return fail(KVC_E_UNSUPPORTED, "n_sink/n_recent must be 16/128 (INT8 protection) or 0/0");
   if (c->group != kvc::kGroup) return fail(KVC_E_UNSUPPORTED, "group must be 32");
   if ((long long)c->max_pages_per_seq * kvc::kPage < c->max_ctx)
     return fail(KVC_E_SHAPE, "max_pages_per_seq * 16 must cover max_ctx");
   if (!c->block_table || !c->seq_lens) return fail(KVC_E_NULL, "block_table or seq_lens is NULL");
   if ((need & kNeedInt4) && (!c->int4_codes || !c->int4_meta))
     return fail(KVC_E_NULL, "int4_codes or int4_meta is NULL");
-  if ((need & kNeedInt8) && (!c->int8_codes || !c->int8_scales))
+  if ((need & kNeedInt8) && protect && (!c->int8_codes || !c->int8_scales))
     return fail(KVC_E_NULL, "int8_codes or int8_scales is NULL");
   if ((need & kNeedMask) && !c->keep_mask) return fail(KVC_E_NULL, "keep_mask is NULL");
   if ((need & kNeedScores) && !c->scores) return fail(KVC_E_NULL, "scores is NULL");
@@ -86,7 +87,8 @@ AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window) {
   // round, else after the chunks.
   constexpr long long kResident = 768;  // 3 workgroups per CU x 256 CUs
   constexpr long long kTarget = 384;
-  const long long end4 = c.max_ctx > kInt8Slots ? (long long)c.max_ctx - kRecent : 0;
+  const long long end4 =
+      c.max_ctx > c.n_sink + c.n_recent ? (long long)c.max_ctx - c.n_recent : 0;
   long long span = end4;  // positions a sequence's chunks must cover
   if (window > 0 && (long long)window + 64 < span) span = (long long)window + 64;
   const long long pairs = (long long)c.batch * c.num_kv_heads;
@@ -172,7 +174,7 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
   if (mlp) {
     st = check_append(k_new, v_new, src, n_new_max, n_new);
     if (st != KVC_OK) return st;
-    if (n_new_max > 0 && n_new_max <= kvc::kRecent)
+    if (n_new_max > 0 && n_new_max <= c->n_recent)
       return launched(kvc::launch_score_topk(*c, mlp, k_new, v_new, src, n_new_max, n_new,
                                              budget_permille, static_cast<kvc::TopkState*>(ws),
                                              stream));
@@ -217,7 +219,7 @@ KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, co
     if (st != KVC_OK) return st;
     // rows appended in this call sit in the protected recent window, so the
     // refresh does not read their scores and both run in one launch
-    if (n_new_max > 0 && n_new_max <= kvc::kRecent)
+    if (n_new_max > 0 && n_new_max <= c->n_recent)
       return launched(kvc::launch_score_block(*c, mlp, k_new, v_new, src, n_new_max, n_new,
                                               budget_permille, block_tokens, recency_window, ws,
                                               stream));
@@ -246,8 +248,8 @@ static kvc_status decode_attention(const kvc_cache* c, int32_t window, const voi
   const int G = num_q_heads / c->num_kv_heads;
   if (G > 4 || (G & (G - 1)))
     return fail(KVC_E_UNSUPPORTED, "num_q_heads/num_kv_heads must be 1, 2 or 4");
-  if ((long long)c->max_ctx > (long long)(kvc::kMaxParts - 1) * kvc::kMaxChunk + kvc::kRecent)
-    return fail(KVC_E_UNSUPPORTED, "max_ctx above 2089088 positions is not supported");
+  if ((long long)c->max_ctx > (long long)(kvc::kMaxParts - 1) * kvc::kMaxChunk + c->n_recent)
+    return fail(KVC_E_UNSUPPORTED, "max_ctx above (255 * 8192 + n_recent) positions is not supported");
   if (window < 0) return fail(KVC_E_SHAPE, "int4_window must be >= 0");
   const kvc::AttnPlan full = kvc::plan_attention(*c, num_q_heads, 0);
   const size_t need = kvc::attention_ws_floats(*c, num_q_heads, full) * sizeof(float);

@@ -11,9 +11,11 @@
 namespace kvc {
 
 constexpr int kPage = 16;
+// INT8 protection: 16 sink and 128 recent positions (kvc_cache.n_sink and
+// n_recent), or none (both 0: every position in INT4). Kernels take the
+// values from the descriptor.
 constexpr int kSink = 16;
 constexpr int kRecent = 128;
-constexpr int kInt8Slots = kSink + kRecent;  // 144
 constexpr int kGroup = 32;
 constexpr int kHidden = 32;
 
@@ -86,19 +88,20 @@ static_assert(sizeof(BlockStateHeader) == 64, "header size");
 // Sized for the smallest block (16 tokens), so that every block size finds
 // the headers at the same offsets.
 inline size_t block_state_stride(const kvc_cache& c) {
-  const int n4 = c.max_ctx > kInt8Slots ? c.max_ctx - kInt8Slots : 0;
+  const int slots = c.n_sink + c.n_recent;
+  const int n4 = c.max_ctx > slots ? c.max_ctx - slots : 0;
   const size_t keys = (size_t)(n4 + kPage - 1) / kPage;
   return sizeof(BlockStateHeader) + (keys + 3) / 4 * 16;
 }
 hipError_t launch_block_topk(const kvc_cache& c, int budget_permille, int block_tokens, int window,
                              void* state, hipStream_t s);
-// Scoring and block refresh in one launch; only for n_new_max <= kRecent.
+// Scoring and block refresh in one launch; only for n_new_max <= n_recent.
 hipError_t launch_score_block(const kvc_cache& c, const float* mlp, const void* k_new,
                               const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
                               int budget_permille, int block_tokens, int window, void* state,
                               hipStream_t s);
 
-// Scoring and refresh in one launch; only for n_new_max <= kRecent.
+// Scoring and refresh in one launch; only for n_new_max <= n_recent.
 hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k_new,
                              const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
                              int budget_permille, TopkState* state, hipStream_t s);

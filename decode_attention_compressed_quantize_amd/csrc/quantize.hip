@@ -35,6 +35,7 @@ struct QuantParams {
   int max_pages;
   int num_pages;
   int max_ctx;
+  int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
 };
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantParams p) {
   }
 
   // ---- INT8 side cache for sink and recent positions of the new length
-  if (pos < kSink || pos >= L - kRecent) {
+  if (p.recent > 0 && (pos < p.sink || pos >= L - p.recent)) {
     float a = fabsf(x[0]);
 #pragma unroll
     for (int e = 1; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
@@ -148,8 +149,8 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantParams p) {
       const float r = fminf(fmaxf(__builtin_rintf(x[e] * inv8), -127.0f), 127.0f);
       q8 |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * e);
     }
-    const int slot = pos < kSink ? pos : kSink + (pos - kSink) % kRecent;
-    const size_t srec = ((size_t)b * p.hkv + h) * kInt8Slots + slot;
+    const int slot = pos < p.sink ? pos : p.sink + (pos - p.sink) % p.recent;
+    const size_t srec = ((size_t)b * p.hkv + h) * (p.sink + p.recent) + slot;
     int8_t* row = p.codes8 + srec * 2 * D + (is_v ? D : 0) + hl * EPL;
     if constexpr (EPL == 4) {
       *reinterpret_cast<uint32_t*>(row) = q8;
@@ -181,6 +182,8 @@ hipError_t launch_quantize_append(const kvc_cache& c, const void* k_new, const v
   p.max_pages = c.max_pages_per_seq;
   p.num_pages = c.num_phys_pages;
   p.max_ctx = c.max_ctx;
+  p.sink = c.n_sink;
+  p.recent = c.n_recent;
   const dim3 grid((unsigned)((p.items + 3) / 4));
   const dim3 block(256);
   const bool bf = src == KVC_BF16;

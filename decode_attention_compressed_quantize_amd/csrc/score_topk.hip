@@ -158,6 +158,7 @@ struct TopkParams {
   int max_ctx;
   int words;
   int budget;
+  int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
 };
 
 // Order-preserving key: larger score -> larger key; NaN -> 0 (below -inf); -0 == +0.
@@ -217,7 +218,8 @@ __device__ inline uint64_t list_pop_front(uint64_t v, int& n) {
 __device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, long long k,
                           const float* sc, uint32_t* mrow, int lane) {
   if (L < 1 || st->magic != kTopkMagic || st->budget != p.budget || st->len != L - 1) return false;
-  const int n4p = L - 1 > kInt8Slots ? L - 1 - kInt8Slots : 0;
+  const int slots = p.sink + p.recent;
+  const int n4p = L - 1 > slots ? L - 1 - slots : 0;
   const long long kp = ((long long)p.budget * n4p) / 1000;
   if (st->k != kp) return false;
   int na = st->na, nb = st->nb;
@@ -225,8 +227,9 @@ __device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, lon
   uint64_t A = lane < na ? st->a[lane] : 0, B = lane < nb ? st->b[lane] : 0;
   int clear_pos = -1, set_pos = -1;
   if (n4 != n4p) {
-    // position kSink + n4p leaves the recent window and becomes a candidate
-    const int xpos = kSink + n4p;
+    // position sink + n4p leaves the recent window (or, without INT8
+    // protection, is the one appended) and becomes a candidate
+    const int xpos = p.sink + n4p;
     const uint64_t x = comp_key(order_key(sc[n4p]), xpos);
     const long long out_before = n4p - kp;  // candidates not kept
     if (k == kp) {
@@ -262,7 +265,8 @@ __device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, lon
     }
   }
   if (lane == 0) {
-    // the new position is protected; then the candidate changes
+    // the new position is protected (without protection it is the candidate,
+    // cleared below if not kept); then the candidate changes
     __hip_atomic_fetch_or(&mrow[(L - 1) >> 5], 1u << ((L - 1) & 31), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
     if (set_pos >= 0)
@@ -302,9 +306,9 @@ __device__ void topk_pair(const TopkParams& p, int h, int b) {
   int L = p.seq_lens[b];
   if (L < 0) L = 0;
   if (L > p.max_ctx) L = p.max_ctx;
-  const int n4 = L > kInt8Slots ? L - kInt8Slots : 0;
+  const int n4 = L > p.sink + p.recent ? L - p.sink - p.recent : 0;
   const long long k = ((long long)p.budget * n4) / 1000;
-  const float* sc = p.scores + ((size_t)b * p.hkv + h) * p.max_ctx + kSink;
+  const float* sc = p.scores + ((size_t)b * p.hkv + h) * p.max_ctx + p.sink;
   uint32_t* mrow = p.mask + ((size_t)b * p.hkv + h) * p.words;
   TopkState* st = p.state ? p.state + (size_t)b * p.hkv + h : nullptr;
 
@@ -413,12 +417,12 @@ __device__ void topk_pair(const TopkParams& p, int h, int b) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int t = w * 32 + i;
-        v[i] = (t >= kSink && t < kSink + n4) ? sc[t - kSink] : 0.0f;
+        v[i] = (t >= p.sink && t < p.sink + n4) ? sc[t - p.sink] : 0.0f;
       }
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int t = w * 32 + i;
-        if (t >= kSink && t < kSink + n4) {
+        if (t >= p.sink && t < p.sink + n4) {
           const uint32_t key = order_key(v[i]);
           if (key > T) gt |= 1u << i;
           else if (key == T) eq |= 1u << i;
@@ -461,8 +465,8 @@ __device__ void topk_pair(const TopkParams& p, int h, int b) {
       for (int i = 0; i < 32; ++i) {
         const int t = w * 32 + i;
         if (t >= L) { bits &= ~(1u << i); continue; }
-        const bool prot = t < kSink || t >= L - kRecent;
-        if (prot || (all && t >= kSink)) bits |= 1u << i;
+        const bool prot = t < p.sink || (p.recent > 0 && t >= L - p.recent);
+        if (prot || (all && t >= p.sink)) bits |= 1u << i;
       }
       mrow[w] = bits;
     }
@@ -539,6 +543,7 @@ struct BlockTopkParams {
   int words;
   int budget;
   int window;
+  int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
 };
 
 constexpr int kBlockWaves = kTopkThreads / 64;
@@ -686,14 +691,15 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   int L = p.seq_lens[b];
   if (L < 0) L = 0;
   if (L > p.max_ctx) L = p.max_ctx;
-  const int n4 = L > kInt8Slots ? L - kInt8Slots : 0;
+  const int sink = p.sink, slots = p.sink + p.recent;
+  const int n4 = L > slots ? L - slots : 0;
   const int c0 = p.window > 0 ? (n4 - p.window > 0 ? n4 - p.window : 0) : 0;
   const int j0 = c0 / B;
   const int nb = n4 > c0 ? (n4 + B - 1) / B - j0 : 0;
   const long long k = ((long long)p.budget * nb) / 1000;
   const bool all = k >= nb;
   const bool select = k > 0 && !all;
-  const float* sc = p.scores + ((size_t)b * p.hkv + h) * p.max_ctx + kSink;
+  const float* sc = p.scores + ((size_t)b * p.hkv + h) * p.max_ctx + sink;
   uint32_t* mrow = p.mask + ((size_t)b * p.hkv + h) * p.words;
   const bool cached = nb <= kBlockKeysLds;
   BlockStateHeader* st = p.state ? reinterpret_cast<BlockStateHeader*>(
@@ -744,7 +750,7 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   int ra = 0;
   bool first_too = false;
   if (valid) {
-    const int n4o = len0 > kInt8Slots ? len0 - kInt8Slots : 0;
+    const int n4o = len0 > slots ? len0 - slots : 0;
     const int c0o = p.window > 0 ? (n4o - p.window > 0 ? n4o - p.window : 0) : 0;
     ra = n4o / B - j0;
     if (ra < 0) ra = 0;
@@ -974,8 +980,9 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   // everything else (evicted, cut, positions >= L) clear; a word is stored only
   // where it differs from what the mask holds. Word w (positions 32w..32w+31)
   // meets at most two blocks, jA and jB, jB starting at position split.
-  const int rec0 = L - kRecent > kSink ? L - kRecent : kSink;
-  const int lo4 = kSink + c0, hi4 = kSink + n4;
+  // protected: [0, min(L, sink)) and [max(sink, L - recent), L) (none without protection)
+  const int rec0 = p.recent == 0 ? L : (L - p.recent > sink ? L - p.recent : sink);
+  const int lo4 = sink + c0, hi4 = sink + n4;
   const bool any_kept = all || select;
   auto kept_block = [&](int j) -> bool {
     const int r = j - j0;
@@ -983,14 +990,14 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   };
   auto word_bits = [&](int w) -> uint32_t {
     const int base = 32 * w;
-    uint32_t bits = range_bits(0, L < kSink ? L : kSink, base) | range_bits(rec0, L, base);
+    uint32_t bits = range_bits(0, L < sink ? L : sink, base) | range_bits(rec0, L, base);
     const uint32_t cand = range_bits(lo4, hi4, base);
     if (cand) {
-      const int jA = (base - kSink + B) / B - 1;  // floor((base - 16) / B), base - 16 >= -B
-      const int jB = (base + 31 - kSink) / B;
-      const int split = kSink + B * jB;
+      const int jA = (base - sink + B) / B - 1;  // floor((base - sink) / B), base - sink >= -B
+      const int jB = (base + 31 - sink) / B;
+      const int split = sink + B * jB;
       uint32_t kb = 0;
-      if (kept_block(jA)) kb |= range_bits(kSink + B * jA, split, base);
+      if (kept_block(jA)) kb |= range_bits(sink + B * jA, split, base);
       if (kept_block(jB)) kb |= range_bits(split, split + B, base);
       bits |= cand & kb;
     }
@@ -1089,6 +1096,8 @@ TopkParams topk_params(const kvc_cache& c, int budget_permille, TopkState* state
   p.max_ctx = c.max_ctx;
   p.words = mask_words(c.max_ctx);
   p.budget = budget_permille;
+  p.sink = c.n_sink;
+  p.recent = c.n_recent;
   return p;
 }
 
@@ -1148,6 +1157,8 @@ static BlockTopkParams block_params(const kvc_cache& c, int budget_permille, int
   p.words = mask_words(c.max_ctx);
   p.budget = budget_permille;
   p.window = window;
+  p.sink = c.n_sink;
+  p.recent = c.n_recent;
   return p;
 }
 

@@ -44,7 +44,7 @@ class LayerCache:
         self.table = torch.from_numpy(table).to(device)
         self.seq_lens = torch.from_numpy(self.lengths.astype(np.int32)).to(device)
         self.cache = Cache(w.batch, w.kv_heads, w.head_dim, self.max_ctx, num_pages,
-                           self.table, self.seq_lens, device=device)
+                           self.table, self.seq_lens, device=device, protect=w.protect)
         self.k_src = {}
         self.v_src = {}
         self._prefill(keep_sources)
@@ -91,8 +91,9 @@ class LayerCache:
         sub.desc = type(c.desc).from_buffer_copy(c.desc)
         D = self.w.head_dim
         sub.desc.batch = b1 - b0
-        sub.desc.int8_codes = c.int8_codes[b0:b1].data_ptr()
-        sub.desc.int8_scales = c.int8_scales[b0:b1].data_ptr()
+        if c.protect:
+            sub.desc.int8_codes = c.int8_codes[b0:b1].data_ptr()
+            sub.desc.int8_scales = c.int8_scales[b0:b1].data_ptr()
         sub.desc.block_table = self.table[b0:b1].data_ptr()
         sub.desc.seq_lens = self.seq_lens[b0:b1].data_ptr()
         sub.desc.keep_mask = c.keep_mask[b0:b1].data_ptr()
@@ -166,9 +167,10 @@ class LayerCache:
         r.table = self.table.clone()
         r.seq_lens = self.seq_lens.clone()
         r.cache = Cache(c.batch, c.kv_heads, c.head_dim, c.max_ctx, c.num_phys_pages, r.table,
-                        r.seq_lens, device=self.device)
+                        r.seq_lens, device=self.device, protect=c.protect)
         for name in ("int4_codes", "int4_meta", "int8_codes", "int8_scales", "keep_mask", "scores"):
-            getattr(r.cache, name).copy_(getattr(c, name))
+            if getattr(c, name) is not None:
+                getattr(r.cache, name).copy_(getattr(c, name))
         r.k_src, r.v_src = {}, {}
         return r
 

@@ -49,6 +49,14 @@
  * are written for every appended position, so a position leaving the
  * 128-window needs no re-encoding: the INT4 region simply grows by one.
  *
+ * Pure KV4 (n_sink = n_recent = 0; the unprotected configuration the KV4-RL
+ * review, section 3, compares against): there is no INT8 region, int8_codes
+ * and int8_scales are neither read nor written (they may be NULL), the INT4
+ * region is [0, L), every mask bit below L is a policy decision (nothing is
+ * protected), and budgets count all L positions. A sequence whose mask keeps
+ * nothing gets out = 0, lse = -inf. Scoring and refresh never run in one
+ * launch in this configuration (the appended positions are candidates).
+ *
  * Conventions: every call is enqueued on the caller's stream and never
  * synchronises; argument errors are returned synchronously; kernels never
  * allocate; the library keeps no state besides a thread-local error string.
@@ -92,8 +100,8 @@ typedef struct kvc_cache {
   int32_t page_size;         /* must be 16 */
   int32_t max_pages_per_seq; /* >= ceil(max_ctx/16) */
   int32_t num_phys_pages;    /* P >= 1 */
-  int32_t n_sink;            /* must be 16 */
-  int32_t n_recent;          /* must be 128 */
+  int32_t n_sink;            /* 16 with INT8 protection, or 0 (pure KV4, see below) */
+  int32_t n_recent;          /* 128 with INT8 protection, or 0 (pure KV4) */
   int32_t group;             /* must be 32 */
   int32_t max_ctx;           /* capacity in positions, >= 1 (attention: <= 2089088) */
   uint8_t* int4_codes;

@@ -16,6 +16,11 @@ from oracle import policy, quant, reference, regions
 D_GROUP = 32
 
 
+def prot(w):
+    """(n_sink, n_recent) of a workload: the INT8-protected counts, or 0, 0 for pure KV4."""
+    return (regions.N_SINK, regions.N_RECENT) if w.protect else (0, 0)
+
+
 def to_f32(src):
     """Source values (bf16 bits uint16 or float32) as float32."""
     if src.dtype == np.uint16:
@@ -55,8 +60,8 @@ def mask_bits(words_row, L):
     return bits[:L].astype(bool)
 
 
-def keep4_from_mask(words_row, L):
-    start, n4 = regions.int4_range(L)
+def keep4_from_mask(words_row, L, n_sink=regions.N_SINK, n_recent=regions.N_RECENT):
+    start, n4 = regions.int4_range(L, n_sink, n_recent)
     return mask_bits(words_row, L)[start:start + n4]
 
 
@@ -64,7 +69,7 @@ def check_codes(w, layer, b, kvh, L, cpu):
     """Bit-exact comparison of one (sequence, kv head) of GPU buffers with the oracle."""
     k = source_np(w, layer, "K", b, L, kvh)
     v = source_np(w, layer, "V", b, L, kvh)
-    enc = reference.encode(k, v)
+    enc = reference.encode(k, v, *prot(w))
     kc, vc, meta = unpage_int4(cpu["int4_codes"], cpu["int4_meta"], cpu["table"], b, kvh, L)
     np.testing.assert_array_equal(kc, quant.pack_nibbles(enc["k4"]), err_msg=f"K INT4 codes b={b} h={kvh}")
     np.testing.assert_array_equal(vc, quant.pack_nibbles(enc["v4"]), err_msg=f"V INT4 codes b={b} h={kvh}")
@@ -72,6 +77,8 @@ def check_codes(w, layer, b, kvh, L, cpu):
     np.testing.assert_array_equal(meta[:, 0, :, 1], enc["k4_min"].view(np.uint16), err_msg="K min")
     np.testing.assert_array_equal(meta[:, 1, :, 0], enc["v4_scale"].view(np.uint16), err_msg="V scale")
     np.testing.assert_array_equal(meta[:, 1, :, 1], enc["v4_min"].view(np.uint16), err_msg="V min")
+    if not w.protect:  # no INT8 side cache
+        return enc
     pos, k8, v8, ks8, vs8 = int8_slot_rows(cpu["int8_codes"], cpu["int8_scales"], b, kvh, L)
     np.testing.assert_array_equal(k8, enc["k8"], err_msg="K INT8 codes")
     np.testing.assert_array_equal(v8, enc["v8"], err_msg="V INT8 codes")
@@ -85,7 +92,7 @@ def oracle_heads(w, layer, b, kvh, L, keep4, q_heads, scale=None):
     k = source_np(w, layer, "K", b, L, kvh)
     v = source_np(w, layer, "V", b, L, kvh)
     q = to_f32(q_heads).astype(np.float64)
-    return reference.decode_group(q, k, v, keep4, scale)
+    return reference.decode_group(q, k, v, keep4, scale, *prot(w))
 
 
 def assert_attention_close(out, lse, ref_out, ref_lse, what=""):
@@ -94,7 +101,12 @@ def assert_attention_close(out, lse, ref_out, ref_lse, what=""):
     ref_out = np.asarray(ref_out, np.float64)
     err = np.abs(out - ref_out).max()
     rel = np.linalg.norm(out - ref_out) / max(np.linalg.norm(ref_out), 1e-30)
-    lerr = np.abs(np.asarray(lse, np.float64) - np.asarray(ref_lse, np.float64)).max()
+    lse = np.asarray(lse, np.float64)
+    ref_lse = np.asarray(ref_lse, np.float64)
+    # nothing attended (possible without INT8 protection): lse = -inf on both sides
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what} lse -inf where the oracle has none"
+    lerr = np.abs(lse[~empty] - ref_lse[~empty]).max() if (~empty).any() else 0.0
     assert err <= 2e-3, f"{what} max-abs {err:.3e}"
     assert rel <= 1e-3, f"{what} rel-L2 {rel:.3e}"
     assert lerr <= 2e-3, f"{what} lse max-abs {lerr:.3e}"

@@ -73,6 +73,14 @@ def test_attention_argument_errors(lib):
     assert attn(lib, desc(page_size=32)) == -3
     assert attn(lib, desc(n_recent=64)) == -3
     assert attn(lib, desc(group=64)) == -3
+    # without INT8 protection (0/0) the INT8 arrays are unused and may be NULL
+    kv4 = dict(n_sink=0, n_recent=0, int8_codes=None, int8_scales=None)
+    assert attn(lib, desc(**kv4), ws=None) == -4       # passes the cache checks
+    assert attn(lib, desc(n_sink=16, n_recent=0)) == -3
+    assert attn(lib, desc(n_sink=0, n_recent=128)) == -3
+    assert attn(lib, desc(int8_codes=None)) == -1      # protected: INT8 arrays required
+    c = desc(**kv4)
+    assert lib.kvc_quantize_append(ctypes.byref(c), FAKE, FAKE, 0, 0, FAKE, None) == 0
     assert attn(lib, desc(max_pages_per_seq=10)) == -2
     assert attn(lib, desc(batch=0)) == -2
     assert attn(lib, desc(), hq=12) == -2          # not a multiple of Hkv

@@ -11,7 +11,7 @@ import pytest
 
 import workloads as W
 from kvc_testlib import (assert_attention_close, check_codes, keep4_from_mask, mask_bits,
-                         oracle_heads, source_np, to_f32)
+                         oracle_heads, prot, source_np, to_f32)
 from oracle import policy, regions
 
 pytestmark = pytest.mark.gpu
@@ -43,8 +43,8 @@ def cpu_buffers(lc):
     return {
         "int4_codes": c.int4_codes.cpu().numpy(),
         "int4_meta": c.int4_meta.cpu().numpy(),
-        "int8_codes": c.int8_codes.cpu().numpy(),
-        "int8_scales": c.int8_scales.cpu().numpy(),
+        "int8_codes": c.int8_codes.cpu().numpy() if c.protect else None,
+        "int8_scales": c.int8_scales.cpu().numpy() if c.protect else None,
         "keep_mask": c.keep_mask.cpu().numpy(),
         "scores": c.scores.cpu().numpy(),
         "table": lc.table_np,
@@ -79,7 +79,7 @@ def policy_keep(w, s4, budget=None):
 
 def expected_keep4(w, lc, cpu, b, kvh, L):
     """Keep flags the oracle expects for one (sequence, kv head)."""
-    start, n4 = regions.int4_range(L)
+    start, n4 = regions.int4_range(L, *prot(w))
     if w.mask == "all":
         return np.ones(n4, bool)
     if w.mask == "bernoulli":
@@ -99,9 +99,9 @@ def check_pair(w, lc, cpu, qn, out, lse, b, kvh):
         check_codes(w, lc.layer, b, kvh, L, cpu)
     if w.mask != "bernoulli":  # masks written by the refresh kernel
         bits = mask_bits(cpu["keep_mask"][b, kvh], cpu["keep_mask"].shape[-1] * 32)
-        assert bits[regions.int8_positions(L)].all(), "protected positions must be kept"
+        assert bits[regions.int8_positions(L, *prot(w))].all(), "protected positions must be kept"
         assert not bits[L:].any(), "positions at or beyond L must be clear"
-    keep4 = keep4_from_mask(cpu["keep_mask"][b, kvh], L)
+    keep4 = keep4_from_mask(cpu["keep_mask"][b, kvh], L, *prot(w))
     np.testing.assert_array_equal(keep4, expected_keep4(w, lc, cpu, b, kvh, L),
                                   err_msg=f"keep mask b={b} h={kvh}")
     if w.mask == "mlp" and L > 0:
@@ -237,12 +237,12 @@ def _decode_topk_run(w, steps, budgets, stall=None, mlp=None):
         scores = lc.cache.scores.cpu().numpy()
         for b in range(w.batch):
             L = int(lens[b])
-            start, n4 = regions.int4_range(L)
+            start, n4 = regions.int4_range(L, *prot(w))
             for h in range(w.kv_heads):
                 bits = mask_bits(maskw[b, h], maskw.shape[-1] * 32)
                 want = policy.topk_keep(scores[b, h, start:start + n4].astype(np.float64), budget)
                 assert np.array_equal(bits[start:start + n4], want), f"step {step} b={b} h={h}"
-                assert bits[regions.int8_positions(L)].all(), f"step {step} b={b} h={h} protected"
+                assert bits[regions.int8_positions(L, *prot(w))].all(), f"step {step} b={b} h={h} protected"
                 assert not bits[L:].any(), f"step {step} b={b} h={h} beyond L"
     return lc
 
@@ -439,12 +439,12 @@ def _block_state_run(w, steps, plan, shrink=None, stall=None):
         scores = lc.cache.scores.cpu().numpy()
         for b in range(w.batch):
             L = int(lens[b])
-            start, n4 = regions.int4_range(L)
+            start, n4 = regions.int4_range(L, *prot(w))
             for h in range(w.kv_heads):
                 bits = mask_bits(maskw[b, h], maskw.shape[-1] * 32)
                 want = policy.block_keep(scores[b, h, start:start + n4], budget, block, window)
                 assert np.array_equal(bits[start:start + n4], want), f"step {step} b={b} h={h}"
-                assert bits[regions.int8_positions(L)].all(), f"step {step} b={b} h={h} protected"
+                assert bits[regions.int8_positions(L, *prot(w))].all(), f"step {step} b={b} h={h} protected"
                 assert not bits[L:].any(), f"step {step} b={b} h={h} beyond L"
     return lc
 
@@ -476,25 +476,70 @@ def test_block_state_many_blocks_per_step():
                      shrink=[(10, 1, 5000)], stall=[(5, 0)])
 
 
-@pytest.mark.parametrize("window", [1, 63, 64, 100, 1000, 2700, 5000])
-def test_windowed_attention_ignores_older_positions(window):
+@pytest.mark.parametrize("window,protect", [(1, True), (63, True), (64, True), (100, True),
+                                            (1000, True), (2700, True), (5000, True), (100, False),
+                                            (2700, False)])
+def test_windowed_attention_ignores_older_positions(window, protect):
     """A token-level mask keeps positions all over the INT4 region; the
     windowed call must attend to exactly those in the last `window` of it."""
     w = W.WORKLOADS["long128k_b10"].replace(name="win", batch=3, ctx_list=(3000, 700, 145),
-                                            budget_permille=500)
+                                            budget_permille=500, protect=protect)
     lc = LayerCache(w)
     cpu = cpu_buffers(lc)
     qn, out, lse = run_attention(lc, window=window)
     G = w.group_size
     for b in range(w.batch):
         L = int(lc.lengths[b])
-        _, n4 = regions.int4_range(L)
+        _, n4 = regions.int4_range(L, *prot(w))
         for h in range(w.kv_heads):
-            keep4 = keep4_from_mask(cpu["keep_mask"][b, h], L).copy()
+            keep4 = keep4_from_mask(cpu["keep_mask"][b, h], L, *prot(w)).copy()
             keep4[: max(0, n4 - window)] = False
             hs = slice(h * G, (h + 1) * G)
             ro, rl = oracle_heads(w, lc.layer, b, h, L, keep4, qn[b, hs])
             assert_attention_close(out[b, hs], lse[b, hs], ro, rl, what=f"window {window} b={b} h={h}")
+
+
+# ---------------------------------------------------------------- pure KV4
+# Without INT8 protection (n_sink = n_recent = 0) every position is INT4 and
+# subject to the mask; the INT8 side cache is absent (NULL in the descriptor).
+@pytest.mark.parametrize("budget", [0, 100, 500, 1000])
+def test_pure_kv4_mlp_edges(budget):
+    lens = (1, 2, 16, 31, 32, 33, 100, 145, 1000, 3000, 0)
+    w = W.WORKLOADS["long128k_kv4_b10"].replace(name="kv4_edges", batch=len(lens), ctx=None,
+                                                ctx_list=lens, budget_permille=budget)
+    check_workload(w)
+
+
+def test_pure_kv4_bernoulli_fp32_mha():
+    w = W.Workload("kv4_mha", 2, 8, 8, 64, ctx_list=(700, 33), src_dtype="f32", mask="bernoulli",
+                   protect=False)
+    check_workload(w)
+
+
+@pytest.mark.parametrize("block,window", [(16, 0), (32, 500)])
+def test_pure_kv4_block_policy(block, window):
+    w = W.WORKLOADS["long128k_kv4_b10"].replace(name="kv4_blk", batch=2, ctx=None,
+                                                ctx_list=(3000, 77), budget_permille=300,
+                                                policy="block", block_tokens=block,
+                                                recency_window=window)
+    check_workload(w)
+
+
+def test_pure_kv4_incremental_topk_every_step():
+    """Each appended position is a candidate at once: it is scored, then the
+    refresh state takes it (two launches); checked after every step."""
+    w = W.WORKLOADS["fullstep"].replace(name="kv4_inc", batch=3, kv_heads=2, q_heads=8, layers=1,
+                                        ctx=900, ctx_list=(1, 200, 900), decode_steps=300,
+                                        protect=False)
+    _decode_topk_run(w, 300, lambda s: 300 if s < 200 else 700, stall=[(20, 1), (150, 2)])
+
+
+def test_pure_kv4_block_state_every_step():
+    w = W.WORKLOADS["fullstep"].replace(name="kv4_blk_state", batch=2, kv_heads=2, q_heads=8,
+                                        layers=1, ctx=1500, ctx_list=(3, 1500), decode_steps=120,
+                                        policy="block", protect=False)
+    _block_state_run(w, 120, lambda s: (250, 0 if s < 60 else 700, 16 if s < 90 else 64),
+                     stall=[(10, 1)])
 
 
 # ---------------------------------------------------------------- full sizes
@@ -517,7 +562,7 @@ def test_full_longtail_sampled():
 
 
 @pytest.mark.parametrize("name", ["long128k_b10", "long128k_b50", "long128k_blk_b10",
-                                  "long128k_r16k_b50"])
+                                  "long128k_r16k_b50", "long128k_kv4_b10", "long128k_kv4_b50"])
 def test_full_long128k_sampled(name):
     w = W.WORKLOADS[name]
     check_workload(w, [(0, 0), (3, 7), (1, 4)])

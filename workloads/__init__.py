@@ -172,6 +172,7 @@ class Workload:
     policy: str = "token"                      # keep policy: "token" top-k or "block" (whole blocks)
     block_tokens: int = 16                     # block size of the "block" policy
     recency_window: int = 0                    # "block" policy: candidates = last W INT4 positions (0 = all)
+    protect: bool = True                       # INT8 sink/recent protection (False: pure KV4)
     outlier_channels: int = 0                  # (kv head, dim) channels scaled x8
     shuffled_pages: bool = True
     decode_steps: int = 0                      # extra capacity for appended tokens
@@ -227,6 +228,11 @@ WORKLOADS = {
                                   budget_permille=100, policy="block", recency_window=16384),
     "long128k_r16k_b50": Workload("long128k_r16k_b50", 4, 32, 8, 128, ctx=131072, mask="mlp",
                                   budget_permille=500, policy="block", recency_window=16384),
+    # The 128K top-k workloads without INT8 protection (pure KV4: every position INT4).
+    "long128k_kv4_b10": Workload("long128k_kv4_b10", 4, 32, 8, 128, ctx=131072, mask="mlp",
+                                 budget_permille=100, protect=False),
+    "long128k_kv4_b50": Workload("long128k_kv4_b50", 4, 32, 8, 128, ctx=131072, mask="mlp",
+                                 budget_permille=500, protect=False),
     # Full decode step: 36 layers, append + score + top-k refresh (30%) + attention.
     "fullstep": Workload("fullstep", 128, 32, 8, 128, layers=36, ctx=32768, mask="mlp",
                          budget_permille=300, decode_steps=64),
