@@ -77,6 +77,12 @@ _SIGNATURES = {
                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                             ctypes.c_void_p]),
     "kvc_block_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
+    "kvc_shadow_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]),
     "kvc_decode_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -273,6 +279,25 @@ def topk_workspace(cache: Cache, device="cuda"):
 
     n = kvc_topk_workspace_bytes(cache)
     return torch.zeros(max(n // 4, 1), dtype=torch.int32, device=device)
+
+
+def kvc_shadow_attention(q, k, v, seq_lens, prompt_lens, shadow, out, lse=None,
+                         softmax_scale: float = 0.0, stream=None):
+    """Learner-side causal attention under recorded shadow rows.
+
+    q [B][T][Hq][D], k and v [B][T][Hkv][D] (bf16), seq_lens and prompt_lens
+    int32 [B], shadow int32 [B][Hkv][rows][ceil(T/32)] (row r: the keep mask
+    used for query position prompt_len + r), out fp32 [B][T][Hq][D], lse fp32
+    [B][T][Hq] or None."""
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    rows = 0 if shadow is None else shadow.shape[2]
+    if shadow is not None and tuple(shadow.shape[:2]) + (shadow.shape[3],) != (B, Hkv, (T + 31) // 32):
+        raise ValueError(f"shadow must be [B][Hkv][rows][{(T + 31) // 32}], got {tuple(shadow.shape)}")
+    _check(lib().kvc_shadow_attention(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, T, Hq, Hkv, D,
+                                      _ptr(seq_lens), _ptr(prompt_lens), _ptr(shadow), rows,
+                                      float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "kvc_shadow_attention")
 
 
 def block_workspace(cache: Cache, block_tokens: int = PAGE, device="cuda"):

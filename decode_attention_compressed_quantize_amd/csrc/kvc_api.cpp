@@ -276,4 +276,32 @@ KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int
                           ws_bytes, stream);
 }
 
+KVC_API kvc_status kvc_shadow_attention(const void* q, const void* k, const void* v, kvc_dtype dtype,
+                                        int32_t batch, int32_t max_len, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        const int32_t* seq_lens, const int32_t* prompt_lens,
+                                        const uint32_t* shadow, int32_t shadow_rows,
+                                        float softmax_scale, float* out, float* lse,
+                                        hipStream_t stream) {
+  if (!q || !k || !v || !out || !seq_lens || !prompt_lens)
+    return fail(KVC_E_NULL, "q, k, v, out, seq_lens or prompt_lens is NULL");
+  if (shadow_rows < 0) return fail(KVC_E_SHAPE, "shadow_rows must be >= 0");
+  if (shadow_rows > 0 && !shadow) return fail(KVC_E_NULL, "shadow is NULL");
+  if (batch < 1 || max_len < 1 || num_kv_heads < 1 || num_q_heads < 1)
+    return fail(KVC_E_SHAPE, "batch, max_len and head counts must be >= 1");
+  if (dtype != KVC_BF16) return fail(KVC_E_UNSUPPORTED, "q, k and v must be BF16");
+  if (head_dim != 64 && head_dim != 128) return fail(KVC_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (num_q_heads % num_kv_heads)
+    return fail(KVC_E_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = num_q_heads / num_kv_heads;
+  if (G > 4 || (G & (G - 1)))
+    return fail(KVC_E_UNSUPPORTED, "num_q_heads/num_kv_heads must be 1, 2 or 4");
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out))
+    return fail(KVC_E_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  return launched(kvc::launch_shadow_attention(q, k, v, batch, max_len, num_q_heads, num_kv_heads,
+                                               head_dim, seq_lens, prompt_lens, shadow,
+                                               shadow_rows, scale, out, lse, stream));
+}
+
 }  // extern "C"

@@ -106,6 +106,13 @@ hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k
                              const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
                              int budget_permille, TopkState* state, hipStream_t s);
 
+// Learner-side causal attention under recorded shadow rows (bf16 Q, K, V).
+hipError_t launch_shadow_attention(const void* q, const void* k, const void* v, int batch,
+                                   int max_len, int num_q_heads, int num_kv_heads, int head_dim,
+                                   const int32_t* seq_lens, const int32_t* prompt_lens,
+                                   const uint32_t* shadow, int shadow_rows, float softmax_scale,
+                                   float* out, float* lse, hipStream_t s);
+
 hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype, int num_q_heads,
                             float softmax_scale, float* out, float* lse, float* ws,
                             const AttnPlan& plan, int window, hipStream_t s);

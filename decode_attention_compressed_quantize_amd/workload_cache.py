@@ -174,6 +174,31 @@ class LayerCache:
         r.k_src, r.v_src = {}, {}
         return r
 
+    # -------------------------------------------------------------- rollout
+    def record_rollout(self, steps: int, ws=None):
+        """Run ``steps`` decode steps (append one source token per sequence,
+        score, refresh the mask with the workload's policy) and record the keep
+        mask after each: int32 [B][Hkv][steps][words], row s belonging to query
+        position (prompt length + s). Returns the record and the new lengths."""
+        import torch
+
+        w = self.w
+        c = self.cache
+        rec = torch.zeros((w.batch, w.kv_heads, steps, c.mask_words), dtype=torch.int32,
+                          device=self.device)
+        one = torch.ones(w.batch, dtype=torch.int32, device=self.device)
+        lens = self.lengths.copy()
+        for s in range(steps):
+            k_new = W.kv_rows_torch(w, self.layer, "K", lens, self.device)[:, None]
+            v_new = W.kv_rows_torch(w, self.layer, "V", lens, self.device)[:, None]
+            lens += 1
+            self.seq_lens.add_(1)
+            kvc_quantize_append(c, k_new, v_new, one)
+            self.refresh(k_new, v_new, one, ws=ws)
+            rec[:, :, s] = c.keep_mask
+        self.lengths = lens
+        return rec, lens
+
     # -------------------------------------------------------------- decode
     def queries(self, step: int = 0):
         return W.queries_torch(self.w, self.layer, step, self.device)

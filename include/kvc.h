@@ -246,6 +246,44 @@ KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int
                                                  float* out, float* lse, void* ws, size_t ws_bytes,
                                                  hipStream_t stream);
 
+/*
+ * kvc_shadow_attention - learner-side causal attention under the recorded
+ * shadow mask.
+ * Source: Shadow Mask Distillation page (arXiv 2605.06850), section 1 and the
+ * Figure 1 caption: the binary keep mask M of every sparse rollout step is
+ * injected into the learner's causal attention (a time-frozen mask), so the
+ * learner's query at a generated position attends to exactly the positions
+ * the rollout attended at that step.
+ *   q            : device bf16 [B][max_len][num_q_heads][D] (learner queries).
+ *   k, v         : device bf16 [B][max_len][num_kv_heads][D] (learner's own
+ *                  dense keys and values; quantization is not replayed).
+ *   dtype        : must be KVC_BF16. D = head_dim: 64 or 128; G = 1, 2 or 4.
+ *   seq_lens     : device int32 [B]: positions [0, L_b) are computed.
+ *   prompt_lens  : device int32 [B]: queries at positions below P_b attend
+ *                  densely and causally (the rollout's prefill).
+ *   shadow       : device uint32 [B][num_kv_heads][shadow_rows][ceil(max_len/32)]:
+ *                  row r is the keep mask (bit t%32 of word t/32, protected
+ *                  positions included) the rollout used for the query at
+ *                  position P_b + r, i.e. the mask at cache length P_b + r + 1;
+ *                  bits above the query's position are ignored. A generated
+ *                  position with no row (r >= shadow_rows) attends nothing.
+ *                  NULL allowed when shadow_rows = 0.
+ *   softmax_scale: logit scale; <= 0 selects 1/sqrt(D).
+ *   out          : device float [B][max_len][num_q_heads][D]; rows at and beyond
+ *                  L_b are not written; a row that attends nothing gets 0.
+ *   lse          : device float [B][max_len][num_q_heads] natural-log
+ *                  log-sum-exp of the scaled logits (-inf if nothing is
+ *                  attended), or NULL.
+ *   q, k, v and out must be 16-byte aligned. Needs no workspace.
+ */
+KVC_API kvc_status kvc_shadow_attention(const void* q, const void* k, const void* v, kvc_dtype dtype,
+                                        int32_t batch, int32_t max_len, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        const int32_t* seq_lens, const int32_t* prompt_lens,
+                                        const uint32_t* shadow, int32_t shadow_rows,
+                                        float softmax_scale, float* out, float* lse,
+                                        hipStream_t stream);
+
 /* Workspace sizes (host-only, no device work). Return 0 for an invalid cache.
  * kvc_topk_workspace_bytes is the size of the optional refresh state of
  * kvc_score_topk_mask: 1056 bytes per (sequence, kv head).

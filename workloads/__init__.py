@@ -340,6 +340,25 @@ def queries_torch(w: Workload, layer: int, step: int, device):
     return x.view(w.batch, w.q_heads, w.head_dim)
 
 
+def learner_queries_np(w: Workload, layer: int, b: int, t0: int, t1: int) -> np.ndarray:
+    """Learner-side queries of sequence ``b`` for positions [t0, t1): [t1-t0][Hq][D]
+    (bf16 bits or float32); element (t, h, d) is stream index (t*Hq + h)*D + d."""
+    Hq, D = w.q_heads, w.head_dim
+    idx = np.arange(t0 * Hq * D, t1 * Hq * D, dtype=np.int64)
+    x = normal_np(stream_key(w.seed, w.name, "LQ", layer, b), idx, w.src_dtype)
+    return x.reshape(t1 - t0, Hq, D)
+
+
+def learner_queries_torch(w: Workload, layer: int, b: int, t0: int, t1: int, device):
+    """Torch twin of :func:`learner_queries_np`."""
+    import torch
+
+    Hq, D = w.q_heads, w.head_dim
+    idx = torch.arange(t0 * Hq * D, t1 * Hq * D, dtype=torch.int64, device=device)
+    x = normal_torch(stream_key(w.seed, w.name, "LQ", layer, b), idx, w.src_dtype)
+    return x.view(t1 - t0, Hq, D)
+
+
 def given_scores_np(w: Workload, layer: int, b: int, length: int) -> np.ndarray:
     """Caller-provided per-token scores ~ N(0,1), float32 [Hkv][length]."""
     idx = np.arange(w.kv_heads * length, dtype=np.int64)
