@@ -196,13 +196,144 @@ def cpu_baseline(layer_names, seconds: float):
                       f"{used} worker processes (1 thread each) and divided by {used}"}
 
 
+# ---------------------------------------------------------------------- learner
+# Learner-side shadow-mask attention: B sequences of a prompt plus generated
+# positions whose keep masks come from a rollout recorded on the GPU (one
+# layer, per-head MLP scores, top-30% refresh every step). A step is one
+# kvc_shadow_attention call over the batch.
+LEARNER = {"learner8k": dict(batch=4, prompt=4096, generated=4096, q_heads=32, kv_heads=8,
+                             head_dim=128, budget_permille=300)}
+
+
+def _learner_pairs(rows_np, prompts, lens, kv_heads):
+    """Attended (kv head, query position, key) triples: dense causal prompt rows plus
+    each generated row's kept positions up to itself."""
+    import numpy as np
+
+    total = 0
+    for b in range(len(lens)):
+        P, L = int(prompts[b]), int(lens[b])
+        total += kv_heads * P * (P + 1) // 2
+        bits = np.unpackbits(np.ascontiguousarray(rows_np[b]).view(np.uint8), axis=-1,
+                             bitorder="little")
+        for r in range(L - P):
+            total += int(bits[:, r, : P + r + 1].sum())
+    return total
+
+
+def _learner_cpu(cfg, w, q, k, v, prompts, rows_np, seconds):
+    """Oracle rows on a bounded sample: float64 masked softmax attention per row."""
+    import numpy as np
+
+    from oracle import shadow as oshadow
+    from oracle import attention
+
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    qn = q[0].float().cpu().numpy().astype(np.float64)
+    kn = k[0].float().cpu().numpy().astype(np.float64)
+    vn = v[0].float().cpu().numpy().astype(np.float64)
+    P = int(prompts[0])
+    bits = np.unpackbits(np.ascontiguousarray(rows_np[0]).view(np.uint8), axis=-1, bitorder="little")
+    rng = np.random.default_rng(0)
+    flops = 0
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        p = int(rng.integers(P, qn.shape[0]))
+        for g in range(cfg["kv_heads"]):
+            pos = oshadow.allowed_positions(p, P, bits[g, p - P].astype(bool))
+            hs = slice(g * G, (g + 1) * G)
+            attention.attend(qn[p, hs], kn[pos, g], vn[pos, g])
+            flops += G * len(pos) * 4 * cfg["head_dim"]
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} generated query positions of sequence 0 (all {cfg['q_heads']} heads), "
+                      f"float64 masked softmax attention, one thread"}
+
+
+def learner_main(args):
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import decode_attention_compressed_quantize_amd as kvc
+    from decode_attention_compressed_quantize_amd.workload_cache import LayerCache
+
+    kvc.lib()
+    cfg = LEARNER[args.workload]
+    w = W.Workload(args.workload, cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
+                   ctx=cfg["prompt"], mask="mlp", budget_permille=cfg["budget_permille"],
+                   decode_steps=cfg["generated"])
+    print(f"bench: recording a {cfg['generated']}-step rollout", file=sys.stderr, flush=True)
+    lc = LayerCache(w, keep_sources=False)
+    prompts = lc.lengths.copy()
+    rows, lens = lc.record_rollout(cfg["generated"], ws=lc.refresh_state())
+    T = int(lens.max())
+    B, Hq, Hkv, D = cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"]
+    q = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((B, T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    for b in range(B):
+        q[b] = W.learner_queries_torch(w, 0, b, 0, T, "cuda")
+        k[b] = W.kv_source_torch(w, 0, "K", b, 0, T, "cuda")
+        v[b] = W.kv_source_torch(w, 0, "V", b, 0, T, "cuda")
+    out = torch.empty((B, T, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda")
+    sl = torch.tensor(lens.astype(np.int32), device="cuda")
+    pl = torch.tensor(prompts.astype(np.int32), device="cuda")
+    rows_np = rows.cpu().numpy()
+    pairs = _learner_pairs(rows_np, prompts, lens, Hkv)
+    flops = pairs * (Hq // Hkv) * 4 * D  # QK^T and PV: 2D + 2D per attended (query head, key)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        kvc.kvc_shadow_attention(q, k, v, sl, pl, rows, out, lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        kvc.kvc_shadow_attention(q, k, v, sl, pl, rows, out, lse)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    kept = pairs / (Hkv * sum(int(L) * (int(L) + 1) // 2 for L in lens))
+    line = {
+        "metric": "learner shadow-mask attention: useful TFLOP/s (attended pairs x 4D)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 MFMA operands, f32 accumulate",
+        "data": "synthetic (seeded normal Q/K/V; shadow rows recorded from a GPU rollout with seeded MLP scores)",
+        "config": {"workload": args.workload, "batch": B, "prompt": cfg["prompt"],
+                   "generated": cfg["generated"], "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "keep_policy": f"token, budget {cfg['budget_permille'] / 10:g}% (generated rows)",
+                   "attended_fraction_of_causal": round(kept, 4)},
+        "roofline": {"kernel": "shadow_attention_kernel (one launch)", "bound": "mfma",
+                     "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "useful_flops_per_call": int(flops)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = _learner_cpu(cfg, w, q, k, v, prompts, rows_np, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 # ---------------------------------------------------------------------- GPU
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long128k", choices=sorted(WORKLOAD_LAYERS))
+    ap.add_argument("--workload", default="long128k", choices=sorted(WORKLOAD_LAYERS) + sorted(LEARNER))
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >1 GiB between reuses")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -212,6 +343,9 @@ def main():
               "(the kernel is measured on one GPU's share; see the sharding notes).",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload in LEARNER:
+        learner_main(args)
+        return
 
     import numpy as np
     import torch

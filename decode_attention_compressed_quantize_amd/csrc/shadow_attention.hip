@@ -13,7 +13,7 @@
 //   - K rows of the 32 keys into LDS, V rows transposed into LDS (gathers of
 //     16-byte pieces; the listed positions are arbitrary);
 //   - S = Q K^T with bf16 MFMA 16x16x32 (Q operands held in registers);
-//   - masked online softmax in log2 units (rows of a 16-lane group);
+//   - masked online softmax in log2 units (row reductions over a 16-lane DPP row);
 //   - O += P V with bf16 MFMA, P split into a high and a low bf16 part so that
 //     P keeps ~16 significant bits.
 // Nothing is computed for keys no row of the tile attends.
@@ -54,10 +54,10 @@ struct SaSmem {
   static constexpr int KS = D + 8;               // K row stride (bf16 elements)
   static constexpr int VS = kStep + 8;           // V^T row stride
   static constexpr int PS = kStep + 8;           // P row stride
-  uint16_t k[2][kStep][KS];  // two buffers: step s computes from one while
-  uint16_t vt[2][D][VS];     // step s + 1's keys are written into the other
-  uint16_t ph[kSaWaves][2][16][PS];
-  uint16_t pl[kSaWaves][2][16][PS];
+  alignas(16) uint16_t k[2][kStep][KS];  // two buffers: step s computes from one while
+  alignas(16) uint16_t vt[2][D][VS];     // step s + 1's keys are written into the other
+  alignas(16) uint16_t ph[kSaWaves][2][16][PS];
+  alignas(16) uint16_t pl[kSaWaves][2][16][PS];
   uint32_t rw[R][kSpan / 32];     // the tile rows' attended-key words over the span
   uint32_t pos[kSpan];            // listed key positions
   uint32_t rmask[kSpan][NRW];     // per listed key: bit i of word q = row r0 + 32q + i attends it
@@ -67,6 +67,26 @@ struct SaSmem {
 __device__ inline float4v mfma_bf16(u32x4 a, u32x4 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Max and sum over the 16 lanes of a DPP row (one row of the MFMA C layout):
+// swap neighbours, swap pairs, mirror within 8, mirror within 16. Every lane
+// ends with the row's result.
+template <int Ctrl>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+__device__ inline float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+  return fmaxf(x, dpp<0x140>(x));  // row_mirror
+}
+__device__ inline float row16_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  return x + dpp<0x140>(x);
 }
 
 // float -> bf16 bits, round to nearest even (finite inputs)
@@ -255,17 +275,13 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
           const int i = 16 * blk + lr + jj;
           const float sa = ((rmA >> i) & 1u) ? sacc[blk][0][jj] * p.alpha : -INFINITY;
           const float sb = ((rmB >> i) & 1u) ? sacc[blk][1][jj] * p.alpha : -INFINITY;
-          float mx = fmaxf(sa, sb);
-#pragma unroll
-          for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+          const float mx = row16_max(fmaxf(sa, sb));
           const float mn = fmaxf(m[blk][jj], mx);
           const float ms = mn == -INFINITY ? 0.0f : mn;
           corr[blk][jj] = __builtin_amdgcn_exp2f(m[blk][jj] - ms);
           const float pa = __builtin_amdgcn_exp2f(sa - ms);
           const float pb = __builtin_amdgcn_exp2f(sb - ms);
-          float rs = pa + pb;
-#pragma unroll
-          for (int o2 = 1; o2 < 16; o2 <<= 1) rs += __shfl_xor(rs, o2);
+          const float rs = row16_sum(pa + pb);
           l[blk][jj] = l[blk][jj] * corr[blk][jj] + rs;
           m[blk][jj] = mn;
           const int pr = lr + jj;
