@@ -57,6 +57,10 @@ class KvcCacheStruct(ctypes.Structure):
         ("seq_lens", ctypes.c_void_p),
         ("keep_mask", ctypes.c_void_p),
         ("scores", ctypes.c_void_p),
+        ("num_host_pages", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("int4_codes_host", ctypes.c_void_p),
+        ("int4_meta_host", ctypes.c_void_p),
     ]
 
 
@@ -77,6 +81,10 @@ _SIGNATURES = {
                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                             ctypes.c_void_p]),
     "kvc_block_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
+    "kvc_find_pages": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p]),
+    "kvc_copy_pages": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_void_p]),
     "kvc_shadow_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -155,7 +163,7 @@ class Cache:
 
     def __init__(self, batch: int, kv_heads: int, head_dim: int, max_ctx: int,
                  num_phys_pages: int, block_table, seq_lens, device="cuda", with_scores=True,
-                 protect: bool = True):
+                 protect: bool = True, host_pages: int = 0):
         import torch
 
         self.batch, self.kv_heads, self.head_dim, self.max_ctx = batch, kv_heads, head_dim, max_ctx
@@ -175,6 +183,15 @@ class Cache:
         self.keep_mask = torch.zeros((batch, kv_heads, self.mask_words), dtype=torch.int32, device=dev)
         self.scores = (torch.zeros((batch, kv_heads, max_ctx), dtype=torch.float32, device=dev)
                        if with_scores else None)
+        # optional host tier: pinned host pages [num_phys_pages, num_phys_pages + host_pages)
+        self.host_pages = host_pages
+        if host_pages > 0:
+            self.int4_codes_host = torch.zeros((host_pages, kv_heads, PAGE, 2, D // 2),
+                                               dtype=torch.uint8, pin_memory=True)
+            self.int4_meta_host = torch.zeros((host_pages, kv_heads, PAGE, 2, D // GROUP, 2),
+                                              dtype=torch.int16, pin_memory=True)
+        else:
+            self.int4_codes_host = self.int4_meta_host = None
         self.block_table = block_table
         self.seq_lens = seq_lens
         assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
@@ -183,7 +200,7 @@ class Cache:
             self.n_sink, self.n_recent, GROUP, max_ctx,
             _ptr(self.int4_codes), _ptr(self.int4_meta), _ptr(self.int8_codes),
             _ptr(self.int8_scales), _ptr(block_table), _ptr(seq_lens), _ptr(self.keep_mask),
-            _ptr(self.scores))
+            _ptr(self.scores), host_pages, 0, _ptr(self.int4_codes_host), _ptr(self.int4_meta_host))
 
     def ref(self):
         return ctypes.byref(self.desc)
@@ -279,6 +296,20 @@ def topk_workspace(cache: Cache, device="cuda"):
 
     n = kvc_topk_workspace_bytes(cache)
     return torch.zeros(max(n // 4, 1), dtype=torch.int32, device=device)
+
+
+def kvc_find_pages(cache: Cache, mode: int, out, count, stream=None):
+    """List logical pages (sequence, page) into ``out`` (int32 [cap][2]); ``count`` (int32 [1])
+    receives how many were found. mode 0: cold device pages, 1: hot host pages."""
+    cap = 0 if out is None else out.shape[0]
+    _check(lib().kvc_find_pages(cache.ref(), int(mode), _ptr(out), cap, _ptr(count), _stream(stream)),
+           "kvc_find_pages")
+
+
+def kvc_copy_pages(cache: Cache, src, dst, stream=None):
+    """Copy physical pages src[i] -> dst[i] (int32 device tensors) of either tier."""
+    _check(lib().kvc_copy_pages(cache.ref(), _ptr(src), _ptr(dst), int(src.numel()), _stream(stream)),
+           "kvc_copy_pages")
 
 
 def kvc_shadow_attention(q, k, v, seq_lens, prompt_lens, shadow, out, lse=None,

@@ -92,6 +92,9 @@ struct AttnParams {
   int nsplit;
   int window;  // > 0: only the last `window` INT4-region positions are read
   int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
+  const uint8_t* codes_h;  // host tier: pages [num_pages, num_pages + host_pages)
+  const uint16_t* meta_h;
+  int host_pages;
 };
 
 __device__ inline float h2f(uint32_t bits16) {
@@ -250,7 +253,7 @@ __device__ inline void store_partial(Smem<D, G>& sm, OF o_of, float* dst) {
 // Per wave: compact the kept positions of its quarter of the chunk, then walk
 // them in 32-token tiles, each a K step (logits, running max, one rescale)
 // followed by a V step (P.V), with the next steps' loads in flight.
-template <int D, int G, bool QBF16>
+template <int D, int G, bool QBF16, bool TIER>
 __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, int split) {
   using S = Shape<D, G>;
   constexpr int NG = S::NG, VD = S::VD, NC = S::NC;
@@ -351,7 +354,7 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       const int q16 = lane >> 4;
       const int page = q16 == 0 ? pa : (q16 == 1 ? pb : (q16 == 2 ? pc : pd));
       const bool kept = ((bits >> lane) & 1u) && pos >= lo && pos < hi && page >= 0 &&
-                        page < p.num_pages;
+                        page < p.num_pages + p.host_pages;
       const uint64_t bal = __ballot(kept);
       if (kept) {
         const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
@@ -412,6 +415,24 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
     // V pieces: 4 lanes per token at D = 128, 2 at D = 64, 16 bytes each
     const uint8_t* vbase = p.codes + D / 2 + (D == 128 ? 16 * (lane & 3) : 16 * (lane & 1));
     const uint8_t* mbase = reinterpret_cast<const uint8_t*>(p.meta) + hf * (MH * 4);
+    // Host tier: records from rec_h0 on belong to host pages; the same
+    // record arithmetic applies from bases shifted back by rec_h0 records.
+    const uint32_t rec_h0 = (uint32_t)p.num_pages * p.hkv * kPage;
+    const uint8_t* kbase_h = nullptr;
+    const uint8_t* vbase_h = nullptr;
+    const uint8_t* mbase_h = nullptr;
+    if constexpr (TIER) {
+      const uintptr_t ch = reinterpret_cast<uintptr_t>(p.codes_h) - (uintptr_t)rec_h0 * D;
+      const uintptr_t mh = reinterpret_cast<uintptr_t>(p.meta_h) - (uintptr_t)rec_h0 * (D / 4);
+      kbase_h = reinterpret_cast<const uint8_t*>(ch) + (kbase - p.codes);
+      vbase_h = reinterpret_cast<const uint8_t*>(ch) + (vbase - p.codes);
+      mbase_h = reinterpret_cast<const uint8_t*>(mh) + hf * (MH * 4);
+    }
+    // address of record `rec` from a device-pool base and its host-tier twin
+    auto at = [&](const uint8_t* dev, const uint8_t* hst, uint32_t rec, uint32_t stride) {
+      if constexpr (TIER) return (rec >= rec_h0 ? hst : dev) + (uint64_t)rec * stride;
+      else return dev + (uint64_t)rec * stride;
+    };
     const int ntile = padded >> 5;  // 32-token tiles
     const int nstep = 2 * ntile;    // K step, then V step, per tile; a multiple of kRing
 
@@ -436,18 +457,18 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       const uint8_t* a1;
       if constexpr (isk) {
         // lane (s, n): K slot s of tokens n and 16 + n (4 lanes per token row)
-        a0 = kbase + (uint64_t)list[it + n] * D;
-        a1 = kbase + (uint64_t)list[it + 16 + n] * D;
+        a0 = at(kbase, kbase_h, list[it + n], D);
+        a1 = at(kbase, kbase_h, list[it + 16 + n], D);
       } else if constexpr (D == 128) {
         // lane (t, j): 16-byte piece j of the V codes of tokens t and 16 + t
-        a0 = vbase + (uint64_t)list[it + (lane >> 2)] * D;
-        a1 = vbase + (uint64_t)list[it + 16 + (lane >> 2)] * D;
+        a0 = at(vbase, vbase_h, list[it + (lane >> 2)], D);
+        a1 = at(vbase, vbase_h, list[it + 16 + (lane >> 2)], D);
       } else {
         // lane (t, j): 16-byte piece j of the V codes of token t
-        a0 = vbase + (uint64_t)list[it + (lane >> 1)] * D;
+        a0 = at(vbase, vbase_h, list[it + (lane >> 1)], D);
         a1 = a0;
       }
-      const uint8_t* am = mbase + (uint64_t)rt * (D / 4) + (isk ? 0 : D / 8);
+      const uint8_t* am = at(mbase, mbase_h, rt, D / 4) + (isk ? 0 : D / 8);
       if constexpr (D == 128) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(a0);
         const u32x4 y = *reinterpret_cast<const u32x4*>(a1);
@@ -847,7 +868,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
   }
 }
 
-template <int D, int G, bool QBF16>
+// TIER: some pages live in the host tier (a separate pool in pinned host memory)
+template <int D, int G, bool QBF16, bool TIER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
   __shared__ Smem<D, G> sm;
   // One-dimensional grid, dispatched in index order and spread round-robin
@@ -874,7 +896,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int np = p.nsplit + 1;
   float* dst = p.parts + (((size_t)b * p.hkv + kvh) * np + split) * G * (2 + D);
   if (split < p.nsplit) {
-    int4_chunk<D, G, QBF16>(p, sm, b, kvh, split);
+    int4_chunk<D, G, QBF16, TIER>(p, sm, b, kvh, split);
     __syncthreads();
     store_partial<D, G>(sm, [&](int w) { return &sm.u.w4[w].ro.o[0][0]; }, dst);
   } else {
@@ -887,8 +909,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 template <int D, int G>
 hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, hipStream_t s) {
   const dim3 grid((unsigned)(p.nsplit + 1) * c.num_kv_heads * c.batch);
-  if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true>), grid, dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((attention_kernel<D, G, false>), grid, dim3(kThreads), 0, s, p);
+  if (p.host_pages > 0) {
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, true>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, false>), grid, dim3(kThreads), 0, s, p);
+  }
   hipLaunchKernelGGL((merge_kernel<D, G>), dim3(G, c.num_kv_heads, c.batch), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
@@ -902,6 +929,9 @@ hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype
   p.window = window;
   p.sink = c.n_sink;
   p.recent = c.n_recent;
+  p.codes_h = c.int4_codes_host;
+  p.meta_h = c.int4_meta_host;
+  p.host_pages = c.num_host_pages;
   p.q = q;
   p.codes = c.int4_codes;
   p.meta = c.int4_meta;

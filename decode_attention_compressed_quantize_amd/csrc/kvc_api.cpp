@@ -46,8 +46,13 @@ kvc_status check_cache(const kvc_cache* c, unsigned need) {
     return fail(KVC_E_NULL, "int8_codes or int8_scales is NULL");
   if ((need & kNeedMask) && !c->keep_mask) return fail(KVC_E_NULL, "keep_mask is NULL");
   if ((need & kNeedScores) && !c->scores) return fail(KVC_E_NULL, "scores is NULL");
+  if (c->num_host_pages < 0) return fail(KVC_E_SHAPE, "num_host_pages must be >= 0");
+  if ((need & kNeedInt4) && c->num_host_pages > 0 && (!c->int4_codes_host || !c->int4_meta_host))
+    return fail(KVC_E_NULL, "int4_codes_host or int4_meta_host is NULL with num_host_pages > 0");
+  if ((long long)c->num_phys_pages + c->num_host_pages > (long long)0x7FFFFFFF / c->num_kv_heads / kvc::kPage)
+    return fail(KVC_E_SHAPE, "too many pages");
   const void* ptrs[] = {c->int4_codes, c->int4_meta, c->int8_codes, c->int8_scales, c->keep_mask,
-                        c->scores};
+                        c->scores, c->int4_codes_host, c->int4_meta_host};
   for (const void* q : ptrs)
     if (misaligned(q)) return fail(KVC_E_UNSUPPORTED, "cache arrays must be 16-byte aligned");
   return KVC_OK;
@@ -274,6 +279,26 @@ KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int
                                                  hipStream_t stream) {
   return decode_attention(c, int4_window, q, q_dtype, num_q_heads, softmax_scale, out, lse, ws,
                           ws_bytes, stream);
+}
+
+KVC_API kvc_status kvc_find_pages(const kvc_cache* c, int32_t mode, int32_t* out, int32_t cap,
+                                  int32_t* count, hipStream_t stream) {
+  kvc_status st = check_cache(c, kNeedMask);
+  if (st != KVC_OK) return st;
+  if (mode != 0 && mode != 1) return fail(KVC_E_SHAPE, "mode must be 0 (cold device pages) or 1 (hot host pages)");
+  if (!count || (cap > 0 && !out)) return fail(KVC_E_NULL, "out or count is NULL");
+  if (cap < 0) return fail(KVC_E_SHAPE, "cap must be >= 0");
+  return launched(kvc::launch_find_pages(*c, mode, out, cap, count, stream));
+}
+
+KVC_API kvc_status kvc_copy_pages(const kvc_cache* c, const int32_t* src, const int32_t* dst,
+                                  int32_t n, hipStream_t stream) {
+  kvc_status st = check_cache(c, kNeedInt4);
+  if (st != KVC_OK) return st;
+  if (n < 0) return fail(KVC_E_SHAPE, "n must be >= 0");
+  if (n == 0) return KVC_OK;
+  if (!src || !dst) return fail(KVC_E_NULL, "src or dst is NULL");
+  return launched(kvc::launch_copy_pages(*c, src, dst, n, stream));
 }
 
 KVC_API kvc_status kvc_shadow_attention(const void* q, const void* k, const void* v, kvc_dtype dtype,

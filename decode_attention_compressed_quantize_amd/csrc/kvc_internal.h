@@ -106,6 +106,12 @@ hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k
                              const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
                              int budget_permille, TopkState* state, hipStream_t s);
 
+// Host tier: page lists and whole-page copies between the two pools.
+hipError_t launch_find_pages(const kvc_cache& c, int mode, int32_t* out, int cap, int32_t* count,
+                             hipStream_t s);
+hipError_t launch_copy_pages(const kvc_cache& c, const int32_t* src, const int32_t* dst, int n,
+                             hipStream_t s);
+
 // Learner-side causal attention under recorded shadow rows (bf16 Q, K, V).
 hipError_t launch_shadow_attention(const void* q, const void* k, const void* v, int batch,
                                    int max_len, int num_q_heads, int num_kv_heads, int head_dim,

@@ -35,7 +35,10 @@ struct QuantParams {
   int max_pages;
   int num_pages;
   int max_ctx;
-  int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
+  int sink, recent;
+  uint8_t* codes_h;  // host tier: pages [num_pages, num_pages + host_pages)
+  uint16_t* meta_h;
+  int host_pages;  // INT8-protected sink and recent positions (16/128, or 0/0)
 };
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantParams p) {
   const int lp = pos / kPage;
   if (lp >= p.max_pages) return;
   const int page = p.block_table[(size_t)b * p.max_pages + lp];
-  if (page < 0 || page >= p.num_pages) return;
+  if (page < 0 || page >= p.num_pages + p.host_pages) return;
 
   const bool is_v = lane >= 32;
   const int hl = lane & 31;
@@ -121,8 +124,11 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantParams p) {
     const float r = fminf(fmaxf(__builtin_rintf(t), 0.0f), 15.0f);
     packed |= (uint32_t)r << (4 * e);
   }
-  const size_t rec = (((size_t)page * p.hkv + h) * kPage + (pos & (kPage - 1)));
-  uint8_t* crow = p.codes + rec * D + (is_v ? D / 2 : 0);
+  const bool host = page >= p.num_pages;  // a page of the host tier
+  uint8_t* const codes = host ? p.codes_h : p.codes;
+  uint16_t* const meta = host ? p.meta_h : p.meta;
+  const size_t rec = (((size_t)(host ? page - p.num_pages : page) * p.hkv + h) * kPage + (pos & (kPage - 1)));
+  uint8_t* crow = codes + rec * D + (is_v ? D / 2 : 0);
   if constexpr (EPL == 4) {
     reinterpret_cast<uint16_t*>(crow)[hl] = (uint16_t)packed;
   } else {
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantParams p) {
   }
   if ((hl % LPG) == 0) {
     const int g = hl / LPG;
-    uint32_t* m = reinterpret_cast<uint32_t*>(p.meta + ((rec * 2 + (is_v ? 1 : 0)) * (D / 32) + g) * 2);
+    uint32_t* m = reinterpret_cast<uint32_t*>(meta + ((rec * 2 + (is_v ? 1 : 0)) * (D / 32) + g) * 2);
     *m = (uint32_t)sh | ((uint32_t)mh << 16);
   }
 
@@ -184,6 +190,9 @@ hipError_t launch_quantize_append(const kvc_cache& c, const void* k_new, const v
   p.max_ctx = c.max_ctx;
   p.sink = c.n_sink;
   p.recent = c.n_recent;
+  p.codes_h = c.int4_codes_host;
+  p.meta_h = c.int4_meta_host;
+  p.host_pages = c.num_host_pages;
   const dim3 grid((unsigned)((p.items + 3) / 4));
   const dim3 block(256);
   const bool bf = src == KVC_BF16;

@@ -13,8 +13,8 @@ import numpy as np
 
 import workloads as W
 
-from . import (Cache, attention_workspace, block_workspace, kvc_quantize_append,
-               kvc_score_block_mask, kvc_score_topk_mask, topk_workspace)
+from . import (Cache, attention_workspace, block_workspace, kvc_copy_pages, kvc_find_pages,
+               kvc_quantize_append, kvc_score_block_mask, kvc_score_topk_mask, topk_workspace)
 
 
 def pack_bits(flags: np.ndarray, words: int) -> np.ndarray:
@@ -30,7 +30,8 @@ class LayerCache:
     """A prefilled cache of one layer of workload ``w`` plus its source tensors."""
 
     def __init__(self, w: W.Workload, layer: int = 0, device="cuda", batch_rows=None,
-                 table: Optional[np.ndarray] = None, keep_sources: bool = True):
+                 table: Optional[np.ndarray] = None, keep_sources: bool = True,
+                 host_pages: int = 0):
         import torch
 
         self.w, self.layer, self.device = w, layer, device
@@ -44,7 +45,11 @@ class LayerCache:
         self.table = torch.from_numpy(table).to(device)
         self.seq_lens = torch.from_numpy(self.lengths.astype(np.int32)).to(device)
         self.cache = Cache(w.batch, w.kv_heads, w.head_dim, self.max_ctx, num_pages,
-                           self.table, self.seq_lens, device=device, protect=w.protect)
+                           self.table, self.seq_lens, device=device, protect=w.protect,
+                           host_pages=host_pages)
+        self.num_pages = num_pages
+        self.host_free = list(range(num_pages, num_pages + host_pages))  # free host-tier page ids
+        self.dev_free = []  # device pages released by demotion
         self.k_src = {}
         self.v_src = {}
         self._prefill(keep_sources)
@@ -158,6 +163,50 @@ class LayerCache:
             return block_workspace(self.cache, self.w.block_tokens, self.device)
         return topk_workspace(self.cache, self.device)
 
+    # -------------------------------------------------------------- tiers
+    def _move_pages(self, mode: int, free: list) -> int:
+        """Find pages (kvc_find_pages ``mode``), copy them to pages from ``free``
+        and point the block table at the copies; returns how many moved."""
+        import torch
+
+        c = self.cache
+        cap = self.w.batch * self.table.shape[1]
+        out = torch.empty((cap, 2), dtype=torch.int32, device=self.device)
+        count = torch.empty(1, dtype=torch.int32, device=self.device)
+        kvc_find_pages(c, mode, out, count)
+        n = min(int(count.item()), cap, len(free))
+        if n == 0:
+            return 0
+        sel = out[:n].long()
+        src = self.table[sel[:, 0], sel[:, 1]].clone()
+        dst = torch.tensor(free[:n], dtype=torch.int32, device=self.device)
+        del free[:n]
+        kvc_copy_pages(c, src, dst)
+        self.table[sel[:, 0], sel[:, 1]] = dst
+        return n, src
+
+    def demote_cold_pages(self) -> int:
+        """Move device pages whose positions are all evicted to the host tier."""
+        r = self._move_pages(0, self.host_free)
+        if not r:
+            return 0
+        n, src = r
+        self.dev_free.extend(src.tolist())
+        return n
+
+    def promote_hot_pages(self) -> int:
+        """Move host-tier pages with a kept position back to released device pages."""
+        r = self._move_pages(1, self.dev_free)
+        if not r:
+            return 0
+        n, src = r
+        self.host_free.extend(src.tolist())
+        return n
+
+    def host_resident_pages(self) -> int:
+        t = self.table
+        return int(((t >= self.num_pages)).sum().item())
+
     def replica(self) -> "LayerCache":
         """An independent copy on the device (same contents, own memory)."""
         import copy
@@ -167,10 +216,12 @@ class LayerCache:
         r.table = self.table.clone()
         r.seq_lens = self.seq_lens.clone()
         r.cache = Cache(c.batch, c.kv_heads, c.head_dim, c.max_ctx, c.num_phys_pages, r.table,
-                        r.seq_lens, device=self.device, protect=c.protect)
-        for name in ("int4_codes", "int4_meta", "int8_codes", "int8_scales", "keep_mask", "scores"):
+                        r.seq_lens, device=self.device, protect=c.protect, host_pages=c.host_pages)
+        for name in ("int4_codes", "int4_meta", "int8_codes", "int8_scales", "keep_mask", "scores",
+                     "int4_codes_host", "int4_meta_host"):
             if getattr(c, name) is not None:
                 getattr(r.cache, name).copy_(getattr(c, name))
+        r.host_free, r.dev_free = list(self.host_free), list(self.dev_free)
         r.k_src, r.v_src = {}, {}
         return r
 

@@ -78,7 +78,7 @@ extern "C" {
 #endif
 
 #define KVC_API __attribute__((visibility("default")))
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum {
   KVC_OK = 0,
@@ -112,6 +112,12 @@ typedef struct kvc_cache {
   const int32_t* seq_lens;
   uint32_t* keep_mask;
   float* scores;
+  /* Optional host tier (temporal tiering, see below): physical pages
+   * [P, P + H) live in pinned host memory, addressed like the device pool. */
+  int32_t num_host_pages;    /* H >= 0 */
+  int32_t reserved;          /* 0 */
+  uint8_t* int4_codes_host;  /* [H][Hkv][16][2][D/2], or NULL when H = 0 */
+  uint16_t* int4_meta_host;  /* [H][Hkv][16][2][D/32][2], or NULL when H = 0 */
 } kvc_cache;
 
 /*
@@ -245,6 +251,34 @@ KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int
                                                  int32_t num_q_heads, float softmax_scale,
                                                  float* out, float* lse, void* ws, size_t ws_bytes,
                                                  hipStream_t stream);
+
+/*
+ * Host tier (temporal tiering). Source: TTKV promo page (arXiv 2604.19769),
+ * strengths section: a temporal-tiered cache keeps hot data in HBM and cold
+ * data in DRAM. Physical page ids [0, P) index the device pool (int4_codes,
+ * int4_meta), ids [P, P + H) the host pool (int4_codes_host, int4_meta_host,
+ * pinned host memory mapped for device access, same layout). Appends and
+ * attention read and write pages of either tier in place, so attention over
+ * a host page streams it over the host link. The caller chooses the policy:
+ *
+ * kvc_find_pages - list logical pages by tier and use, for moving them.
+ *   mode 0: device-pool pages whose 16 positions all lie in the INT4 region
+ *           ([n_sink, L - n_recent)) and are evicted for every kv head (cold);
+ *   mode 1: host-pool pages with at least one kept position (hot again).
+ *   out   : device int32 [cap][2] of (sequence, logical page), in no order.
+ *   count : device int32, set to the number of pages found (which may exceed
+ *           cap; only cap entries are written). Nothing else is modified.
+ *
+ * kvc_copy_pages - for i < n, copy physical page src[i] to dst[i] (INT4 codes
+ *   and meta of every kv head), pages of either tier. src, dst: device int32
+ *   [n]; out-of-range ids or src == dst skip the entry. The destinations must
+ *   be distinct and none may also be a source. The block table is not
+ *   changed: the caller points logical pages at their new physical pages.
+ */
+KVC_API kvc_status kvc_find_pages(const kvc_cache* c, int32_t mode, int32_t* out, int32_t cap,
+                                  int32_t* count, hipStream_t stream);
+KVC_API kvc_status kvc_copy_pages(const kvc_cache* c, const int32_t* src, const int32_t* dst,
+                                  int32_t n, hipStream_t stream);
 
 /*
  * kvc_shadow_attention - learner-side causal attention under the recorded

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert kvc.kvc_abi_version() == 1
+    assert kvc.kvc_abi_version() == 2
     assert kvc.kvc_status_string(0) == "ok"
     assert kvc.kvc_status_string(-4) == "workspace too small"
 
@@ -161,6 +161,20 @@ def test_block_mask_argument_errors(lib):
     # more than 131072 blocks per sequence
     big = 131072 * 16 + 1
     assert call(desc(max_ctx=big, max_pages_per_seq=(big + 15) // 16)) == -3
+
+
+def test_tier_argument_errors(lib):
+    c = desc(num_host_pages=4)            # host pool pointers missing
+    assert lib.kvc_copy_pages(ctypes.byref(c), FAKE, FAKE, 1, None) == -1
+    assert attn(lib, c) == -1
+    assert attn(lib, desc(num_host_pages=-1)) == -2
+    ok = desc(num_host_pages=4, int4_codes_host=FAKE, int4_meta_host=FAKE)
+    assert attn(lib, ok, ws=None) == -4   # passes the cache checks
+    assert lib.kvc_copy_pages(ctypes.byref(ok), FAKE, FAKE, 0, None) == 0
+    assert lib.kvc_copy_pages(ctypes.byref(ok), None, FAKE, 3, None) == -1
+    assert lib.kvc_find_pages(ctypes.byref(ok), 2, FAKE, 8, FAKE, None) == -2
+    assert lib.kvc_find_pages(ctypes.byref(ok), 0, None, 8, FAKE, None) == -1
+    assert attn(lib, desc(num_host_pages=4, int4_codes_host=FAKE + 4, int4_meta_host=FAKE)) == -3
 
 
 def test_block_workspace_size(lib):
