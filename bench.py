@@ -30,6 +30,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+HOST_LINK_PEAK_GBS = 64.0  # PCIe Gen5 x16, one direction
+# Host tier: "cold" demotes pages whose positions are all evicted after the
+# prefill; "all" moves every whole INT4-region page to the host tier.
+TIER_MODE = {"long128k_tiered": "cold", "long128k_streamed": "all"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_long128k_traffic.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_compressed_quantize_amd", "csrc", "attention.hip")
 
@@ -38,6 +42,8 @@ WORKLOAD_LAYERS = {
     "long128k_blocks": ["long128k_blk_b10", "long128k_blk_b50"],
     "long128k_recent16k": ["long128k_r16k_b10", "long128k_r16k_b50"],
     "long128k_kv4": ["long128k_kv4_b10", "long128k_kv4_b50"],
+    "long128k_tiered": ["long128k_blk_b10", "long128k_blk_b50"],
+    "long128k_streamed": ["long128k_b10"],
     "uniform4k": ["uniform4k"],
     "longtail": ["longtail"],
     "fullstep": ["fullstep"] * 36,
@@ -362,8 +368,15 @@ def main():
     per_replica_bytes = 0
     layers = []
     print(f"bench: building {args.workload} ({len(base)} layer caches per replica)", file=sys.stderr, flush=True)
+    tier = TIER_MODE.get(args.workload)
+    host_moved = 0
     for li, w in enumerate(base):
-        lc = LayerCache(w, layer=li, device=dev, keep_sources=False)
+        host = W.page_table(w, li)[1] if tier else 0
+        lc = LayerCache(w, layer=li, device=dev, keep_sources=False, host_pages=host)
+        if tier == "cold":
+            host_moved += lc.demote_cold_pages()
+        elif tier == "all":
+            host_moved += lc.stream_int4_region()
         layers.append(lc)
         per_replica_bytes += lc.cache.nbytes()
     replicas = args.replicas
@@ -371,6 +384,8 @@ def main():
                            for lc in layers)
     if replicas <= 0:
         replicas = max(1, math.ceil((1 << 30) / read_per_replica) + 1) if len(base) < 8 else 1
+    if tier == "all":
+        replicas = 1  # host-tier reads are not served by the GPU's caches
     # replicas are device copies of the prefilled caches, within 96 GiB in all
     replicas = max(1, min(replicas, int((96 << 30) // max(1, per_replica_bytes))))
     reps = [layers]
@@ -493,6 +508,12 @@ def main():
                              + (f", budget {w.budget_permille / 10:g}%" if w.budget_permille else ""))
                             for w in base[:2]],
         },
+        "host_tier": None if not tier else {
+            "mode": {"cold": "pages with every position evicted demoted after the prefill",
+                     "all": "every whole INT4-region page in the host tier"}[tier],
+            "pages_in_host_tier_per_replica": host_moved,
+            "int4_pages_per_replica": int(sum(lc.num_pages for lc in layers)),
+        },
         "decode_steps_per_s": round(1000.0 / ms, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "attention": {"ms_per_call": round(a_ms, 5), "GBs": round(a_gbs, 1), "per_layer": detail,
@@ -500,11 +521,11 @@ def main():
         "roofline": {
             "kernel": "kvc_decode_attention call: attention_kernel (INT4 chunks + INT8 region) "
                       "then merge_kernel, timed together with HIP events on the launch stream",
-            "bound": "hbm",
+            "bound": "host-link" if tier == "all" else "hbm",
             "achieved": round(a_gbs, 1),
-            "peak": HBM_PEAK_GBS,
+            "peak": HOST_LINK_PEAK_GBS if tier == "all" else HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(a_gbs / (HOST_LINK_PEAK_GBS if tier == "all" else HBM_PEAK_GBS), 4),
             "traffic": measured_traffic(args.workload),
             "algorithmic_bytes_per_call": int(sum(attn_bytes) / len(attn_bytes)),
         },

@@ -203,6 +203,27 @@ class LayerCache:
         self.host_free.extend(src.tolist())
         return n
 
+    def stream_int4_region(self) -> int:
+        """Move every whole page of the INT4 region to the host tier, so that all
+        kept INT4 positions are read over the host link."""
+        import torch
+
+        ns, nr = (16, 128) if self.w.protect else (0, 0)
+        pairs = [(b, lp) for b in range(self.w.batch)
+                 for lp in range(ns // 16, max(0, int(self.lengths[b]) - nr) // 16)
+                 if int(self.table_np[b, lp]) < self.num_pages]
+        pairs = pairs[: len(self.host_free)]
+        if not pairs:
+            return 0
+        idx = torch.tensor(pairs, dtype=torch.long, device=self.device)
+        src = self.table[idx[:, 0], idx[:, 1]].clone()
+        dst = torch.tensor(self.host_free[: len(pairs)], dtype=torch.int32, device=self.device)
+        del self.host_free[: len(pairs)]
+        kvc_copy_pages(self.cache, src, dst)
+        self.table[idx[:, 0], idx[:, 1]] = dst
+        self.dev_free.extend(src.tolist())
+        return len(pairs)
+
     def host_resident_pages(self) -> int:
         t = self.table
         return int(((t >= self.num_pages)).sum().item())
