@@ -473,6 +473,8 @@ def main():
     gbs = step_bytes / args.steps / (ms * 1e-3) / 1e9
 
     attn_ms = [e0.elapsed_time(e1) for e0, e1, _, _ in attn_events]
+    print("bench: attention call times (ms): " + " ".join(f"{w.name[-3:]}:{t:.4f}" for (_, _, w, _), t in
+                                                     zip(attn_events, attn_ms)), file=sys.stderr, flush=True)
     attn_bytes = [algorithmic_bytes(w, L, kept_counts(w, L)) for _, _, w, L in attn_events]
     a_ms = sum(attn_ms) / len(attn_ms)
     a_gbs = (sum(attn_bytes) / len(attn_bytes)) / (a_ms * 1e-3) / 1e9

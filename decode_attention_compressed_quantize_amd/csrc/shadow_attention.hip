@@ -24,6 +24,7 @@ namespace kvc {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -89,11 +90,6 @@ __device__ inline float row16_sum(float x) {
   return x + dpp<0x140>(x);
 }
 
-// float -> bf16 bits, round to nearest even (finite inputs)
-__device__ inline uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 template <int D, int G>
 __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowParams p) {
@@ -284,17 +280,25 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
           const float rs = row16_sum(pa + pb);
           l[blk][jj] = l[blk][jj] * corr[blk][jj] + rs;
           m[blk][jj] = mn;
+          // P = high + low bf16 parts (round to nearest even, hardware conversion)
           const int pr = lr + jj;
-          const uint32_t ha = bf16_rne(pa), hb = bf16_rne(pb);
-          sm.ph[wave][blk][pr][lane & 15] = (uint16_t)ha;
-          sm.ph[wave][blk][pr][16 + (lane & 15)] = (uint16_t)hb;
-          sm.pl[wave][blk][pr][lane & 15] = (uint16_t)bf16_rne(pa - __uint_as_float(ha << 16));
-          sm.pl[wave][blk][pr][16 + (lane & 15)] = (uint16_t)bf16_rne(pb - __uint_as_float(hb << 16));
+          const bf16x2 hi = {(__bf16)pa, (__bf16)pb};
+          const bf16x2 lo = {(__bf16)(pa - (float)hi[0]), (__bf16)(pb - (float)hi[1])};
+          const uint32_t hw = __builtin_bit_cast(uint32_t, hi), lw = __builtin_bit_cast(uint32_t, lo);
+          sm.ph[wave][blk][pr][lane & 15] = (uint16_t)hw;
+          sm.ph[wave][blk][pr][16 + (lane & 15)] = (uint16_t)(hw >> 16);
+          sm.pl[wave][blk][pr][lane & 15] = (uint16_t)lw;
+          sm.pl[wave][blk][pr][16 + (lane & 15)] = (uint16_t)(lw >> 16);
         }
+        // O needs rescaling only where a row maximum rose (corr < 1)
+        const bool rose = corr[blk][0] != 1.0f || corr[blk][1] != 1.0f || corr[blk][2] != 1.0f ||
+                          corr[blk][3] != 1.0f;
+        if (__ballot(rose) != 0) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+          for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) o[blk][t][jj] *= corr[blk][jj];
+            for (int jj = 0; jj < 4; ++jj) o[blk][t][jj] *= corr[blk][jj];
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
