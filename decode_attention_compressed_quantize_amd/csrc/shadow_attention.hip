@@ -12,10 +12,13 @@
 // rows attend each one, then walks the list 32 keys at a time:
 //   - K rows of the 32 keys into LDS, V rows transposed into LDS (gathers of
 //     16-byte pieces; the listed positions are arbitrary);
-//   - S = Q K^T with bf16 MFMA 16x16x32 (Q operands held in registers);
-//   - masked online softmax in log2 units (row reductions over a 16-lane DPP row);
-//   - O += P V with bf16 MFMA, P split into a high and a low bf16 part so that
-//     P keeps ~16 significant bits.
+//   - S^T = K Q^T with bf16 MFMA 16x16x32 (Q operands held in registers), so
+//     that each lane holds eight keys of one query row;
+//   - masked online softmax in log2 units, lane-local: the row maximum is
+//     refreshed (across the row's four lanes) only when a score passes it by a
+//     fixed slack, and row sums are reduced once at the end;
+//   - O^T += V^T P^T with bf16 MFMA, P^T straight from registers, split into a
+//     high and a low bf16 part so that P keeps ~16 significant bits.
 // Nothing is computed for keys no row of the tile attends.
 
 #include "kvc_internal.h"
@@ -54,14 +57,11 @@ struct SaSmem {
   static constexpr int NRW = R / 32;             // 32-row words of a key's row mask
   static constexpr int KS = D + 8;               // K row stride (bf16 elements)
   static constexpr int VS = kStep + 8;           // V^T row stride
-  static constexpr int PS = kStep + 8;           // P row stride
   alignas(16) uint16_t k[2][kStep][KS];  // two buffers: step s computes from one while
   alignas(16) uint16_t vt[2][D][VS];     // step s + 1's keys are written into the other
-  alignas(16) uint16_t ph[kSaWaves][2][16][PS];
-  alignas(16) uint16_t pl[kSaWaves][2][16][PS];
+  alignas(16) uint32_t rmask[NRW][kSpan];  // listed key x: bit i of word q = row r0 + 32q + i attends it
   uint32_t rw[R][kSpan / 32];     // the tile rows' attended-key words over the span
   uint32_t pos[kSpan];            // listed key positions
-  uint32_t rmask[kSpan][NRW];     // per listed key: bit i of word q = row r0 + 32q + i attends it
   uint32_t wcnt[kSaWaves];
 };
 
@@ -70,33 +70,29 @@ __device__ inline float4v mfma_bf16(u32x4 a, u32x4 b, float4v c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Max and sum over the 16 lanes of a DPP row (one row of the MFMA C layout):
-// swap neighbours, swap pairs, mirror within 8, mirror within 16. Every lane
-// ends with the row's result.
-template <int Ctrl>
-__device__ inline float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
-}
-__device__ inline float row16_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-  return fmaxf(x, dpp<0x140>(x));  // row_mirror
-}
-__device__ inline float row16_sum(float x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  return x + dpp<0x140>(x);
+// Column of V^T that holds key e of a 32-key step. S^T = K Q^T leaves lane
+// group g (lanes 16g .. 16g + 15) with keys 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3
+// of its query row; taking those eight keys as MFMA k indices 8g .. 8g + 7 makes
+// the lane's probabilities the B operand of O^T = V^T P^T as they stand, so V^T
+// stores its key columns in that order.
+__device__ inline int vt_col(int e) { return 8 * ((e & 15) >> 2) + 4 * (e >> 4) + (e & 3); }
+
+// s where bit i of w is set, else -inf
+__device__ inline float keep_or_neg_inf(float s, uint32_t w, int i) {
+  const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)w, i, 1);
+  return __uint_as_float((__float_as_uint(s) & keep) | (0xFF800000u & ~keep));
 }
 
+// Scores may exceed the row maximum used for the exponentials by this much
+// (log2 units) before the maximum is refreshed: probabilities stay below 2^8.
+constexpr float kSlack = 8.0f;
 
 template <int D, int G>
 __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowParams p) {
   using S = SaSmem<D, G>;
   constexpr int R = S::R, NRW = S::NRW;
   constexpr int NC = D / 32;  // MFMA k-chunks over head_dim
-  constexpr int NT = D / 16;  // output column tiles
+  constexpr int NT = D / 16;  // output head_dim tiles
   constexpr int NL = kStep * (D / 8) / kSaThreads;  // 16-byte K (and V) pieces per thread per step
   __shared__ S sm;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -113,15 +109,16 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
   const int rend = r0 + R < L ? r0 + R : L;  // rows [r0, rend), keys [0, rend)
   const int g = wave % G, rb = wave / G;
   const int qh = h * G + g;
-  const int wrow0 = r0 + 32 * rb;  // this wave's 32 rows: two MFMA row blocks of 16
+  const int wrow0 = r0 + 32 * rb;  // this wave's 32 rows: two MFMA column blocks of 16
+  const int lg = lane >> 4;        // lane group: keys 4lg .. 4lg + 3 of each 16-key tile
 
-  // Q operands (A of QK^T): lane holds row wrow0 + 16 * blk + lane % 16,
+  // Q operands (B of S^T = K Q^T): lane holds row wrow0 + 16 * blk + lane % 16,
   // head_dim entries 32c + 8 * (lane / 16) .. + 7 of chunk c
   u32x4 qa[2][NC];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int row = wrow0 + 16 * blk + (lane & 15);
-    const uint16_t* qp = p.q + (((size_t)b * p.max_len + row) * p.hq + qh) * D + 8 * (lane >> 4);
+    const uint16_t* qp = p.q + (((size_t)b * p.max_len + row) * p.hq + qh) * D + 8 * lg;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -129,20 +126,22 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
     }
   }
 
-  // lane's rows in the C layout: 16 * blk + 4 * (lane / 16) + jj of the wave's 32
-  const int lr = 4 * (lane >> 4);
-  float m[2][4], l[2][4];
+  // Per lane and column block: the query row wrow0 + 16 * blk + lane % 16. m is
+  // the row maximum the exponentials are taken against (log2 units, the same in
+  // the row's four lane groups), lsum the lane's share of the row sum, o the
+  // O^T tiles (head_dim 16t + 4 * (lane / 16) + j of the row).
+  float m[2], nm[2], cap[2], lsum[2];
   float4v o[2][NT];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      m[blk][jj] = -INFINITY;
-      l[blk][jj] = 0.0f;
-    }
+    m[blk] = -INFINITY;
+    nm[blk] = 0.0f;
+    cap[blk] = -INFINITY;  // raw scores above cap refresh the maximum
+    lsum[blk] = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) o[blk][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  const float inv_alpha = 1.0f / p.alpha;
 
   const uint32_t* srow = p.shadow + ((size_t)b * p.hkv + h) * p.rows * (size_t)p.words;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -199,7 +198,7 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
         const int at = base + (int)__popcll(bal & below);
         sm.pos[at] = (uint32_t)(cb + jl);
 #pragma unroll
-        for (int q = 0; q < NRW; ++q) sm.rmask[at][q] = rm[q];
+        for (int q = 0; q < NRW; ++q) sm.rmask[q][at] = rm[q];
       }
       total += add;
       __syncthreads();
@@ -209,117 +208,176 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
     for (int x = total + (int)threadIdx.x; x < padded; x += kSaThreads) {
       sm.pos[x] = sm.pos[0];
 #pragma unroll
-      for (int q = 0; q < NRW; ++q) sm.rmask[x][q] = 0;
+      for (int q = 0; q < NRW; ++q) sm.rmask[q][x] = 0;
     }
     __syncthreads();
 
-    // ---- 32 listed keys per step. Thread piece x covers key x % 32 and
-    // head_dim chunk x / 32 (so a wave's V^T writes fill consecutive banks);
-    // the next step's pieces are loaded while this one computes.
+    // ---- 32 listed keys per step, software-pipelined: while step s's
+    // probabilities are formed (VALU), the MFMA unit computes step s + 1's
+    // scores, so K runs one step ahead of V. LDS holds K(s + 1) and V(s)
+    // during step s, which writes K(s + 2) and V(s + 1) into the buffers read
+    // in step s - 1. Thread piece x covers key x % 32 and head_dim chunk x / 32
+    // (so a wave's V^T writes fill consecutive banks). Step indices past the
+    // end are clamped to the last step: their loads stay in bounds and their
+    // results are never used.
+    const int nsteps = padded / kStep;
     u32x4 kr[NL], vr[NL];
-    auto gather = [&](int s0) {
+    auto gather_k = [&](int st) {
+      st = st < nsteps ? st : nsteps - 1;
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
         const int x = (int)threadIdx.x + u * kSaThreads;
         const int e = x % kStep, c = x / kStep;
-        const size_t off = (((size_t)b * p.max_len + sm.pos[s0 + e]) * p.hkv + h) * D + 8 * c;
-        kr[u] = *reinterpret_cast<const u32x4*>(p.k + off);
-        vr[u] = *reinterpret_cast<const u32x4*>(p.v + off);
+        kr[u] = *reinterpret_cast<const u32x4*>(
+            p.k + (((size_t)b * p.max_len + sm.pos[st * kStep + e]) * p.hkv + h) * D + 8 * c);
       }
     };
-    auto stage = [&](int buf) {
+    auto gather_v = [&](int st) {
+      st = st < nsteps ? st : nsteps - 1;
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
         const int x = (int)threadIdx.x + u * kSaThreads;
         const int e = x % kStep, c = x / kStep;
-        *reinterpret_cast<u32x4*>(&sm.k[buf][e][8 * c]) = kr[u];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) sm.vt[buf][8 * c + t][e] = (uint16_t)(vr[u][t >> 1] >> (16 * (t & 1)));
+        vr[u] = *reinterpret_cast<const u32x4*>(
+            p.v + (((size_t)b * p.max_len + sm.pos[st * kStep + e]) * p.hkv + h) * D + 8 * c);
       }
     };
-    if (padded > 0) {
-      gather(0);
-      stage(0);
-    }
-    __syncthreads();
-    for (int s0 = 0, buf = 0; s0 < padded; s0 += kStep, buf ^= 1) {
-      const bool more = s0 + kStep < padded;
-      if (more) gather(s0 + kStep);
-      // S = Q K^T for both row blocks; each K operand read once
-      float4v sacc[2][2];
+    auto stage_k = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const int x = (int)threadIdx.x + u * kSaThreads;
+        *reinterpret_cast<u32x4*>(&sm.k[buf][x % kStep][8 * (x / kStep)]) = kr[u];
+      }
+    };
+    auto stage_v = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const int x = (int)threadIdx.x + u * kSaThreads;
+        const int e = x % kStep, c = x / kStep;
+        const int col = vt_col(e);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) sm.vt[buf][8 * c + t][col] = (uint16_t)(vr[u][t >> 1] >> (16 * (t & 1)));
+      }
+    };
+    // S^T = K Q^T from K buffer kb: tile t2 holds keys 16 t2 .. + 15 (rows) of
+    // the block's 16 query rows (columns)
+    auto scores = [&](int kb, float4v (&st)[2][2]) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) sacc[blk][t2] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t2 = 0; t2 < 2; ++t2) st[blk][t2] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const u32x4 kb4 =
-              *reinterpret_cast<const u32x4*>(&sm.k[buf][16 * t2 + (lane & 15)][32 * c + 8 * (lane >> 4)]);
-          sacc[0][t2] = mfma_bf16(qa[0][c], kb4, sacc[0][t2]);
-          sacc[1][t2] = mfma_bf16(qa[1][c], kb4, sacc[1][t2]);
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(&sm.k[kb][16 * t2 + (lane & 15)][32 * c + 8 * lg]);
+          st[0][t2] = mfma_bf16(ka, qa[0][c], st[0][t2]);
+          st[1][t2] = mfma_bf16(ka, qa[1][c], st[1][t2]);
         }
       }
-      const uint32_t rmA = sm.rmask[s0 + (lane & 15)][rb];
-      const uint32_t rmB = sm.rmask[s0 + 16 + (lane & 15)][rb];
-      float corr[2][4];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int i = 16 * blk + lr + jj;
-          const float sa = ((rmA >> i) & 1u) ? sacc[blk][0][jj] * p.alpha : -INFINITY;
-          const float sb = ((rmB >> i) & 1u) ? sacc[blk][1][jj] * p.alpha : -INFINITY;
-          const float mx = row16_max(fmaxf(sa, sb));
-          const float mn = fmaxf(m[blk][jj], mx);
-          const float ms = mn == -INFINITY ? 0.0f : mn;
-          corr[blk][jj] = __builtin_amdgcn_exp2f(m[blk][jj] - ms);
-          const float pa = __builtin_amdgcn_exp2f(sa - ms);
-          const float pb = __builtin_amdgcn_exp2f(sb - ms);
-          const float rs = row16_sum(pa + pb);
-          l[blk][jj] = l[blk][jj] * corr[blk][jj] + rs;
-          m[blk][jj] = mn;
-          // P = high + low bf16 parts (round to nearest even, hardware conversion)
-          const int pr = lr + jj;
-          const bf16x2 hi = {(__bf16)pa, (__bf16)pb};
-          const bf16x2 lo = {(__bf16)(pa - (float)hi[0]), (__bf16)(pb - (float)hi[1])};
-          const uint32_t hw = __builtin_bit_cast(uint32_t, hi), lw = __builtin_bit_cast(uint32_t, lo);
-          sm.ph[wave][blk][pr][lane & 15] = (uint16_t)hw;
-          sm.ph[wave][blk][pr][16 + (lane & 15)] = (uint16_t)(hw >> 16);
-          sm.pl[wave][blk][pr][lane & 15] = (uint16_t)lw;
-          sm.pl[wave][blk][pr][16 + (lane & 15)] = (uint16_t)(lw >> 16);
-        }
-        // O needs rescaling only where a row maximum rose (corr < 1)
-        const bool rose = corr[blk][0] != 1.0f || corr[blk][1] != 1.0f || corr[blk][2] != 1.0f ||
-                          corr[blk][3] != 1.0f;
-        if (__ballot(rose) != 0) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) o[blk][t][jj] *= corr[blk][jj];
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // O += P V (A = P rows x keys, B = V^T keys x head_dim columns), each V operand read once
-      u32x4 pha[2], pla[2];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        pha[blk] = *reinterpret_cast<const u32x4*>(&sm.ph[wave][blk][lane & 15][8 * (lane >> 4)]);
-        pla[blk] = *reinterpret_cast<const u32x4*>(&sm.pl[wave][blk][lane & 15][8 * (lane >> 4)]);
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 vb = *reinterpret_cast<const u32x4*>(&sm.vt[buf][16 * t + (lane & 15)][8 * (lane >> 4)]);
+    };
+    float4v st[2][2];
+    if (nsteps > 0) {
+      gather_k(0);
+      gather_v(0);
+      stage_k(0);
+      stage_v(0);
+      gather_k(1);
+      stage_k(1);
+      __syncthreads();
+      scores(0, st);
+    }
+    for (int s = 0; s < nsteps; ++s) {
+      const int s0 = s * kStep;
+      gather_k(s + 2);
+      gather_v(s + 1);
+      // row masks of the lane's eight keys; skipped when the wave's 32 rows attend all 32 keys
+      const u32x4 wa = *reinterpret_cast<const u32x4*>(&sm.rmask[rb][s0 + 4 * lg]);
+      const u32x4 wb = *reinterpret_cast<const u32x4*>(&sm.rmask[rb][s0 + 16 + 4 * lg]);
+      const uint32_t every = wa[0] & wa[1] & wa[2] & wa[3] & wb[0] & wb[1] & wb[2] & wb[3];
+      if (__ballot(every != ~0u) != 0) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-          o[blk][t] = mfma_bf16(pha[blk], vb, o[blk][t]);
-          o[blk][t] = mfma_bf16(pla[blk], vb, o[blk][t]);
+          const int i = 16 * blk + (lane & 15);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            st[blk][0][j] = keep_or_neg_inf(st[blk][0][j], wa[j], i);
+            st[blk][1][j] = keep_or_neg_inf(st[blk][1][j], wb[j], i);
+          }
         }
       }
-      if (more) stage(buf ^ 1);  // the other buffer was last read in the previous step
+      // refresh a block's row maxima only where some score passed its cap
+      bool up[2];
+      float lmax[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const float4v x = st[blk][0], y = st[blk][1];
+        lmax[blk] = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
+        up[blk] = lmax[blk] > cap[blk];
+      }
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        if (__ballot(up[blk]) == 0) continue;
+        float mx = lmax[blk];
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m[blk], mx * p.alpha);
+        const float ms = mn == -INFINITY ? 0.0f : mn;
+        const float corr = __builtin_amdgcn_exp2f(m[blk] - ms);
+        m[blk] = mn;
+        nm[blk] = -ms;
+        cap[blk] = (mn + kSlack) * inv_alpha;
+        lsum[blk] *= corr;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[blk][t] *= corr;
+      }
+      // next step's scores; their MFMAs interleave with the exponentials below
+      float4v sn[2][2];
+      scores((s + 1) & 1, sn);
+      // P^T = exp2(alpha S^T - m): high + low bf16 parts (round to nearest even,
+      // hardware conversion), already in the B operand layout of O^T = V^T P^T
+      u32x4 ph[2], pl[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[blk][0][j], p.alpha, nm[blk]));
+          pv[4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[blk][1][j], p.alpha, nm[blk]));
+        }
+        lsum[blk] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 hi = {(__bf16)pv[2 * e], (__bf16)pv[2 * e + 1]};
+          const uint32_t hw = __builtin_bit_cast(uint32_t, hi);
+          const float h0 = __uint_as_float(hw << 16), h1 = __uint_as_float(hw & 0xFFFF0000u);
+          const bf16x2 lo = {(__bf16)(pv[2 * e] - h0), (__bf16)(pv[2 * e + 1] - h1)};
+          ph[blk][e] = hw;
+          pl[blk][e] = __builtin_bit_cast(uint32_t, lo);
+        }
+      }
+      // O^T += V^T P^T (A = V^T head_dim rows x keys, B = P^T keys x query rows), each V^T operand read once
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x4 va = *reinterpret_cast<const u32x4*>(&sm.vt[s & 1][16 * t + (lane & 15)][8 * lg]);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          o[blk][t] = mfma_bf16(va, ph[blk], o[blk][t]);
+          o[blk][t] = mfma_bf16(va, pl[blk], o[blk][t]);
+        }
+      }
+      stage_k(s & 1);
+      stage_v((s + 1) & 1);
+      // issue order: each score MFMA followed by six VALU instructions
+#pragma unroll
+      for (int i = 0; i < 2 * 2 * NC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) st[blk][t2] = sn[blk][t2];
       __syncthreads();
     }
   }
@@ -327,18 +385,17 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
   // ---- out = O / l, lse = ln 2 * (m + log2 l); rows that attend nothing get 0 and -inf
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
+    float l = lsum[blk];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int row = wrow0 + 16 * blk + (lane & 15);
+    if (row >= L) continue;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float* op = p.out + (((size_t)b * p.max_len + row) * p.hq + qh) * D + 4 * lg;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int row = wrow0 + 16 * blk + lr + jj;
-      if (row >= L) continue;
-      const float inv = l[blk][jj] > 0.0f ? 1.0f / l[blk][jj] : 0.0f;
-      float* op = p.out + (((size_t)b * p.max_len + row) * p.hq + qh) * D + (lane & 15);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) op[16 * t] = o[blk][t][jj] * inv;
-      if (p.lse && (lane & 15) == 0)
-        p.lse[((size_t)b * p.max_len + row) * p.hq + qh] =
-            l[blk][jj] > 0.0f ? (m[blk][jj] + log2f(l[blk][jj])) * kLn2 : -INFINITY;
-    }
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<float4v*>(op + 16 * t) = o[blk][t] * inv;
+    if (p.lse && lg == 0)
+      p.lse[((size_t)b * p.max_len + row) * p.hq + qh] = l > 0.0f ? (m[blk] + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
