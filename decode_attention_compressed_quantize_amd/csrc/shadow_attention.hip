@@ -3,22 +3,23 @@
 // rollout step is injected into the learner's causal attention, so that each
 // generated position's query attends to exactly what the rollout attended).
 //
-// One workgroup per (sequence, kv head, tile of R query rows); R = 32 * 4 / G,
+// One workgroup per (sequence, kv head, tile of R query rows); R = 32 * 8 / G,
 // so that each wave owns 32 rows (two MFMA row blocks sharing every K and V
 // operand read) of one query head and the waves share every key tile. Per span
-// of 512 key positions the workgroup lists the keys that
+// of up to 2048 / (R / 32) key positions the workgroup lists the keys that
 // any of its rows attends (prompt rows: all keys up to the row; generated rows:
 // the shadow row's bits up to the row) together with an R-bit mask of which
 // rows attend each one, then walks the list 32 keys at a time:
-//   - K rows of the 32 keys into LDS, V rows transposed into LDS (gathers of
-//     16-byte pieces; the listed positions are arbitrary);
+//   - K and V rows of the 32 keys into LDS (gathers of 16-byte pieces; the
+//     listed positions are arbitrary);
 //   - S^T = K Q^T with bf16 MFMA 16x16x32 (Q operands held in registers), so
 //     that each lane holds eight keys of one query row;
 //   - masked online softmax in log2 units, lane-local: the row maximum is
 //     refreshed (across the row's four lanes) only when a score passes it by a
 //     fixed slack, and row sums are reduced once at the end;
-//   - O^T += V^T P^T with bf16 MFMA, P^T straight from registers, split into a
-//     high and a low bf16 part so that P keeps ~16 significant bits.
+//   - O^T += V^T P^T with bf16 MFMA, V^T through transposing LDS reads, P^T
+//     straight from registers, split into a high and a low bf16 part so that
+//     P keeps ~16 significant bits.
 // Nothing is computed for keys no row of the tile attends.
 
 #include "kvc_internal.h"
@@ -31,10 +32,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSaThreads = 256;
-constexpr int kSaWaves = 4;
+constexpr int kSaThreads = 512;
+constexpr int kSaWaves = 8;
 constexpr int kStep = 32;   // listed keys per MFMA step
-constexpr int kSpan = 512;  // key positions listed at a time
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -55,13 +55,17 @@ template <int D, int G>
 struct SaSmem {
   static constexpr int R = 32 * (kSaWaves / G);  // query rows per workgroup (32 per wave)
   static constexpr int NRW = R / 32;             // 32-row words of a key's row mask
-  static constexpr int KS = D + 8;               // K row stride (bf16 elements)
-  static constexpr int VS = kStep + 8;           // V^T row stride
-  alignas(16) uint16_t k[2][kStep][KS];  // two buffers: step s computes from one while
-  alignas(16) uint16_t vt[2][D][VS];     // step s + 1's keys are written into the other
-  alignas(16) uint32_t rmask[NRW][kSpan];  // listed key x: bit i of word q = row r0 + 32q + i attends it
-  uint32_t rw[R][kSpan / 32];     // the tile rows' attended-key words over the span
-  uint32_t pos[kSpan];            // listed key positions
+  static constexpr int SPAN = 2048 / NRW;        // key positions listed at a time
+  // Row strides (bf16 elements) that keep the 16-byte operand reads free of
+  // bank conflicts: LDS serves them 32 lanes at a time over 128 four-byte
+  // banks, so the 32 lanes' 16-byte pieces (16 rows x 2 column chunks) must
+  // fall on distinct bank quadruples.
+  static constexpr int KS = D + 16;  // K and V rows: 72 or 40 dwords apart
+  alignas(16) uint16_t k[2][kStep][KS];  // two buffers each: a step computes from one
+  alignas(16) uint16_t v[2][kStep][KS];  // while later keys are written into the other
+  alignas(16) uint32_t rmask[NRW][SPAN];  // listed key x: bit i of word q = row r0 + 32q + i attends it
+  uint32_t rw[R][SPAN / 32];     // the tile rows' attended-key words over the span
+  uint32_t pos[SPAN];            // listed key positions
   uint32_t wcnt[kSaWaves];
 };
 
@@ -70,12 +74,25 @@ __device__ inline float4v mfma_bf16(u32x4 a, u32x4 b, float4v c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Column of V^T that holds key e of a 32-key step. S^T = K Q^T leaves lane
-// group g (lanes 16g .. 16g + 15) with keys 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3
-// of its query row; taking those eight keys as MFMA k indices 8g .. 8g + 7 makes
-// the lane's probabilities the B operand of O^T = V^T P^T as they stand, so V^T
-// stores its key columns in that order.
-__device__ inline int vt_col(int e) { return 8 * ((e & 15) >> 2) + 4 * (e >> 4) + (e & 3); }
+// S^T = K Q^T leaves lane group g (lanes 16g .. 16g + 15) with keys 4g .. 4g + 3
+// and 16 + 4g .. 16 + 4g + 3 of its query row; taking those eight keys as MFMA
+// k indices 8g .. 8g + 7 makes the lane's probabilities the B operand of
+// O^T = V^T P^T as they stand. The V^T operand in that key order comes from V
+// rows in LDS through two transposing reads (ds_read_b64_tr_b16): within a
+// 16-lane group, lane 4m + q addresses head_dim entries d0 + 4q .. + 3 of key m
+// and lane i receives entry d0 + i of keys 0 .. 3.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+__device__ inline uint2 read_tr16(const uint16_t* p) {
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Piece x (0 .. 32 * D / 8 - 1) of a 32-key step: key and head_dim chunk. The
+// 32 lanes of a half wave take 16 keys x 2 chunks, so their 16-byte K writes
+// fall on distinct bank quadruples.
+__device__ inline int piece_key(int x) { return (x & 15) | (((x >> 5) & 1) << 4); }
+__device__ inline int piece_chunk(int x) { return ((x >> 4) & 1) | ((x >> 6) << 1); }
 
 // s where bit i of w is set, else -inf
 __device__ inline float keep_or_neg_inf(float s, uint32_t w, int i) {
@@ -88,12 +105,13 @@ __device__ inline float keep_or_neg_inf(float s, uint32_t w, int i) {
 constexpr float kSlack = 8.0f;
 
 template <int D, int G>
-__global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowParams p) {
+__global__ __launch_bounds__(kSaThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void shadow_attention_kernel(ShadowParams p) {
   using S = SaSmem<D, G>;
   constexpr int R = S::R, NRW = S::NRW;
   constexpr int NC = D / 32;  // MFMA k-chunks over head_dim
   constexpr int NT = D / 16;  // output head_dim tiles
-  constexpr int NL = kStep * (D / 8) / kSaThreads;  // 16-byte K (and V) pieces per thread per step
+  constexpr int kPieces = kStep * (D / 8);  // 16-byte K (and V) pieces per step
+  constexpr int NL = (kPieces + kSaThreads - 1) / kSaThreads;  // per thread
   __shared__ S sm;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int pairs = p.hkv * p.batch;
@@ -145,8 +163,8 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
 
   const uint32_t* srow = p.shadow + ((size_t)b * p.hkv + h) * p.rows * (size_t)p.words;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  for (int cb = 0; cb < rend; cb += kSpan) {
-    const int ce = cb + kSpan < rend ? cb + kSpan : rend;
+  for (int cb = 0; cb < rend; cb += S::SPAN) {
+    const int ce = cb + S::SPAN < rend ? cb + S::SPAN : rend;
     const int nw = (ce - cb + 31) / 32;
     // ---- the rows' attended-key words over the span (causal limit applied)
     for (int x = threadIdx.x; x < R * nw; x += kSaThreads) {
@@ -215,61 +233,45 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
     // ---- 32 listed keys per step, software-pipelined: while step s's
     // probabilities are formed (VALU), the MFMA unit computes step s + 1's
     // scores, so K runs one step ahead of V. LDS holds K(s + 1) and V(s)
-    // during step s, which writes K(s + 2) and V(s + 1) into the buffers read
-    // in step s - 1. Thread piece x covers key x % 32 and head_dim chunk x / 32
-    // (so a wave's V^T writes fill consecutive banks). Step indices past the
-    // end are clamped to the last step: their loads stay in bounds and their
-    // results are never used.
+    // during step s, which writes K(s + 2) and V(s + 1) (gathered into
+    // registers during step s - 1) into the buffers read in step s - 1 and
+    // gathers K(s + 3) and V(s + 2). Thread piece x covers one key and one
+    // 8-element head_dim chunk (see piece_key / piece_chunk). Step indices past
+    // the end are clamped to the last step: their loads stay in bounds and
+    // their results are never used.
     const int nsteps = padded / kStep;
-    u32x4 kr[NL], vr[NL];
-    auto gather_k = [&](int st) {
+    typedef u32x4 Pieces[NL];
+    auto gather = [&](const uint16_t* src, int st, Pieces& r) {
       st = st < nsteps ? st : nsteps - 1;
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
         const int x = (int)threadIdx.x + u * kSaThreads;
-        const int e = x % kStep, c = x / kStep;
-        kr[u] = *reinterpret_cast<const u32x4*>(
-            p.k + (((size_t)b * p.max_len + sm.pos[st * kStep + e]) * p.hkv + h) * D + 8 * c);
+        if (kPieces % kSaThreads != 0 && x >= kPieces) continue;
+        const int e = piece_key(x), c = piece_chunk(x);
+        r[u] = *reinterpret_cast<const u32x4*>(
+            src + (((size_t)b * p.max_len + sm.pos[st * kStep + e]) * p.hkv + h) * D + 8 * c);
       }
     };
-    auto gather_v = [&](int st) {
-      st = st < nsteps ? st : nsteps - 1;
+    auto stage = [&](uint16_t (&dst)[kStep][S::KS], const Pieces& r) {
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
         const int x = (int)threadIdx.x + u * kSaThreads;
-        const int e = x % kStep, c = x / kStep;
-        vr[u] = *reinterpret_cast<const u32x4*>(
-            p.v + (((size_t)b * p.max_len + sm.pos[st * kStep + e]) * p.hkv + h) * D + 8 * c);
-      }
-    };
-    auto stage_k = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const int x = (int)threadIdx.x + u * kSaThreads;
-        *reinterpret_cast<u32x4*>(&sm.k[buf][x % kStep][8 * (x / kStep)]) = kr[u];
-      }
-    };
-    auto stage_v = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const int x = (int)threadIdx.x + u * kSaThreads;
-        const int e = x % kStep, c = x / kStep;
-        const int col = vt_col(e);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) sm.vt[buf][8 * c + t][col] = (uint16_t)(vr[u][t >> 1] >> (16 * (t & 1)));
+        if (kPieces % kSaThreads != 0 && x >= kPieces) continue;
+        *reinterpret_cast<u32x4*>(&dst[piece_key(x)][8 * piece_chunk(x)]) = r[u];
       }
     };
     // S^T = K Q^T from K buffer kb: tile t2 holds keys 16 t2 .. + 15 (rows) of
-    // the block's 16 query rows (columns)
+    // the block's 16 query rows (columns); chunk-outer order keeps four
+    // independent accumulators between dependent MFMAs
     auto scores = [&](int kb, float4v (&st)[2][2]) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) st[blk][t2] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
+      for (int c = 0; c < NC; ++c) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+        for (int t2 = 0; t2 < 2; ++t2) {
           const u32x4 ka = *reinterpret_cast<const u32x4*>(&sm.k[kb][16 * t2 + (lane & 15)][32 * c + 8 * lg]);
           st[0][t2] = mfma_bf16(ka, qa[0][c], st[0][t2]);
           st[1][t2] = mfma_bf16(ka, qa[1][c], st[1][t2]);
@@ -277,20 +279,25 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
       }
     };
     float4v st[2][2];
+    Pieces ka_, va_, kb_, vb_;  // two register sets that swap roles every step
     if (nsteps > 0) {
-      gather_k(0);
-      gather_v(0);
-      stage_k(0);
-      stage_v(0);
-      gather_k(1);
-      stage_k(1);
+      gather(p.k, 0, ka_);
+      gather(p.v, 0, va_);
+      gather(p.k, 1, kb_);
+      stage(sm.k[0], ka_);
+      stage(sm.v[0], va_);
+      stage(sm.k[1], kb_);
+      gather(p.k, 2, ka_);
+      gather(p.v, 1, va_);
       __syncthreads();
       scores(0, st);
+      __syncthreads();  // step 0 overwrites K(0) with K(2)
     }
-    for (int s = 0; s < nsteps; ++s) {
+    // kst / vst hold K(s + 2) / V(s + 1); kld / vld receive K(s + 3) / V(s + 2)
+    auto step = [&](int s, const Pieces& kst, const Pieces& vst, Pieces& kld, Pieces& vld) {
       const int s0 = s * kStep;
-      gather_k(s + 2);
-      gather_v(s + 1);
+      gather(p.k, s + 3, kld);
+      gather(p.v, s + 2, vld);
       // row masks of the lane's eight keys; skipped when the wave's 32 rows attend all 32 keys
       const u32x4 wa = *reinterpret_cast<const u32x4*>(&sm.rmask[rb][s0 + 4 * lg]);
       const u32x4 wb = *reinterpret_cast<const u32x4*>(&sm.rmask[rb][s0 + 16 + 4 * lg]);
@@ -333,6 +340,7 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
       }
       // next step's scores; their MFMAs interleave with the exponentials below
       float4v sn[2][2];
+      u32x4 va[NT];
       scores((s + 1) & 1, sn);
       // P^T = exp2(alpha S^T - m): high + low bf16 parts (round to nearest even,
       // hardware conversion), already in the B operand layout of O^T = V^T P^T
@@ -356,29 +364,46 @@ __global__ __launch_bounds__(kSaThreads) void shadow_attention_kernel(ShadowPara
           pl[blk][e] = __builtin_bit_cast(uint32_t, lo);
         }
       }
-      // O^T += V^T P^T (A = V^T head_dim rows x keys, B = P^T keys x query rows), each V^T operand read once
+      // O^T += V^T P^T (A = V^T head_dim rows x keys, B = P^T keys x query rows):
+      // every V^T operand read once, high parts first so that the two MFMAs
+      // into one accumulator sit 2 * NT apart
+      {
+        const uint16_t* vb = &sm.v[s & 1][4 * lg + ((lane & 15) >> 2)][4 * (lane & 3)];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 va = *reinterpret_cast<const u32x4*>(&sm.vt[s & 1][16 * t + (lane & 15)][8 * lg]);
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          o[blk][t] = mfma_bf16(va, ph[blk], o[blk][t]);
-          o[blk][t] = mfma_bf16(va, pl[blk], o[blk][t]);
+        for (int t = 0; t < NT; ++t) {
+          const uint2 a = read_tr16(vb + 16 * t), c = read_tr16(vb + 16 * S::KS + 16 * t);
+          va[t] = u32x4{a.x, a.y, c.x, c.y};
         }
       }
-      stage_k(s & 1);
-      stage_v((s + 1) & 1);
-      // issue order: each score MFMA followed by six VALU instructions
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) o[blk][t] = mfma_bf16(va[t], ph[blk], o[blk][t]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) o[blk][t] = mfma_bf16(va[t], pl[blk], o[blk][t]);
+      stage(sm.k[s & 1], kst);
+      stage(sm.v[(s + 1) & 1], vst);
+      // issue order: the K operand reads, each score MFMA followed by four
+      // VALU instructions, the V^T operand reads, the remaining VALU work,
+      // then the products
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NC, 0);
 #pragma unroll
       for (int i = 0; i < 2 * 2 * NC; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NT, 0);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) st[blk][t2] = sn[blk][t2];
       __syncthreads();
+    };
+    for (int s = 0; s < nsteps; s += 2) {
+      step(s, ka_, va_, kb_, vb_);
+      if (s + 1 < nsteps) step(s + 1, kb_, vb_, ka_, va_);
     }
   }
 
