@@ -338,7 +338,8 @@ __global__ __launch_bounds__(kSaThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
         for (int t = 0; t < NT; ++t) o[blk][t] *= corr;
       }
-      // next step's scores; their MFMAs interleave with the exponentials below
+      // next step's scores: independent of the exponentials below, so the
+      // scheduler can overlap the two
       float4v sn[2][2];
       u32x4 va[NT];
       scores((s + 1) & 1, sn);
@@ -385,16 +386,6 @@ __global__ __launch_bounds__(kSaThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int blk = 0; blk < 2; ++blk) o[blk][t] = mfma_bf16(va[t], pl[blk], o[blk][t]);
       stage(sm.k[s & 1], kst);
       stage(sm.v[(s + 1) & 1], vst);
-      // issue order: the K operand reads, each score MFMA followed by four
-      // VALU instructions, the V^T operand reads, the remaining VALU work,
-      // then the products
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NC, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * 2 * NC; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NT, 0);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
