@@ -319,49 +319,51 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       for (int r = 0; r < 8; ++r) qraw[m][r] = qe[8 * m + perm[r]];
   }
 
-  // ---- compact the kept positions of this wave's range into an LDS list
+  // ---- compact the kept positions of this wave's range into an LDS list.
+  // Lane l owns mask word l of the range (positions w0 + 32l .. + 31, at most
+  // 64 words) and the block-table entries of its two pages; a bit-sliced
+  // ballot scan gives each lane its offset, and each lane writes its kept
+  // records in position order, so the list is in position order.
   uint32_t* list = wv.ro.rec;
   int cnt = 0;
   {
     const uint32_t* mrow = p.mask + ((size_t)b * p.hkv + kvh) * p.words;
     const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-    // one load for the range's mask words (<= 64) and two for its pages (<= 128),
-    // all kept in registers and broadcast with readlane while compacting
-    uint32_t myword = 0;
-    if (lane < q4 / 32 && w0 + 32 * lane < hi) myword = mrow[(w0 >> 5) + lane];
-    int32_t pg0 = -1, pg1 = -1;
-    if (lane < q4 / 16 && w0 + 16 * lane < hi) pg0 = bt[(w0 >> 4) + lane];
-    if (64 + lane < q4 / 16 && w0 + 16 * (64 + lane) < hi) pg1 = bt[(w0 >> 4) + 64 + lane];
-    for (int r = 0; w0 + 64 * r < hi; ++r) {
-      const uint32_t wlo = __builtin_amdgcn_readlane(myword, 2 * r);
-      const uint32_t whi = __builtin_amdgcn_readlane(myword, 2 * r + 1);
-      const uint64_t bits = (uint64_t)wlo | ((uint64_t)whi << 32);
-      const int pos = w0 + 64 * r + lane;
-      // pages 4r .. 4r+3 cover this round; lane takes page 4r + lane / 16
-      const int src = 4 * r;
-      int32_t pa, pb, pc, pd;
-      if (src < 64) {
-        pa = __builtin_amdgcn_readlane(pg0, src);
-        pb = __builtin_amdgcn_readlane(pg0, src + 1);
-        pc = __builtin_amdgcn_readlane(pg0, src + 2);
-        pd = __builtin_amdgcn_readlane(pg0, src + 3);
-      } else {
-        pa = __builtin_amdgcn_readlane(pg1, src - 64);
-        pb = __builtin_amdgcn_readlane(pg1, src - 63);
-        pc = __builtin_amdgcn_readlane(pg1, src - 62);
-        pd = __builtin_amdgcn_readlane(pg1, src - 61);
-      }
-      const int q16 = lane >> 4;
-      const int page = q16 == 0 ? pa : (q16 == 1 ? pb : (q16 == 2 ? pc : pd));
-      const bool kept = ((bits >> lane) & 1u) && pos >= lo && pos < hi && page >= 0 &&
-                        page < p.num_pages + p.host_pages;
-      const uint64_t bal = __ballot(kept);
-      if (kept) {
-        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        list[cnt + rank] = ((uint32_t)page * p.hkv + kvh) * kPage + (pos & (kPage - 1));
-      }
-      cnt += __popcll(bal);
+    const int p0 = w0 + 32 * lane;  // first position of the lane's word
+    uint32_t word = 0;
+    int32_t pga = -1, pgb = -1;
+    if (lane < q4 / 32 && p0 < hi) {
+      word = mrow[p0 >> 5];
+      pga = bt[p0 >> 4];
+      if (p0 + 16 < hi) pgb = bt[(p0 >> 4) + 1];
+    }
+    // keep positions in [lo, hi) of valid pages only
+    const int from = lo - p0, to = hi - p0;  // bit range [from, to) of the word
+    if (to <= 0 || from >= 32) word = 0;
+    else {
+      if (from > 0) word &= ~0u << from;
+      if (to < 32) word &= (1u << to) - 1u;
+    }
+    const int lim = p.num_pages + p.host_pages;
+    if (pga < 0 || pga >= lim) word &= 0xFFFF0000u;
+    if (pgb < 0 || pgb >= lim) word &= 0x0000FFFFu;
+    // exclusive prefix of the lanes' popcounts (each <= 32: six bit planes)
+    const uint32_t pc = (uint32_t)__popc(word);
+    int off = 0;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      const uint64_t plane = __ballot((pc >> bit) & 1u);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(plane >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)plane, 0));
+      off += below << bit;
+      cnt += __popcll(plane) << bit;
+    }
+    const uint32_t rec_a = ((uint32_t)pga * p.hkv + kvh) * kPage;
+    const uint32_t rec_b = ((uint32_t)pgb * p.hkv + kvh) * kPage;
+    while (word != 0) {
+      const int bit = __builtin_ctz(word);
+      word &= word - 1u;
+      list[off++] = (bit < 16 ? rec_a : rec_b) + (uint32_t)(bit & 15);
     }
   }
   cnt = __builtin_amdgcn_readfirstlane(cnt);  // wave-uniform: keeps the main loop scalar
