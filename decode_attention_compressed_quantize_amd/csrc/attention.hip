@@ -16,10 +16,10 @@
 // index order, so results do not depend on scheduling.
 //
 // INT4 chunk, per wave (a quarter of the chunk):
-//  * The kept positions (keep-mask bits) are compacted with ballot/mbcnt into
-//    an LDS list of token-record indices, so evicted tokens cost no HBM reads.
-//    The mask words and block-table entries of the wave's range are fetched
-//    with one load each.
+//  * The kept positions (keep-mask bits) are compacted into an LDS list of
+//    token-record indices, so evicted tokens cost no HBM reads: each lane
+//    loads one mask word and the block-table entries of its two pages, and a
+//    ballot scan of the lanes' popcounts gives each lane where its records go.
 //  * The list is walked in 32-token tiles, each as two steps: a K step (K
 //    codes and K meta) that writes the tile's logits to LDS, raises the
 //    running max per head and rescales the accumulators once, and a V step
@@ -210,8 +210,7 @@ struct Smem {
   struct Int8 {
     float q[G][D];
     int8_t vcode[kWaves][36][D];
-    float vscale[kWaves][36];
-    float p[kWaves][G][36];
+    float p[kWaves][36][G];
     float o[kWaves][G][D];
   };
   union {
@@ -760,6 +759,7 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = sc[0] * dot[h];
   }
+  // p of slot j for the G heads, side by side, so the P.V loop reads them at once
   float m[G], l[G], o[G][CPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -767,18 +767,25 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
     m[h] = mx;
     const float pr = valid ? __builtin_amdgcn_exp2f(s[h] - mx) : 0.0f;
     l[h] = wave_sum(pr);
-    if (lane < 36) sm.u.i8.p[wave][h][lane] = pr * sc[1];
+    if (lane < 36) sm.u.i8.p[wave][lane][h] = pr * sc[1];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  for (int j = 0; j < cntw; ++j) {
+  // P.V over all 36 slots of the wave: slots past cntw have p = 0 (their
+  // codes are whatever the buffer holds, always finite), so the loop has a
+  // fixed trip count and its LDS reads can be issued together
+#pragma unroll 12
+  for (int j = 0; j < 36; ++j) {
+    float pj[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pj[h] = sm.u.i8.p[wave][j][h];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const float v = (float)sm.u.i8.vcode[wave][j][lane * CPL + c];
 #pragma unroll
-      for (int h = 0; h < G; ++h) o[h][c] = fmaf(sm.u.i8.p[wave][h][j], v, o[h][c]);
+      for (int h = 0; h < G; ++h) o[h][c] = fmaf(pj[h], v, o[h][c]);
     }
   }
   if (lane < G) {
