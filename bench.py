@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import math
 import os
 import sys
@@ -476,15 +477,20 @@ def main():
     print("bench: attention call times (ms): " + " ".join(f"{w.name[-3:]}:{t:.4f}" for (_, _, w, _), t in
                                                      zip(attn_events, attn_ms)), file=sys.stderr, flush=True)
     attn_bytes = [algorithmic_bytes(w, L, kept_counts(w, L)) for _, _, w, L in attn_events]
-    a_ms = sum(attn_ms) / len(attn_ms)
-    a_gbs = (sum(attn_bytes) / len(attn_bytes)) / (a_ms * 1e-3) / 1e9
+    # per layer: the median call time (a rare slow call, e.g. the first timed one, does not
+    # move it) against the mean algorithmic bytes; the call figure averages the layers
     per_budget = {}
     for (e0, e1, w, L), t, bb in zip(attn_events, attn_ms, attn_bytes):
-        d = per_budget.setdefault(w.name, [0.0, 0])
-        d[0] += t
-        d[1] += bb
-    detail = {n: {"attention_ms": round(v[0] / (len(attn_ms) / len(per_budget)), 4),
-                  "attention_GBs": round(v[1] / (v[0] * 1e-3) / 1e9, 1)} for n, v in per_budget.items()}
+        d = per_budget.setdefault(w.name, ([], []))
+        d[0].append(t)
+        d[1].append(bb)
+    med = {n: statistics.median(v[0]) for n, v in per_budget.items()}
+    mean_bytes = {n: sum(v[1]) / len(v[1]) for n, v in per_budget.items()}
+    detail = {n: {"attention_ms": round(med[n], 4),
+                  "attention_GBs": round(mean_bytes[n] / (med[n] * 1e-3) / 1e9, 1)} for n in per_budget}
+    a_ms = sum(med.values()) / len(med)
+    a_bytes = sum(mean_bytes.values()) / len(mean_bytes)
+    a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
 
     line = {
         "metric": "compressed-KV decode attention: KV bytes GB/s (% HBM peak), decode steps/s",
@@ -519,7 +525,8 @@ def main():
         "decode_steps_per_s": round(1000.0 / ms, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "attention": {"ms_per_call": round(a_ms, 5), "GBs": round(a_gbs, 1), "per_layer": detail,
-                      "timed_calls": len(attn_ms), "timed_every_nth_step": TIME_EVERY},
+                      "timed_calls": len(attn_ms), "timed_every_nth_step": TIME_EVERY,
+                      "statistic": "median call time per layer, averaged over the layers"},
         "roofline": {
             "kernel": "kvc_decode_attention call: attention_kernel (INT4 chunks + INT8 region) "
                       "then merge_kernel, timed together with HIP events on the launch stream",
@@ -529,7 +536,7 @@ def main():
             "unit": "GB/s",
             "frac": round(a_gbs / (HOST_LINK_PEAK_GBS if tier == "all" else HBM_PEAK_GBS), 4),
             "traffic": measured_traffic(args.workload),
-            "algorithmic_bytes_per_call": int(sum(attn_bytes) / len(attn_bytes)),
+            "algorithmic_bytes_per_call": int(a_bytes),
         },
         "cpu_baseline": None,
     }
