@@ -436,9 +436,8 @@ def main():
             s = st["n"]
             st["n"] += 1
             st["lens"] += 1
-            kvc.kvc_quantize_append(lc.cache, st["k"][s], st["v"][s], st["one"])
             w = lc.w
-            lc.refresh(st["k"][s], st["v"][s], st["one"], ws=st["state"])
+            lc.append_refresh(st["k"][s], st["v"][s], st["one"], ws=st["state"])
             if record:
                 e0, e1 = events.pop()
                 e0.record(stream)

@@ -194,6 +194,35 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
                                    mlp != nullptr, stream));
 }
 
+KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* mlp,
+                                              const void* k_new, const void* v_new, kvc_dtype src,
+                                              int32_t n_new_max, const int32_t* n_new,
+                                              int32_t budget_permille, void* ws, size_t ws_bytes,
+                                              hipStream_t stream) {
+  kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8 | kNeedMask | kNeedScores);
+  if (st != KVC_OK) return st;
+  st = check_append(k_new, v_new, src, n_new_max, n_new);
+  if (st != KVC_OK) return st;
+  if (budget_permille < 0 || budget_permille > 1000)
+    return fail(KVC_E_SHAPE, "budget_permille must be in [0, 1000]");
+  if (ws) {
+    if (ws_bytes < (size_t)c->batch * c->num_kv_heads * sizeof(kvc::TopkState))
+      return fail(KVC_E_WORKSPACE, "top-k workspace too small");
+    if (misaligned(ws)) return fail(KVC_E_UNSUPPORTED, "ws must be 16-byte aligned");
+  }
+  // rows appended in this call sit in the protected recent window: the
+  // refresh reads neither their codes nor their scores, so all three run in
+  // one launch; otherwise the two calls run in order
+  if (mlp && n_new_max > 0 && n_new_max <= c->n_recent)
+    return launched(kvc::launch_append_score_topk(*c, mlp, k_new, v_new, src, n_new_max, n_new,
+                                                  budget_permille, static_cast<kvc::TopkState*>(ws),
+                                                  stream));
+  st = kvc_quantize_append(c, k_new, v_new, src, n_new_max, n_new, stream);
+  if (st != KVC_OK) return st;
+  return kvc_score_topk_mask(c, mlp, k_new, v_new, src, n_new_max, n_new, budget_permille, ws,
+                             ws_bytes, stream);
+}
+
 KVC_API size_t kvc_block_workspace_bytes(const kvc_cache* c, int32_t block_tokens) {
   if (check_cache(c, 0) != KVC_OK) return 0;
   if (block_tokens != 16 && block_tokens != 32 && block_tokens != 64) return 0;

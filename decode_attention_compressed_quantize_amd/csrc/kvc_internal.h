@@ -105,6 +105,10 @@ hipError_t launch_score_block(const kvc_cache& c, const float* mlp, const void* 
 hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k_new,
                              const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
                              int budget_permille, TopkState* state, hipStream_t s);
+hipError_t launch_append_score_topk(const kvc_cache& c, const float* mlp, const void* k_new,
+                                    const void* v_new, kvc_dtype src, int n_new_max,
+                                    const int32_t* n_new, int budget_permille, TopkState* state,
+                                    hipStream_t s);
 
 // Host tier: page lists and whole-page copies between the two pools.
 hipError_t launch_find_pages(const kvc_cache& c, int mode, int32_t* out, int cap, int32_t* count,

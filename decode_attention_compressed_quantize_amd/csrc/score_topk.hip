@@ -22,6 +22,7 @@
 // only when the state does not apply (first call, new budget, several new
 // positions, caller-written scores, a list run dry).
 #include "kvc_internal.h"
+#include "quant_row.h"
 
 namespace kvc {
 namespace {
@@ -1059,6 +1060,34 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(ScoreParams sp
   score_row<D, BF16>(sp, m, h, f, threadIdx.x % kScoreThreads, xs[q], wsum[q]);
 }
 
+// The same, with the encoding of the appended rows in the same launch:
+// workgroups [pairs, pairs + nq) encode kTopkThreads / 64 (sequence, appended
+// token, kv head) items each, one per wave. Nothing the encoding writes is
+// read by the refresh or the scorer.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kTopkThreads) void append_score_topk_kernel(QuantParams qp, ScoreParams sp,
+                                                                         TopkParams tp, int nq) {
+  __shared__ float xs[kTopkThreads / kScoreThreads][2 * D];
+  __shared__ float wsum[kTopkThreads / kScoreThreads][kScoreThreads / 64];
+  const int pairs = tp.hkv * sp.batch;
+  if ((int)blockIdx.x < pairs) {
+    topk_pair(tp, blockIdx.x % tp.hkv, blockIdx.x / tp.hkv);
+    return;
+  }
+  if ((int)blockIdx.x < pairs + nq) {
+    const long long item = (long long)(blockIdx.x - pairs) * (kTopkThreads / 64) + (threadIdx.x >> 6);
+    quantize_item<D, BF16>(qp, item, threadIdx.x & 63);
+    return;
+  }
+  const int g = blockIdx.x - pairs - nq;
+  const int h = g % sp.hkv;
+  const int q = threadIdx.x / kScoreThreads;
+  const long long f = (long long)(g / sp.hkv) * (kTopkThreads / kScoreThreads) + q;
+  ScorerSlice<D> m;
+  m.load(sp, h, threadIdx.x % kScoreThreads);
+  score_row<D, BF16>(sp, m, h, f, threadIdx.x % kScoreThreads, xs[q], wsum[q]);
+}
+
 }  // namespace
 
 namespace {
@@ -1220,6 +1249,28 @@ hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k
   } else {
     if (bf) hipLaunchKernelGGL((score_topk_kernel<64, true>), grid, dim3(kTopkThreads), 0, s, sp, tp);
     else hipLaunchKernelGGL((score_topk_kernel<64, false>), grid, dim3(kTopkThreads), 0, s, sp, tp);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_score_topk(const kvc_cache& c, const float* mlp, const void* k_new,
+                                    const void* v_new, kvc_dtype src, int n_new_max,
+                                    const int32_t* n_new, int budget_permille, TopkState* state,
+                                    hipStream_t s) {
+  const QuantParams qp = quant_params(c, k_new, v_new, n_new_max, n_new);
+  const ScoreParams sp = score_params(c, mlp, k_new, v_new, n_new_max, n_new);
+  const TopkParams tp = topk_params(c, budget_permille, state, true);
+  const long long rows = (long long)c.batch * n_new_max;
+  const long long quads = (rows + 3) / 4;
+  const int nq = (int)((qp.items + kTopkThreads / 64 - 1) / (kTopkThreads / 64));
+  const dim3 grid((unsigned)((long long)c.batch * c.num_kv_heads + nq + quads * c.num_kv_heads));
+  const bool bf = src == KVC_BF16;
+  if (c.head_dim == 128) {
+    if (bf) hipLaunchKernelGGL((append_score_topk_kernel<128, true>), grid, dim3(kTopkThreads), 0, s, qp, sp, tp, nq);
+    else hipLaunchKernelGGL((append_score_topk_kernel<128, false>), grid, dim3(kTopkThreads), 0, s, qp, sp, tp, nq);
+  } else {
+    if (bf) hipLaunchKernelGGL((append_score_topk_kernel<64, true>), grid, dim3(kTopkThreads), 0, s, qp, sp, tp, nq);
+    else hipLaunchKernelGGL((append_score_topk_kernel<64, false>), grid, dim3(kTopkThreads), 0, s, qp, sp, tp, nq);
   }
   return hipGetLastError();
 }

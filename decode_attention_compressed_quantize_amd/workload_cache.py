@@ -14,7 +14,8 @@ import numpy as np
 import workloads as W
 
 from . import (Cache, attention_workspace, block_workspace, kvc_copy_pages, kvc_find_pages,
-               kvc_quantize_append, kvc_score_block_mask, kvc_score_topk_mask, topk_workspace)
+               kvc_append_score_topk_mask, kvc_quantize_append, kvc_score_block_mask,
+               kvc_score_topk_mask, topk_workspace)
 
 
 def pack_bits(flags: np.ndarray, words: int) -> np.ndarray:
@@ -153,6 +154,18 @@ class LayerCache:
         else:
             kvc_score_topk_mask(self.cache, mlp, k_new, v_new, n_new, budget, ws=ws, stream=stream)
 
+    def append_refresh(self, k_new, v_new, n_new, ws=None, stream=None):
+        """One decode-step update: append the rows, score them and refresh the
+        keep mask (one launch for the token policy with MLP scores)."""
+        w = self.w
+        if not self.block_policy and w.mask == "mlp" and getattr(self, "mlp", None) is not None:
+            budget = w.budget_permille
+            kvc_append_score_topk_mask(self.cache, self.mlp, k_new, v_new, n_new, budget, ws=ws,
+                                       stream=stream)
+            return
+        kvc_quantize_append(self.cache, k_new, v_new, n_new, stream=stream)
+        self.refresh(k_new, v_new, n_new, ws=ws, stream=stream)
+
     @property
     def block_policy(self) -> bool:
         return self.w.policy == "block" and self.w.mask in ("scores", "mlp")
@@ -265,8 +278,7 @@ class LayerCache:
             v_new = W.kv_rows_torch(w, self.layer, "V", lens, self.device)[:, None]
             lens += 1
             self.seq_lens.add_(1)
-            kvc_quantize_append(c, k_new, v_new, one)
-            self.refresh(k_new, v_new, one, ws=ws)
+            self.append_refresh(k_new, v_new, one, ws=ws)
             rec[:, :, s] = c.keep_mask
         self.lengths = lens
         return rec, lens

@@ -171,6 +171,25 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
                                        size_t ws_bytes, hipStream_t stream);
 
 /*
+ * kvc_append_score_topk_mask - one decode-step update of a layer's cache:
+ * kvc_quantize_append followed by kvc_score_topk_mask with the same arguments,
+ * with the same results, in a single launch when that is possible.
+ * Source: KV4-RL review, section 3 (quantize-on-append into the INT4 store and
+ * the INT8 side cache) and KVP promo page, section "Core mechanism" (score the
+ * new tokens, rank, truncate), steps that one decode step performs in order.
+ *   Arguments, ownership and errors as for the two calls. When mlp != NULL and
+ *   1 <= n_new_max <= n_recent, every appended position lies in the protected
+ *   recent window, whose codes and scores the refresh does not read, so the
+ *   encoding, the scoring and the refresh run as one launch; otherwise the two
+ *   calls run in order on the stream.
+ */
+KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* mlp,
+                                              const void* k_new, const void* v_new, kvc_dtype src,
+                                              int32_t n_new_max, const int32_t* n_new,
+                                              int32_t budget_permille, void* ws, size_t ws_bytes,
+                                              hipStream_t stream);
+
+/*
  * kvc_score_block_mask - score appended tokens and refresh the keep mask at
  * block granularity, after an optional recency cut.
  * Source: KVP promo page (arXiv 2602.10238), section "Engineering limits": a

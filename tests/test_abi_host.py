@@ -119,6 +119,18 @@ def test_append_and_topk_argument_errors(lib):
     assert r == -1
     r = lib.kvc_score_topk_mask(ctypes.byref(c), None, None, None, 0, 0, None, 500, FAKE, 1024, None)
     assert r == -4  # state smaller than kvc_topk_workspace_bytes
+    # the fused update checks what both calls check, before any work
+    fused = lib.kvc_append_score_topk_mask
+    assert fused(None, FAKE, FAKE, FAKE, 0, 1, FAKE, 500, None, 0, None) == -1
+    assert fused(ctypes.byref(c), FAKE, FAKE, FAKE, 0, 1, FAKE, 1001, None, 0, None) == -2
+    assert fused(ctypes.byref(c), FAKE, FAKE, FAKE, 0, -1, FAKE, 500, None, 0, None) == -2
+    assert fused(ctypes.byref(c), FAKE, None, FAKE, 0, 1, FAKE, 500, None, 0, None) == -1
+    assert fused(ctypes.byref(c), FAKE, FAKE, FAKE, 7, 1, FAKE, 500, None, 0, None) == -3
+    assert fused(ctypes.byref(c), FAKE, FAKE, FAKE, 0, 1, FAKE, 500, FAKE, 1024, None) == -4
+    assert fused(ctypes.byref(desc(scores=None)), FAKE, FAKE, FAKE, 0, 1, FAKE, 500, None, 0,
+                 None) == -1
+    assert fused(ctypes.byref(desc(int8_codes=None)), FAKE, FAKE, FAKE, 0, 1, FAKE, 500, None, 0,
+                 None) == -1
 
 
 def test_workspace_size_covers_every_split(lib):

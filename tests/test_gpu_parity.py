@@ -182,9 +182,11 @@ def test_identity_vs_shuffled_pages_and_rerun_are_bit_identical():
 
 
 # ---------------------------------------------------------------- decode steps
-def test_decode_steps_cross_window_and_budget():
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_steps_cross_window_and_budget(fused):
     """Append one token per step (ring overwrite, INT4 region growth, score,
-    top-k refresh) and check every step against the oracle at the new length."""
+    top-k refresh) and check every step against the oracle at the new length;
+    fused: the three through kvc_append_score_topk_mask."""
     m = kvc()
     w = W.WORKLOADS["fullstep"].replace(name="steps", batch=3, layers=1, ctx=130,
                                         decode_steps=40, ctx_list=(130, 150, 300))
@@ -197,14 +199,53 @@ def test_decode_steps_cross_window_and_budget():
         lens += 1
         lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
         lc.lengths = lens.copy()
-        m.kvc_quantize_append(lc.cache, k_new, v_new, one)
-        m.kvc_score_topk_mask(lc.cache, lc.mlp, k_new, v_new, one, w.budget_permille)
+        if fused:
+            m.kvc_append_score_topk_mask(lc.cache, lc.mlp, k_new, v_new, one, w.budget_permille)
+        else:
+            m.kvc_quantize_append(lc.cache, k_new, v_new, one)
+            m.kvc_score_topk_mask(lc.cache, lc.mlp, k_new, v_new, one, w.budget_permille)
         if step % 5 == 0 or step in (14, 15, 16):
             cpu = cpu_buffers(lc)
             qn, out, lse = run_attention(lc, step=step)
             for b in range(w.batch):
                 for h in (0, w.kv_heads - 1):
                     check_pair(w, lc, cpu, qn, out, lse, b, h)
+
+
+@pytest.mark.parametrize("protect", [True, False])
+def test_fused_append_refresh_matches_separate_calls(protect):
+    """kvc_append_score_topk_mask leaves codes, meta, the INT8 side cache,
+    scores, keep mask and refresh state bit-identical to kvc_quantize_append
+    followed by kvc_score_topk_mask (one launch with INT8 protection, the two
+    calls in order without); a sequence that appends nothing at one step
+    forces a full refresh there."""
+    m = kvc()
+    w = W.WORKLOADS["fullstep"].replace(name=f"fused_{int(protect)}", batch=3, layers=1, ctx=300,
+                                        decode_steps=30, ctx_list=(150, 300, 520), protect=protect)
+    a, b = LayerCache(w), LayerCache(w)
+    sa, sb = a.refresh_state(), b.refresh_state()
+    lens = a.lengths.copy()
+    for step in range(30):
+        n_new = np.ones(w.batch, np.int32)
+        if step == 7:
+            n_new[1] = 0
+        k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+        v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+        lens += n_new
+        nn = torch.from_numpy(n_new).cuda()
+        for lc in (a, b):
+            lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        m.kvc_quantize_append(a.cache, k_new, v_new, nn)
+        m.kvc_score_topk_mask(a.cache, a.mlp, k_new, v_new, nn, w.budget_permille, ws=sa)
+        m.kvc_append_score_topk_mask(b.cache, b.mlp, k_new, v_new, nn, w.budget_permille, ws=sb)
+        torch.cuda.synchronize()
+        for name in ("int4_codes", "int4_meta", "int8_codes", "int8_scales", "scores", "keep_mask"):
+            x, y = getattr(a.cache, name), getattr(b.cache, name)
+            if x is None:
+                assert y is None and not protect
+                continue
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"step {step}: {name} differs"
+        assert torch.equal(sa, sb), f"step {step}: refresh state differs"
 
 
 def _decode_topk_run(w, steps, budgets, stall=None, mlp=None):
