@@ -60,6 +60,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRing = 4;  // INT4 steps in flight per wave (the one in use plus three prefetched)
 static_assert(kRing % 2 == 0, "ring slots alternate between K and V steps");
+static_assert(kMaxChunk / kWaves <= 64 * 32, "the compaction gives each lane one mask word of a wave's range");
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
