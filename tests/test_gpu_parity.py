@@ -181,6 +181,39 @@ def test_identity_vs_shuffled_pages_and_rerun_are_bit_identical():
     assert np.array_equal(oa, ob) and np.array_equal(la, lb)
 
 
+@pytest.mark.parametrize("window", [0, 1000])
+def test_out_of_range_pages_are_skipped_like_evicted_positions(window):
+    """Block-table entries that are negative or past the page pool are skipped
+    by the attention: the call is bit-identical to one over the correct table
+    with those pages' keep bits cleared (whole region and a window)."""
+    w = W.Workload("badpages", 3, 32, 8, 128, ctx_list=(3000, 5200, 700), mask="mlp",
+                   budget_permille=400)
+    lc = LayerCache(w)
+    ntab = lc.table.shape[1]
+    bad = {0: [3, 20, 40], 1: [10, 100, 250, 300], 2: [12]}  # logical pages in the INT4 region
+    m = lc.cache.keep_mask.cpu().numpy().view(np.uint32).copy()
+    for b, pages in bad.items():
+        for lp in pages:
+            assert 16 * lp >= 16 and 16 * lp + 16 <= int(lc.lengths[b]) - 128 and lp < ntab
+            for t in range(16 * lp, 16 * lp + 16):
+                m[b, :, t // 32] &= np.uint32(0xFFFFFFFF ^ (1 << (t % 32)))
+    want_mask = torch.from_numpy(m.view(np.int32)).cuda()
+    q = lc.queries(0)
+    good_table = lc.table.clone()
+    good_mask = lc.cache.keep_mask.clone()
+    # reference: correct table, mask bits of the bad pages cleared
+    lc.cache.keep_mask.copy_(want_mask)
+    ref_out, ref_lse = run_attention(lc, q=q, window=window)[1:]
+    # bad table entries, original mask
+    lc.cache.keep_mask.copy_(good_mask)
+    for i, (b, pages) in enumerate(bad.items()):
+        for j, lp in enumerate(pages):
+            lc.table[b, lp] = -1 if (i + j) % 2 == 0 else lc.num_pages + 7 + j
+    got_out, got_lse = run_attention(lc, q=q, window=window)[1:]
+    lc.table.copy_(good_table)
+    assert np.array_equal(got_out, ref_out) and np.array_equal(got_lse, ref_lse)
+
+
 # ---------------------------------------------------------------- decode steps
 @pytest.mark.parametrize("fused", [False, True])
 def test_decode_steps_cross_window_and_budget(fused):
