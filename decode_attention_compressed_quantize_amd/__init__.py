@@ -7,7 +7,7 @@ library has not been built.
 
 The functions mirror the C ABI in ``include/kvc.h``:
 ``kvc_quantize_append``, ``kvc_score_topk_mask``, ``kvc_append_score_topk_mask``,
-``kvc_score_block_mask``, ``kvc_decode_attention``,
+``kvc_score_block_mask``, ``kvc_append_score_block_mask``, ``kvc_decode_attention``,
 ``kvc_attention_workspace_bytes``, ``kvc_topk_workspace_bytes``,
 ``kvc_status_string``, ``kvc_last_error``, ``kvc_abi_version``.
 :class:`Cache` owns the torch tensors of one layer's compressed cache and the
@@ -80,6 +80,11 @@ _SIGNATURES = {
                                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                                   ctypes.c_size_t, ctypes.c_void_p]),
     "kvc_score_block_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]),
+    "kvc_append_score_block_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_int, ctypes.c_int32,
                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
@@ -267,6 +272,20 @@ def kvc_append_score_topk_mask(cache: Cache, mlp, k_new, v_new, n_new, budget_pe
                                             _dtype_code(k_new), n_max, _ptr(n_new),
                                             int(budget_permille), _ptr(ws), nbytes, _stream(stream)),
            "kvc_append_score_topk_mask")
+
+
+def kvc_append_score_block_mask(cache: Cache, mlp, k_new, v_new, n_new, budget_permille: int,
+                                recency_window: int = 0, block_tokens: int = PAGE, ws=None,
+                                stream=None):
+    """kvc_quantize_append then kvc_score_block_mask with the same arguments, in one
+    launch when every appended row lands in the protected recent window."""
+    n_max = k_new.shape[1]
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().kvc_append_score_block_mask(cache.ref(), _ptr(mlp), _ptr(k_new), _ptr(v_new),
+                                             _dtype_code(k_new), n_max, _ptr(n_new),
+                                             int(budget_permille), int(block_tokens),
+                                             int(recency_window), _ptr(ws), nbytes, _stream(stream)),
+           "kvc_append_score_block_mask")
 
 
 def kvc_score_block_mask(cache: Cache, mlp, k_new, v_new, n_new, budget_permille: int,

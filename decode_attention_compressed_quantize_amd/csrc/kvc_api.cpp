@@ -256,7 +256,7 @@ KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, co
     if (n_new_max > 0 && n_new_max <= c->n_recent)
       return launched(kvc::launch_score_block(*c, mlp, k_new, v_new, src, n_new_max, n_new,
                                               budget_permille, block_tokens, recency_window, ws,
-                                              stream));
+                                              false, stream));
     if (n_new_max > 0) {
       st = launched(kvc::launch_score(*c, mlp, k_new, v_new, src, n_new_max, n_new, stream));
       if (st != KVC_OK) return st;
@@ -264,6 +264,39 @@ KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, co
   }
   return launched(
       kvc::launch_block_topk(*c, budget_permille, block_tokens, recency_window, ws, stream));
+}
+
+KVC_API kvc_status kvc_append_score_block_mask(const kvc_cache* c, const float* mlp,
+                                               const void* k_new, const void* v_new, kvc_dtype src,
+                                               int32_t n_new_max, const int32_t* n_new,
+                                               int32_t budget_permille, int32_t block_tokens,
+                                               int32_t recency_window, void* ws, size_t ws_bytes,
+                                               hipStream_t stream) {
+  kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8 | kNeedMask | kNeedScores);
+  if (st != KVC_OK) return st;
+  st = check_append(k_new, v_new, src, n_new_max, n_new);
+  if (st != KVC_OK) return st;
+  if (budget_permille < 0 || budget_permille > 1000)
+    return fail(KVC_E_SHAPE, "budget_permille must be in [0, 1000]");
+  if (block_tokens != 16 && block_tokens != 32 && block_tokens != 64)
+    return fail(KVC_E_UNSUPPORTED, "block_tokens must be 16, 32 or 64");
+  if ((long long)c->max_ctx > (long long)kvc::kMaxBlocks * block_tokens)
+    return fail(KVC_E_UNSUPPORTED, "too many blocks per sequence");
+  if (recency_window < 0) return fail(KVC_E_SHAPE, "recency_window must be >= 0");
+  if (ws) {
+    if (ws_bytes < kvc_block_workspace_bytes(c, block_tokens))
+      return fail(KVC_E_WORKSPACE, "block refresh state smaller than kvc_block_workspace_bytes");
+    if (misaligned(ws)) return fail(KVC_E_UNSUPPORTED, "block refresh state must be 16-byte aligned");
+  }
+  // as kvc_append_score_topk_mask: one launch when the rows land in the protected window
+  if (mlp && n_new_max > 0 && n_new_max <= c->n_recent)
+    return launched(kvc::launch_score_block(*c, mlp, k_new, v_new, src, n_new_max, n_new,
+                                            budget_permille, block_tokens, recency_window, ws,
+                                            true, stream));
+  st = kvc_quantize_append(c, k_new, v_new, src, n_new_max, n_new, stream);
+  if (st != KVC_OK) return st;
+  return kvc_score_block_mask(c, mlp, k_new, v_new, src, n_new_max, n_new, budget_permille,
+                              block_tokens, recency_window, ws, ws_bytes, stream);
 }
 
 static kvc_status decode_attention(const kvc_cache* c, int32_t window, const void* q,

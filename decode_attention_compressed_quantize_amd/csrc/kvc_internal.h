@@ -96,10 +96,11 @@ inline size_t block_state_stride(const kvc_cache& c) {
 hipError_t launch_block_topk(const kvc_cache& c, int budget_permille, int block_tokens, int window,
                              void* state, hipStream_t s);
 // Scoring and block refresh in one launch; only for n_new_max <= n_recent.
+// encode: also the quantize-on-append of the same rows (as launch_quantize_append)
 hipError_t launch_score_block(const kvc_cache& c, const float* mlp, const void* k_new,
                               const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
                               int budget_permille, int block_tokens, int window, void* state,
-                              hipStream_t s);
+                              bool encode, hipStream_t s);
 
 // Scoring and refresh in one launch; only for n_new_max <= n_recent.
 hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k_new,

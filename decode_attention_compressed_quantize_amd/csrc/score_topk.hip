@@ -1155,7 +1155,8 @@ hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state
 }
 
 template <int D, bool BF16, int B>
-__global__ __launch_bounds__(kTopkThreads) void score_block_kernel(ScoreParams sp, BlockTopkParams bp) {
+__global__ __launch_bounds__(kTopkThreads) void score_block_kernel(ScoreParams sp, BlockTopkParams bp,
+                                                                  QuantParams qp, int nq) {
   __shared__ BlockLds sm;
   __shared__ float xs[kTopkThreads / kScoreThreads][2 * D];
   __shared__ float wsum[kTopkThreads / kScoreThreads][kScoreThreads / 64];
@@ -1164,7 +1165,14 @@ __global__ __launch_bounds__(kTopkThreads) void score_block_kernel(ScoreParams s
     block_topk_pair<B>(bp, sm, blockIdx.x % bp.hkv, blockIdx.x / bp.hkv);
     return;
   }
-  const int g = blockIdx.x - pairs;
+  // workgroups [pairs, pairs + nq) encode the appended rows (nq = 0: the
+  // caller appended them already), one item per wave
+  if ((int)blockIdx.x < pairs + nq) {
+    const long long item = (long long)(blockIdx.x - pairs) * (kTopkThreads / 64) + (threadIdx.x >> 6);
+    quantize_item<D, BF16>(qp, item, threadIdx.x & 63);
+    return;
+  }
+  const int g = blockIdx.x - pairs - nq;
   const int h = g % sp.hkv;
   const int q = threadIdx.x / kScoreThreads;
   const long long f = (long long)(g / sp.hkv) * (kTopkThreads / kScoreThreads) + q;
@@ -1206,30 +1214,33 @@ hipError_t launch_block_topk(const kvc_cache& c, int budget_permille, int block_
 
 template <int D, bool BF16>
 static void launch_score_block_d(const dim3& grid, int block_tokens, const ScoreParams& sp,
-                                 const BlockTopkParams& bp, hipStream_t s) {
+                                 const BlockTopkParams& bp, const QuantParams& qp, int nq,
+                                 hipStream_t s) {
   const dim3 block(kTopkThreads);
-  if (block_tokens == 16) hipLaunchKernelGGL((score_block_kernel<D, BF16, 16>), grid, block, 0, s, sp, bp);
-  else if (block_tokens == 32) hipLaunchKernelGGL((score_block_kernel<D, BF16, 32>), grid, block, 0, s, sp, bp);
-  else hipLaunchKernelGGL((score_block_kernel<D, BF16, 64>), grid, block, 0, s, sp, bp);
+  if (block_tokens == 16) hipLaunchKernelGGL((score_block_kernel<D, BF16, 16>), grid, block, 0, s, sp, bp, qp, nq);
+  else if (block_tokens == 32) hipLaunchKernelGGL((score_block_kernel<D, BF16, 32>), grid, block, 0, s, sp, bp, qp, nq);
+  else hipLaunchKernelGGL((score_block_kernel<D, BF16, 64>), grid, block, 0, s, sp, bp, qp, nq);
 }
 
 hipError_t launch_score_block(const kvc_cache& c, const float* mlp, const void* k_new,
                               const void* v_new, kvc_dtype src, int n_new_max, const int32_t* n_new,
                               int budget_permille, int block_tokens, int window, void* state,
-                              hipStream_t s) {
+                              bool encode, hipStream_t s) {
   if (block_tokens != 16 && block_tokens != 32 && block_tokens != 64) return hipErrorInvalidValue;
   const ScoreParams sp = score_params(c, mlp, k_new, v_new, n_new_max, n_new);
   const BlockTopkParams bp = block_params(c, budget_permille, block_tokens, window, state);
+  const QuantParams qp = quant_params(c, k_new, v_new, n_new_max, n_new);
+  const int nq = encode ? (int)((qp.items + kTopkThreads / 64 - 1) / (kTopkThreads / 64)) : 0;
   const long long rows = (long long)c.batch * n_new_max;
   const long long quads = (rows + 3) / 4;
-  const dim3 grid((unsigned)((long long)c.batch * c.num_kv_heads + quads * c.num_kv_heads));
+  const dim3 grid((unsigned)((long long)c.batch * c.num_kv_heads + nq + quads * c.num_kv_heads));
   const bool bf = src == KVC_BF16;
   if (c.head_dim == 128) {
-    if (bf) launch_score_block_d<128, true>(grid, block_tokens, sp, bp, s);
-    else launch_score_block_d<128, false>(grid, block_tokens, sp, bp, s);
+    if (bf) launch_score_block_d<128, true>(grid, block_tokens, sp, bp, qp, nq, s);
+    else launch_score_block_d<128, false>(grid, block_tokens, sp, bp, qp, nq, s);
   } else {
-    if (bf) launch_score_block_d<64, true>(grid, block_tokens, sp, bp, s);
-    else launch_score_block_d<64, false>(grid, block_tokens, sp, bp, s);
+    if (bf) launch_score_block_d<64, true>(grid, block_tokens, sp, bp, qp, nq, s);
+    else launch_score_block_d<64, false>(grid, block_tokens, sp, bp, qp, nq, s);
   }
   return hipGetLastError();
 }

@@ -14,8 +14,8 @@ import numpy as np
 import workloads as W
 
 from . import (Cache, attention_workspace, block_workspace, kvc_copy_pages, kvc_find_pages,
-               kvc_append_score_topk_mask, kvc_quantize_append, kvc_score_block_mask,
-               kvc_score_topk_mask, topk_workspace)
+               kvc_append_score_block_mask, kvc_append_score_topk_mask, kvc_quantize_append,
+               kvc_score_block_mask, kvc_score_topk_mask, topk_workspace)
 
 
 def pack_bits(flags: np.ndarray, words: int) -> np.ndarray:
@@ -158,10 +158,14 @@ class LayerCache:
         """One decode-step update: append the rows, score them and refresh the
         keep mask (one launch for the token policy with MLP scores)."""
         w = self.w
-        if not self.block_policy and w.mask == "mlp" and getattr(self, "mlp", None) is not None:
-            budget = w.budget_permille
-            kvc_append_score_topk_mask(self.cache, self.mlp, k_new, v_new, n_new, budget, ws=ws,
-                                       stream=stream)
+        if w.mask == "mlp" and getattr(self, "mlp", None) is not None:
+            if self.block_policy:
+                kvc_append_score_block_mask(self.cache, self.mlp, k_new, v_new, n_new,
+                                            w.budget_permille, w.recency_window, w.block_tokens,
+                                            ws=ws, stream=stream)
+            else:
+                kvc_append_score_topk_mask(self.cache, self.mlp, k_new, v_new, n_new,
+                                           w.budget_permille, ws=ws, stream=stream)
             return
         kvc_quantize_append(self.cache, k_new, v_new, n_new, stream=stream)
         self.refresh(k_new, v_new, n_new, ws=ws, stream=stream)

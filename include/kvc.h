@@ -231,6 +231,21 @@ KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, co
                                         size_t ws_bytes, hipStream_t stream);
 
 /*
+ * kvc_append_score_block_mask - kvc_quantize_append followed by
+ * kvc_score_block_mask with the same arguments, with the same results, in a
+ * single launch when that is possible (the block-policy counterpart of
+ * kvc_append_score_topk_mask, under the same condition: mlp != NULL and
+ * 1 <= n_new_max <= n_recent). Arguments, ownership and errors as for the two
+ * calls. Sources as for those two calls.
+ */
+KVC_API kvc_status kvc_append_score_block_mask(const kvc_cache* c, const float* mlp,
+                                               const void* k_new, const void* v_new, kvc_dtype src,
+                                               int32_t n_new_max, const int32_t* n_new,
+                                               int32_t budget_permille, int32_t block_tokens,
+                                               int32_t recency_window, void* ws, size_t ws_bytes,
+                                               hipStream_t stream);
+
+/*
  * kvc_decode_attention - one decode query per sequence over the compressed cache.
  * Source: KV4-RL review, section 3 (INT4 and INT8 regions processed
  * independently, outputs combined by an exact softmax merge).

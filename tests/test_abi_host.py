@@ -131,6 +131,12 @@ def test_append_and_topk_argument_errors(lib):
                  None) == -1
     assert fused(ctypes.byref(desc(int8_codes=None)), FAKE, FAKE, FAKE, 0, 1, FAKE, 500, None, 0,
                  None) == -1
+    fb = lib.kvc_append_score_block_mask
+    assert fb(None, FAKE, FAKE, FAKE, 0, 1, FAKE, 500, 16, 0, None, 0, None) == -1
+    assert fb(ctypes.byref(c), FAKE, FAKE, FAKE, 0, 1, FAKE, 500, 24, 0, None, 0, None) == -3
+    assert fb(ctypes.byref(c), FAKE, FAKE, FAKE, 0, 1, FAKE, 500, 16, -1, None, 0, None) == -2
+    assert fb(ctypes.byref(c), FAKE, FAKE, FAKE, 0, 1, FAKE, -1, 16, 0, None, 0, None) == -2
+    assert fb(ctypes.byref(c), FAKE, FAKE, FAKE, 0, 1, FAKE, 500, 16, 0, FAKE, 64, None) == -4
 
 
 def test_workspace_size_covers_every_split(lib):

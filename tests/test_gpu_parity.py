@@ -245,16 +245,21 @@ def test_decode_steps_cross_window_and_budget(fused):
                     check_pair(w, lc, cpu, qn, out, lse, b, h)
 
 
-@pytest.mark.parametrize("protect", [True, False])
-def test_fused_append_refresh_matches_separate_calls(protect):
-    """kvc_append_score_topk_mask leaves codes, meta, the INT8 side cache,
-    scores, keep mask and refresh state bit-identical to kvc_quantize_append
-    followed by kvc_score_topk_mask (one launch with INT8 protection, the two
-    calls in order without); a sequence that appends nothing at one step
-    forces a full refresh there."""
+@pytest.mark.parametrize("policy,protect", [("token", True), ("token", False), ("block", True),
+                                            ("block", False)])
+def test_fused_append_refresh_matches_separate_calls(policy, protect):
+    """kvc_append_score_topk_mask / kvc_append_score_block_mask leave codes,
+    meta, the INT8 side cache, scores, keep mask and refresh state
+    bit-identical to kvc_quantize_append followed by kvc_score_topk_mask /
+    kvc_score_block_mask (one launch with INT8 protection, the calls in order
+    without); a sequence that appends nothing at one step forces a full
+    refresh there. The block case uses 32-token blocks and a 200-position
+    recency window."""
     m = kvc()
-    w = W.WORKLOADS["fullstep"].replace(name=f"fused_{int(protect)}", batch=3, layers=1, ctx=300,
-                                        decode_steps=30, ctx_list=(150, 300, 520), protect=protect)
+    w = W.WORKLOADS["fullstep"].replace(name=f"fused_{policy}_{int(protect)}", batch=3, layers=1,
+                                        ctx=300, decode_steps=30, ctx_list=(150, 300, 520),
+                                        protect=protect, policy=policy, block_tokens=32,
+                                        recency_window=200 if policy == "block" else 0)
     a, b = LayerCache(w), LayerCache(w)
     sa, sb = a.refresh_state(), b.refresh_state()
     lens = a.lengths.copy()
@@ -269,8 +274,13 @@ def test_fused_append_refresh_matches_separate_calls(protect):
         for lc in (a, b):
             lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
         m.kvc_quantize_append(a.cache, k_new, v_new, nn)
-        m.kvc_score_topk_mask(a.cache, a.mlp, k_new, v_new, nn, w.budget_permille, ws=sa)
-        m.kvc_append_score_topk_mask(b.cache, b.mlp, k_new, v_new, nn, w.budget_permille, ws=sb)
+        if policy == "block":
+            m.kvc_score_block_mask(a.cache, a.mlp, k_new, v_new, nn, w.budget_permille, 200, 32, ws=sa)
+            m.kvc_append_score_block_mask(b.cache, b.mlp, k_new, v_new, nn, w.budget_permille, 200, 32,
+                                          ws=sb)
+        else:
+            m.kvc_score_topk_mask(a.cache, a.mlp, k_new, v_new, nn, w.budget_permille, ws=sa)
+            m.kvc_append_score_topk_mask(b.cache, b.mlp, k_new, v_new, nn, w.budget_permille, ws=sb)
         torch.cuda.synchronize()
         for name in ("int4_codes", "int4_meta", "int8_codes", "int8_scales", "scores", "keep_mask"):
             x, y = getattr(a.cache, name), getattr(b.cache, name)
