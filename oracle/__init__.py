@@ -19,6 +19,8 @@ arithmetic, float64 for attention):
                   positions (the plain definition), split partials and the
                   exact log-sum-exp merge (used only by invariant tests).
 * ``reference`` - the composition for one (sequence, kv head).
+* ``dense``     - the uncompressed baseline: bfloat16 rows, every position
+                  attended (what the INT4 cache is measured against).
 
 Sources: the KV4-RL review page ("KV4-RL: Unlocking Faster Asynchronous
 Rollouts for RLVR with INT4 KV Cache Quantization"), section 3 "Method & Key
@@ -28,4 +30,4 @@ page (arXiv 2605.06850), Figure 1 caption. The numeric rules the pages leave
 open (group size, scale format, rounding, tie-breaking) follow the readings
 listed in each function's docstring.
 """
-from . import quant, regions, policy, attention, reference  # noqa: F401
+from . import quant, regions, policy, attention, reference, dense  # noqa: F401
