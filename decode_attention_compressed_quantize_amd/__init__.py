@@ -9,9 +9,12 @@ The functions mirror the C ABI in ``include/kvc.h``:
 ``kvc_quantize_append``, ``kvc_score_topk_mask``, ``kvc_append_score_topk_mask``,
 ``kvc_score_block_mask``, ``kvc_append_score_block_mask``, ``kvc_decode_attention``,
 ``kvc_attention_workspace_bytes``, ``kvc_topk_workspace_bytes``,
-``kvc_status_string``, ``kvc_last_error``, ``kvc_abi_version``.
+``kvc_status_string``, ``kvc_last_error``, ``kvc_abi_version``, and for the dense
+bfloat16 baseline ``kvc_dense_append``, ``kvc_dense_decode_attention``,
+``kvc_dense_attention_workspace_bytes``.
 :class:`Cache` owns the torch tensors of one layer's compressed cache and the
-``kvc_cache`` descriptor that points at them.
+``kvc_cache`` descriptor that points at them; :class:`DenseCache` does the same
+for a dense bfloat16 cache (``kvc_dense_cache``).
 """
 from __future__ import annotations
 
@@ -64,6 +67,22 @@ class KvcCacheStruct(ctypes.Structure):
     ]
 
 
+class KvcDenseCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_phys_pages", ctypes.c_int32),
+        ("max_ctx", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("kv", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 # exported name -> (restype, argtypes)
@@ -108,6 +127,14 @@ _SIGNATURES = {
                                                      ctypes.c_int, ctypes.c_int32, ctypes.c_float,
                                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                      ctypes.c_size_t, ctypes.c_void_p]),
+    "kvc_dense_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
+    "kvc_dense_decode_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                                  ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                                  ctypes.c_void_p]),
+    "kvc_dense_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
     "kvc_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
     "kvc_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "kvc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -379,4 +406,62 @@ def attention_workspace(cache: Cache, num_q_heads: int, device="cuda"):
     import torch
 
     n = kvc_attention_workspace_bytes(cache, num_q_heads)
+    return torch.zeros(max(n // 4, 1), dtype=torch.float32, device=device)
+
+
+# ---------------------------------------------------------------- dense baseline
+class DenseCache:
+    """Device tensors of one layer's dense bfloat16 paged cache plus its descriptor.
+
+    ``kv`` is int16 [P][Hkv][16][2][D] holding bfloat16 bits (per token the K
+    row then the V row); ``block_table`` and ``seq_lens`` as for :class:`Cache`.
+    """
+
+    def __init__(self, batch: int, kv_heads: int, head_dim: int, max_ctx: int,
+                 num_phys_pages: int, block_table, seq_lens, device="cuda"):
+        import torch
+
+        self.batch, self.kv_heads, self.head_dim, self.max_ctx = batch, kv_heads, head_dim, max_ctx
+        self.num_phys_pages = num_phys_pages
+        self.kv = torch.zeros((num_phys_pages, kv_heads, PAGE, 2, head_dim), dtype=torch.int16,
+                              device=torch.device(device))
+        self.block_table = block_table
+        self.seq_lens = seq_lens
+        assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+        self.desc = KvcDenseCacheStruct(batch, kv_heads, head_dim, PAGE, block_table.shape[1],
+                                        num_phys_pages, max_ctx, 0, _ptr(self.kv),
+                                        _ptr(block_table), _ptr(seq_lens))
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+    def nbytes(self) -> int:
+        return self.kv.numel() * self.kv.element_size()
+
+
+def kvc_dense_append(cache: DenseCache, k_new, v_new, n_new, stream=None):
+    """Store k_new, v_new ([B][n_new_max][Hkv][D], bf16 or fp32) at each sequence's last
+    n_new[b] positions (seq_lens already counting them)."""
+    _check(lib().kvc_dense_append(cache.ref(), _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                  k_new.shape[1], _ptr(n_new), _stream(stream)), "kvc_dense_append")
+
+
+def kvc_dense_attention_workspace_bytes(cache: DenseCache, num_q_heads: int) -> int:
+    return int(lib().kvc_dense_attention_workspace_bytes(cache.ref(), num_q_heads))
+
+
+def kvc_dense_decode_attention(cache: DenseCache, q, out, lse, ws, softmax_scale: float = 0.0,
+                               stream=None):
+    """Decode attention of q ([B][Hq][D]) over every cached position into out and lse."""
+    nbytes = ws.numel() * ws.element_size()
+    _check(lib().kvc_dense_decode_attention(cache.ref(), _ptr(q), _dtype_code(q), q.shape[1],
+                                            float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                            nbytes, _stream(stream)), "kvc_dense_decode_attention")
+
+
+def dense_workspace(cache: DenseCache, num_q_heads: int, device="cuda"):
+    """Allocate a workspace of the size kvc_dense_decode_attention needs."""
+    import torch
+
+    n = kvc_dense_attention_workspace_bytes(cache, num_q_heads)
     return torch.zeros(max(n // 4, 1), dtype=torch.float32, device=device)

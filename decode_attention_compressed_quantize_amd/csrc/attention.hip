@@ -932,6 +932,34 @@ hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, hipStr
 
 }  // namespace
 
+hipError_t launch_merge(const float* parts, int parts_per_pair, int batch, int hkv, int G, int D,
+                        float* out, float* lse, hipStream_t s) {
+  AttnParams p{};
+  p.parts = const_cast<float*>(parts);
+  p.nsplit = parts_per_pair - 1;
+  p.hkv = hkv;
+  p.batch = batch;
+  p.out = out;
+  p.lse = lse;
+  const dim3 grid(G, hkv, batch), block(kThreads);
+  if (D == 128) {
+    switch (G) {
+      case 1: hipLaunchKernelGGL((merge_kernel<128, 1>), grid, block, 0, s, p); break;
+      case 2: hipLaunchKernelGGL((merge_kernel<128, 2>), grid, block, 0, s, p); break;
+      case 4: hipLaunchKernelGGL((merge_kernel<128, 4>), grid, block, 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (G) {
+      case 1: hipLaunchKernelGGL((merge_kernel<64, 1>), grid, block, 0, s, p); break;
+      case 2: hipLaunchKernelGGL((merge_kernel<64, 2>), grid, block, 0, s, p); break;
+      case 4: hipLaunchKernelGGL((merge_kernel<64, 4>), grid, block, 0, s, p); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype, int num_q_heads,
                             float softmax_scale, float* out, float* lse, float* ws,
                             const AttnPlan& plan, int window, hipStream_t s) {

@@ -67,6 +67,21 @@ kvc_status check_append(const void* k_new, const void* v_new, kvc_dtype src, int
   return KVC_OK;
 }
 
+kvc_status check_dense(const kvc_dense_cache* c) {
+  if (!c) return fail(KVC_E_NULL, "dense cache descriptor is NULL");
+  if (c->batch < 1 || c->num_kv_heads < 1 || c->max_ctx < 1 || c->num_phys_pages < 1)
+    return fail(KVC_E_SHAPE, "batch, num_kv_heads, max_ctx and num_phys_pages must be >= 1");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(KVC_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->page_size != kvc::kPage) return fail(KVC_E_UNSUPPORTED, "page_size must be 16");
+  if ((long long)c->max_pages_per_seq * kvc::kPage < c->max_ctx)
+    return fail(KVC_E_SHAPE, "max_pages_per_seq * 16 must cover max_ctx");
+  if (!c->kv || !c->block_table || !c->seq_lens)
+    return fail(KVC_E_NULL, "kv, block_table or seq_lens is NULL");
+  if (misaligned(c->kv)) return fail(KVC_E_UNSUPPORTED, "kv must be 16-byte aligned");
+  return KVC_OK;
+}
+
 kvc_status launched(hipError_t e) {
   if (e != hipSuccess) {
     g_last_error = std::string("kernel launch failed: ") + hipGetErrorString(e);
@@ -118,6 +133,25 @@ AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window) {
       p.nsplit = (int)((span + c2 - 1) / c2);
     }
   }
+  return p;
+}
+
+DensePlan plan_dense(const kvc_dense_cache& c) {
+  // Chunks of whole 32-token wave tiles (4 waves: multiples of 128), long
+  // enough for about two resident workgroups per CU on 256 CUs, and short
+  // enough that one wave's pages fit its two registers of page ids.
+  constexpr long long kTarget = 512;
+  const long long pairs = (long long)c.batch * c.num_kv_heads;
+  const long long span = c.max_ctx;
+  long long chunk = (pairs * span + kTarget - 1) / kTarget;
+  const long long fit = (span + kMaxParts - 1) / kMaxParts;  // nsplit <= kMaxParts
+  if (chunk < fit) chunk = fit;
+  chunk = (chunk + 127) / 128 * 128;
+  if (chunk < 512) chunk = 512;
+  if (chunk > kDenseMaxChunk) chunk = kDenseMaxChunk;
+  DensePlan p;
+  p.chunk = (int)chunk;
+  p.nsplit = (int)((span + chunk - 1) / chunk);
   return p;
 }
 
@@ -389,6 +423,50 @@ KVC_API kvc_status kvc_shadow_attention(const void* q, const void* k, const void
   return launched(kvc::launch_shadow_attention(q, k, v, batch, max_len, num_q_heads, num_kv_heads,
                                                head_dim, seq_lens, prompt_lens, shadow,
                                                shadow_rows, scale, out, lse, stream));
+}
+
+KVC_API kvc_status kvc_dense_append(const kvc_dense_cache* c, const void* k_new, const void* v_new,
+                                    kvc_dtype src, int32_t n_new_max, const int32_t* n_new,
+                                    hipStream_t stream) {
+  kvc_status st = check_dense(c);
+  if (st != KVC_OK) return st;
+  st = check_append(k_new, v_new, src, n_new_max, n_new);
+  if (st != KVC_OK) return st;
+  if (n_new_max == 0) return KVC_OK;
+  if (misaligned(k_new) || misaligned(v_new))
+    return fail(KVC_E_UNSUPPORTED, "k_new and v_new must be 16-byte aligned");
+  return launched(kvc::launch_dense_append(*c, k_new, v_new, src, n_new_max, n_new, stream));
+}
+
+KVC_API size_t kvc_dense_attention_workspace_bytes(const kvc_dense_cache* c, int32_t num_q_heads) {
+  if (check_dense(c) != KVC_OK || num_q_heads < 1 || num_q_heads % c->num_kv_heads) return 0;
+  return kvc::dense_ws_floats(*c, num_q_heads, kvc::plan_dense(*c)) * sizeof(float);
+}
+
+KVC_API kvc_status kvc_dense_decode_attention(const kvc_dense_cache* c, const void* q,
+                                              kvc_dtype q_dtype, int32_t num_q_heads,
+                                              float softmax_scale, float* out, float* lse,
+                                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  kvc_status st = check_dense(c);
+  if (st != KVC_OK) return st;
+  if (!q || !out) return fail(KVC_E_NULL, "q or out is NULL");
+  if (misaligned(q) || misaligned(out) || misaligned(ws))
+    return fail(KVC_E_UNSUPPORTED, "q, out and ws must be 16-byte aligned");
+  if (q_dtype != KVC_BF16 && q_dtype != KVC_F32)
+    return fail(KVC_E_UNSUPPORTED, "q_dtype must be BF16 or F32");
+  if (num_q_heads < 1 || num_q_heads % c->num_kv_heads)
+    return fail(KVC_E_SHAPE, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int G = num_q_heads / c->num_kv_heads;
+  if (G > 4 || (G & (G - 1)))
+    return fail(KVC_E_UNSUPPORTED, "num_q_heads/num_kv_heads must be 1, 2 or 4");
+  if ((long long)c->max_ctx > (long long)kvc::kMaxParts * kvc::kDenseMaxChunk)
+    return fail(KVC_E_UNSUPPORTED, "max_ctx above 256 * 8192 positions is not supported");
+  const kvc::DensePlan plan = kvc::plan_dense(*c);
+  const size_t need = kvc::dense_ws_floats(*c, num_q_heads, plan) * sizeof(float);
+  if (!ws || ws_bytes < need) return fail(KVC_E_WORKSPACE, "dense attention workspace too small");
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
+  return launched(kvc::launch_dense_attention(*c, q, q_dtype, num_q_heads, scale, out, lse,
+                                              static_cast<float*>(ws), plan, stream));
 }
 
 }  // extern "C"

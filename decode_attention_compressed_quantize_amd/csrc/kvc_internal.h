@@ -128,4 +128,25 @@ hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype
                             float softmax_scale, float* out, float* lse, float* ws,
                             const AttnPlan& plan, int window, hipStream_t s);
 
+// Exact log-sum-exp merge of `parts_per_pair` partials per (sequence, kv head),
+// laid out float [B][Hkv][parts_per_pair][G][2 + D] as (m in log2 units, l, o).
+hipError_t launch_merge(const float* parts, int parts_per_pair, int batch, int hkv, int G, int D,
+                        float* out, float* lse, hipStream_t s);
+
+// Dense bfloat16 paged cache (the uncompressed baseline).
+constexpr int kDenseMaxChunk = 8192;  // positions per chunk workgroup (4 waves x 128 pages)
+struct DensePlan {
+  int chunk;   // positions per chunk (multiple of 128, <= kDenseMaxChunk)
+  int nsplit;  // chunks (= partials) per (sequence, kv head), <= kMaxParts
+};
+DensePlan plan_dense(const kvc_dense_cache& c);
+inline size_t dense_ws_floats(const kvc_dense_cache& c, int num_q_heads, const DensePlan& p) {
+  return (size_t)c.batch * num_q_heads * (size_t)p.nsplit * (size_t)(2 + c.head_dim);
+}
+hipError_t launch_dense_append(const kvc_dense_cache& c, const void* k_new, const void* v_new,
+                               kvc_dtype src, int n_new_max, const int32_t* n_new, hipStream_t s);
+hipError_t launch_dense_attention(const kvc_dense_cache& c, const void* q, kvc_dtype q_dtype,
+                                  int num_q_heads, float softmax_scale, float* out, float* lse,
+                                  float* ws, const DensePlan& plan, hipStream_t s);
+
 }  // namespace kvc

@@ -13,9 +13,10 @@ import numpy as np
 
 import workloads as W
 
-from . import (Cache, attention_workspace, block_workspace, kvc_copy_pages, kvc_find_pages,
-               kvc_append_score_block_mask, kvc_append_score_topk_mask, kvc_quantize_append,
-               kvc_score_block_mask, kvc_score_topk_mask, topk_workspace)
+from . import (Cache, DenseCache, attention_workspace, block_workspace, dense_workspace,
+               kvc_copy_pages, kvc_dense_append, kvc_find_pages, kvc_append_score_block_mask,
+               kvc_append_score_topk_mask, kvc_quantize_append, kvc_score_block_mask,
+               kvc_score_topk_mask, topk_workspace)
 
 
 def pack_bits(flags: np.ndarray, words: int) -> np.ndarray:
@@ -293,3 +294,84 @@ class LayerCache:
 
     def workspace(self):
         return attention_workspace(self.cache, self.w.q_heads, self.device)
+
+
+class DenseLayerCache:
+    """A prefilled dense bfloat16 cache of one layer of workload ``w`` (the
+    uncompressed baseline), with the same page table and source rows as
+    :class:`LayerCache` builds for that workload and layer."""
+
+    def __init__(self, w: W.Workload, layer: int = 0, device="cuda", table: Optional[np.ndarray] = None):
+        import torch
+
+        self.w, self.layer, self.device = w, layer, device
+        self.lengths = w.lengths()
+        if table is None:
+            table, num_pages = W.page_table(w, layer)
+        else:
+            num_pages = int(table.max()) + 1
+        self.table_np = table
+        self.max_ctx = w.max_ctx()
+        self.table = torch.from_numpy(table).to(device)
+        self.seq_lens = torch.from_numpy(self.lengths.astype(np.int32)).to(device)
+        self.cache = DenseCache(w.batch, w.kv_heads, w.head_dim, self.max_ctx, num_pages,
+                                self.table, self.seq_lens, device=device)
+        self.num_pages = num_pages
+        self._prefill()
+
+    def _prefill(self):
+        import torch
+
+        w = self.w
+        dt = torch.bfloat16 if w.src_dtype == "bf16" else torch.float32
+        lmax = int(self.lengths.max())
+        if lmax == 0:
+            return
+        per = max(1, int(2 ** 31 // max(1, lmax * w.kv_heads * w.head_dim * 2)))
+        for b0 in range(0, w.batch, per):
+            b1 = min(w.batch, b0 + per)
+            k_new = torch.zeros((b1 - b0, lmax, w.kv_heads, w.head_dim), dtype=dt, device=self.device)
+            v_new = torch.zeros_like(k_new)
+            n_new = torch.zeros(w.batch, dtype=torch.int32, device=self.device)
+            for b in range(b0, b1):
+                L = int(self.lengths[b])
+                k_new[b - b0, :L] = W.kv_source_torch(w, self.layer, "K", b, 0, L, self.device)
+                v_new[b - b0, :L] = W.kv_source_torch(w, self.layer, "V", b, 0, L, self.device)
+                n_new[b] = L
+            sub = self._sub_cache(b0, b1)
+            kvc_dense_append(sub, k_new, v_new, n_new[b0:b1])
+            del k_new, v_new
+
+    def _sub_cache(self, b0: int, b1: int) -> DenseCache:
+        if b0 == 0 and b1 == self.w.batch:
+            return self.cache
+        import copy
+
+        sub = copy.copy(self.cache)
+        sub.desc = type(self.cache.desc).from_buffer_copy(self.cache.desc)
+        sub.desc.batch = b1 - b0
+        sub.desc.block_table = self.table[b0:b1].data_ptr()
+        sub.desc.seq_lens = self.seq_lens[b0:b1].data_ptr()
+        return sub
+
+    def replica(self) -> "DenseLayerCache":
+        """An independent copy on the device (same contents, own memory)."""
+        import copy
+
+        c = self.cache
+        r = copy.copy(self)
+        r.table = self.table.clone()
+        r.seq_lens = self.seq_lens.clone()
+        r.cache = DenseCache(c.batch, c.kv_heads, c.head_dim, c.max_ctx, c.num_phys_pages, r.table,
+                             r.seq_lens, device=self.device)
+        r.cache.kv.copy_(c.kv)
+        return r
+
+    def append(self, k_new, v_new, n_new, stream=None):
+        kvc_dense_append(self.cache, k_new, v_new, n_new, stream=stream)
+
+    def queries(self, step: int = 0):
+        return W.queries_torch(self.w, self.layer, step, self.device)
+
+    def workspace(self):
+        return dense_workspace(self.cache, self.w.q_heads, self.device)

@@ -78,7 +78,7 @@ extern "C" {
 #endif
 
 #define KVC_API __attribute__((visibility("default")))
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum {
   KVC_OK = 0,
@@ -351,6 +351,63 @@ KVC_API kvc_status kvc_shadow_attention(const void* q, const void* k, const void
                                         const uint32_t* shadow, int32_t shadow_rows,
                                         float softmax_scale, float* out, float* lse,
                                         hipStream_t stream);
+
+/*
+ * Dense bfloat16 paged cache: the uncompressed baseline.
+ * Source: KV4-RL review, section 3 - the INT4 cache's rollout speedups are
+ * measured against BF16 rollout, whose KV cache holds every K and V row in
+ * bfloat16 and whose decode attention reads every cached position. These
+ * calls provide that baseline on the same paging and call shape as the
+ * compressed cache, for comparison on one harness.
+ *   kv          uint16 [P][Hkv][16][2][D]   bfloat16 bits; per token the K row
+ *               then the V row (4*D bytes per token and kv head).
+ *   block_table int32  [B][max_pages_per_seq], seq_lens int32 [B]: as in
+ *               kvc_cache (seq_lens never written by the library).
+ */
+typedef struct kvc_dense_cache {
+  int32_t batch;             /* B >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1 */
+  int32_t head_dim;          /* D: 64 or 128 */
+  int32_t page_size;         /* must be 16 */
+  int32_t max_pages_per_seq; /* >= ceil(max_ctx/16) */
+  int32_t num_phys_pages;    /* P >= 1 */
+  int32_t max_ctx;           /* capacity in positions, >= 1 (attention: <= 2097152) */
+  int32_t reserved;          /* 0 */
+  uint16_t* kv;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+} kvc_dense_cache;
+
+/*
+ * kvc_dense_append - store appended K/V rows in the dense cache.
+ *   k_new, v_new, n_new, n_new_max, src: as kvc_quantize_append (row j of
+ *   sequence b is position seq_lens[b]-n_new[b]+j). A float32 row is stored
+ *   as its bfloat16 round-to-nearest-even, a bfloat16 row unchanged.
+ *   Positions outside [0, max_ctx) and pages whose table entry is outside
+ *   [0, P) are skipped. k_new and v_new must be 16-byte aligned.
+ */
+KVC_API kvc_status kvc_dense_append(const kvc_dense_cache* c, const void* k_new, const void* v_new,
+                                    kvc_dtype src, int32_t n_new_max, const int32_t* n_new,
+                                    hipStream_t stream);
+
+/*
+ * kvc_dense_decode_attention - decode attention over every position of the
+ * dense cache.
+ *   q, q_dtype, num_q_heads, softmax_scale, out, lse: as kvc_decode_attention
+ *   (G = num_q_heads/num_kv_heads in {1, 2, 4}); out[b][h] attends to the
+ *   positions [0, seq_lens[b]) of kv head h/G, each read in bfloat16; logits
+ *   (q . k)*softmax_scale with a float32 query used at float32 accuracy.
+ *   ws, ws_bytes : device scratch of at least
+ *                  kvc_dense_attention_workspace_bytes(c, num_q_heads) bytes.
+ *   Positions whose page's table entry is outside [0, P) are skipped (not
+ *   attended). L = 0 yields out = 0, lse = -inf. kv, q, out and ws must be
+ *   16-byte aligned.
+ */
+KVC_API kvc_status kvc_dense_decode_attention(const kvc_dense_cache* c, const void* q,
+                                              kvc_dtype q_dtype, int32_t num_q_heads,
+                                              float softmax_scale, float* out, float* lse,
+                                              void* ws, size_t ws_bytes, hipStream_t stream);
+KVC_API size_t kvc_dense_attention_workspace_bytes(const kvc_dense_cache* c, int32_t num_q_heads);
 
 /* Workspace sizes (host-only, no device work). Return 0 for an invalid cache.
  * kvc_topk_workspace_bytes is the size of the optional refresh state of

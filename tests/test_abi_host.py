@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert kvc.kvc_abi_version() == 2
+    assert kvc.kvc_abi_version() == 3
     assert kvc.kvc_status_string(0) == "ok"
     assert kvc.kvc_status_string(-4) == "workspace too small"
 
@@ -207,3 +207,60 @@ def test_block_workspace_size(lib):
             assert lib.kvc_block_workspace_bytes(ctypes.byref(c), B) == 2 * 8 * stride
     assert lib.kvc_block_workspace_bytes(ctypes.byref(desc()), 8) == 0
     assert lib.kvc_block_workspace_bytes(ctypes.byref(desc(head_dim=96)), 16) == 0
+
+
+def ddesc(**kw):
+    d = dict(batch=2, num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=64,
+             num_phys_pages=128, max_ctx=1024, reserved=0, kv=FAKE, block_table=FAKE, seq_lens=FAKE)
+    d.update(kw)
+    return kvc.KvcDenseCacheStruct(**d)
+
+
+def dattn(lib, c, q=FAKE, hq=32, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.kvc_dense_decode_attention(ctypes.byref(c) if c is not None else None, q, 0, hq, 0.0,
+                                          out, None, ws, ws_bytes, None)
+
+
+def test_dense_argument_errors(lib):
+    assert dattn(lib, None) == -1
+    assert dattn(lib, ddesc(kv=None)) == -1
+    assert dattn(lib, ddesc(block_table=None)) == -1
+    assert dattn(lib, ddesc(), q=None) == -1
+    assert dattn(lib, ddesc(head_dim=96)) == -3
+    assert dattn(lib, ddesc(page_size=32)) == -3
+    assert dattn(lib, ddesc(max_pages_per_seq=10)) == -2
+    assert dattn(lib, ddesc(batch=0)) == -2
+    assert dattn(lib, ddesc(), hq=12) == -2
+    assert dattn(lib, ddesc(), hq=64) == -3
+    assert dattn(lib, ddesc(kv=FAKE + 2)) == -3
+    assert dattn(lib, ddesc(), q=FAKE + 4) == -3
+    assert dattn(lib, ddesc(), ws=None) == -4
+    assert dattn(lib, ddesc(), ws_bytes=16) == -4
+    big = 256 * 8192 + 1
+    assert dattn(lib, ddesc(max_ctx=big, max_pages_per_seq=(big + 15) // 16)) == -3
+    c = ddesc()
+    app = lib.kvc_dense_append
+    assert app(None, FAKE, FAKE, 0, 1, FAKE, None) == -1
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, -1, FAKE, None) == -2
+    assert app(ctypes.byref(c), None, FAKE, 0, 1, FAKE, None) == -1
+    assert app(ctypes.byref(c), FAKE, FAKE, 7, 1, FAKE, None) == -3
+    assert app(ctypes.byref(c), FAKE + 2, FAKE, 0, 1, FAKE, None) == -3
+    assert app(ctypes.byref(c), FAKE, FAKE, 0, 0, FAKE, None) == 0  # no-op
+
+
+def test_dense_workspace_size(lib):
+    # one (m, l, o[D]) partial per query head per chunk; chunks of at most 8192 positions,
+    # at most 256 of them, and about 512 chunk workgroups once the work allows it
+    for max_ctx, batch in ((1, 1), (100, 2), (4096, 64), (131072, 4), (131072 + 32, 4),
+                           (256 * 8192, 1)):
+        c = ddesc(max_ctx=max_ctx, batch=batch, max_pages_per_seq=(max_ctx + 15) // 16)
+        n = lib.kvc_dense_attention_workspace_bytes(ctypes.byref(c), 32)
+        per_split = batch * 32 * (128 + 2) * 4
+        assert n % per_split == 0
+        nsplit = n // per_split
+        assert 1 <= nsplit <= 256
+        assert nsplit * 8192 >= max_ctx
+    c = ddesc(max_ctx=131072, batch=4, max_pages_per_seq=8192)
+    assert lib.kvc_dense_attention_workspace_bytes(ctypes.byref(c), 32) == 4 * 32 * 130 * 4 * 16
+    assert lib.kvc_dense_attention_workspace_bytes(ctypes.byref(ddesc(head_dim=96)), 32) == 0
+    assert lib.kvc_dense_attention_workspace_bytes(ctypes.byref(ddesc()), 12) == 0
