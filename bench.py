@@ -50,6 +50,9 @@ WORKLOAD_LAYERS = {
     "fullstep": ["fullstep"] * 36,
     "tiny": ["tiny"],
 }
+# The uncompressed baseline: a dense bfloat16 paged cache of the same shape as
+# long128k (two layers per step), every position attended.
+DENSE = {"long128k_dense": dict(batch=4, q_heads=32, kv_heads=8, head_dim=128, ctx=131072, layers=2)}
 
 
 def algorithmic_bytes(w, lengths, keep4_counts):
@@ -203,6 +206,164 @@ def cpu_baseline(layer_names, seconds: float):
                       f"{used} worker processes (1 thread each) and divided by {used}"}
 
 
+# ---------------------------------------------------------------------- dense baseline
+def dense_bytes(w, lengths):
+    """Bytes one dense attention call must move: every position's K and V rows in
+    bfloat16, the block table, queries, outputs and LSE."""
+    D, Hkv, Hq = w.head_dim, w.kv_heads, w.q_heads
+    total = 0
+    for L in lengths:
+        L = int(L)
+        total += Hkv * L * 4 * D + ((L + 15) // 16) * 4 + Hq * (D * 2 + D * 4 + 4)
+    return total
+
+
+def _cpu_dense_pair(args):
+    """Oracle dense attention for one (workload, b, kvh): returns (bytes, seconds)."""
+    name, b, kvh = args
+    from threadpoolctl import threadpool_limits
+
+    import numpy as np
+
+    import workloads as W
+    from oracle import dense
+
+    with threadpool_limits(1):
+        cfg = DENSE[name]
+        w = W.Workload(name, cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
+                       ctx=cfg["ctx"])
+        L = int(w.lengths()[b])
+        k = W.bf16_bits_to_f32(W.kv_source_np(w, 0, "K", b, 0, L, kvh=kvh))
+        v = W.bf16_bits_to_f32(W.kv_source_np(w, 0, "V", b, 0, L, kvh=kvh))
+        G = w.group_size
+        q = W.bf16_bits_to_f32(W.queries_np(w, 0, 0)[b, kvh * G:(kvh + 1) * G]).astype(np.float64)
+        t0 = time.perf_counter()
+        dense.decode_group(q, k, v, "bf16")
+        return L * 4 * w.head_dim, time.perf_counter() - t0
+
+
+def dense_main(args):
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import decode_attention_compressed_quantize_amd as kvc
+    from decode_attention_compressed_quantize_amd.workload_cache import DenseLayerCache
+
+    kvc.lib()
+    cfg = DENSE[args.workload]
+    total_steps = args.warmup + args.steps
+    print(f"bench: building {args.workload} ({cfg['layers']} dense layer caches)", file=sys.stderr,
+          flush=True)
+    layers = []
+    for li in range(cfg["layers"]):
+        w = W.Workload(args.workload, cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"],
+                       ctx=cfg["ctx"], decode_steps=total_steps + 1)
+        layers.append(DenseLayerCache(w, layer=li))
+    for lc in layers[1:]:  # the layers of one batch share one lengths tensor
+        lc.seq_lens = layers[0].seq_lens
+        lc.cache.seq_lens = layers[0].seq_lens
+        lc.cache.desc.seq_lens = layers[0].seq_lens.data_ptr()
+    dev = "cuda"
+    inputs = []
+    for li, lc in enumerate(layers):
+        w = lc.w
+        L0 = lc.lengths.copy()
+        ks, vs, qs = [], [], []
+        for s in range(total_steps + 1):
+            ks.append(W.kv_rows_torch(w, li, "K", L0 + s, dev)[:, None])
+            vs.append(W.kv_rows_torch(w, li, "V", L0 + s, dev)[:, None])
+            qs.append(W.queries_torch(w, li, s + 1, dev))
+        inputs.append({"k": ks, "v": vs, "q": qs, "ws": lc.workspace(),
+                       "out": torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev),
+                       "lse": torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev),
+                       "one": torch.ones(w.batch, dtype=torch.int32, device=dev)})
+    lens = layers[0].lengths.astype(np.int64).copy()
+    stream = torch.cuda.current_stream()
+    TIME_EVERY = 4
+    attn = []
+
+    def step(i, record):
+        layers[0].seq_lens.add_(1)
+        lens[:] += 1
+        byts = 0
+        for li, lc in enumerate(layers):
+            st = inputs[li]
+            lc.append(st["k"][i], st["v"][i], st["one"])
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            kvc.kvc_dense_decode_attention(lc.cache, st["q"][i], st["out"], st["lse"], st["ws"])
+            if record:
+                e1.record(stream)
+                attn.append((e0, e1))
+            byts += dense_bytes(lc.w, lens)
+        return byts
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_bytes = 0
+    t0.record(stream)
+    for i in range(args.warmup, total_steps):
+        step_bytes += step(i, (i - args.warmup) % TIME_EVERY == 0)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gbs = step_bytes / args.steps / (ms * 1e-3) / 1e9
+    a_ms = statistics.median(e0.elapsed_time(e1) for e0, e1 in attn)
+    a_bytes = dense_bytes(layers[0].w, lens)
+    a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+    print(f"bench: dense attention call times (ms): " +
+          " ".join(f"{e0.elapsed_time(e1):.4f}" for e0, e1 in attn), file=sys.stderr, flush=True)
+    w = layers[0].w
+    line = {
+        "metric": "dense bf16 KV decode attention (uncompressed baseline): KV bytes GB/s (% HBM peak), decode steps/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 K/V, bf16 MFMA logits (two-part query), f32 P.V and accumulate",
+        "data": "synthetic (seeded normal K/V/Q)",
+        "config": {"workload": args.workload, "layers": f"{cfg['layers']} x dense bf16",
+                   "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "head_dim": w.head_dim, "context": cfg["ctx"], "replicas": 1,
+                   "keep_policy": "none (every position attended)"},
+        "decode_steps_per_s": round(1000.0 / ms, 2),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "attention": {"ms_per_call": round(a_ms, 5), "GBs": round(a_gbs, 1), "timed_calls": len(attn),
+                      "timed_every_nth_step": TIME_EVERY, "statistic": "median call time"},
+        "roofline": {"kernel": "kvc_dense_decode_attention call: dense_attention_kernel then "
+                               "merge_kernel, timed together with HIP events on the launch stream",
+                     "bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_call": int(a_bytes)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        import multiprocessing as mp
+
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+        sample = [(args.workload, b, h) for b in range(w.batch) for h in range(w.kv_heads)][:cores]
+        with mp.get_context("spawn").Pool(len(sample)) as pool:
+            res = pool.map(_cpu_dense_pair, sample)
+        busy = sum(r[1] for r in res)
+        line["cpu_baseline"] = {
+            "value": round(sum(r[0] for r in res) / (busy / len(sample)) / 1e9, 4), "unit": "GB/s",
+            "cores": len(sample), "kind": "oracle",
+            "sample": f"{len(sample)} (sequence, kv head) pairs of {args.workload}: float64 dense "
+                      f"softmax attention over bf16 rows, busy time summed over {len(sample)} "
+                      f"worker processes (1 thread each) and divided by {len(sample)}"}
+    print(json.dumps(line), flush=True)
+
+
 # ---------------------------------------------------------------------- learner
 # Learner-side shadow-mask attention: B sequences of a prompt plus generated
 # positions whose keep masks come from a rollout recorded on the GPU (one
@@ -340,7 +501,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long128k", choices=sorted(WORKLOAD_LAYERS) + sorted(LEARNER))
+    ap.add_argument("--workload", default="long128k",
+                    choices=sorted(WORKLOAD_LAYERS) + sorted(LEARNER) + sorted(DENSE))
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >1 GiB between reuses")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -352,6 +514,9 @@ def main():
         sys.exit(2)
     if args.workload in LEARNER:
         learner_main(args)
+        return
+    if args.workload in DENSE:
+        dense_main(args)
         return
 
     import numpy as np
