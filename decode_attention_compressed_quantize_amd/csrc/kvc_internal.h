@@ -82,7 +82,11 @@ struct BlockStateHeader {
   int32_t budget;   // budget_permille of thr
   uint32_t thr;     // key of the k-th largest block (when has_thr)
   int32_t has_thr;
-  int32_t pad[9];
+  // counts of the stored keys above and equal to thr, valid (has_cnt) when
+  // the mask was written as exactly "kept = key >= thr"
+  uint32_t gt, eq;
+  int32_t has_cnt;
+  int32_t pad[6];
 };
 static_assert(sizeof(BlockStateHeader) == 64, "header size");
 // Sized for the smallest block (16 tokens), so that every block size finds

@@ -684,6 +684,27 @@ __device__ inline uint32_t block_key_direct(const float* sc, int j, int c0, int 
   return order_key(sum / (float)(e - a));
 }
 
+// Mask word w (positions 32w..32w+31) of a sequence of length L: protected
+// positions [0, min(L, sink)) and [rec0, L) set, candidates [lo4, hi4) set
+// where their block is kept; a word meets at most two blocks, jA and jB.
+template <int B, typename Kept>
+__device__ inline uint32_t block_mask_word(int w, int L, int sink, int rec0, int lo4, int hi4,
+                                           Kept kept_block) {
+  const int base = 32 * w;
+  uint32_t bits = range_bits(0, L < sink ? L : sink, base) | range_bits(rec0, L, base);
+  const uint32_t cand = range_bits(lo4, hi4, base);
+  if (cand) {
+    const int jA = (base - sink + B) / B - 1;  // floor((base - sink) / B), base - sink >= -B
+    const int jB = (base + 31 - sink) / B;
+    const int split = sink + B * jB;
+    uint32_t kb = 0;
+    if (kept_block(jA)) kb |= range_bits(sink + B * jA, split, base);
+    if (kept_block(jB)) kb |= range_bits(split, split + B, base);
+    bits |= cand & kb;
+  }
+  return bits;
+}
+
 template <int B>
 __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, int b) {
   static_assert(B == 16 || B == 32 || B == 64, "block size");
@@ -710,15 +731,6 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   // keys are stored (LDS cache, state) only where something keeps them
   const bool need_keys = (select && cached) || st != nullptr;
 
-  // ---- everything that does not depend on the state is loaded up front: the
-  // previous mask words, the state's keys (into LDS), and the keys of the first
-  // and the last candidate block (the ones a one-token step changes)
-  uint32_t old_w[kOldWords];
-#pragma unroll
-  for (int m = 0; m < kOldWords; ++m) {
-    const int w = tid + m * kTopkThreads;
-    old_w[m] = w < p.words ? mrow[w] : 0u;
-  }
   bool valid = false, thr_ok = false;
   int len0 = 0;
   uint32_t thr0 = 0;
@@ -729,6 +741,29 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
             len0 <= L;
     thr_ok = valid && st->has_thr != 0 && st->budget == p.budget;
     thr0 = st->thr;
+  }
+  // keys above / equal to thr0 as the state left them, and which old keys leave
+  const int n4o = len0 > slots ? len0 - slots : 0;
+  const int c0o = p.window > 0 ? (n4o - p.window > 0 ? n4o - p.window : 0) : 0;
+  const int j0o = c0o / B;
+  const int nbo = n4o > c0o ? (n4o + B - 1) / B - j0o : 0;
+  const int nrem = j0 > j0o ? j0 - j0o : 0;  // blocks the moved cut removed: [j0o, j0)
+  uint32_t gt_st = 0, eq_st = 0;
+  bool counted = false;
+  if (thr_ok && select && cached && st->has_cnt != 0 && nrem <= kTopkThreads) {
+    gt_st = st->gt;
+    eq_st = st->eq;
+    counted = true;
+  }
+
+  // ---- everything the full refresh reads is loaded up front: the previous
+  // mask words, the state's keys (into LDS), and the keys of the first and the
+  // last candidate block (the ones a one-token step changes)
+  uint32_t old_w[kOldWords];
+#pragma unroll
+  for (int m = 0; m < kOldWords; ++m) {
+    const int w = tid + m * kTopkThreads;
+    old_w[m] = w < p.words ? mrow[w] : 0u;
   }
   int spec_r = -1;
   uint32_t spec_key = 0;
@@ -741,6 +776,14 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
 #pragma unroll 8
     for (int i = tid; i < nb; i += kTopkThreads) sm.keys[i] = skeys[j0 + i];
   }
+  // counted: the counts against thr0 follow from the keys that change (the
+  // removed ones, loaded here, and the recomputed ones below), not a full pass
+  int dgt = 0, deq = 0;
+  if (counted && tid < nrem && tid < nbo) {
+    const uint32_t old = skeys[j0o + tid];
+    dgt -= old > thr0;
+    deq -= old == thr0;
+  }
   // the previous mask words are needed only at the end; keep them here, with
   // this round of loads, instead of a round trip of their own later
 #pragma unroll
@@ -751,8 +794,6 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   int ra = 0;
   bool first_too = false;
   if (valid) {
-    const int n4o = len0 > slots ? len0 - slots : 0;
-    const int c0o = p.window > 0 ? (n4o - p.window > 0 ? n4o - p.window : 0) : 0;
     ra = n4o / B - j0;
     if (ra < 0) ra = 0;
     if (ra > nb) ra = nb;
@@ -761,6 +802,16 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   __syncthreads();  // header read and state keys in LDS before anything is rewritten
 
   auto store_key = [&](int r, uint32_t key) {
+    if (counted) {  // each recomputed block is stored by exactly one thread
+      const int a = j0 + r;
+      if (a >= j0o && a < j0o + nbo) {
+        const uint32_t old = sm.keys[r];
+        dgt -= old > thr0;
+        deq -= old == thr0;
+      }
+      dgt += key > thr0;
+      deq += key == thr0;
+    }
     if (cached) sm.keys[r] = key;
     if (st) skeys[j0 + r] = key;
   };
@@ -831,13 +882,21 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
       // it, then move it to the next distinct key up or down while it selects
       // more or fewer than k blocks (a few keys change from call to call)
       uint32_t gt = 0, eq = 0;
+      if (counted) {
+        gt = (uint32_t)dgt;
+        eq = (uint32_t)deq;
+        block_sum2(sm, gt, eq, lane, wid);
+        gt += gt_st;
+        eq += eq_st;
+      } else {
 #pragma unroll 8
-      for (int i = tid; i < nb; i += kTopkThreads) {
-        const uint32_t key = key_of(i);
-        gt += key > thr0;
-        eq += key == thr0;
+        for (int i = tid; i < nb; i += kTopkThreads) {
+          const uint32_t key = key_of(i);
+          gt += key > thr0;
+          eq += key == thr0;
+        }
+        block_sum2(sm, gt, eq, lane, wid);
       }
-      block_sum2(sm, gt, eq, lane, wid);
       uint32_t t = thr0;
       for (int step = 0; step < 4; ++step) {
         if ((long long)gt < k && k <= (long long)gt + eq) {
@@ -964,13 +1023,15 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
     __syncthreads();
   }
 
-  // ---- kept-block bitmap when kept means key >= T (or every block): one
-  // ballot per 64-block segment (the tie case filled it above)
-  if (all || by_key) {
+  // ---- kept-block bitmap when kept means key >= T and the keys are not in
+  // LDS: one ballot per 64-block segment (the tie case filled it above; with
+  // every block kept, or the keys in LDS, the words test the keys directly)
+  const bool direct = all || (by_key && cached);
+  if (by_key && !cached) {
     const int nseg = (nb + 63) / 64;
     for (int sg = wid; sg < nseg; sg += kBlockWaves) {
       const int i = 64 * sg + lane;
-      const uint64_t ks = __ballot(i < nb && (all || key_of(i) >= T));
+      const uint64_t ks = __ballot(i < nb && key_of(i) >= T);
       if (lane == 0) sm.kept_bits[2 * sg] = (uint32_t)ks;
       if (lane == 32) sm.kept_bits[2 * sg + 1] = (uint32_t)(ks >> 32);
     }
@@ -987,22 +1048,12 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   const bool any_kept = all || select;
   auto kept_block = [&](int j) -> bool {
     const int r = j - j0;
-    return any_kept && r >= 0 && r < nb && ((sm.kept_bits[r >> 5] >> (r & 31)) & 1u);
+    if (!any_kept || r < 0 || r >= nb) return false;
+    if (direct) return all || sm.keys[r] >= T;
+    return ((sm.kept_bits[r >> 5] >> (r & 31)) & 1u) != 0;
   };
   auto word_bits = [&](int w) -> uint32_t {
-    const int base = 32 * w;
-    uint32_t bits = range_bits(0, L < sink ? L : sink, base) | range_bits(rec0, L, base);
-    const uint32_t cand = range_bits(lo4, hi4, base);
-    if (cand) {
-      const int jA = (base - sink + B) / B - 1;  // floor((base - sink) / B), base - sink >= -B
-      const int jB = (base + 31 - sink) / B;
-      const int split = sink + B * jB;
-      uint32_t kb = 0;
-      if (kept_block(jA)) kb |= range_bits(sink + B * jA, split, base);
-      if (kept_block(jB)) kb |= range_bits(split, split + B, base);
-      bits |= cand & kb;
-    }
-    return bits;
+    return block_mask_word<B>(w, L, sink, rec0, lo4, hi4, kept_block);
   };
 #pragma unroll
   for (int m = 0; m < kOldWords; ++m) {
@@ -1024,6 +1075,9 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
     st->budget = p.budget;
     st->thr = T;
     st->has_thr = select ? 1 : 0;
+    st->gt = (uint32_t)(k - need);
+    st->eq = (uint32_t)eqT;
+    st->has_cnt = select && by_key ? 1 : 0;
   }
 }
 
