@@ -35,8 +35,14 @@ HOST_LINK_PEAK_GBS = 64.0  # PCIe Gen5 x16, one direction
 # Host tier: "cold" demotes pages whose positions are all evicted after the
 # prefill; "all" moves every whole INT4-region page to the host tier.
 TIER_MODE = {"long128k_tiered": "cold", "long128k_streamed": "all"}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_long128k_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_compressed_quantize_amd", "csrc", "attention.hip")
+# rocprofv3 PMC summaries of the attention call: workload -> (summary, kernel source it was taken with)
+_CSRC = os.path.join(ROOT, "decode_attention_compressed_quantize_amd", "csrc")
+TRAFFIC = {
+    "long128k": (os.path.join(ROOT, "profiles", "attention_long128k_traffic.txt"),
+                 os.path.join(_CSRC, "attention.hip")),
+    "long128k_dense": (os.path.join(ROOT, "profiles", "attention_long128k_dense_traffic.txt"),
+                       os.path.join(_CSRC, "dense_attention.hip")),
+}
 
 WORKLOAD_LAYERS = {
     "long128k": ["long128k_b10", "long128k_b50"],
@@ -115,15 +121,16 @@ def measured_traffic(workload: str):
     """
     import hashlib
 
-    if workload != "long128k" or not os.path.exists(TRAFFIC_FILE):
+    if workload not in TRAFFIC or not os.path.exists(TRAFFIC[workload][0]):
         return None
+    summary, source = TRAFFIC[workload]
     fields = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(summary) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    src = hashlib.sha256(open(source, "rb").read()).hexdigest()
     if fields.get("kernel_source_sha256") != src:
         return None
     try:
@@ -342,7 +349,7 @@ def dense_main(args):
         "roofline": {"kernel": "kvc_dense_decode_attention call: dense_attention_kernel then "
                                "merge_kernel, timed together with HIP events on the launch stream",
                      "bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_call": int(a_bytes)},
         "cpu_baseline": None,
     }
