@@ -139,6 +139,36 @@ def measured_traffic(workload: str):
         return None
 
 
+def read_ceiling_gbs():
+    """The streaming-read rate of this GPU: kvc_stream_read_probe over a 4 GiB buffer
+    (16-byte loads, every word read once), median of 10 calls between HIP events."""
+    import torch
+
+    import decode_attention_compressed_quantize_amd as kvc
+
+    buf = torch.empty(1 << 30, dtype=torch.int32, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        kvc.kvc_stream_read_probe(buf, out)
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvc.kvc_stream_read_probe(buf, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del buf
+    return (4 << 30) / (statistics.median(ts) * 1e-3) / 1e9
+
+
+def add_read_ceiling(line):
+    """Also state the attention call's rate against the measured streaming-read ceiling."""
+    ceil = read_ceiling_gbs()
+    line["roofline"]["read_ceiling_GBs"] = round(ceil, 1)
+    line["roofline"]["frac_of_read_ceiling"] = round(line["roofline"]["achieved"] / ceil, 4)
+
+
 # ---------------------------------------------------------------------- CPU
 def _cpu_pair(args):
     """Oracle attention phase for one (workload, b, kvh): returns (bytes, seconds)."""
@@ -353,6 +383,7 @@ def dense_main(args):
                      "algorithmic_bytes_per_call": int(a_bytes)},
         "cpu_baseline": None,
     }
+    add_read_ceiling(line)
     if not args.no_cpu:
         import multiprocessing as mp
 
@@ -711,6 +742,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if tier != "all":
+        add_read_ceiling(line)
     if not args.no_cpu:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(names, args.cpu_seconds)

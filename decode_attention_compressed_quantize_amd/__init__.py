@@ -135,6 +135,8 @@ _SIGNATURES = {
                                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                                   ctypes.c_void_p]),
     "kvc_dense_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
+    "kvc_stream_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
     "kvc_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
     "kvc_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "kvc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -465,3 +467,10 @@ def dense_workspace(cache: DenseCache, num_q_heads: int, device="cuda"):
 
     n = kvc_dense_attention_workspace_bytes(cache, num_q_heads)
     return torch.zeros(max(n // 4, 1), dtype=torch.float32, device=device)
+
+
+def kvc_stream_read_probe(buf, out, stream=None):
+    """Read every byte of ``buf`` once (16-byte loads); XOR-fold its 32-bit words into
+    ``out`` (int32 [1], zeroed by the caller). A measurement aid for the read ceiling."""
+    _check(lib().kvc_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                       _stream(stream)), "kvc_stream_read_probe")

@@ -469,4 +469,12 @@ KVC_API kvc_status kvc_dense_decode_attention(const kvc_dense_cache* c, const vo
                                               static_cast<float*>(ws), plan, stream));
 }
 
+KVC_API kvc_status kvc_stream_read_probe(const void* buf, size_t bytes, uint32_t* out,
+                                         hipStream_t stream) {
+  if (bytes == 0) return KVC_OK;
+  if (!buf || !out) return fail(KVC_E_NULL, "buf or out is NULL");
+  if (misaligned(buf) || bytes % 16) return fail(KVC_E_UNSUPPORTED, "buf must be 16-byte aligned and bytes a multiple of 16");
+  return launched(kvc::launch_stream_read(buf, bytes, out, stream));
+}
+
 }  // extern "C"

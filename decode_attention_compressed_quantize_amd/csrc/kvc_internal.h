@@ -153,4 +153,7 @@ hipError_t launch_dense_attention(const kvc_dense_cache& c, const void* q, kvc_d
                                   int num_q_heads, float softmax_scale, float* out, float* lse,
                                   float* ws, const DensePlan& plan, hipStream_t s);
 
+// Streaming-read probe (measurement aid): XOR of every 32-bit word into *out.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t s);
+
 }  // namespace kvc

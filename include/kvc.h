@@ -409,6 +409,18 @@ KVC_API kvc_status kvc_dense_decode_attention(const kvc_dense_cache* c, const vo
                                               void* ws, size_t ws_bytes, hipStream_t stream);
 KVC_API size_t kvc_dense_attention_workspace_bytes(const kvc_dense_cache* c, int32_t num_q_heads);
 
+/*
+ * kvc_stream_read_probe - a measurement aid, not a step of the method: read a
+ * device buffer once with plain 16-byte loads and XOR every 32-bit word into
+ * *out (which the caller zeroes first), so that the attention kernels'
+ * bandwidth can also be stated against the read rate this part reaches on a
+ * streaming pattern, next to the vendor peak.
+ *   buf   : device, 16-byte aligned; bytes: a multiple of 16 (0 is a no-op).
+ *   out   : device uint32, receives the XOR fold (exact, checkable).
+ */
+KVC_API kvc_status kvc_stream_read_probe(const void* buf, size_t bytes, uint32_t* out,
+                                         hipStream_t stream);
+
 /* Workspace sizes (host-only, no device work). Return 0 for an invalid cache.
  * kvc_topk_workspace_bytes is the size of the optional refresh state of
  * kvc_score_topk_mask: 1056 bytes per (sequence, kv head).

@@ -264,3 +264,12 @@ def test_dense_workspace_size(lib):
     assert lib.kvc_dense_attention_workspace_bytes(ctypes.byref(c), 32) == 4 * 32 * 130 * 4 * 16
     assert lib.kvc_dense_attention_workspace_bytes(ctypes.byref(ddesc(head_dim=96)), 32) == 0
     assert lib.kvc_dense_attention_workspace_bytes(ctypes.byref(ddesc()), 12) == 0
+
+
+def test_read_probe_argument_errors(lib):
+    probe = lib.kvc_stream_read_probe
+    assert probe(None, 0, None, None) == 0            # nothing to read
+    assert probe(None, 64, FAKE, None) == -1
+    assert probe(FAKE, 64, None, None) == -1
+    assert probe(FAKE + 4, 64, FAKE, None) == -3      # 16-byte alignment
+    assert probe(FAKE, 60, FAKE, None) == -3          # whole 16-byte pieces
