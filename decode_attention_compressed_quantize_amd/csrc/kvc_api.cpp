@@ -474,6 +474,7 @@ KVC_API kvc_status kvc_stream_read_probe(const void* buf, size_t bytes, uint32_t
   if (bytes == 0) return KVC_OK;
   if (!buf || !out) return fail(KVC_E_NULL, "buf or out is NULL");
   if (misaligned(buf) || bytes % 16) return fail(KVC_E_UNSUPPORTED, "buf must be 16-byte aligned and bytes a multiple of 16");
+  if (reinterpret_cast<uintptr_t>(out) & 3u) return fail(KVC_E_UNSUPPORTED, "out must be 4-byte aligned");
   return launched(kvc::launch_stream_read(buf, bytes, out, stream));
 }
 

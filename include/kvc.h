@@ -416,7 +416,7 @@ KVC_API size_t kvc_dense_attention_workspace_bytes(const kvc_dense_cache* c, int
  * bandwidth can also be stated against the read rate this part reaches on a
  * streaming pattern, next to the vendor peak.
  *   buf   : device, 16-byte aligned; bytes: a multiple of 16 (0 is a no-op).
- *   out   : device uint32, receives the XOR fold (exact, checkable).
+ *   out   : device uint32 (4-byte aligned), receives the XOR fold (exact, checkable).
  */
 KVC_API kvc_status kvc_stream_read_probe(const void* buf, size_t bytes, uint32_t* out,
                                          hipStream_t stream);

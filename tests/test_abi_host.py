@@ -273,3 +273,4 @@ def test_read_probe_argument_errors(lib):
     assert probe(FAKE, 64, None, None) == -1
     assert probe(FAKE + 4, 64, FAKE, None) == -3      # 16-byte alignment
     assert probe(FAKE, 60, FAKE, None) == -3          # whole 16-byte pieces
+    assert probe(FAKE, 64, FAKE + 2, None) == -3      # out is written atomically
