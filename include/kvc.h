@@ -213,10 +213,11 @@ KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* m
  *                  kvc_block_workspace_bytes(c, block_tokens) bytes, 16-byte
  *                  aligned, that the caller keeps for this cache from call to
  *                  call (zero-filled before the first call). It holds each
- *                  block's key and the last threshold per (sequence, kv head);
- *                  a call recomputes only the keys of blocks whose candidates
- *                  changed since the length it recorded, and tries the previous
- *                  threshold before a full selection. A different block size or
+ *                  block's key, the last threshold and how many keys lie above
+ *                  and at it per (sequence, kv head); a call recomputes only the
+ *                  keys of blocks whose candidates changed since the length it
+ *                  recorded, updates those counts by them, and tries the
+ *                  previous threshold before a full selection. A different block size or
  *                  window, or a shorter sequence, rebuilds the state. With NULL
  *                  every call works from all scores. The mask is the one defined
  *                  above either way. The state assumes the scores below the
