@@ -801,81 +801,67 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
 }
 
 // ------------------------------------------------------------------ merge
-// One workgroup per (query head, kv head, sequence) merges the nsplit + 1
-// partials in index order: M = max_j m_j, w_j = 2^(m_j - M) (0 for empty
-// partials), out = sum_j w_j o_j / sum_j w_j l_j,
-// lse = ln 2 * (M + log2 sum_j w_j l_j). All loads are issued in parallel:
-// one (m, l) pair per thread, then D/4 float4 columns x 8 partial sums.
+// One wave per (query head, kv head, sequence) merges the partials in a fixed
+// order (outputs summed in index order): M = max_j m_j, w_j = 2^(m_j - M) (0 for empty partials),
+// out = sum_j w_j o_j / sum_j w_j l_j, lse = ln 2 * (M + log2 sum_j w_j l_j).
+// Lane l owns output channels [l*CPL, l*CPL + CPL); the (m, l) pairs and the
+// lane's slices of the first kPre partials are loaded together up front.
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void merge_kernel(AttnParams p) {
-  constexpr int NF = D / 4;       // float4 columns
-  constexpr int R = kThreads / NF;  // threads per column
+__global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
+  constexpr int CPL = D / 64;  // channels per lane
+  constexpr int kPre = 32;     // partials whose slices are loaded up front
+  typedef float fcpl __attribute__((ext_vector_type(CPL)));
   __shared__ float wts[kMaxParts];
-  __shared__ float red[kThreads / 64][2];
-  __shared__ float4v part_acc[kThreads];
   const int h = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lane = threadIdx.x;
   const int np = p.nsplit + 1;
   const float* parts = p.parts + ((size_t)b * p.hkv + kvh) * np * G * (2 + D) + (size_t)h * (2 + D);
   const size_t pstride = (size_t)G * (2 + D);
-  // this thread's first kPre float4 slices of the partial outputs, issued
-  // together with the (m, l) loads
-  constexpr int kPre = 128 / R;
-  float4v pre[kPre];
-  {
-    const int c4 = tid % NF, r = tid / NF;
+  fcpl pre[kPre];
 #pragma unroll
-    for (int i = 0; i < kPre; ++i) {
-      const int j = r + i * R;
-      const int jj = j < np ? j : np - 1;
-      pre[i] = *reinterpret_cast<const float4v*>(parts + jj * pstride + 2 + 4 * c4);
+  for (int j = 0; j < kPre; ++j) {
+    const int jj = j < np ? j : np - 1;
+    pre[j] = *reinterpret_cast<const fcpl*>(parts + jj * pstride + 2 + CPL * lane);
+  }
+  // (m, l) of partials lane, lane + 64, ...: at most kMaxParts / 64 per lane
+  constexpr int kML = kMaxParts / 64;
+  float mj[kML], lj[kML];
+#pragma unroll
+  for (int r = 0; r < kML; ++r) {
+    const int j = lane + 64 * r;
+    mj[r] = -INFINITY;
+    lj[r] = 0.0f;
+    if (j < np) {
+      const float2v ml = *reinterpret_cast<const float2v*>(parts + j * pstride);
+      mj[r] = ml[0];
+      lj[r] = ml[1];
     }
   }
-  float mj = -INFINITY, lj = 0.0f;
-  if (tid < np) {
-    const float2v ml = *reinterpret_cast<const float2v*>(parts + tid * pstride);
-    mj = ml[0];
-    lj = ml[1];
+  float M = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kML; ++r) M = fmaxf(M, mj[r]);
+  M = wave_max(M);
+  float den = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kML; ++r) {
+    const int j = lane + 64 * r;
+    const float w = (mj[r] == -INFINITY || M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj[r] - M);
+    den += w * lj[r];
+    if (j < np) wts[j] = w;
   }
-  float M = mj;
+  den = wave_sum(den);
+  __builtin_amdgcn_wave_barrier();  // one wave: its LDS writes are seen by its later reads
+  fcpl acc = {};
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if (lane == 0) red[wid][0] = M;
-  __syncthreads();
-  M = red[0][0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red[w][0]);
-  const float wj = (mj == -INFINITY || M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
-  if (tid < np) wts[tid] = wj;
-  float den = wj * lj;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
-  __syncthreads();
-  if (lane == 0) red[wid][1] = den;
-  __syncthreads();
-  den = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) den += red[w][1];
-  const int c4 = tid % NF, r = tid / NF;
-  float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int i = 0; i < kPre; ++i) {
-    const int j = r + i * R;
-    if (j < np) acc += wts[j] * pre[i];
-  }
+  for (int j = 0; j < kPre; ++j)
+    if (j < np) acc += wts[j] * pre[j];
   // every partial is written by the attention kernel, so no load is skipped
-  for (int j = r + kPre * R; j < np; j += R)
-    acc += wts[j] * *reinterpret_cast<const float4v*>(parts + j * pstride + 2 + 4 * c4);
-  part_acc[tid] = acc;
-  __syncthreads();
-  if (r == 0) {
-#pragma unroll
-    for (int q = 1; q < R; ++q) acc += part_acc[q * NF + c4];
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    const size_t oq = (size_t)b * p.hkv * G + kvh * G + h;
-    *reinterpret_cast<float4v*>(p.out + oq * D + 4 * c4) = acc * inv;
-    if (c4 == 0 && p.lse) p.lse[oq] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
-  }
+  for (int j = kPre; j < np; ++j)
+    acc += wts[j] * *reinterpret_cast<const fcpl*>(parts + j * pstride + 2 + CPL * lane);
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  const size_t oq = (size_t)b * p.hkv * G + kvh * G + h;
+  *reinterpret_cast<fcpl*>(p.out + oq * D + CPL * lane) = acc * inv;
+  if (lane == 0 && p.lse) p.lse[oq] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
 }
 
 // TIER: some pages live in the host tier (a separate pool in pinned host memory)
@@ -926,7 +912,7 @@ hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, hipStr
     if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false>), grid, dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((attention_kernel<D, G, false, false>), grid, dim3(kThreads), 0, s, p);
   }
-  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(G, c.num_kv_heads, c.batch), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(G, c.num_kv_heads, c.batch), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -941,7 +927,7 @@ hipError_t launch_merge(const float* parts, int parts_per_pair, int batch, int h
   p.batch = batch;
   p.out = out;
   p.lse = lse;
-  const dim3 grid(G, hkv, batch), block(kThreads);
+  const dim3 grid(G, hkv, batch), block(64);
   if (D == 128) {
     switch (G) {
       case 1: hipLaunchKernelGGL((merge_kernel<128, 1>), grid, block, 0, s, p); break;
