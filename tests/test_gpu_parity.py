@@ -291,6 +291,41 @@ def test_fused_append_refresh_matches_separate_calls(policy, protect):
         assert torch.equal(sa, sb), f"step {step}: refresh state differs"
 
 
+@pytest.mark.parametrize("batch", [40, 130])
+def test_fused_append_refresh_large_batches(batch):
+    """Large batches (320 and 1040 (sequence, kv head) pairs, more top-k
+    workgroups than one resident round): every buffer and the refresh state
+    must stay bit-identical to the separate calls, also at steps where all kv
+    heads of some sequences need the full refresh (a sequence appending
+    nothing)."""
+    m = kvc()
+    w = W.WORKLOADS["fullstep"].replace(name=f"fused_large_{batch}", batch=batch, layers=1, ctx=300,
+                                        decode_steps=12)
+    a, b = LayerCache(w), LayerCache(w)
+    sa, sb = a.refresh_state(), b.refresh_state()
+    lens = a.lengths.copy()
+    for step in range(12):
+        n_new = np.ones(w.batch, np.int32)
+        if step == 4:
+            n_new[1] = 0
+        if step == 7:
+            n_new[[0, batch - 1]] = 0
+        k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+        v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+        lens += n_new
+        nn = torch.from_numpy(n_new).cuda()
+        for lc in (a, b):
+            lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        m.kvc_quantize_append(a.cache, k_new, v_new, nn)
+        m.kvc_score_topk_mask(a.cache, a.mlp, k_new, v_new, nn, w.budget_permille, ws=sa)
+        m.kvc_append_score_topk_mask(b.cache, b.mlp, k_new, v_new, nn, w.budget_permille, ws=sb)
+        torch.cuda.synchronize()
+        for name in ("int4_codes", "int4_meta", "int8_codes", "int8_scales", "scores", "keep_mask"):
+            x, y = getattr(a.cache, name), getattr(b.cache, name)
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"step {step}: {name} differs"
+        assert torch.equal(sa, sb), f"step {step}: refresh state differs"
+
+
 def _decode_topk_run(w, steps, budgets, stall=None, mlp=None):
     """Decode steps with a top-k refresh state; the keep mask is checked
     against the oracle's top-k of the GPU's own scores after every step.
