@@ -57,6 +57,11 @@
  * nothing gets out = 0, lse = -inf. Scoring and refresh never run in one
  * launch in this configuration (the appended positions are candidates).
  *
+ * Besides the compressed cache, the library holds the uncompressed baseline
+ * the pages measure against (a dense bfloat16 paged cache, kvc_dense_cache,
+ * with kvc_dense_append and kvc_dense_decode_attention) and a streaming-read
+ * probe used as a measurement aid (kvc_stream_read_probe).
+ *
  * Conventions: every call is enqueued on the caller's stream and never
  * synchronises; argument errors are returned synchronously; kernels never
  * allocate; the library keeps no state besides a thread-local error string.
