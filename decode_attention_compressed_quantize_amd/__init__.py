@@ -123,6 +123,9 @@ _SIGNATURES = {
                                             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                             ctypes.c_void_p]),
+    "kvc_decode_attention_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                                    ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                                                    ctypes.c_void_p, ctypes.c_void_p]),
     "kvc_decode_attention_windowed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                                      ctypes.c_int, ctypes.c_int32, ctypes.c_float,
                                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -342,6 +345,17 @@ def kvc_decode_attention(cache: Cache, q, out, lse, ws, softmax_scale: float = 0
     _check(lib().kvc_decode_attention(cache.ref(), _ptr(q), _dtype_code(q), q.shape[1],
                                       float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), nbytes,
                                       _stream(stream)), "kvc_decode_attention")
+
+
+def kvc_decode_attention_noalloc(cache: Cache, q, out, lse, softmax_scale: float = 0.0, stream=None):
+    """kvc_decode_attention with the library's own per-GPU scratch instead of a workspace
+    (no device allocation; calls that overlap on one GPU race)."""
+    _check(lib().kvc_decode_attention_noalloc(cache.ref(), _ptr(q), _dtype_code(q), q.shape[1],
+                                              float(softmax_scale), _ptr(out), _ptr(lse),
+                                              _stream(stream)), "kvc_decode_attention_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def kvc_decode_attention_windowed(cache: Cache, int4_window: int, q, out, lse, ws,

@@ -1,8 +1,10 @@
 // libkvc host layer: argument validation, split planning, workspace sizing
 // and kernel launches behind the C ABI declared in include/kvc.h.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kvc_internal.h"
@@ -366,6 +368,64 @@ KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_d
                                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   return decode_attention(c, 0, q, q_dtype, num_q_heads, softmax_scale, out, lse, ws, ws_bytes,
                           stream);
+}
+
+// Scratch of the allocation-free attention entry point: one copy per GPU,
+// held by the loaded code object until the process ends. Host code never
+// uses this name as an address; it uses the per-device pointer that
+// hipGetSymbolAddress returned for it.
+static __device__ __align__(256) unsigned char scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; NULL on failure.
+void* scratch_ptr(kvc_status* st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *st = fail(KVC_E_LAUNCH, "no current HIP device (or device index above 63)");
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_error = std::string("hipGetSymbolAddress of the attention scratch failed: ") +
+                     hipGetErrorString(e);
+      *st = KVC_E_LAUNCH;
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+}  // namespace
+
+KVC_API kvc_status kvc_decode_attention_noalloc(const kvc_cache* c, const void* q,
+                                                kvc_dtype q_dtype, int32_t num_q_heads,
+                                                float softmax_scale, float* out, float* lse,
+                                                hipStream_t stream) {
+  kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8 | kNeedMask);
+  if (st != KVC_OK) return st;
+  const size_t need = kvc_attention_workspace_bytes(c, num_q_heads);
+  if (need > (size_t)KVC_NOALLOC_SCRATCH_BYTES) {
+    char msg[160];
+    std::snprintf(msg, sizeof msg,
+                  "this cache needs %zu bytes of attention scratch; the allocation-free entry point "
+                  "holds %d bytes (use kvc_decode_attention with a workspace)",
+                  need, KVC_NOALLOC_SCRATCH_BYTES);
+    return fail(KVC_E_WORKSPACE, msg);
+  }
+  void* ws = scratch_ptr(&st);
+  if (!ws) return st;
+  return decode_attention(c, 0, q, q_dtype, num_q_heads, softmax_scale, out, lse, ws,
+                          (size_t)KVC_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int4_window,

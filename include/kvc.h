@@ -293,6 +293,30 @@ KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int
                                                  hipStream_t stream);
 
 /*
+ * kvc_decode_attention_noalloc - kvc_decode_attention without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   The per-chunk partials go to a scratch array of KVC_NOALLOC_SCRATCH_BYTES
+ *   (16 MiB) that the library holds in device memory, one copy per GPU, from
+ *   when the library is loaded until the process ends; its address is looked
+ *   up on each device's first call (with that device current). The call
+ *   allocates nothing and frees nothing.
+ *   Arguments, results and errors as kvc_decode_attention (the same kernels
+ *   run); KVC_E_WORKSPACE when kvc_attention_workspace_bytes(c, num_q_heads)
+ *   exceeds KVC_NOALLOC_SCRATCH_BYTES (the caller then needs
+ *   kvc_decode_attention with a workspace of its own). The scratch needs no
+ *   clearing: every entry a call reads was written earlier in the same call.
+ *   All calls on one GPU share its scratch array, so calls that overlap in
+ *   time on one GPU (on different streams, or from different threads) race
+ *   and give unspecified results; calls ordered on one stream are safe.
+ */
+#define KVC_NOALLOC_SCRATCH_BYTES 16777216
+KVC_API kvc_status kvc_decode_attention_noalloc(const kvc_cache* c, const void* q,
+                                                kvc_dtype q_dtype, int32_t num_q_heads,
+                                                float softmax_scale, float* out, float* lse,
+                                                hipStream_t stream);
+
+/*
  * Host tier (temporal tiering). Source: TTKV promo page (arXiv 2604.19769),
  * strengths section: a temporal-tiered cache keeps hot data in HBM and cold
  * data in DRAM. Physical page ids [0, P) index the device pool (int4_codes,

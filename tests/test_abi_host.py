@@ -101,6 +101,19 @@ def test_attention_argument_errors(lib):
                                              FAKE, 16, None) == -4
 
 
+def test_noalloc_attention_argument_errors(lib):
+    """The allocation-free entry point validates like kvc_decode_attention and refuses
+    a cache whose partials exceed its fixed scratch, before any device work."""
+    na = lib.kvc_decode_attention_noalloc
+    assert na(None, FAKE, 0, 32, 0.0, FAKE, None, None) == -1
+    assert na(ctypes.byref(desc(head_dim=96)), FAKE, 0, 32, 0.0, FAKE, None, None) == -3
+    big = desc(batch=4096, max_ctx=1 << 20, max_pages_per_seq=1 << 16)
+    need = lib.kvc_attention_workspace_bytes(ctypes.byref(big), 32)
+    assert need > kvc.NOALLOC_SCRATCH_BYTES
+    assert na(ctypes.byref(big), FAKE, 0, 32, 0.0, FAKE, None, None) == -4
+    assert "scratch" in kvc.kvc_last_error()
+
+
 def test_append_and_topk_argument_errors(lib):
     c = desc()
     r = lib.kvc_quantize_append(ctypes.byref(c), FAKE, FAKE, 0, -1, FAKE, None)
