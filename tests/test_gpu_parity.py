@@ -92,6 +92,25 @@ def expected_keep4(w, lc, cpu, b, kvh, L):
     return policy_keep(w, s[start:start + n4])
 
 
+def fp64_mask_disagreements(w, keep4, s64_all, L):
+    """Compare a GPU token mask with the oracle's mask over float64 MLP scores.
+
+    The GPU ranks its float32 scores, so the two masks may differ only where
+    float32 rounding can reorder scores: every disagreeing position must lie
+    within 2e-4 of the k-th largest float64 score. Returns how many differ."""
+    start, n4 = regions.int4_range(L, *prot(w))
+    s64 = np.asarray(s64_all[start:start + n4], np.float64)
+    want64 = policy.topk_keep(s64, w.budget_permille)
+    diff = np.flatnonzero(keep4 != want64)
+    if diff.size:
+        k = policy.budget_k(n4, w.budget_permille)
+        kth = np.sort(s64)[::-1][k - 1]
+        far = diff[np.abs(s64[diff] - kth) > 2e-4]
+        assert far.size == 0, (f"{w.name} L={L}: {far.size} mask bits differ from the fp64-score "
+                               f"mask away from the k-th score {kth:.6g}, first at {far[:8] + start}")
+    return int(diff.size)
+
+
 def check_pair(w, lc, cpu, qn, out, lse, b, kvh):
     L = int(lc.lengths[b])
     G = w.group_size
@@ -110,6 +129,10 @@ def check_pair(w, lc, cpu, qn, out, lse, b, kvh):
         ref = policy.mlp_scores(k, v, lc.mlp_np[kvh])
         got = cpu["scores"][b, kvh, :L].astype(np.float64)
         assert np.abs(got - ref).max() <= 1e-4, f"scores b={b} h={kvh}"
+        if w.policy == "token":
+            n_dis = fp64_mask_disagreements(w, keep4, ref, L)
+            print(f"    {w.name} b={b} kvh={kvh}: {n_dis} mask bits differ from the fp64-score "
+                  f"mask (all within 2e-4 of the k-th score)", flush=True)
     hs = slice(kvh * G, (kvh + 1) * G)
     if L == 0:
         assert (out[b, hs] == 0).all() and np.isneginf(lse[b, hs]).all()
