@@ -482,6 +482,19 @@ def test_block_mask_special_scores(kind, block, window, budget):
     _block_mask_only(lengths, 2, scores, budget, block, window)
 
 
+def test_block_mean_float32_position_order():
+    """The block kernel sums each block's scores in float32 in position order,
+    like the oracle: [1e8, 1 x 15] averages to 6250000.0 there and loses to
+    [1e8, 8, 0 x 14] at 6250000.5 (float64 or pairwise sums would rank them
+    the other way), in either order of the two blocks."""
+    a = [1e8] + [1.0] * 15
+    b = [1e8, 8.0] + [0.0] * 14
+    scores = np.zeros((2, 1, 176), np.float32)
+    scores[0, 0, 16:48] = a + b
+    scores[1, 0, 16:48] = b + a
+    _block_mask_only([176, 176], 1, scores, 500, 16, 0)
+
+
 def test_block_mask_max_context():
     """The longest context the cache accepts, 16-token blocks (130559 of them)."""
     L = 2089088

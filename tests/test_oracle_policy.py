@@ -184,3 +184,30 @@ def test_block_policy_invariants():
         nb = (n4 + 15) // 16 - c0 // 16 if n4 > c0 else 0
         kept_blocks = sum(1 for j in range(c0 // 16, (n4 + 15) // 16) if keep[max(16 * j, c0)])
         assert kept_blocks == budget * nb // 1000
+
+
+def test_block_mean_is_float32_in_position_order():
+    """Pins the summation the block policy's reading fixes: a block's score is its
+    candidates' scores added one by one in position order in float32, then divided
+    by their count. Worked by hand (float32 has an ulp of 8 at 1e8, ties to even):
+
+      block 0 = [1e8, 1 x 15]:    1e8 + 1 rounds back to 1e8 every time -> sum 1e8,
+                                  mean 6250000.0 (the exact mean is 6250000.9375)
+      block 1 = [1e8, 8, 0 x 14]: 1e8 + 8 = 100000008 is exact -> mean 6250000.5
+
+    so keeping one of the two blocks keeps block 1. Summing in float64 would keep
+    block 0 (6250000.9375 > 6250000.5), and numpy's pairwise float32 mean gives
+    block 0 100000008 / 16 as well (a tie, which keeps the lower block 0): either
+    mistake flips the result.
+    """
+    a = [1e8] + [1.0] * 15
+    b = [1e8, 8.0] + [0.0] * 14
+    s = np.array(a + b, np.float32)
+    keep = policy.block_keep(s, 500, block=16)
+    assert not keep[:16].any() and keep[16:].all()
+    # the two other summations really do rank the blocks the other way round
+    assert np.float64(np.mean(np.array(a, np.float32))) == np.float64(np.mean(np.array(b, np.float32)))
+    assert math.fsum(a) / 16 > math.fsum(b) / 16
+    # with the blocks swapped the float32 reading still prefers the [1e8, 8, ...] block
+    keep = policy.block_keep(np.array(b + a, np.float32), 500, block=16)
+    assert keep[:16].all() and not keep[16:].any()
