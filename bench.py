@@ -544,6 +544,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >1 GiB between reuses")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pool", choices=["auto", "on", "off"], default="auto",
+                    help="kept-record pool (auto: on for the token top-k policy, whose refresh "
+                         "maintains it; the block policy and the host tier read through the mask)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -574,9 +577,15 @@ def main():
     print(f"bench: building {args.workload} ({len(base)} layer caches per replica)", file=sys.stderr, flush=True)
     tier = TIER_MODE.get(args.workload)
     host_moved = 0
+    def pooled(w):
+        if args.pool == "off" or tier:
+            return False
+        return w.policy == "token" and w.recency_window == 0 and w.mask in ("mlp", "scores", "all")
+
     for li, w in enumerate(base):
         host = W.page_table(w, li)[1] if tier else 0
-        lc = LayerCache(w, layer=li, device=dev, keep_sources=False, host_pages=host)
+        lc = LayerCache(w, layer=li, device=dev, keep_sources=False, host_pages=host,
+                        pool=pooled(w))
         if tier == "cold":
             host_moved += lc.demote_cold_pages()
         elif tier == "all":
@@ -713,6 +722,7 @@ def main():
             "batch": base[0].batch, "q_heads": base[0].q_heads, "kv_heads": base[0].kv_heads,
             "head_dim": base[0].head_dim, "context": int(base[0].lengths().max()),
             "replicas": replicas,
+            "kept_record_pool": bool(pooled(base[0])),
             "keep_policy": [(f"{w.policy}" + (f"{w.block_tokens}" if w.policy == "block" else "")
                              + (f", recency window {w.recency_window}" if w.recency_window else "")
                              + (f", budget {w.budget_permille / 10:g}%" if w.budget_permille else ""))

@@ -8,7 +8,8 @@ library has not been built.
 The functions mirror the C ABI in ``include/kvc.h``:
 ``kvc_quantize_append``, ``kvc_score_topk_mask``, ``kvc_append_score_topk_mask``,
 ``kvc_score_block_mask``, ``kvc_append_score_block_mask``, ``kvc_decode_attention``,
-``kvc_attention_workspace_bytes``, ``kvc_topk_workspace_bytes``,
+``kvc_attention_workspace_bytes``, ``kvc_topk_workspace_bytes``, ``kvc_pool_build``,
+``kvc_pool_bytes``, ``kvc_decode_attention_noalloc``,
 ``kvc_status_string``, ``kvc_last_error``, ``kvc_abi_version``, and for the dense
 bfloat16 baseline ``kvc_dense_append``, ``kvc_dense_decode_attention``,
 ``kvc_dense_attention_workspace_bytes``.
@@ -64,7 +65,19 @@ class KvcCacheStruct(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("int4_codes_host", ctypes.c_void_p),
         ("int4_meta_host", ctypes.c_void_p),
+        ("pool_capacity", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
+        ("pool", ctypes.c_void_p),
+        ("pool_slot", ctypes.c_void_p),
+        ("pool_header", ctypes.c_void_p),
+        ("errors", ctypes.c_void_p),
     ]
+
+
+# bits of the error word
+KVC_ERR_LENGTH = 1
+KVC_ERR_PAGE = 2
+KVC_ERR_POOL = 4
 
 
 class KvcDenseCacheStruct(ctypes.Structure):
@@ -141,6 +154,8 @@ _SIGNATURES = {
     "kvc_stream_read_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                              ctypes.c_void_p]),
     "kvc_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p, ctypes.c_int32]),
+    "kvc_pool_build": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "kvc_pool_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "kvc_topk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "kvc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvc_last_error": (ctypes.c_char_p, []),
@@ -200,11 +215,14 @@ class Cache:
     device tensors owned by the caller; ``seq_lens`` must hold the lengths
     after any append of the current step. ``protect=False`` builds the
     unprotected (pure KV4) cache: no INT8 side cache, n_sink = n_recent = 0.
+    ``pool_capacity`` > 0 (a multiple of 64) adds a kept-record pool of that
+    many records per (sequence, kv head); ``errors=True`` adds the error word.
     """
 
     def __init__(self, batch: int, kv_heads: int, head_dim: int, max_ctx: int,
                  num_phys_pages: int, block_table, seq_lens, device="cuda", with_scores=True,
-                 protect: bool = True, host_pages: int = 0):
+                 protect: bool = True, host_pages: int = 0, pool_capacity: int = 0,
+                 errors: bool = False):
         import torch
 
         self.batch, self.kv_heads, self.head_dim, self.max_ctx = batch, kv_heads, head_dim, max_ctx
@@ -233,6 +251,17 @@ class Cache:
                                               dtype=torch.int16, pin_memory=True)
         else:
             self.int4_codes_host = self.int4_meta_host = None
+        # optional kept-record pool: [B][Hkv][cap/32][40*D] bytes, slot map, headers
+        self.pool_capacity = pool_capacity
+        if pool_capacity > 0:
+            self.pool = torch.zeros((batch, kv_heads, pool_capacity // 32, 40 * D), dtype=torch.uint8,
+                                    device=dev)
+            self.pool_slot = torch.zeros((batch, kv_heads, max_ctx + pool_capacity), dtype=torch.int32,
+                                         device=dev)
+            self.pool_header = torch.zeros((batch, kv_heads, 4), dtype=torch.int32, device=dev)
+        else:
+            self.pool = self.pool_slot = self.pool_header = None
+        self.errors = torch.zeros(4, dtype=torch.int32, device=dev) if errors else None
         self.block_table = block_table
         self.seq_lens = seq_lens
         assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
@@ -241,14 +270,20 @@ class Cache:
             self.n_sink, self.n_recent, GROUP, max_ctx,
             _ptr(self.int4_codes), _ptr(self.int4_meta), _ptr(self.int8_codes),
             _ptr(self.int8_scales), _ptr(block_table), _ptr(seq_lens), _ptr(self.keep_mask),
-            _ptr(self.scores), host_pages, 0, _ptr(self.int4_codes_host), _ptr(self.int4_meta_host))
+            _ptr(self.scores), host_pages, 0, _ptr(self.int4_codes_host), _ptr(self.int4_meta_host),
+            pool_capacity, 0, _ptr(self.pool), _ptr(self.pool_slot), _ptr(self.pool_header),
+            _ptr(self.errors))
 
     def ref(self):
         return ctypes.byref(self.desc)
 
+    def error_bits(self) -> int:
+        """The error word (KVC_ERR_* bits); 0 when the cache has none."""
+        return 0 if self.errors is None else int(self.errors[0].item())
+
     def nbytes(self) -> int:
         ts = [self.int4_codes, self.int4_meta, self.int8_codes, self.int8_scales, self.keep_mask,
-              self.scores]
+              self.scores, self.pool, self.pool_slot, self.pool_header]
         ts = [t for t in ts if t is not None]
         return sum(t.numel() * t.element_size() for t in ts)
 
@@ -271,6 +306,15 @@ def kvc_attention_workspace_bytes(cache: Cache, num_q_heads: int) -> int:
 
 def kvc_topk_workspace_bytes(cache: Cache) -> int:
     return lib().kvc_topk_workspace_bytes(cache.ref())
+
+
+def kvc_pool_bytes(cache: Cache) -> int:
+    return int(lib().kvc_pool_bytes(cache.ref()))
+
+
+def kvc_pool_build(cache: Cache, stream=None):
+    """Rebuild the cache's kept-record pool from its keep mask (masks written by the caller)."""
+    _check(lib().kvc_pool_build(cache.ref(), _stream(stream)), "kvc_pool_build")
 
 
 def kvc_quantize_append(cache: Cache, k_new, v_new, n_new, stream=None):

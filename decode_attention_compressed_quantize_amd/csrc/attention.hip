@@ -7,45 +7,40 @@
 // protected region uses high-fidelity probability-value arithmetic, read here
 // as float32 P and float32 decoded V.
 //
-// Work decomposition: one workgroup (4 waves) per (sequence, kv head, INT4
-// chunk of `chunk` positions), plus one workgroup per (sequence, kv head) for
-// the INT8 region. Every workgroup writes one unnormalised partial
-// (m, l, o[D]) per query head: m is the max logit in log2 units
-// (logit * log2 e), l = sum 2^(s - m), o = sum 2^(s - m) * v. The merge
-// kernel combines the nsplit + 1 partials of each (sequence, kv head) in
-// index order, so results do not depend on scheduling.
+// Work decomposition: one workgroup (4 waves) per INT4 chunk and one per
+// (sequence, kv head) for the INT8 region. Every workgroup writes one
+// unnormalised partial (m, l, o[D]) per query head: m is the max logit in log2
+// units (logit * log2 e), l = sum 2^(s - m), o = sum 2^(s - m) * v. The merge
+// kernel combines the partials of each (sequence, kv head) in a fixed order,
+// so results do not depend on scheduling. The INT4 records come either from
+// the paged store through the keep mask (mask mode: chunk j of a (sequence,
+// kv head) is a range of positions whose kept records are gathered), or from
+// the kept-record pool (pool mode: chunk j is the j-th of nsplit equal shares
+// of that pool's record count, read as contiguous tiles).
 //
-// INT4 chunk, per wave (a quarter of the chunk):
-//  * The kept positions (keep-mask bits) are compacted into an LDS list of
-//    token-record indices, so evicted tokens cost no HBM reads: each lane
-//    loads one mask word and the block-table entries of its two pages, and a
-//    ballot scan of the lanes' popcounts gives each lane where its records go.
-//  * The list is walked in 32-token tiles, each as two steps: a K step (K
-//    codes and K meta) that writes the tile's logits to LDS, raises the
-//    running max per head and rescales the accumulators once, and a V step
-//    (V codes and V meta, whose line the K step has just brought into L2)
-//    that accumulates P.V with p = 2^(s - max). The steps form one stream
-//    behind a ring of kRing register tiles, so the loads of the next steps
-//    are in flight during each step's arithmetic.
-//  * Logits use v_mfma_f32_16x16x32_f16 with the raw codes: a nibble n becomes
-//    the fp16 value 1024 + n (or 1024 + 16n) by OR-ing it into 0x6400, which is
-//    exact; one MFMA row is one token, one column one (group, head) pair, and
-//    the query operand (q, zero outside the column's own group) makes
-//    each column accumulate exactly one group's dot product. The accumulators
-//    start at -sum(q) * 1024, so the offset cancels inside the MFMA; the
-//    per-group scale and min are then applied in float32:
-//      s = sum_g scale_g (q_g . c_g) + min_g sum(q_g)   (rows = tokens).
-//    The exponentials 2^(s - max) are taken once per (token, head) and left
-//    in LDS for the V step.
-//  * P.V uses the same MFMA with rows = (group, head) pairs, whose P operand
-//    is p * V_scale[token][group] in fp16, and columns = channels 8n + m read
-//    from V-code dword n; the codes enter as the exact fp16 subnormals
-//    c * 2^-24 or c * 2^-20 (one AND each, no offset). One more MFMA against
-//    a constant 1.0 operand sums the fp16 P operand per row, which centres the
-//    codes at 8: the fp16 rounding of P then weighs (c - 8) instead of c. Only
-//    rows whose group matches the column's channel group are kept. The side
-//    term sum_t p_t V_min + 8 p_t V_scale is accumulated in float32.
+// INT4 tile of 32 tokens, per wave, in two steps:
+//  * K step, logits on v_mfma_f32_16x16x32_f16. A code nibble enters as the
+//    exact fp16 subnormal c * 2^-24 (low nibble of a half) or c * 2^-20 (the
+//    next nibble), one AND per two values; one MFMA row is one token, one
+//    column one (group, head) pair, and the query operand (q scaled per head
+//    by a power of two into fp16's top binade, divided by 16 in the slots of
+//    second nibbles, zero outside the column's group) makes each column one
+//    group's dot product, exact up to float32 accumulation. A float32 query
+//    enters as two fp16 parts (two MFMAs). Scale and min are then applied in
+//    float32:  s = sum_g scale_g (q_g . c_g) + min_g sum(q_g).
+//    The group columns of a head are summed (rotations from the widest, so
+//    every column of a head holds the same bits), the running max per head
+//    rises when the tile's max does (then the accumulators are rescaled), and
+//    each lane takes p = 2^(s - max) of the eight (token, head) pairs its
+//    rows hold - exactly the P entries its lanes feed to the V step.
+//  * V step, P.V on the same MFMA: rows are (group, head) pairs, columns
+//    channels 8n + m of V-code dword n; the P operand is p * V_scale as two
+//    fp16 parts, the second scaled by 2^11 into its own accumulator (so
+//    probabilities far below fp16's range still count); codes enter as exact
+//    fp16 subnormals. Only rows whose group matches the column's channel
+//    group are kept. sum_t p_t V_min is accumulated in float32.
 #include "kvc_internal.h"
+#include "pool_layout.h"
 
 #include <type_traits>
 
@@ -54,11 +49,10 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr uint32_t kMagic = 0x64006400u;   // fp16 1024.0 in both halves
-constexpr uint32_t kOne = 0x3C003C00u;     // fp16 1.0 in both halves
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRing = 4;  // INT4 steps in flight per wave (the one in use plus three prefetched)
+constexpr int kRing = 4;      // INT4 steps in flight per wave (the one in use plus three prefetched)
+constexpr float kLoScale = 2048.0f;  // the second fp16 part of P, scaled up by 2^11
 static_assert(kRing % 2 == 0, "ring slots alternate between K and V steps");
 static_assert(kMaxChunk / kWaves <= 64 * 32, "the compaction gives each lane one mask word of a wave's range");
 
@@ -78,7 +72,7 @@ struct AttnParams {
   const int32_t* block_table;
   const int32_t* seq_lens;
   const uint32_t* mask;
-  float* parts;  // [B][Hkv][nsplit + 1][G][2 + D]
+  float* parts;
   float* out;
   float* lse;
   float alpha;  // softmax scale * log2(e)
@@ -96,7 +90,20 @@ struct AttnParams {
   const uint8_t* codes_h;  // host tier: pages [num_pages, num_pages + host_pages)
   const uint16_t* meta_h;
   int host_pages;
+  // pool mode
+  const uint8_t* pool;
+  const int32_t* pool_header;
+  int pool_cap;
+  uint32_t* errors;
 };
+
+__device__ inline void flag(const AttnParams& p, uint32_t bit) {
+  if (p.errors) __hip_atomic_fetch_or(p.errors, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline int clamp_len(const AttnParams& p, int L) {
+  return L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+}
 
 __device__ inline float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
@@ -112,15 +119,12 @@ __device__ inline uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2v));
 }
 
-__device__ inline float4v mfma16x16x32(half8 a, half8 b, float4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+__device__ inline float2v unpack_f16x2(uint32_t u) {
+  return __builtin_convertvector(__builtin_bit_cast(half2v, u), float2v);
 }
 
-// (x & m) | c in one VALU op: gfx950's three-input bitwise op with truth
-// table 0xEA (bit i of the table is f(a, b, c) for i = 4a + 2b + c).
-// Written out because the compiler emits a separate and + or otherwise.
-__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
-  return __builtin_amdgcn_bitop3_b32(x, m, c, 0xEA);
+__device__ inline float4v mfma16x16x32(half8 a, half8 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Rotate right by N lanes within each row of 16 lanes.
@@ -181,30 +185,30 @@ __device__ inline float load_q(const void* q, size_t off) {
   else return reinterpret_cast<const float*>(q)[off];
 }
 
+// 2^e as a float for -126 <= e <= 127.
+__device__ inline float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
 template <int D, int G>
 struct Shape {
   static constexpr int NG = D / 32;   // quantisation groups per row = QK MFMAs per 16 tokens
   static constexpr int SB = D / 8;    // K-code bytes held per lane slot
   static constexpr int VD = D / 8;    // V-code dwords per token
   static constexpr int NC = NG * G;   // distinct (group, head) columns, <= 16
+  static constexpr int MH = NG / 2;   // meta dwords per half row (mask mode staging)
 };
 
-// LDS of one workgroup. The INT4 path gives each wave its own region (kept
-// list, pass-1 logits - later reused for the wave's output -, and staging for
-// one tile of V codes and meta); the INT8 path overlays its own buffers.
+// LDS of one workgroup. Mask mode gives each wave its own region (kept list -
+// later reused for the wave's output - and staging for one step's V codes
+// and meta); pool mode needs only the outputs; the INT8 path overlays its own.
 template <int D, int G>
 struct Smem {
   static constexpr int kListCap = kMaxChunk / kWaves;  // positions per wave
-  // Row strides padded so that the 16-lane row groups of a wave fall into
-  // different LDS banks on the P.V operand reads.
-  static constexpr int kLgStride = 48;    // 32 logits + 16
-  static constexpr int kVStride = D / 8 + 4;
+  static constexpr int kVStride = D / 8 + 4;           // V-code row stride (dwords)
   struct Wave4 {
     union {
       uint32_t rec[kListCap + 32];        // token-record indices, padded with copies
       float o[G][D];                      // the wave's unnormalised output (after the list)
     } ro;
-    float logit[G][kLgStride];            // the current tile's logits / alpha, then p
     uint32_t vbuf[32][kVStride];          // V codes of the current 32 tokens
     uint32_t mbuf[32][D / 32];            // K or V (scale | min << 16) of the current 32 tokens
   };
@@ -214,9 +218,13 @@ struct Smem {
     float p[kWaves][36][G];
     float o[kWaves][G][D];
   };
+  // pool mode: each wave's ring of kStage tiles filled by direct-to-LDS loads;
+  // after its last tile the wave's output o[G][D] goes to the start of its ring
+  static constexpr int kStage = 15360 / (40 * D);
   union {
     Wave4 w4[kWaves];
     Int8 i8;
+    uint8_t stage[kWaves][kStage][40 * D];
   } u;
   float m[kWaves][G];
   float l[kWaves][G];
@@ -249,46 +257,40 @@ __device__ inline void store_partial(Smem<D, G>& sm, OF o_of, float* dst) {
   }
 }
 
-// ------------------------------------------------------------------ INT4 chunk
-// Per wave: compact the kept positions of its quarter of the chunk, then walk
-// them in 32-token tiles, each a K step (logits, running max, one rescale)
-// followed by a V step (P.V), with the next steps' loads in flight.
-template <int D, int G, bool QBF16, bool TIER>
-__device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, int split) {
+// ------------------------------------------------------------------ INT4 core
+// The per-wave state of the INT4 region and the two steps of a 32-token tile.
+// Lane (s, n), s = lane / 16, n = lane % 16: column n is (group gc, head hc);
+// the lane's C rows, and its P entries, are the tokens tok(i) = 4s + i
+// (i < 4) and 16 + 4s + (i - 4) (i >= 4) of the tile.
+template <int D, int G, bool QF32>
+struct Int4Core {
   using S = Shape<D, G>;
-  constexpr int NG = S::NG, VD = S::VD, NC = S::NC;
-  constexpr int MH = NG / 2;  // meta words per half row (K or V part)
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int s = lane >> 4;         // row slot
-  const int n = lane & 15;         // column
-  const int gc = (n / G) % NG;     // column's group
-  const int hc = n % G;            // column's head
-  const int tl = lane >> 1;        // token this lane stages (compact loads)
-  const int hf = lane & 1;         // which half of that token's row
-  auto& wv = sm.u.w4[wave];
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
-  const int slots = p.sink + p.recent;
-  const int n4 = L > slots ? L - slots : 0;
-  // INT4 region [r0, r1), or its last `window` positions; chunks start at
-  // base (0, or the window's start rounded down to 64 positions)
-  int r0 = p.sink, base = 0;
-  const int r1 = p.sink + n4;
-  if (p.window > 0 && r1 - p.window > r0) {
-    r0 = r1 - p.window;
-    base = r0 & ~63;
-  }
-  const int q4 = p.chunk / kWaves;
-  const int w0 = base + split * p.chunk + wave * q4;
-  const int lo = w0 > r0 ? w0 : r0;
-  const int hi = w0 + q4 < r1 ? w0 + q4 : r1;
+  static constexpr int NG = S::NG, VD = S::VD, NC = S::NC;
+  int lane, s, n, gc, hc, vdw;
+  float m_col, l_col, vm1;
+  float alpha_h;  // softmax scale * log2 e / 2^(e - 24) for the column's head
+  float qsp;      // sum of the column's group of q, times 2^(e - 24)
+  half8 bqh[NG];
+  half8 bql[QF32 ? NG : 1];
+  float4v acc[8], accl[8];
 
-  // The query entries this lane feeds to the QK product (code s*D/4 + 8m + perm[r]
-  // of its column's head), loaded first so their latency overlaps the compaction.
-  float qraw[NG][8];
-  {
-    // the lane's D/4 query entries are contiguous: a few 16-byte loads
+  __device__ int tok(int i) const { return i < 4 ? 4 * s + i : 16 + 4 * s + (i - 4); }
+
+  // Query operands of column (gc, hc): entries s*D/4 + 8m + perm[r] of the
+  // head (only the slot of group gc is non-zero), scaled by 2^e with e chosen
+  // per head so that the largest |q| lands in [2^14, 2^15).
+  template <bool QBF16>
+  __device__ void setup(const AttnParams& p, int b, int kvh) {
+    lane = threadIdx.x & 63;
+    s = lane >> 4;
+    n = lane & 15;
+    gc = (n / G) % NG;
+    hc = n % G;
+    vdw = n % VD;
+    m_col = -INFINITY;
+    l_col = vm1 = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = accl[m] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     constexpr int NE = D / 4;
     const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + hc) * D + s * NE;
     float qe[NE];
@@ -312,12 +314,244 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
         for (int k = 0; k < 4; ++k) qe[4 * i + k] = x[k];
       }
     }
+    // the head's largest magnitude (its D entries are spread over the four rows)
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) mx = fmaxf(mx, fabsf(qe[i]));
+    mx = rows_max(mx);
+    int e = 0;
+    if (mx > 0.0f) {
+      const int ex = (int)((__float_as_uint(mx) >> 23) & 255u) - 127;  // floor(log2 mx) for normal mx
+      e = 14 - ex;
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    }
+    const float qsc = exp2i(e);
+    alpha_h = p.alpha * exp2i(24 - e);
+    const int slot_group = (s * D / 4) / 32;
+    const bool active = slot_group == gc;
     const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    float qs = 0.0f;
 #pragma unroll
-    for (int m = 0; m < NG; ++m)
+    for (int m = 0; m < NG; ++m) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) qraw[m][r] = qe[8 * m + perm[r]];
+      for (int r = 0; r < 8; ++r) {
+        const bool x16 = (r == 2 || r == 3 || r == 6 || r == 7);
+        const float qv = active ? qe[8 * m + perm[r]] : 0.0f;
+        qs += qv;
+        const float v = qv * qsc * (x16 ? 0.0625f : 1.0f);  // powers of two: exact
+        const _Float16 hi = (_Float16)v;
+        bqh[m][r] = hi;
+        if constexpr (QF32) bql[m][r] = (_Float16)(v - (float)hi);
+      }
+    }
+    // every entry of the column's group sits in exactly one active slot
+    qsp = rows_sum(qs) * exp2i(e - 24);
   }
+
+  // K step: logits of the tile, running max, p of the lane's eight tokens.
+  // Tokens at or past lim are not attended (their logits are set to -inf).
+  __device__ void k_step(const uint32_t (&kc0)[NG], const uint32_t (&kc1)[NG], const uint32_t (&km)[8],
+                         int lim, float (&pr)[8]) {
+    float4v c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = c0;
+#pragma unroll
+    for (int m = 0; m < NG; ++m) {
+      uint32_t x = kc0[m];
+      uint32_t y = x >> 8;
+      half8 a = as_half8(x & 0x000F000Fu, x & 0x00F000F0u, y & 0x000F000Fu, y & 0x00F000F0u);
+      c0 = mfma16x16x32(a, bqh[m], c0);
+      if constexpr (QF32) c0 = mfma16x16x32(a, bql[m], c0);
+      x = kc1[m];
+      y = x >> 8;
+      a = as_half8(x & 0x000F000Fu, x & 0x00F000F0u, y & 0x000F000Fu, y & 0x00F000F0u);
+      c1 = mfma16x16x32(a, bqh[m], c1);
+      if constexpr (QF32) c1 = mfma16x16x32(a, bql[m], c1);
+    }
+    // u_g = scale_g (q_g . c_g) + min_g sum(q_g), both scaled by 2^(e - 24)
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float d = i < 4 ? c0[i] : c1[i - 4];
+      sv[i] = fmaf(h2f(km[i] & 0xFFFFu), d, fmaf(h2f(km[i] >> 16), qsp, 0.0f));
+    }
+    // sum the group columns of each head, widest rotation first: columns
+    // repeat with period NC, so each step adds a pair (x, y) on one lane and
+    // (y, x) on its partner, and every column of a head ends with equal bits
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (NC >= 8 * G) sv[i] += row_ror<4 * G>(sv[i]);
+      if constexpr (NC >= 4 * G) sv[i] += row_ror<2 * G>(sv[i]);
+      if constexpr (NC >= 2 * G) sv[i] += row_ror<G>(sv[i]);
+    }
+    if (lim < 32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (tok(i) >= lim) sv[i] = -INFINITY;
+    }
+    float tmax = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
+    const float mnew = fmaxf(m_col, alpha_h * rows_max(tmax));
+    if (__ballot(mnew > m_col) != 0) {
+      const float f = __builtin_amdgcn_exp2f(m_col - mnew);  // 0 on the first tile
+      l_col *= f;
+      vm1 *= f;
+      // accumulator row 4s + j belongs to head j % G (G divides 4); lane
+      // h < G has column (0, h), so it holds head h's factor
+      float fh[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        fh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), h));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float fj = fh[j % G];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          acc[m][j] *= fj;
+          accl[m][j] *= fj;
+        }
+      }
+      m_col = mnew;
+    }
+    const float mc = m_col == -INFINITY ? 0.0f : m_col;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(fmaf(alpha_h, sv[i], -mc));
+      lsum += pr[i];
+    }
+    l_col += lsum;
+  }
+
+  // V step: P.V of the tile. vm holds the V meta of group gc of the lane's
+  // tokens; for tokens at or past lim it is replaced by zeros (p is 0 there,
+  // and the stored meta of such a slot may be anything).
+  __device__ void v_step(const uint32_t (&vc)[8], const uint32_t (&vmi)[8], const float (&pr)[8],
+                         int lim) {
+    uint32_t vm[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vm[i] = vmi[i];
+    if (lim < 32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (tok(i) >= lim) vm[i] = 0u;
+    }
+    float ps[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ps[i] = fmaf(pr[i], h2f(vm[i] & 0xFFFFu), 0.0f);
+      vm1 = fmaf(pr[i], h2f(vm[i] >> 16), vm1);
+    }
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ph[k] = pack_f16x2(ps[2 * k], ps[2 * k + 1]);
+      const float2v hf = unpack_f16x2(ph[k]);
+      pl[k] = pack_f16x2(fmaf(hf[0], -kLoScale, ps[2 * k] * kLoScale),
+                         fmaf(hf[1], -kLoScale, ps[2 * k + 1] * kLoScale));
+    }
+    const half8 Ah = as_half8(ph[0], ph[1], ph[2], ph[3]);
+    const half8 Al = as_half8(pl[0], pl[1], pl[2], pl[3]);
+    // V codes of tokens (2q, 2q+1) paired into the halves of one dword
+    uint32_t xv[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xv[q] = __builtin_amdgcn_perm(vc[2 * q + 1], vc[2 * q], 0x05040100u);      // channels 0..3
+      xv[4 + q] = __builtin_amdgcn_perm(vc[2 * q + 1], vc[2 * q], 0x07060302u);  // channels 4..7
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      uint32_t bw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x = xv[(m / 4) * 4 + q];
+        const uint32_t y = (m & 2) ? x >> 8 : x;
+        bw[q] = y & ((m & 1) ? 0x00F000F0u : 0x000F000Fu);
+      }
+      const half8 B = as_half8(bw[0], bw[1], bw[2], bw[3]);
+      acc[m] = mfma16x16x32(Ah, B, acc[m]);
+      accl[m] = mfma16x16x32(Al, B, accl[m]);
+    }
+  }
+
+  // The wave's (m, l) per head and its output into LDS (o: [G][D]).
+  __device__ void finish(float (&msh)[G], float (&lsh)[G], float (&vmsh)[16], float* o, bool any) {
+    if (any) {
+      l_col = rows_sum(l_col);  // lane h < G: the sum over the tile rows of head h
+      vm1 = rows_sum(vm1);
+    }
+    if (lane < G) {
+      msh[lane] = any ? m_col : -INFINITY;  // lane h < G has column (0, h)
+      lsh[lane] = any ? l_col : 0.0f;
+    }
+    if (lane < 16) vmsh[lane] = vm1;  // side term of row (g, h) = lane g*G + h
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    if (!any) {
+      for (int i = lane; i < G * D; i += 64) o[i] = 0.0f;
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * s + j;
+      const int g = (row / G) % NG, h = row % G;
+      if (row < NC && g == n / 4 && n < VD) {
+        // channel 8n + m: sum p V_scale c, with c entering as c * 2^-24 (m even)
+        // or c * 2^-20 (m odd)
+        const float side = vmsh[g * G + h];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float v = fmaf(accl[m][j], 1.0f / kLoScale, acc[m][j]);
+          o[h * D + 8 * n + m] = fmaf(v, (m & 1) ? 1048576.0f : 16777216.0f, side);
+        }
+      }
+    }
+  }
+};
+
+// One step's loads: K step = K codes of tokens n and 16 + n (slot s) and meta;
+// V step = V codes and meta. Mask mode keeps them raw (meta and V codes are
+// transposed through LDS when the step runs); pool mode loads them in the
+// core's order (kc0 = w[0..NG), kc1 = w[4..4+NG), meta = w[8..16); V codes
+// = w[0..8), V meta = w[8..16)).
+struct Step {
+  uint32_t w[16];
+};
+
+// ------------------------------------------------------------------ INT4, mask mode
+// Per wave: compact the kept positions of its quarter of the chunk into an
+// LDS list of token-record indices, then walk them in 32-token tiles (a K step
+// then a V step each) behind a ring of kRing register steps.
+template <int D, int G, bool QBF16, bool TIER>
+__device__ void int4_mask_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, int split) {
+  using S = Shape<D, G>;
+  constexpr int NG = S::NG, MH = S::MH;
+  Int4Core<D, G, !QBF16> core;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int s = lane >> 4;
+  const int n = lane & 15;
+  const int tl = lane >> 1;  // token this lane stages (compact loads)
+  const int hf = lane & 1;   // which half of that token's row
+  auto& wv = sm.u.w4[wave];
+  int L = p.seq_lens[b];
+  if ((L < 0 || L > p.max_ctx) && lane == 0 && wave == 0 && split == 0) flag(p, KVC_ERR_LENGTH);
+  L = clamp_len(p, L);
+  const int slots = p.sink + p.recent;
+  const int n4 = L > slots ? L - slots : 0;
+  // INT4 region [r0, r1), or its last `window` positions; chunks start at
+  // base (0, or the window's start rounded down to 64 positions)
+  int r0 = p.sink, base = 0;
+  const int r1 = p.sink + n4;
+  if (p.window > 0 && r1 - p.window > r0) {
+    r0 = r1 - p.window;
+    base = r0 & ~63;
+  }
+  const int q4 = p.chunk / kWaves;
+  const int w0 = base + split * p.chunk + wave * q4;
+  const int lo = w0 > r0 ? w0 : r0;
+  const int hi = w0 + q4 < r1 ? w0 + q4 : r1;
+
+  core.template setup<QBF16>(p, b, kvh);
 
   // ---- compact the kept positions of this wave's range into an LDS list.
   // Lane l owns mask word l of the range (positions w0 + 32l .. + 31, at most
@@ -345,8 +579,10 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       if (to < 32) word &= (1u << to) - 1u;
     }
     const int lim = p.num_pages + p.host_pages;
-    if (pga < 0 || pga >= lim) word &= 0xFFFF0000u;
-    if (pgb < 0 || pgb >= lim) word &= 0x0000FFFFu;
+    bool bad = false;
+    if (pga < 0 || pga >= lim) { bad |= (word & 0x0000FFFFu) != 0; word &= 0xFFFF0000u; }
+    if (pgb < 0 || pgb >= lim) { bad |= (word & 0xFFFF0000u) != 0; word &= 0x0000FFFFu; }
+    if (__ballot(bad) != 0 && lane == 0) flag(p, KVC_ERR_PAGE);
     // exclusive prefix of the lanes' popcounts (each <= 32: six bit planes)
     const uint32_t pc = (uint32_t)__popc(word);
     int off = 0;
@@ -369,8 +605,7 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
   cnt = __builtin_amdgcn_readfirstlane(cnt);  // wave-uniform: keeps the main loop scalar
   // Pad the list with copies of its first entry to a whole number of ring
   // turns (kRing steps = kRing / 2 tiles), so the unrolled main loop needs no
-  // per-step guard: a guard there turns into divergent branches, across which
-  // the compiler can only drain every outstanding load. Padded tokens get p = 0.
+  // per-step guard; padded tokens are not attended (the steps' lim).
   constexpr int kTurn = 16 * kRing;  // tokens per ring turn
   const int padded = (cnt + kTurn - 1) / kTurn * kTurn;
   if (cnt > 0) {
@@ -378,41 +613,7 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
     for (int i = cnt + lane; i < padded; i += 64) list[i] = fill;
   }
 
-  // Per lane: m_col and l_col belong to head hc (the lane's column head),
-  // vm1/vm2 to accumulator row (gc, hc) of the P operand; acc holds P.V with
-  // rows (group, head) and columns channels, acc_one = sum of the fp16 P
-  // operand per row.
-  float m_col = -INFINITY, l_col = 0.0f, vm1 = 0.0f, vm2 = 0.0f;
-  float4v acc[8], acc_one = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = acc_one;
-
   if (cnt > 0) {
-    // ---- query operands: column (gc, hc) holds q for group gc only, divided
-    // by 16 in the k slots whose codes enter as 1024 + 16c (exact in fp16 for
-    // a bf16 query)
-    const int slot_group = (s * D / 4) / 32;
-    const bool active = slot_group == gc;
-    const float alpha = p.alpha;
-    half8 bq[NG];
-    float off = 0.0f, qs = 0.0f;
-#pragma unroll
-    for (int m = 0; m < NG; ++m) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const bool x16 = (r == 2 || r == 3 || r == 6 || r == 7);
-        const float qv = active ? qraw[m][r] : 0.0f;
-        qs += qv;
-        const _Float16 qh = (_Float16)(x16 ? qv * 0.0625f : qv);
-        bq[m][r] = qh;
-        off += (float)qh * 1024.0f;
-      }
-    }
-    // every code of the column's group sits in exactly one active slot
-    off = rows_sum(off);
-    qs = rows_sum(qs);
-    // QK accumulators start at -off, which removes the 1024 of every code
-    const float4v offv = {-off, -off, -off, -off};
     const uint8_t* kbase = p.codes + s * S::SB;
     // V pieces: 4 lanes per token at D = 128, 2 at D = 64, 16 bytes each
     const uint8_t* vbase = p.codes + D / 2 + (D == 128 ? 16 * (lane & 3) : 16 * (lane & 1));
@@ -438,19 +639,13 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
     const int ntile = padded >> 5;  // 32-token tiles
     const int nstep = 2 * ntile;    // K step, then V step, per tile; a multiple of kRing
 
-    // One stream of steps: step 2j brings K codes and K meta of tile j, step
-    // 2j + 1 the V codes and V meta of the same tokens. The V half of a token
-    // record shares the 128-byte line of its K half, so it is read from L2
-    // right after the K step brought the line in. Both kinds load the same
-    // registers with the same instructions (two loads of NG code dwords, one
-    // of MH meta dwords), so the ring never drains between them.
-    struct Tile {
-      uint32_t c[2 * NG];
-      uint32_t mh[MH];
-    };
-    // kind: true for a K step, false for a V step; steps past the end reload
-    // the last tile (L2 hits, results unused)
-    auto fetch = [&](auto kind, int step, Tile& t) {
+    // Step 2j brings K codes and K meta of tile j, step 2j + 1 the V codes and
+    // V meta of the same tokens. The V half of a token record shares the
+    // 128-byte line of its K half, so it is read from L2 right after the K
+    // step brought the line in. Both kinds load the same registers with the
+    // same instructions (two loads of code dwords, one of meta dwords), so the
+    // ring never drains between them. Steps past the end reload the last tile.
+    auto fetch = [&](auto kind, int step, Step& t) {
       constexpr bool isk = decltype(kind)::value;
       const int tile = step >> 1;
       const int it = 32 * (tile < ntile ? tile : ntile - 1);
@@ -476,179 +671,66 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
         const u32x4 y = *reinterpret_cast<const u32x4*>(a1);
         const u32x2 mm = *reinterpret_cast<const u32x2*>(am);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) { t.c[m] = x[m]; t.c[4 + m] = y[m]; }
-        t.mh[0] = mm[0];
-        t.mh[1] = mm[1];
+        for (int m = 0; m < 4; ++m) { t.w[m] = x[m]; t.w[4 + m] = y[m]; }
+        t.w[8] = mm[0];
+        t.w[9] = mm[1];
       } else if constexpr (isk) {
         const u32x2 x = *reinterpret_cast<const u32x2*>(a0);
         const u32x2 y = *reinterpret_cast<const u32x2*>(a1);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) { t.c[m] = x[m]; t.c[2 + m] = y[m]; }
-        t.mh[0] = *reinterpret_cast<const uint32_t*>(am);
+        for (int m = 0; m < 2; ++m) { t.w[m] = x[m]; t.w[4 + m] = y[m]; }
+        t.w[8] = *reinterpret_cast<const uint32_t*>(am);
       } else {
         const u32x4 x = *reinterpret_cast<const u32x4*>(a0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) t.c[m] = x[m];
-        t.mh[0] = *reinterpret_cast<const uint32_t*>(am);
+        for (int m = 0; m < 4; ++m) t.w[m] = x[m];
+        t.w[8] = *reinterpret_cast<const uint32_t*>(am);
       }
     };
 
-    // ---- K step: logits of 32 tokens, running max, rescale when it rises,
-    // then p = 2^(s - max) of every (token, head) once, into LDS
-    auto compute1 = [&](const Tile& t, int it) {
+    float pr[8];
+    // K step: stage the K meta, read the lane's eight (token, group gc) words
+    auto kstep = [&](const Step& t, int tile) {
 #pragma unroll
-      for (int m = 0; m < MH; ++m) wv.mbuf[tl][hf * MH + m] = t.mh[m];
+      for (int m = 0; m < MH; ++m) wv.mbuf[tl][hf * MH + m] = t.w[8 + m];
       __builtin_amdgcn_wave_barrier();
-      // QK: C[token][(g,h)] = q_g . c_g (codes taken as 1024 + c)
-      float4v c0 = offv, c1 = offv;
+      uint32_t kc0[NG], kc1[NG], km[8];
 #pragma unroll
-      for (int m = 0; m < NG; ++m) {
-        uint32_t x = t.c[m];
-        uint32_t y = x >> 8;
-        half8 a = as_half8(and_or(x, 0x000F000Fu, kMagic), and_or(x, 0x00F000F0u, kMagic),
-                           and_or(y, 0x000F000Fu, kMagic), and_or(y, 0x00F000F0u, kMagic));
-        c0 = mfma16x16x32(a, bq[m], c0);
-        x = t.c[NG + m];
-        y = x >> 8;
-        a = as_half8(and_or(x, 0x000F000Fu, kMagic), and_or(x, 0x00F000F0u, kMagic),
-                     and_or(y, 0x000F000Fu, kMagic), and_or(y, 0x00F000F0u, kMagic));
-        c1 = mfma16x16x32(a, bq[m], c1);
-      }
-      // u_g = scale_g (q_g . c_g) + min_g sum(q_g); the logit in log2 units is
-      // alpha * sum_g u_g, with alpha applied in the exponent below
-      float sv[8];
+      for (int m = 0; m < NG; ++m) { kc0[m] = t.w[m]; kc1[m] = t.w[4 + m]; }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = i < 4 ? 4 * s + i : 16 + 4 * s + (i - 4);
-        const uint32_t km = wv.mbuf[tok][gc];
-        const float d = i < 4 ? c0[i] : c1[i - 4];
-        sv[i] = fmaf(h2f(km & 0xFFFFu), d, fmaf(h2f(km >> 16), qs, 0.0f));
-      }
-      // sum the group columns of each head (columns h, h+G, h+2G, ... within a row)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (NC >= 2 * G) sv[i] += row_ror<G>(sv[i]);
-        if constexpr (NC >= 4 * G) sv[i] += row_ror<2 * G>(sv[i]);
-        if constexpr (NC >= 8 * G) sv[i] += row_ror<4 * G>(sv[i]);
-        if constexpr (NC >= 16 * G) sv[i] += row_ror<8 * G>(sv[i]);
-      }
-      // Padding tokens past cnt repeat list[0], whose logit tile 0 has already
-      // folded into the max, so they cannot raise it; they get p = 0 below.
-      float tmax = sv[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
-      if (n < G) {
-        const float4v lo4 = {sv[0], sv[1], sv[2], sv[3]};
-        const float4v hi4 = {sv[4], sv[5], sv[6], sv[7]};
-        *reinterpret_cast<float4v*>(&wv.logit[n][4 * s]) = lo4;
-        *reinterpret_cast<float4v*>(&wv.logit[n][16 + 4 * s]) = hi4;
-      }
-      // every tile holds at least one kept token, so the new max is finite
-      // (m_col is in log2 units, alpha > 0)
-      const float mnew = fmaxf(m_col, alpha * rows_max(tmax));
-      if (__ballot(mnew > m_col) != 0) {
-        const float f = __builtin_amdgcn_exp2f(m_col - mnew);  // 0 on the first tile
-        l_col *= f;
-        vm1 *= f;
-        vm2 *= f;
-        // accumulator row 4s + j belongs to head j % G (G divides 4); lane
-        // h < G has column (0, h), so it holds head h's factor
-        float fh[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          fh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), h));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float fj = fh[j % G];
-#pragma unroll
-          for (int m = 0; m < 8; ++m) acc[m][j] *= fj;
-          acc_one[j] *= fj;
-        }
-      }
-      m_col = mnew;
+      for (int i = 0; i < 8; ++i) km[i] = wv.mbuf[core.tok(i)][core.gc];
       __builtin_amdgcn_wave_barrier();
-      // p for (head hc, tokens of this lane): 2 per lane at G = 4, 1 at G = 2,
-      // 1 on half the lanes at G = 1
-      const int lim = cnt - it;  // tokens of this tile below lim are real
-      if constexpr (G == 4) {
-        const int k2 = 2 * (4 * s + n / 4);
-        float2v lg = *reinterpret_cast<const float2v*>(&wv.logit[hc][k2]);
-        lg[0] = k2 < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, lg[0], -m_col)) : 0.0f;
-        lg[1] = k2 + 1 < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, lg[1], -m_col)) : 0.0f;
-        l_col += lg[0] + lg[1];
-        *reinterpret_cast<float2v*>(&wv.logit[hc][k2]) = lg;
-      } else {
-        const int k = G == 2 ? 8 * s + n / 2 : 16 * s + n;
-        if (k < 32) {
-          const float pr = k < lim ? __builtin_amdgcn_exp2f(fmaf(alpha, wv.logit[hc][k], -m_col)) : 0.0f;
-          l_col += pr;
-          wv.logit[hc][k] = pr;
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
+      core.k_step(kc0, kc1, km, cnt - 32 * tile, pr);
     };
-
-    // ---- V step: P.V of the same 32 tokens. V codes enter the MFMA as the
-    // exact fp16 subnormals c * 2^-24 (low nibble of a half) and c * 2^-20
-    // (second nibble), so no offset has to be removed afterwards.
-    const int vdw = n % VD;
-    auto compute2 = [&](const Tile& t) {
+    // V step: stage V codes and meta, read the lane's eight dwords of each
+    auto vstep = [&](const Step& t, int tile) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         if constexpr (D == 128) {
-          wv.vbuf[lane >> 2][4 * (lane & 3) + m] = t.c[m];
-          wv.vbuf[16 + (lane >> 2)][4 * (lane & 3) + m] = t.c[4 + m];
+          wv.vbuf[lane >> 2][4 * (lane & 3) + m] = t.w[m];
+          wv.vbuf[16 + (lane >> 2)][4 * (lane & 3) + m] = t.w[4 + m];
         } else {
-          wv.vbuf[lane >> 1][4 * (lane & 1) + m] = t.c[m];
+          wv.vbuf[lane >> 1][4 * (lane & 1) + m] = t.w[m];
         }
       }
 #pragma unroll
-      for (int m = 0; m < MH; ++m) wv.mbuf[tl][hf * MH + m] = t.mh[m];
+      for (int m = 0; m < MH; ++m) wv.mbuf[tl][hf * MH + m] = t.w[8 + m];
       __builtin_amdgcn_wave_barrier();
-      const float4v pv0 = *reinterpret_cast<const float4v*>(&wv.logit[hc][4 * s]);
-      const float4v pv1 = *reinterpret_cast<const float4v*>(&wv.logit[hc][16 + 4 * s]);
-      uint32_t vd[8];
-      float pp[8];
+      uint32_t vc[8], vm[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int tok = i < 4 ? 4 * s + i : 16 + 4 * s + (i - 4);
-        vd[i] = wv.vbuf[tok][vdw];
-        const uint32_t vmeta = wv.mbuf[tok][gc];
-        const float pr = i < 4 ? pv0[i] : pv1[i - 4];
-        const float ps = fmaf(pr, h2f(vmeta & 0xFFFFu), 0.0f);
-        vm1 = fmaf(pr, h2f(vmeta >> 16), vm1);
-        vm2 += ps;
-        pp[i] = ps;
+        vc[i] = wv.vbuf[core.tok(i)][core.vdw];
+        vm[i] = wv.mbuf[core.tok(i)][core.gc];
       }
-      const half8 A = as_half8(pack_f16x2(pp[0], pp[1]), pack_f16x2(pp[2], pp[3]),
-                               pack_f16x2(pp[4], pp[5]), pack_f16x2(pp[6], pp[7]));
-      // V codes of tokens (2q, 2q+1) paired into the halves of one dword
-      uint32_t xv[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        xv[q] = __builtin_amdgcn_perm(vd[2 * q + 1], vd[2 * q], 0x05040100u);      // channels 0..3
-        xv[4 + q] = __builtin_amdgcn_perm(vd[2 * q + 1], vd[2 * q], 0x07060302u);  // channels 4..7
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        uint32_t bw[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t x = xv[(m / 4) * 4 + q];
-          const uint32_t y = (m & 2) ? x >> 8 : x;
-          bw[q] = y & ((m & 1) ? 0x00F000F0u : 0x000F000Fu);
-        }
-        acc[m] = mfma16x16x32(A, as_half8(bw[0], bw[1], bw[2], bw[3]), acc[m]);
-      }
-      acc_one = mfma16x16x32(A, as_half8(kOne, kOne, kOne, kOne), acc_one);
       __builtin_amdgcn_wave_barrier();
+      core.v_step(vc, vm, pr, cnt - 32 * tile);
     };
 
     // slot j of the ring always holds a step of parity j, so every unrolled
     // slot knows its kind at compile time
     using KStep = std::integral_constant<bool, true>;
     using VStep = std::integral_constant<bool, false>;
-    Tile ring[kRing];
+    Step ring[kRing];
 #pragma unroll
     for (int j = 0; j < kRing - 1; ++j) {
       if (j % 2 == 0) fetch(KStep{}, j, ring[j]);
@@ -659,46 +741,159 @@ __device__ void int4_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, 
       for (int j = 0; j < kRing; ++j) {
         if ((j + kRing - 1) % 2 == 0) fetch(KStep{}, step + j + kRing - 1, ring[(j + kRing - 1) % kRing]);
         else fetch(VStep{}, step + j + kRing - 1, ring[(j + kRing - 1) % kRing]);
-        if (j % 2 == 0) compute1(ring[j], 16 * (step + j));
-        else compute2(ring[j]);
+        if (j % 2 == 0) kstep(ring[j], (step + j) >> 1);
+        else vstep(ring[j], (step + j) >> 1);
       }
     }
-    // l: sum over the lanes of each head (all rows, columns h, h+G, ...)
-    l_col = rows_sum(l_col);
-    if constexpr (G < 16) l_col += row_ror<G>(l_col);
-    if constexpr (2 * G < 16) l_col += row_ror<2 * G>(l_col);
-    if constexpr (4 * G < 16) l_col += row_ror<4 * G>(l_col);
-    if constexpr (8 * G < 16) l_col += row_ror<8 * G>(l_col);
-    vm1 = rows_sum(vm1);
-    vm2 = rows_sum(vm2);
   }
+  core.finish(sm.m[wave], sm.l[wave], sm.vm[wave], &wv.ro.o[0][0], cnt > 0);
+}
 
-  // ---- this wave's (m, l, o) into LDS (o reuses the list area)
-  if (lane < G) {
-    sm.m[wave][lane] = m_col;  // lane h < G has column (0, h)
-    sm.l[wave][lane] = l_col;
+// ------------------------------------------------------------------ INT4, pool mode
+// Reads one staged tile of the lane's pieces from LDS: K codes of tokens n and
+// 16 + n (slot s), then for each half h of the lane's eight tokens the K meta
+// of group gc, the V-code dword vdw and the V meta of group gc. The wait for
+// the tile's direct-to-LDS loads (all but the VMC issued after it) and the LDS
+// reads' own completion are inside the one asm block, so no read is in flight
+// when it ends; LDS reads of the compiler's would make it wait for every
+// outstanding direct-to-LDS load instead.
+template <int D, int VMC>
+__device__ inline void read_staged(uint32_t lds, uint32_t o_kc, uint32_t o_km, uint32_t o_vc,
+                                   uint32_t o_vm, u32x4 (&r)[8]) {
+  constexpr int NG = D / 32, VD = D / 8;
+  constexpr int KMH = 4 * NG * 16, VCH = 4 * VD * 16;  // byte offset of the second half
+  if constexpr (D == 128) {
+    asm volatile(
+        "s_waitcnt vmcnt(%8)\n\t"
+        "ds_read_b128 %0, %9\n\t"
+        "ds_read_b128 %1, %9 offset:1024\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %10 offset:%11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %12 offset:%13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %14 offset:%11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7])
+        : "n"(VMC), "v"(lds + o_kc), "v"(lds + o_km), "n"(KMH), "v"(lds + o_vc), "n"(VCH),
+          "v"(lds + o_vm)
+        : "memory");
+  } else {
+    u32x2 k0, k1;
+    asm volatile(
+        "s_waitcnt vmcnt(%8)\n\t"
+        "ds_read_b64 %0, %9\n\t"
+        "ds_read_b64 %1, %9 offset:512\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %10 offset:%11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %12 offset:%13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %14 offset:%11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k0), "=&v"(k1), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7])
+        : "n"(VMC), "v"(lds + o_kc), "v"(lds + o_km), "n"(KMH), "v"(lds + o_vc), "n"(VCH),
+          "v"(lds + o_vm)
+        : "memory");
+    r[0] = u32x4{k0[0], k0[1], 0u, 0u};
+    r[1] = u32x4{k1[0], k1[1], 0u, 0u};
   }
-  // side term of row (g, h): sum_t p (V_min + 8 V_scale)
-  if (lane < 16) sm.vm[wave][lane] = fmaf(8.0f, vm2, vm1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
+}
+
+// Chunk `split` of the pool of (b, kvh): records [r0, r1), the split-th of
+// nsplit equal shares (whole 32-record tiles) of the pool's count. Tile
+// t0 + wave + 4j goes to wave `wave` (the four waves read neighbouring tiles
+// at any time). Each wave streams its tiles through a ring of kStage LDS
+// buffers filled by direct-to-LDS loads (one 16-byte piece per lane per
+// instruction, whole contiguous tiles), so kStage tiles are in flight per
+// wave without holding registers; a tile's pieces then come out of LDS in
+// the order the core consumes them. The pool header load is issued before
+// the query's, so both are in flight together.
+template <int D, int G, bool QBF16>
+__device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, int split) {
+  using S = Shape<D, G>;
+  constexpr int NG = S::NG, VD = S::VD;
+  constexpr int TILE = 40 * D, KM = 16 * D, VC = 20 * D, VM = 36 * D;
+  constexpr int NB = Smem<D, G>::kStage;
+  // direct-to-LDS loads per tile and wave: 1 KB pieces (16 bytes a lane), then
+  // 256-byte pieces (4 bytes a lane) for the rest of a D = 64 tile
+  constexpr int NL16 = TILE / 1024, NL4 = (TILE % 1024) / 256, NL = NL16 + NL4;
+  Int4Core<D, G, !QBF16> core;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int pair = b * p.hkv + kvh;
+  const u32x4 hdr = *reinterpret_cast<const u32x4*>(p.pool_header + 4 * (size_t)pair);
+  const int L = p.seq_lens[b];
+  core.template setup<QBF16>(p, b, kvh);
+  int cnt = 0;
+  if (hdr[2] == kPoolMagic) {
+    cnt = (int)hdr[0];
+    cnt = cnt < 0 ? 0 : (cnt > p.pool_cap ? p.pool_cap : cnt);
+  }
+  // the pool must describe the current length (reported once per pair)
+  if (split == 0 && threadIdx.x == 0 && (hdr[2] != kPoolMagic || (int)hdr[1] != clamp_len(p, L)))
+    flag(p, KVC_ERR_POOL);
+  const int share = ((cnt + p.nsplit - 1) / p.nsplit + kPoolTile - 1) / kPoolTile * kPoolTile;
+  const int r0 = split * share;
+  const int r1 = r0 + share < cnt ? r0 + share : cnt;
+  const int t0 = r0 / kPoolTile;
+  const int ntiles = r1 > r0 ? (r1 - r0 + kPoolTile - 1) / kPoolTile : 0;
+  const int ntw = __builtin_amdgcn_readfirstlane(ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0);
+  if (ntw > 0) {
+    const uint8_t* base = p.pool + (size_t)pair * pool_pair_bytes(D, p.pool_cap);
+    const int s = lane >> 4;
+    const uint32_t o_kc = (uint32_t)lane * S::SB;
+    const uint32_t o_km = KM + (s * NG + core.gc) * 16;
+    const uint32_t o_vc = VC + (s * VD + core.vdw) * 16;
+    const uint32_t o_vm = VM + (s * NG + core.gc) * 16;
+    uint8_t* ring = &sm.u.stage[wave][0][0];
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+    // direct-to-LDS loads of tile jt of this wave (past its last tile: the last again)
+    auto issue = [&](int jt, int k) {
+      const uint8_t* src = base + (size_t)(t0 + wave + kWaves * (jt < ntw ? jt : ntw - 1)) * TILE;
+      uint8_t* dst = ring + k * TILE;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 4 * s + j;
-    const int g = (row / G) % NG, h = row % G;
-    const bool ok = row < NC && g == n / 4 && n < VD && cnt > 0;
-    if (ok) {
-      // channel 8n + m: sum p V_scale c, with c entering as c * 2^-24 (m even)
-      // or c * 2^-20 (m odd); minus 8 sum p V_scale re-centres the codes
-      const float side = sm.vm[wave][g * G + h] - 8.0f * acc_one[j];
+      for (int i = 0; i < NL16; ++i)
+        __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
+                                         (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
-        wv.ro.o[h][8 * n + m] = fmaf(acc[m][j], (m & 1) ? 1048576.0f : 16777216.0f, side);
+      for (int i = 0; i < NL4; ++i)
+        __builtin_amdgcn_global_load_lds(src + NL16 * 1024 + i * 256 + lane * 4,
+                                         (__attribute__((address_space(3))) void*)(dst + NL16 * 1024 + i * 256),
+                                         4, 0, 0);
+    };
+#pragma unroll
+    for (int k = 0; k < NB; ++k) issue(k, k);
+    float pr[8];
+    for (int jt0 = 0; jt0 < ntw; jt0 += NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int jt = jt0 + k;
+        if (jt >= ntw) break;
+        u32x4 r[8];
+        read_staged<D, NL * (NB - 1)>(ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
+        issue(jt + NB, k);
+        const int lim = r1 - 32 * (t0 + wave + kWaves * jt);
+        uint32_t kc0[NG], kc1[NG], km[8], vc[8], vm[8];
+#pragma unroll
+        for (int m = 0; m < NG; ++m) { kc0[m] = r[0][m]; kc1[m] = r[1][m]; }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          km[i] = r[2][i]; km[4 + i] = r[3][i];
+          vc[i] = r[4][i]; vc[4 + i] = r[5][i];
+          vm[i] = r[6][i]; vm[4 + i] = r[7][i];
+        }
+        core.k_step(kc0, kc1, km, lim, pr);
+        core.v_step(vc, vm, pr, lim);
+      }
     }
   }
-  if (cnt == 0) {
-    for (int i = lane; i < G * D; i += 64) wv.ro.o[i / D][i % D] = 0.0f;
-  }
+  // the wave's output goes to the start of its own ring (its loads are done first)
+  __builtin_amdgcn_s_waitcnt(0);
+  core.finish(sm.m[wave], sm.l[wave], sm.vm[wave], reinterpret_cast<float*>(&sm.u.stage[wave][0][0]),
+              ntw > 0);
 }
 
 // ------------------------------------------------------------------ INT8 region
@@ -736,7 +931,8 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
     sm.u.i8.q[h][d] = load_q<QBF16>(p.q, ((size_t)b * p.hkv * G + kvh * G + h) * D + d) * p.alpha;
   }
   int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
+  if ((L < 0 || L > p.max_ctx) && threadIdx.x == 0) flag(p, KVC_ERR_LENGTH);
+  L = clamp_len(p, L);
   const int nvalid = L < slots ? L : slots;
   const int cntw = nvalid - wave * 36 < 0 ? 0 : (nvalid - wave * 36 > 36 ? 36 : nvalid - wave * 36);
   const bool valid = lane < cntw;
@@ -768,15 +964,16 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
     m[h] = mx;
     const float pr = valid ? __builtin_amdgcn_exp2f(s[h] - mx) : 0.0f;
     l[h] = wave_sum(pr);
-    if (lane < 36) sm.u.i8.p[wave][lane][h] = pr * sc[1];
+    // slots past cntw hold whatever the buffer holds: their weight is exactly 0
+    if (lane < 36) sm.u.i8.p[wave][lane][h] = valid ? pr * sc[1] : 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
   }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
-  // P.V over all 36 slots of the wave: slots past cntw have p = 0 (their
-  // codes are whatever the buffer holds, always finite), so the loop has a
-  // fixed trip count and its LDS reads can be issued together
+  // P.V over all 36 slots of the wave: slots past cntw have weight 0 and
+  // codes that are finite integers whatever the buffer holds, so the loop has
+  // a fixed trip count and its LDS reads can be issued together
 #pragma unroll 12
   for (int j = 0; j < 36; ++j) {
     float pj[G];
@@ -801,8 +998,9 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
 }
 
 // ------------------------------------------------------------------ merge
-// One wave per (query head, kv head, sequence) merges the partials in a fixed
-// order (outputs summed in index order): M = max_j m_j, w_j = 2^(m_j - M) (0 for empty partials),
+// One wave per (query head, kv head, sequence) merges the nsplit + 1 partials
+// of its (sequence, kv head) in a fixed order (outputs summed in index
+// order): M = max_j m_j, w_j = 2^(m_j - M) (0 for empty partials),
 // out = sum_j w_j o_j / sum_j w_j l_j, lse = ln 2 * (M + log2 sum_j w_j l_j).
 // Lane l owns output channels [l*CPL, l*CPL + CPL); the (m, l) pairs and the
 // lane's slices of the first kPre partials are loaded together up front.
@@ -815,13 +1013,14 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
   const int h = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int np = p.nsplit + 1;
-  const float* parts = p.parts + ((size_t)b * p.hkv + kvh) * np * G * (2 + D) + (size_t)h * (2 + D);
   const size_t pstride = (size_t)G * (2 + D);
+  const float* run = p.parts + ((size_t)b * p.hkv + kvh) * np * pstride + (size_t)h * (2 + D);
+  auto part = [&](int j) -> const float* { return run + (size_t)j * pstride; };
   fcpl pre[kPre];
 #pragma unroll
   for (int j = 0; j < kPre; ++j) {
     const int jj = j < np ? j : np - 1;
-    pre[j] = *reinterpret_cast<const fcpl*>(parts + jj * pstride + 2 + CPL * lane);
+    pre[j] = *reinterpret_cast<const fcpl*>(part(jj) + 2 + CPL * lane);
   }
   // (m, l) of partials lane, lane + 64, ...: at most kMaxParts / 64 per lane
   constexpr int kML = kMaxParts / 64;
@@ -832,7 +1031,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
     mj[r] = -INFINITY;
     lj[r] = 0.0f;
     if (j < np) {
-      const float2v ml = *reinterpret_cast<const float2v*>(parts + j * pstride);
+      const float2v ml = *reinterpret_cast<const float2v*>(part(j));
       mj[r] = ml[0];
       lj[r] = ml[1];
     }
@@ -856,16 +1055,16 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
   for (int j = 0; j < kPre; ++j)
     if (j < np) acc += wts[j] * pre[j];
   // every partial is written by the attention kernel, so no load is skipped
-  for (int j = kPre; j < np; ++j)
-    acc += wts[j] * *reinterpret_cast<const fcpl*>(parts + j * pstride + 2 + CPL * lane);
+  for (int j = kPre; j < np; ++j) acc += wts[j] * *reinterpret_cast<const fcpl*>(part(j) + 2 + CPL * lane);
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   const size_t oq = (size_t)b * p.hkv * G + kvh * G + h;
   *reinterpret_cast<fcpl*>(p.out + oq * D + CPL * lane) = acc * inv;
   if (lane == 0 && p.lse) p.lse[oq] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
 }
 
-// TIER: some pages live in the host tier (a separate pool in pinned host memory)
-template <int D, int G, bool QBF16, bool TIER>
+// TIER: some pages live in the host tier (a separate pool in pinned host memory).
+// POOL: the INT4 records come from the kept-record pool.
+template <int D, int G, bool QBF16, bool TIER, bool POOL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
   __shared__ Smem<D, G> sm;
   // One-dimensional grid, dispatched in index order and spread round-robin
@@ -892,9 +1091,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int np = p.nsplit + 1;
   float* dst = p.parts + (((size_t)b * p.hkv + kvh) * np + split) * G * (2 + D);
   if (split < p.nsplit) {
-    int4_chunk<D, G, QBF16, TIER>(p, sm, b, kvh, split);
-    __syncthreads();
-    store_partial<D, G>(sm, [&](int w) { return &sm.u.w4[w].ro.o[0][0]; }, dst);
+    if constexpr (POOL) {
+      int4_pool_chunk<D, G, QBF16>(p, sm, b, kvh, split);
+      __syncthreads();
+      store_partial<D, G>(sm, [&](int w) { return reinterpret_cast<float*>(&sm.u.stage[w][0][0]); }, dst);
+    } else {
+      int4_mask_chunk<D, G, QBF16, TIER>(p, sm, b, kvh, split);
+      __syncthreads();
+      store_partial<D, G>(sm, [&](int w) { return &sm.u.w4[w].ro.o[0][0]; }, dst);
+    }
   } else {
     int8_region<D, G, QBF16>(p, sm, b, kvh);
     __syncthreads();
@@ -903,14 +1108,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 template <int D, int G>
-hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, hipStream_t s) {
+hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, bool pool, hipStream_t s) {
   const dim3 grid((unsigned)(p.nsplit + 1) * c.num_kv_heads * c.batch);
-  if (p.host_pages > 0) {
-    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((attention_kernel<D, G, false, true>), grid, dim3(kThreads), 0, s, p);
+  if (pool) {
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, false, true>), grid, dim3(kThreads), 0, s, p);
+  } else if (p.host_pages > 0) {
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, true, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, true, false>), grid, dim3(kThreads), 0, s, p);
   } else {
-    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((attention_kernel<D, G, false, false>), grid, dim3(kThreads), 0, s, p);
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, false, false>), grid, dim3(kThreads), 0, s, p);
   }
   hipLaunchKernelGGL((merge_kernel<D, G>), dim3(G, c.num_kv_heads, c.batch), dim3(64), 0, s, p);
   return hipGetLastError();
@@ -949,7 +1157,7 @@ hipError_t launch_merge(const float* parts, int parts_per_pair, int batch, int h
 hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype, int num_q_heads,
                             float softmax_scale, float* out, float* lse, float* ws,
                             const AttnPlan& plan, int window, hipStream_t s) {
-  AttnParams p;
+  AttnParams p{};
   p.window = window;
   p.sink = c.n_sink;
   p.recent = c.n_recent;
@@ -977,19 +1185,26 @@ hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype
   p.chunk = plan.chunk;
   p.nsplit = plan.nsplit;
   p.int8_first = plan.int8_first;
+  p.errors = c.errors;
   const int G = num_q_heads / c.num_kv_heads;
+  if (plan.pool) {
+    p.pool = c.pool;
+    p.pool_header = c.pool_header;
+    p.pool_cap = c.pool_capacity;
+  }
   const bool bf = q_dtype == KVC_BF16;
+  const bool pool = plan.pool != 0;
   if (c.head_dim == 128) {
     switch (G) {
-      case 1: return launch_dq<128, 1>(c, p, bf, s);
-      case 2: return launch_dq<128, 2>(c, p, bf, s);
-      case 4: return launch_dq<128, 4>(c, p, bf, s);
+      case 1: return launch_dq<128, 1>(c, p, bf, pool, s);
+      case 2: return launch_dq<128, 2>(c, p, bf, pool, s);
+      case 4: return launch_dq<128, 4>(c, p, bf, pool, s);
     }
   } else {
     switch (G) {
-      case 1: return launch_dq<64, 1>(c, p, bf, s);
-      case 2: return launch_dq<64, 2>(c, p, bf, s);
-      case 4: return launch_dq<64, 4>(c, p, bf, s);
+      case 1: return launch_dq<64, 1>(c, p, bf, pool, s);
+      case 2: return launch_dq<64, 2>(c, p, bf, pool, s);
+      case 4: return launch_dq<64, 4>(c, p, bf, pool, s);
     }
   }
   return hipErrorInvalidValue;

@@ -54,9 +54,33 @@ kvc_status check_cache(const kvc_cache* c, unsigned need) {
   if ((long long)c->num_phys_pages + c->num_host_pages > (long long)0x7FFFFFFF / c->num_kv_heads / kvc::kPage)
     return fail(KVC_E_SHAPE, "too many pages");
   const void* ptrs[] = {c->int4_codes, c->int4_meta, c->int8_codes, c->int8_scales, c->keep_mask,
-                        c->scores, c->int4_codes_host, c->int4_meta_host};
+                        c->scores, c->int4_codes_host, c->int4_meta_host, c->pool, c->pool_header};
   for (const void* q : ptrs)
     if (misaligned(q)) return fail(KVC_E_UNSUPPORTED, "cache arrays must be 16-byte aligned");
+  if (c->pool_capacity < 0 || c->pool_capacity % 64)
+    return fail(KVC_E_SHAPE, "pool_capacity must be 0 or a positive multiple of 64");
+  if (c->pool_capacity > 0) {
+    if (!c->pool || !c->pool_slot || !c->pool_header)
+      return fail(KVC_E_NULL, "pool, pool_slot or pool_header is NULL with pool_capacity > 0");
+    if ((long long)c->pool_capacity * 40 * c->head_dim / 32 > 0x7FFFFFFFLL)
+      return fail(KVC_E_SHAPE, "pool_capacity too large");
+  }
+  if (reinterpret_cast<uintptr_t>(c->errors) & 3u)
+    return fail(KVC_E_UNSUPPORTED, "errors must be 4-byte aligned");
+  return KVC_OK;
+}
+
+// INT4-region positions of a max_ctx-long sequence (the most a pool can need).
+long long int4_capacity(const kvc_cache* c) {
+  const int slots = c->n_sink + c->n_recent;
+  return c->max_ctx > slots ? (long long)c->max_ctx - slots : 0;
+}
+
+// A refresh that maintains a pool must not keep more records than it holds.
+kvc_status check_pool_budget(const kvc_cache* c, int budget_permille) {
+  if (c->pool_capacity <= 0) return KVC_OK;
+  if ((long long)budget_permille * int4_capacity(c) / 1000 > c->pool_capacity)
+    return fail(KVC_E_SHAPE, "the budget can keep more records than pool_capacity holds");
   return KVC_OK;
 }
 
@@ -96,17 +120,29 @@ kvc_status launched(hipError_t e) {
 
 namespace kvc {
 
-AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window) {
-  // INT4 chunk j covers positions [base + j*chunk, base + (j+1)*chunk) of the
-  // INT4 region [16, max_ctx - 128), base = 0 (with a window: the window's
-  // first position rounded down to 64). Chunks are made as long as the
-  // per-wave list allows while leaving at least about kTarget chunk
-  // workgroups: a long list keeps a workgroup's load pipeline full and pays
-  // its set-up (mask and block-table loads, compaction) and epilogue rarely.
-  // Measured on 256 CUs, ~512 long chunk workgroups beat one or two full
-  // resident rounds (768 or 1536 workgroups at three per CU) at 10% and 50%
-  // kept. The short INT8-region workgroups go first when they fit in one
-  // round, else after the chunks.
+// Pool mode: chunks per (sequence, kv head) such that the chunk and INT8-region
+// workgroups of a call fit one resident round of two workgroups per CU on 256
+// CUs when the pairs allow it (fewer, longer chunks pay set-up and epilogue
+// less often: measured faster than 2x or 4x as many at 10% and 50% kept),
+// one chunk per pair otherwise; a chunk keeps at least 512 records.
+constexpr long long kPoolSlots = 512;
+
+AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window, bool pool) {
+  if (pool) {
+    AttnPlan p{};
+    const long long pairs = (long long)c.batch * c.num_kv_heads;
+    const int prot = c.n_sink + c.n_recent > 0 ? 1 : 0;
+    long long j = kPoolSlots / pairs - prot;
+    const long long by_size = c.pool_capacity / 512;
+    if (j > by_size) j = by_size;
+    if (j > kMaxParts - 1) j = kMaxParts - 1;
+    if (j < 1) j = 1;
+    p.pool = 1;
+    p.nsplit = (int)j;
+    p.chunk = 0;
+    p.int8_first = pairs <= 768 ? 1 : 0;
+    return p;
+  }
   constexpr long long kResident = 768;  // 3 workgroups per CU x 256 CUs
   constexpr long long kTarget = 384;
   const long long end4 =
@@ -120,7 +156,7 @@ AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window) {
   chunk = (chunk + 255) / 256 * 256;
   if (chunk < 1024) chunk = 1024;
   if (chunk > kMaxChunk) chunk = kMaxChunk;
-  AttnPlan p;
+  AttnPlan p{};
   p.chunk = (int)chunk;
   p.nsplit = span > 0 ? (int)((span + chunk - 1) / chunk) : 1;
   p.int8_first = pairs <= kResident ? 1 : 0;
@@ -180,7 +216,26 @@ KVC_API const char* kvc_status_string(kvc_status s) {
 KVC_API size_t kvc_attention_workspace_bytes(const kvc_cache* c, int32_t num_q_heads) {
   if (check_cache(c, 0) != KVC_OK || num_q_heads < 1 || num_q_heads % c->num_kv_heads) return 0;
   const kvc::AttnPlan p = kvc::plan_attention(*c, num_q_heads, 0);
-  return kvc::attention_ws_floats(*c, num_q_heads, p) * sizeof(float);
+  size_t n = kvc::attention_ws_floats(*c, num_q_heads, p);
+  if (c->pool_capacity > 0) {  // the windowed call still plans by positions
+    const size_t np = kvc::attention_ws_floats(*c, num_q_heads, kvc::plan_attention(*c, num_q_heads, 0, true));
+    if (np > n) n = np;
+  }
+  return (n * sizeof(float) + 15) / 16 * 16;
+}
+
+KVC_API size_t kvc_pool_bytes(const kvc_cache* c) {
+  if (check_cache(c, 0) != KVC_OK || c->pool_capacity <= 0) return 0;
+  return (size_t)c->batch * c->num_kv_heads * (size_t)(c->pool_capacity / 32) * 40 * c->head_dim;
+}
+
+KVC_API kvc_status kvc_pool_build(const kvc_cache* c, hipStream_t stream) {
+  kvc_status st = check_cache(c, kNeedInt4 | kNeedMask);
+  if (st != KVC_OK) return st;
+  if (c->pool_capacity <= 0) return fail(KVC_E_UNSUPPORTED, "the cache has no pool (pool_capacity = 0)");
+  if ((long long)c->batch * c->num_kv_heads > 65535)
+    return fail(KVC_E_UNSUPPORTED, "more than 65535 (sequence, kv head) pairs");
+  return launched(kvc::launch_pool_build(*c, stream));
 }
 
 KVC_API size_t kvc_topk_workspace_bytes(const kvc_cache* c) {
@@ -203,10 +258,12 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
                                        const void* v_new, kvc_dtype src, int32_t n_new_max,
                                        const int32_t* n_new, int32_t budget_permille, void* ws,
                                        size_t ws_bytes, hipStream_t stream) {
-  kvc_status st = check_cache(c, kNeedMask | kNeedScores);
+  kvc_status st = check_cache(c, kNeedMask | kNeedScores | (c && c->pool_capacity > 0 ? kNeedInt4 : 0u));
   if (st != KVC_OK) return st;
   if (budget_permille < 0 || budget_permille > 1000)
     return fail(KVC_E_SHAPE, "budget_permille must be in [0, 1000]");
+  st = check_pool_budget(c, budget_permille);
+  if (st != KVC_OK) return st;
   if (ws) {
     if (ws_bytes < (size_t)c->batch * c->num_kv_heads * sizeof(kvc::TopkState))
       return fail(KVC_E_WORKSPACE, "top-k workspace too small");
@@ -241,6 +298,8 @@ KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* m
   if (st != KVC_OK) return st;
   if (budget_permille < 0 || budget_permille > 1000)
     return fail(KVC_E_SHAPE, "budget_permille must be in [0, 1000]");
+  st = check_pool_budget(c, budget_permille);
+  if (st != KVC_OK) return st;
   if (ws) {
     if (ws_bytes < (size_t)c->batch * c->num_kv_heads * sizeof(kvc::TopkState))
       return fail(KVC_E_WORKSPACE, "top-k workspace too small");
@@ -272,6 +331,8 @@ KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, co
                                         size_t ws_bytes, hipStream_t stream) {
   kvc_status st = check_cache(c, kNeedMask | kNeedScores);
   if (st != KVC_OK) return st;
+  if (c->pool_capacity > 0)
+    return fail(KVC_E_UNSUPPORTED, "the block policy does not maintain a kept-record pool");
   if (budget_permille < 0 || budget_permille > 1000)
     return fail(KVC_E_SHAPE, "budget_permille must be in [0, 1000]");
   if (block_tokens != 16 && block_tokens != 32 && block_tokens != 64)
@@ -310,6 +371,8 @@ KVC_API kvc_status kvc_append_score_block_mask(const kvc_cache* c, const float* 
                                                hipStream_t stream) {
   kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8 | kNeedMask | kNeedScores);
   if (st != KVC_OK) return st;
+  if (c->pool_capacity > 0)
+    return fail(KVC_E_UNSUPPORTED, "the block policy does not maintain a kept-record pool");
   st = check_append(k_new, v_new, src, n_new_max, n_new);
   if (st != KVC_OK) return st;
   if (budget_permille < 0 || budget_permille > 1000)
@@ -354,10 +417,10 @@ static kvc_status decode_attention(const kvc_cache* c, int32_t window, const voi
   if ((long long)c->max_ctx > (long long)(kvc::kMaxParts - 1) * kvc::kMaxChunk + c->n_recent)
     return fail(KVC_E_UNSUPPORTED, "max_ctx above (255 * 8192 + n_recent) positions is not supported");
   if (window < 0) return fail(KVC_E_SHAPE, "int4_window must be >= 0");
-  const kvc::AttnPlan full = kvc::plan_attention(*c, num_q_heads, 0);
-  const size_t need = kvc::attention_ws_floats(*c, num_q_heads, full) * sizeof(float);
+  const bool pool = c->pool_capacity > 0 && window == 0;
+  const size_t need = kvc_attention_workspace_bytes(c, num_q_heads);
   if (!ws || ws_bytes < need) return fail(KVC_E_WORKSPACE, "attention workspace too small");
-  const kvc::AttnPlan plan = window > 0 ? kvc::plan_attention(*c, num_q_heads, window) : full;
+  const kvc::AttnPlan plan = kvc::plan_attention(*c, num_q_heads, window, pool);
   const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
   return launched(kvc::launch_attention(*c, q, q_dtype, num_q_heads, scale, out, lse,
                                         static_cast<float*>(ws), plan, window, stream));

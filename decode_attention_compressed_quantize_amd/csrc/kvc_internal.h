@@ -29,13 +29,19 @@ struct AttnPlan {
   int chunk;   // positions per INT4 chunk (multiple of 256, 1024 .. kMaxChunk)
   int nsplit;  // INT4 chunks per (sequence, kv head); partial index nsplit is the INT8 region
   int int8_first;  // dispatch order: INT8-region workgroups before (1) or after (0) the chunks
+  // Pool mode (the cache has a kept-record pool and the call reads all of it):
+  // chunk j of a (sequence, kv head) is the j-th of nsplit equal shares of its
+  // pool's record count (the workspace layout is the same as mask mode's).
+  int pool;
 };
 
 // window > 0: chunks cover only the last `window` INT4-region positions.
-AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window);
+// pool: plan the pool mode (only with window == 0 and a pool in the cache).
+AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window, bool pool = false);
 
 // Attention workspace: partials float [B][Hkv][nsplit + 1][G][2 + D] as
-// (m, l, o[0..D-1]) with m in log2 units. No initialisation needed.
+// (m, l, o[0..D-1]) with m in log2 units (chunk j at j, the INT8 region at
+// nsplit). No initialisation needed.
 inline size_t attention_ws_floats(const kvc_cache& c, int num_q_heads, const AttnPlan& p) {
   return (size_t)c.batch * num_q_heads * (size_t)(p.nsplit + 1) * (size_t)(2 + c.head_dim);
 }
@@ -152,6 +158,9 @@ hipError_t launch_dense_append(const kvc_dense_cache& c, const void* k_new, cons
 hipError_t launch_dense_attention(const kvc_dense_cache& c, const void* q, kvc_dtype q_dtype,
                                   int num_q_heads, float softmax_scale, float* out, float* lse,
                                   float* ws, const DensePlan& plan, hipStream_t s);
+
+// Kept-record pool rebuilt from the keep mask (layout in pool_layout.h).
+hipError_t launch_pool_build(const kvc_cache& c, hipStream_t s);
 
 // Streaming-read probe (measurement aid): XOR of every 32-bit word into *out.
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t s);

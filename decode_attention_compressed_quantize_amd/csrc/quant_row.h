@@ -38,6 +38,9 @@ struct QuantParams {
   uint8_t* codes_h;  // host tier: pages [num_pages, num_pages + host_pages)
   uint16_t* meta_h;
   int host_pages;  // INT8-protected sink and recent positions (16/128, or 0/0)
+  // kept-record pool headers [B][Hkv][4], or null: rows that rewrite INT4
+  // records the pool may hold clear its validity word
+  int32_t* pool_header;
 };
 
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -97,6 +100,7 @@ inline QuantParams quant_params(const kvc_cache& c, const void* k_new, const voi
   p.codes_h = c.int4_codes_host;
   p.meta_h = c.int4_meta_host;
   p.host_pages = c.num_host_pages;
+  p.pool_header = nullptr;
   return p;
 }
 
@@ -118,6 +122,13 @@ __device__ inline void quantize_item(const QuantParams& p, long long item, int l
   const int L = p.seq_lens[b];
   const int pos = L - nn + j;
   if (pos < 0 || pos >= p.max_ctx || L > p.max_ctx) return;
+  if (p.pool_header && j == 0 && lane == 0) {
+    // a pool describing length H holds records of positions in [sink, H - recent);
+    // rows [pos, L) that reach into that range make it stale
+    int32_t* ph = p.pool_header + 4 * ((size_t)b * p.hkv + h);
+    const int lo = pos > p.sink ? pos : p.sink;
+    if (lo < L && lo < ph[1] - p.recent) ph[2] = 0;
+  }
   const int lp = pos / kPage;
   if (lp >= p.max_pages) return;
   const int page = p.block_table[(size_t)b * p.max_pages + lp];

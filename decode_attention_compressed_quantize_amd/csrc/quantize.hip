@@ -18,7 +18,8 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(QuantParams p) {
 hipError_t launch_quantize_append(const kvc_cache& c, const void* k_new, const void* v_new,
                                   kvc_dtype src, int n_new_max, const int32_t* n_new,
                                   hipStream_t s) {
-  const QuantParams p = quant_params(c, k_new, v_new, n_new_max, n_new);
+  QuantParams p = quant_params(c, k_new, v_new, n_new_max, n_new);
+  if (c.pool_capacity > 0) p.pool_header = c.pool_header;
   const dim3 grid((unsigned)((p.items + 3) / 4));
   const dim3 block(256);
   const bool bf = src == KVC_BF16;

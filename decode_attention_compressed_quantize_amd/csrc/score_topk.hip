@@ -22,6 +22,7 @@
 // only when the state does not apply (first call, new budget, several new
 // positions, caller-written scores, a list run dry).
 #include "kvc_internal.h"
+#include "pool_layout.h"
 #include "quant_row.h"
 
 namespace kvc {
@@ -74,7 +75,7 @@ struct ScorerSlice {
 };
 
 template <int D, bool BF16>
-__device__ void score_row(const ScoreParams& p, const ScorerSlice<D>& m, int h, long long f, int gtid,
+__device__ __attribute__((always_inline)) void score_row(const ScoreParams& p, const ScorerSlice<D>& m, int h, long long f, int gtid,
                           float* xs, float* wsum) {
   constexpr int IN = 2 * D;
   constexpr int PART = IN / 8;
@@ -160,6 +161,7 @@ struct TopkParams {
   int words;
   int budget;
   int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
+  PoolRef pool;      // kept-record pool maintained with the mask (pool.cap = 0: none)
 };
 
 // Order-preserving key: larger score -> larger key; NaN -> 0 (below -inf); -0 == +0.
@@ -216,13 +218,18 @@ __device__ inline uint64_t list_pop_front(uint64_t v, int& n) {
 // Applies one appended position (length L - 1 -> L) to the mask and the lists.
 // Returns false, having written nothing, when the state does not describe
 // length L - 1 under this budget or a list it needs has run out.
-__device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, long long k,
-                          const float* sc, uint32_t* mrow, int lane) {
+__device__ __attribute__((always_inline)) bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, long long k,
+                          const float* sc, uint32_t* mrow, int lane, int b, int h) {
   if (L < 1 || st->magic != kTopkMagic || st->budget != p.budget || st->len != L - 1) return false;
   const int slots = p.sink + p.recent;
   const int n4p = L - 1 > slots ? L - 1 - slots : 0;
   const long long kp = ((long long)p.budget * n4p) / 1000;
   if (st->k != kp) return false;
+  const int pair = b * p.hkv + h;
+  int32_t* phdr = p.pool.cap > 0 ? p.pool.header + 4 * (size_t)pair : nullptr;
+  // the pool must hold exactly the kept records of length L - 1
+  if (phdr && (phdr[2] != (int32_t)kPoolMagic || phdr[1] != L - 1 || phdr[0] != kp)) return false;
+  int ins_pos = -1, ins_slot = -1;  // pool: the record of ins_pos goes to ins_slot
   int na = st->na, nb = st->nb;
   if (na < 0 || na > kTopkBuf || nb < 0 || nb > kTopkBuf) return false;
   uint64_t A = lane < na ? st->a[lane] : 0, B = lane < nb ? st->b[lane] : 0;
@@ -242,6 +249,8 @@ __device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, lon
         const uint64_t a0 = wave_at(A, 0);
         if (x > a0) {  // x displaces the smallest kept key
           clear_pos = comp_pos(a0);
+          ins_pos = xpos;
+          if (phdr) ins_slot = pool_slot_of(p.pool, pair)[clear_pos];
           const bool whole = na == k;
           A = list_pop_front(A, na);
           B = list_push_front(B, nb, a0, lane);
@@ -252,18 +261,29 @@ __device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, lon
         }
       }
     } else {  // one more kept: x or the best key not kept
+      ins_slot = (int)kp;  // the pool grows by one record
       if (out_before == 0 || (nb > 0 && x > wave_at(B, 0))) {
         A = list_insert<true>(A, na, x, na == kp, lane);
+        ins_pos = xpos;
       } else {
         if (nb == 0) return false;
         const uint64_t z = wave_at(B, 0);
         set_pos = comp_pos(z);
+        ins_pos = set_pos;
         B = list_pop_front(B, nb);
         A = list_push_front(A, na, z, lane);
         clear_pos = xpos;
         B = list_insert<false>(B, nb, x, nb == out_before - 1, lane);
       }
     }
+  }
+  int ins_page = -1;
+  if (phdr && ins_pos >= 0) {
+    // a slot outside the kept records or a page outside the pools: rebuild instead
+    if (ins_slot < 0 || ins_slot > kp || (ins_slot == kp && k == kp) || ins_slot >= p.pool.cap)
+      return false;
+    ins_page = pool_page(p.pool, b, ins_pos);
+    if (ins_page < 0) return false;
   }
   if (lane == 0) {
     // the new position is protected (without protection it is the candidate,
@@ -283,7 +303,174 @@ __device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, lon
   }
   if (lane < na) st->a[lane] = A;
   if (lane < nb) st->b[lane] = B;
+  if (phdr) {
+    if (ins_pos >= 0) {
+      pool_copy_wave(p.pool, pair, h, ins_page, ins_pos, ins_slot, lane);
+      if (lane == 0) {
+        pool_slot_of(p.pool, pair)[ins_pos] = ins_slot;
+        pool_pos_of(p.pool, pair)[ins_slot] = ins_pos;
+      }
+    }
+    if (lane == 0) {
+      phdr[0] = (int32_t)k;
+      phdr[1] = L;
+    }
+  }
   return true;
+}
+
+// ---- kept-record pool in a full refresh. The mask pass compares each old
+// mask word with the new one and lists, in position order, the kept INT4
+// records that leave and those that enter; if the pool held exactly the old
+// kept set and the lists fit, only those records move: entering records fill
+// the slots of leaving ones (then extend the pool), and when the pool shrinks
+// the records left in its tail move into the remaining holes below the new
+// count. Otherwise the pool is rebuilt from the new mask (slots in position
+// order).
+constexpr int kDiffCap = 1024;  // changed records a refresh applies in place (one per thread)
+static_assert(kDiffCap == kTopkThreads, "one changed record per thread");
+struct PoolLds {
+  int32_t rem[kDiffCap];   // positions leaving (position order); later the live tail slots
+  int32_t add[kDiffCap];   // positions entering (position order)
+  int32_t hole[kDiffCap];  // slot of rem[i]
+  int32_t low[kDiffCap];   // holes below the new count, in rem order
+  int32_t flag[kDiffCap];  // tail slot j (cnt_new + j) stays live
+  uint32_t scan[kTopkThreads / 64];
+  uint32_t oldpop;
+};
+
+// Block-wide exclusive prefix of one value per thread (in thread order).
+__device__ inline uint32_t block_excl(uint32_t v, uint32_t* scan, uint32_t& total, int lane, int wid) {
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) scan[wid] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  total = 0;
+  for (int q = 0; q < kTopkThreads / 64; ++q) {
+    const uint32_t x = scan[q];
+    if (q < wid) base += x;
+    total += x;
+  }
+  return base + incl - v;
+}
+
+// Bits of mask word w (positions 32w..32w+31) in [lo4, hi4).
+__device__ inline uint32_t region_bits(int w, uint32_t word, int lo4, int hi4) {
+  const int lo = lo4 - 32 * w, hi = hi4 - 32 * w;
+  if (hi <= 0 || lo >= 32) return 0u;
+  if (lo > 0) word &= ~0u << lo;
+  if (hi < 32) word &= (1u << hi) - 1u;
+  return word;
+}
+
+// The same, restricted to positions whose page is in the pools; pga / pgb
+// receive the pages of the word's two halves.
+__device__ inline uint32_t pool_word_bits(const PoolRef& r, int b, int w, uint32_t word, int lo4,
+                                          int hi4, int& pga, int& pgb) {
+  word = region_bits(w, word, lo4, hi4);
+  if (word & 0x0000FFFFu) {
+    pga = pool_page(r, b, 32 * w);
+    if (pga < 0) word &= 0xFFFF0000u;
+  }
+  if (word & 0xFFFF0000u) {
+    pgb = pool_page(r, b, 32 * w + 16);
+    if (pgb < 0) word &= 0x0000FFFFu;
+  }
+  return word;
+}
+
+// Rebuild: every kept INT4 record of the new mask into slots 0, 1, ... in
+// position order. Thread t reads back the words it wrote itself in the mask
+// pass (same word-to-thread assignment), so no other thread's store is read.
+// Returns the record count.
+__device__ __attribute__((always_inline)) long long pool_rebuild(const TopkParams& p, PoolLds& ps, int pair, int b, int h, int n4,
+                                  const uint32_t* mrow) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int32_t* slot_of = pool_slot_of(p.pool, pair);
+  int32_t* pos_of = pool_pos_of(p.pool, pair);
+  long long pcarry = 0;
+  for (int w0 = 0; w0 < p.words; w0 += kTopkThreads) {
+    const int w = w0 + tid;
+    int pga = -1, pgb = -1;
+    uint32_t k4 = w < p.words ? pool_word_bits(p.pool, b, w, mrow[w], p.sink, p.sink + n4, pga, pgb) : 0u;
+    uint32_t total;
+    long long slot = pcarry + block_excl((uint32_t)__popc(k4), ps.scan, total, lane, wid);
+    while (k4 != 0) {
+      const int bit = __builtin_ctz(k4);
+      k4 &= k4 - 1u;
+      const int pos = 32 * w + bit;
+      if (slot < p.pool.cap) {
+        pool_copy_thread(p.pool, pair, h, bit < 16 ? pga : pgb, pos, (int)slot);
+        slot_of[pos] = (int32_t)slot;
+        pos_of[slot] = pos;
+      }
+      ++slot;
+    }
+    pcarry += total;
+  }
+  return pcarry;
+}
+
+// Applies nR leaving and nA entering records (lists in ps) to a pool of
+// cnt_old records; returns the new count, or -1 (nothing changed) when the
+// map does not place the leaving records in distinct slots below cnt_old.
+__device__ __attribute__((always_inline)) int pool_apply(const TopkParams& p, PoolLds& ps, int pair, int b, int h, int cnt_old,
+                          int nR, int nA) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int32_t* slot_of = pool_slot_of(p.pool, pair);
+  int32_t* pos_of = pool_pos_of(p.pool, pair);
+  const int cnt_new = cnt_old - nR + nA;
+  int hs = -1;
+  if (tid < nR) {
+    hs = slot_of[ps.rem[tid]];
+    if (hs < 0 || hs >= cnt_old || pos_of[hs] != ps.rem[tid]) hs = -1;  // both maps must agree
+    ps.hole[tid] = hs;
+  }
+  if (__syncthreads_or(tid < nR && hs < 0)) return -1;
+  auto put = [&](int pos, int dst) {
+    const int page = pool_page(p.pool, b, pos);
+    if (page >= 0) pool_copy_thread(p.pool, pair, h, page, pos, dst);
+    slot_of[pos] = dst;
+    pos_of[dst] = pos;
+  };
+  if (nA >= nR) {
+    if (tid < nA) put(ps.add[tid], tid < nR ? ps.hole[tid] : cnt_old + (tid - nR));
+    return cnt_new;
+  }
+  // the pool shrinks: holes below cnt_new take the entering records, then the
+  // records that stay live in the tail [cnt_new, cnt_old)
+  const int tail = nR - nA;
+  if (tid < tail) ps.flag[tid] = 1;
+  __syncthreads();
+  if (tid < nR && ps.hole[tid] >= cnt_new) ps.flag[ps.hole[tid] - cnt_new] = 0;
+  __syncthreads();
+  uint32_t nlow, nlive;
+  const bool lowh = tid < nR && ps.hole[tid] < cnt_new;
+  const uint32_t il = block_excl(lowh ? 1u : 0u, ps.scan, nlow, lane, wid);
+  if (lowh) ps.low[il] = ps.hole[tid];
+  const bool live = tid < tail && ps.flag[tid] != 0;
+  const uint32_t iv = block_excl(live ? 1u : 0u, ps.scan, nlive, lane, wid);
+  if (live) ps.rem[iv] = cnt_new + tid;
+  __syncthreads();
+  if (tid < (int)nlow) {
+    const int dst = ps.low[tid];
+    if (tid < nA) {
+      put(ps.add[tid], dst);
+    } else if (tid - nA < (int)nlive) {
+      const int from = ps.rem[tid - nA];
+      const int pos = pos_of[from];
+      pool_move_thread(p.pool, pair, from, dst);
+      if (pos >= 0 && pos < p.max_ctx) slot_of[pos] = dst;
+      pos_of[dst] = pos;
+    }
+  }
+  return cnt_new;
 }
 
 // ---- full refresh. An exact radix select over the 32-bit score keys (4
@@ -294,19 +481,22 @@ __device__ bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, lon
 // key above the threshold and the lowest positions equal to it (the unique
 // answer under "score descending, then position ascending"), and collects the
 // keys between the two outer ranks; sorted, they give the lists.
-__device__ void topk_pair(const TopkParams& p, int h, int b) {
+__device__ __attribute__((always_inline)) void topk_pair(const TopkParams& p, int h, int b) {
   __shared__ uint32_t hist[3][256];
   __shared__ uint32_t scan[kTopkThreads / 64];
   __shared__ uint32_t sel_digit[3], sel_above[3];
   __shared__ uint64_t cand[kCandCap];
   __shared__ uint32_t ncand;
   __shared__ int done;
+  __shared__ PoolLds ps;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   int L = p.seq_lens[b];
-  if (L < 0) L = 0;
-  if (L > p.max_ctx) L = p.max_ctx;
+  if (L < 0 || L > p.max_ctx) {
+    if (tid == 0) report_error(p.pool.errors, KVC_ERR_LENGTH);
+    L = L < 0 ? 0 : p.max_ctx;
+  }
   const int n4 = L > p.sink + p.recent ? L - p.sink - p.recent : 0;
   const long long k = ((long long)p.budget * n4) / 1000;
   const float* sc = p.scores + ((size_t)b * p.hkv + h) * p.max_ctx + p.sink;
@@ -314,12 +504,28 @@ __device__ void topk_pair(const TopkParams& p, int h, int b) {
   TopkState* st = p.state ? p.state + (size_t)b * p.hkv + h : nullptr;
 
   if (wid == 0) {
-    const bool ok = st && p.incremental && topk_step(p, st, L, n4, k, sc, mrow, lane);
+    const bool ok = st && p.incremental && topk_step(p, st, L, n4, k, sc, mrow, lane, b, h);
     if (lane == 0) done = ok ? 1 : 0;
     if (lane == 0) ncand = 0;
+    if (lane == 0) ps.oldpop = 0;
   }
   __syncthreads();
   if (done) return;
+  // a pool that holds exactly the kept records of an earlier length is
+  // updated by the records that change; anything else is rebuilt
+  const bool pooled = p.pool.cap > 0;
+  const int pair = b * p.hkv + h;
+  int len_old = -1, cnt_old = 0;
+  if (pooled) {
+    const int32_t* ph = p.pool.header + 4 * (size_t)pair;
+    if ((uint32_t)ph[2] == kPoolMagic && ph[1] >= 0 && ph[1] <= p.max_ctx && ph[0] >= 0 &&
+        ph[0] <= p.pool.cap) {
+      len_old = ph[1];
+      cnt_old = ph[0];
+    }
+  }
+  const bool diff = len_old >= 0;
+  const int n4_old = len_old > p.sink + p.recent ? len_old - p.sink - p.recent : 0;
 
   // ---- radix select: target 0 = rank k, 1 = rank k - 63, 2 = rank k + 64
   const bool all = k >= n4;
@@ -408,8 +614,12 @@ __device__ void topk_pair(const TopkParams& p, int h, int b) {
   const uint32_t lo = rank[2] > 0 ? prefix[2] : 0u;
   const long long above_hi = rank[1] > 0 ? rank[1] - remaining[1] : 0;
 
-  // ---- in-order pass: one mask word per thread, block-wide running count of keys == T
+  // ---- in-order pass: one mask word per thread, block-wide running count of
+  // keys == T. With a pool in diff mode, the records leaving and entering are
+  // listed in position order (rcarry / acarry count them so far).
   long long carry = 0;
+  long long rcarry = 0, acarry = 0;
+  uint32_t oldpop = 0;
   for (int w0 = 0; w0 < p.words; w0 += kTopkThreads) {
     const int w = w0 + tid;
     uint32_t gt = 0, eq = 0;  // bit masks over the word's INT4 positions
@@ -451,7 +661,9 @@ __device__ void topk_pair(const TopkParams& p, int h, int b) {
       tile_total += v;
     }
     const long long before = carry + wave_base + (incl - cnt);
+    uint32_t wbits = 0, oldw = 0;  // the word as written, and as it was
     if (w < p.words) {
+      if (pooled && diff) oldw = mrow[w];
       uint32_t bits = (k > 0 && !all) ? gt : 0u;
       if (eq && k > 0 && !all) {
         long long r = before;
@@ -470,9 +682,52 @@ __device__ void topk_pair(const TopkParams& p, int h, int b) {
         if (prot || (all && t >= p.sink)) bits |= 1u << i;
       }
       mrow[w] = bits;
+      wbits = bits;
     }
     carry += tile_total;
+    if (pooled && diff) {
+      uint32_t remw = 0, addw = 0;
+      if (w < p.words) {
+        int pa = -1, pb = -1;
+        // the old records are not read, so their pages are not looked up
+        const uint32_t old_in = region_bits(w, oldw, p.sink, p.sink + n4_old);
+        const uint32_t new_in = pool_word_bits(p.pool, b, w, wbits, p.sink, p.sink + n4, pa, pb);
+        oldpop += (uint32_t)__popc(old_in);
+        remw = old_in & ~new_in;
+        addw = new_in & ~old_in;
+      }
+      uint32_t both;
+      const uint32_t ex = block_excl((uint32_t)__popc(remw) | ((uint32_t)__popc(addw) << 16), ps.scan,
+                                     both, lane, wid);
+      long long ir = rcarry + (ex & 0xFFFFu), ia = acarry + (ex >> 16);
+      for (; remw; remw &= remw - 1u, ++ir)
+        if (ir < kDiffCap) ps.rem[ir] = 32 * w + __builtin_ctz(remw);
+      for (; addw; addw &= addw - 1u, ++ia)
+        if (ia < kDiffCap) ps.add[ia] = 32 * w + __builtin_ctz(addw);
+      rcarry += both & 0xFFFFu;
+      acarry += both >> 16;
+    }
     __syncthreads();
+  }
+  if (pooled) {
+    if (diff) atomicAdd(&ps.oldpop, oldpop);
+    __syncthreads();
+    const long long cnt_new = (long long)cnt_old - rcarry + acarry;
+    long long count = -1;
+    if (diff && rcarry <= kDiffCap && acarry <= kDiffCap && ps.oldpop == (uint32_t)cnt_old &&
+        cnt_new <= p.pool.cap)
+      count = pool_apply(p, ps, pair, b, h, cnt_old, (int)rcarry, (int)acarry);
+    if (count < 0) count = pool_rebuild(p, ps, pair, b, h, n4, mrow);
+    __syncthreads();
+    if (tid == 0) {
+      int32_t* phdr = p.pool.header + 4 * (size_t)pair;
+      const bool fits = count <= p.pool.cap;
+      if (!fits) report_error(p.pool.errors, KVC_ERR_POOL);
+      phdr[0] = (int32_t)(fits ? count : p.pool.cap);
+      phdr[1] = L;
+      phdr[2] = fits ? (int32_t)kPoolMagic : 0;
+      phdr[3] = 0;
+    }
   }
   if (!st) return;
 
@@ -1181,6 +1436,7 @@ TopkParams topk_params(const kvc_cache& c, int budget_permille, TopkState* state
   p.budget = budget_permille;
   p.sink = c.n_sink;
   p.recent = c.n_recent;
+  p.pool = pool_ref(c);
   return p;
 }
 

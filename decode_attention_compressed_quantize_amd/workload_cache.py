@@ -15,8 +15,20 @@ import workloads as W
 
 from . import (Cache, DenseCache, attention_workspace, block_workspace, dense_workspace,
                kvc_copy_pages, kvc_dense_append, kvc_find_pages, kvc_append_score_block_mask,
-               kvc_append_score_topk_mask, kvc_quantize_append, kvc_score_block_mask,
-               kvc_score_topk_mask, topk_workspace)
+               kvc_append_score_topk_mask, kvc_pool_build, kvc_quantize_append,
+               kvc_score_block_mask, kvc_score_topk_mask, topk_workspace)
+
+
+def pool_capacity_for(w: W.Workload) -> int:
+    """Pool records per (sequence, kv head) that the workload's keep policy can need:
+    its budget of the INT4 region of a max_ctx-long sequence, rounded up to 64."""
+    slots = 144 if w.protect else 0
+    n4max = max(0, w.max_ctx() - slots)
+    if w.mask in ("scores", "mlp") and w.policy == "token":
+        keep = (w.budget_permille * n4max) // 1000
+    else:
+        keep = n4max
+    return max(64, (keep + 63) // 64 * 64)
 
 
 def pack_bits(flags: np.ndarray, words: int) -> np.ndarray:
@@ -33,10 +45,11 @@ class LayerCache:
 
     def __init__(self, w: W.Workload, layer: int = 0, device="cuda", batch_rows=None,
                  table: Optional[np.ndarray] = None, keep_sources: bool = True,
-                 host_pages: int = 0):
+                 host_pages: int = 0, pool: bool = False, errors: bool = False):
         import torch
 
         self.w, self.layer, self.device = w, layer, device
+        self.pooled = pool
         self.lengths = w.lengths()
         if table is None:
             table, num_pages = W.page_table(w, layer)
@@ -48,7 +61,8 @@ class LayerCache:
         self.seq_lens = torch.from_numpy(self.lengths.astype(np.int32)).to(device)
         self.cache = Cache(w.batch, w.kv_heads, w.head_dim, self.max_ctx, num_pages,
                            self.table, self.seq_lens, device=device, protect=w.protect,
-                           host_pages=host_pages)
+                           host_pages=host_pages,
+                           pool_capacity=pool_capacity_for(w) if pool else 0, errors=errors)
         self.num_pages = num_pages
         self.host_free = list(range(num_pages, num_pages + host_pages))  # free host-tier page ids
         self.dev_free = []  # device pages released by demotion
@@ -105,6 +119,10 @@ class LayerCache:
         sub.desc.seq_lens = self.seq_lens[b0:b1].data_ptr()
         sub.desc.keep_mask = c.keep_mask[b0:b1].data_ptr()
         sub.desc.scores = c.scores[b0:b1].data_ptr()
+        if c.pool is not None:
+            sub.desc.pool = c.pool[b0:b1].data_ptr()
+            sub.desc.pool_slot = c.pool_slot[b0:b1].data_ptr()
+            sub.desc.pool_header = c.pool_header[b0:b1].data_ptr()
         return sub
 
     def _mlp_subset(self, sub, k_new, v_new, n_new):
@@ -128,6 +146,8 @@ class LayerCache:
                     L = int(self.lengths[b])
                     rows[b, h] = pack_bits(W.bernoulli_keep_np(w, self.layer, b, h, L), c.mask_words)
             c.keep_mask.copy_(torch.from_numpy(rows))
+            if c.pool is not None:
+                kvc_pool_build(c)
         elif w.mask == "all":
             kvc_score_topk_mask(c, None, None, None, None, 1000)
         elif w.mask in ("scores", "mlp"):
@@ -255,9 +275,10 @@ class LayerCache:
         r.table = self.table.clone()
         r.seq_lens = self.seq_lens.clone()
         r.cache = Cache(c.batch, c.kv_heads, c.head_dim, c.max_ctx, c.num_phys_pages, r.table,
-                        r.seq_lens, device=self.device, protect=c.protect, host_pages=c.host_pages)
+                        r.seq_lens, device=self.device, protect=c.protect, host_pages=c.host_pages,
+                        pool_capacity=c.pool_capacity, errors=c.errors is not None)
         for name in ("int4_codes", "int4_meta", "int8_codes", "int8_scales", "keep_mask", "scores",
-                     "int4_codes_host", "int4_meta_host"):
+                     "int4_codes_host", "int4_meta_host", "pool", "pool_slot", "pool_header"):
             if getattr(c, name) is not None:
                 getattr(r.cache, name).copy_(getattr(c, name))
         r.host_free, r.dev_free = list(self.host_free), list(self.dev_free)

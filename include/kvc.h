@@ -62,14 +62,67 @@
  * with kvc_dense_append and kvc_dense_decode_attention) and a streaming-read
  * probe used as a measurement aid (kvc_stream_read_probe).
  *
+ * Kept-record pool (optional; pool_capacity > 0): per (sequence, kv head) a
+ * compact copy of the INT4 records of the kept INT4-region positions, so that
+ * attention streams exactly the bytes it needs (160 per kept token at D = 128)
+ * instead of gathering 128-byte code lines and the shared lines of their
+ * per-token meta. The keep mask stays the definition of what is attended; the
+ * pool is derived from it and maintained by the calls that write the mask:
+ *   pool        uint8 [B][Hkv][pool_capacity/32][40*D]  records in tiles of 32,
+ *               in an internal order of bytes (treat as opaque); slots
+ *               [0, count) hold the kept records in no particular order.
+ *   pool_slot   int32 [B][Hkv][max_ctx + pool_capacity]  two maps: entry
+ *               pos < max_ctx holds the slot of kept INT4-region position
+ *               pos, entry max_ctx + s the position whose record is in slot
+ *               s < count (other entries unspecified).
+ *   pool_header int32 [B][Hkv][4]  (count, length, magic, 0): the kept count,
+ *               the sequence length the pool describes and a validity word.
+ * kvc_score_topk_mask / kvc_append_score_topk_mask update the pool with the
+ * mask: a decode step copies at most one record per (sequence, kv head); a
+ * full refresh copies the records that enter the kept set, into the slots of
+ * those that leave (moving tail records down when the set shrinks), as long as
+ * the header is valid and at most 1024 records leave and 1024 enter; otherwise
+ * it rebuilds the pool from the mask. That update assumes the pool still holds
+ * what the previous call left there. kvc_quantize_append clears the validity
+ * word of a (sequence, kv head) whose appended rows reach below n_recent
+ * positions short of the length the pool describes (a sequence written
+ * afresh, a rollback), so the next refresh rebuilds; a caller that changes INT4 records, the mask or the
+ * pool by other means zeroes pool_header (or calls kvc_pool_build).
+ * kvc_pool_build rebuilds the pool from the mask for callers that write the
+ * mask themselves. kvc_decode_attention reads the
+ * pool instead of the mask when pool_capacity > 0, so the pool must describe
+ * the current lengths: after an append, refresh (or kvc_pool_build) before
+ * attending. pool_capacity (a multiple of 64) must hold the largest kept
+ * count, floor(budget_permille * n4 / 1000) at n4 = max_ctx - 144 (- 0 without
+ * INT8 protection); the refresh returns KVC_E_SHAPE when the budget could
+ * exceed it. The block policy does not maintain a pool (KVC_E_UNSUPPORTED
+ * with pool_capacity > 0), and kvc_decode_attention_windowed reads the mask.
+ *
+ * Error word (optional; errors != NULL): kernels OR KVC_ERR_* bits into
+ * errors[0] when they meet device contents they cannot use (a length outside
+ * [0, max_ctx], a block-table entry outside the page pools for a position
+ * below the length, a pool that does not describe the current length). The
+ * affected positions are skipped, so the outputs are unspecified; the word
+ * tells the caller so. The library never clears it.
+ *
+ * Shrinking a length (rolling a sequence back) leaves the INT8 ring slots of
+ * the positions that are now the most recent holding the later positions
+ * that overwrote them: after lowering seq_lens[b] to L, append again (with
+ * kvc_quantize_append or the fused update) the source rows of positions
+ * [max(16, L - 128), L) of that sequence before attending, and refresh the
+ * mask (a refresh after a shrink is a full one).
+ *
  * Conventions: every call is enqueued on the caller's stream and never
  * synchronises; argument errors are returned synchronously; kernels never
  * allocate; the library keeps no state besides a thread-local error string.
  * The cache arrays and the q, out and ws buffers of attention must be 16-byte
  * aligned (device allocations are); a misaligned one gives KVC_E_UNSUPPORTED.
  * Device contents (lengths, table entries) are trusted: out-of-range page ids
- * or lengths are skipped by the kernels rather than dereferenced, which leaves
- * the affected outputs unspecified.
+ * or lengths are skipped by the kernels rather than dereferenced (and flagged
+ * in the error word when there is one), which leaves the affected outputs
+ * unspecified. Appended K/V rows must be finite: a NaN entry does not
+ * propagate into the stored scale and min (their group min and max ignore
+ * it), so the stored codes of such a row are unspecified.
  */
 #ifndef KVC_H
 #define KVC_H
@@ -83,7 +136,7 @@ extern "C" {
 #endif
 
 #define KVC_API __attribute__((visibility("default")))
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum {
   KVC_OK = 0,
@@ -123,7 +176,20 @@ typedef struct kvc_cache {
   int32_t reserved;          /* 0 */
   uint8_t* int4_codes_host;  /* [H][Hkv][16][2][D/2], or NULL when H = 0 */
   uint16_t* int4_meta_host;  /* [H][Hkv][16][2][D/32][2], or NULL when H = 0 */
+  /* Optional kept-record pool (see above): 0, or records per (sequence, kv
+   * head), a multiple of 64; with 0 the three pool pointers are unused. */
+  int32_t pool_capacity;
+  int32_t reserved2;         /* 0 */
+  uint8_t* pool;             /* [B][Hkv][pool_capacity/32][40*D] */
+  int32_t* pool_slot;        /* [B][Hkv][max_ctx + pool_capacity] */
+  int32_t* pool_header;      /* [B][Hkv][4] */
+  uint32_t* errors;          /* device uint32 [1] of KVC_ERR_* bits, or NULL */
 } kvc_cache;
+
+/* Bits of the error word (kvc_cache.errors). */
+#define KVC_ERR_LENGTH 1u      /* a seq_lens entry outside [0, max_ctx] (clamped) */
+#define KVC_ERR_PAGE 2u        /* a block-table entry outside the page pools (skipped) */
+#define KVC_ERR_POOL 4u        /* attention found a pool that does not describe the length */
 
 /*
  * kvc_quantize_append - encode appended tokens into the cache.
@@ -266,7 +332,14 @@ KVC_API kvc_status kvc_append_score_block_mask(const kvc_cache* c, const float* 
  *                  per-chunk partials; its contents on entry do not matter.
  *                  Calls sharing one workspace must not overlap.
  *   Attends to the INT8 positions and to the INT4-region positions whose
- *   keep_mask bit is set. A sequence with L = 0 yields out = 0, lse = -inf.
+ *   keep_mask bit is set (with a pool: to the pool's records, which are those
+ *   positions when the pool describes the current length). A sequence with
+ *   L = 0 yields out = 0, lse = -inf.
+ *   Accuracy: logits are float32-accurate for any finite query (the query is
+ *   scaled per head by a power of two into fp16's range and, when float32,
+ *   split into two fp16 parts; codes enter the matrix instructions exactly);
+ *   probabilities enter the P.V product as two fp16 parts. Inputs whose
+ *   logits (q . k * softmax_scale) exceed float32's range are unsupported.
  */
 KVC_API kvc_status kvc_decode_attention(const kvc_cache* c, const void* q, kvc_dtype q_dtype,
                                         int32_t num_q_heads, float softmax_scale, float* out,
@@ -291,6 +364,27 @@ KVC_API kvc_status kvc_decode_attention_windowed(const kvc_cache* c, int32_t int
                                                  int32_t num_q_heads, float softmax_scale,
                                                  float* out, float* lse, void* ws, size_t ws_bytes,
                                                  hipStream_t stream);
+
+/*
+ * kvc_pool_build - rebuild the kept-record pool from the keep mask.
+ * Source: KV4-RL review, section 3 (attention over the paged INT4 store and
+ * the INT8 side cache) and the Shadow Mask Distillation page, Figure 1 caption
+ * (the mask of retained indices decides what is attended): the pool is a
+ * compact copy of the INT4 records the mask keeps, so that attention reads
+ * only those.
+ *   For every (sequence, kv head): copies the INT4 record (codes and meta) of
+ *   each INT4-region position whose keep_mask bit is set into slots
+ *   0, 1, ... in position order, writes pool_slot for them and sets
+ *   pool_header to (count, seq_lens[b], valid). Needs int4_codes, int4_meta,
+ *   block_table, seq_lens, keep_mask and the pool arrays. KVC_E_UNSUPPORTED
+ *   without a pool; KVC_E_SHAPE when pool_capacity is not a multiple of 64 or
+ *   cannot hold max_ctx - 144 records (the whole INT4 region; the call does
+ *   not know a budget). Calls that refresh the mask keep the pool up to date
+ *   themselves; this call is for masks written by the caller.
+ * kvc_pool_bytes - bytes of the pool array for c->pool_capacity (0 if none).
+ */
+KVC_API kvc_status kvc_pool_build(const kvc_cache* c, hipStream_t stream);
+KVC_API size_t kvc_pool_bytes(const kvc_cache* c);
 
 /*
  * kvc_decode_attention_noalloc - kvc_decode_attention without a workspace

@@ -111,3 +111,57 @@ def assert_attention_close(out, lse, ref_out, ref_lse, what=""):
     assert rel <= 1e-3, f"{what} rel-L2 {rel:.3e}"
     assert lerr <= 2e-3, f"{what} lse max-abs {lerr:.3e}"
     return err, rel, lerr
+
+
+POOL_MAGIC = 0x4B565031
+
+
+def unpack_pool(pool_pair, D, n):
+    """Records of slots [0, n) of one (sequence, kv head)'s pool (uint8 [tiles][40*D]) ->
+    (K codes [n][D/2], V codes [n][D/2], meta uint16 [n][2][D/32][2]).
+
+    Tile layout (32 records): K codes as pieces (t // 16, s, t % 16) of D/8 bytes
+    (bytes [s*D/8, (s+1)*D/8) of token t), then K meta, V codes and V meta as
+    dwords indexed [r(t)][g or d][t % 4] with r(t) = 4 (t // 16) + (t % 16) // 4."""
+    NG, SB, VD = D // 32, D // 8, D // 8
+    nt = (n + 31) // 32
+    tiles = np.ascontiguousarray(pool_pair[:nt]).reshape(nt, 40 * D)
+    t = np.arange(32)
+    r_t = ((t >> 4) << 2) + ((t & 15) >> 2)
+    j_t = t & 3
+    kc = tiles[:, :16 * D].reshape(nt, 2, 4, 16, SB).transpose(0, 1, 3, 2, 4).reshape(nt, 32, 4 * SB)
+    km = tiles[:, 16 * D:20 * D].copy().view(np.uint32).reshape(nt, 8, NG, 4)
+    vc = tiles[:, 20 * D:36 * D].copy().view(np.uint32).reshape(nt, 8, VD, 4)
+    vm = tiles[:, 36 * D:40 * D].copy().view(np.uint32).reshape(nt, 8, NG, 4)
+    kmeta = km[:, r_t, :, j_t].transpose(1, 0, 2)   # [nt][32][NG]
+    vcode = vc[:, r_t, :, j_t].transpose(1, 0, 2)   # [nt][32][VD]
+    vmeta = vm[:, r_t, :, j_t].transpose(1, 0, 2)
+    kcodes = kc.reshape(nt * 32, D // 2)[:n]
+    vcodes = np.ascontiguousarray(vcode.reshape(nt * 32, VD)).view(np.uint8).reshape(nt * 32, D // 2)[:n]
+    meta = np.stack([kmeta.reshape(nt * 32, NG), vmeta.reshape(nt * 32, NG)], axis=1)[:n]
+    return kcodes, vcodes, np.ascontiguousarray(meta).view(np.uint16).reshape(n, 2, NG, 2)
+
+
+def check_pool(cpu, b, kvh, L, keep4, D, n_sink=regions.N_SINK):
+    """The pool of one (sequence, kv head) holds exactly the kept INT4 records, bit for bit:
+    header (count, length, magic), a slot per kept position covering [0, count) once, and
+    each slot's record equal to the paged record of its position. Returns the count."""
+    hdr = cpu["pool_header"][b, kvh]
+    kept = n_sink + np.flatnonzero(np.asarray(keep4, bool))
+    n = kept.size
+    assert int(hdr[2]) & 0xFFFFFFFF == POOL_MAGIC, f"pool b={b} h={kvh}: not valid"
+    assert int(hdr[1]) == L, f"pool b={b} h={kvh}: length {int(hdr[1])}, expected {L}"
+    assert int(hdr[0]) == n, f"pool b={b} h={kvh}: {int(hdr[0])} records, mask keeps {n}"
+    if n == 0:
+        return 0
+    maps = cpu["pool_slot"][b, kvh]
+    max_ctx = maps.shape[0] - cpu["pool"].shape[2] * 32
+    slots = maps[kept].astype(np.int64)
+    assert np.array_equal(np.sort(slots), np.arange(n)), f"pool b={b} h={kvh}: slots are not 0..{n - 1}"
+    np.testing.assert_array_equal(maps[max_ctx + slots], kept, err_msg=f"pool b={b} h={kvh}: slot->position map")
+    kc, vc, meta = unpage_int4(cpu["int4_codes"], cpu["int4_meta"], cpu["table"], b, kvh, L)
+    pk, pv, pm = unpack_pool(cpu["pool"][b, kvh], D, n)
+    np.testing.assert_array_equal(pk[slots], kc[kept], err_msg=f"pool K codes b={b} h={kvh}")
+    np.testing.assert_array_equal(pv[slots], vc[kept], err_msg=f"pool V codes b={b} h={kvh}")
+    np.testing.assert_array_equal(pm[slots], meta[kept], err_msg=f"pool meta b={b} h={kvh}")
+    return n

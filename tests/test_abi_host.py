@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert kvc.kvc_abi_version() == 3
+    assert kvc.kvc_abi_version() == 4
     assert kvc.kvc_status_string(0) == "ok"
     assert kvc.kvc_status_string(-4) == "workspace too small"
 
@@ -112,6 +112,36 @@ def test_noalloc_attention_argument_errors(lib):
     assert need > kvc.NOALLOC_SCRATCH_BYTES
     assert na(ctypes.byref(big), FAKE, 0, 32, 0.0, FAKE, None, None) == -4
     assert "scratch" in kvc.kvc_last_error()
+
+
+def test_pool_argument_errors(lib):
+    """Pool fields are validated before any device work."""
+    c = desc(pool_capacity=100, pool=FAKE, pool_slot=FAKE, pool_header=FAKE)
+    assert attn(lib, c) == -2                                   # not a multiple of 64
+    c = desc(pool_capacity=128, pool=None, pool_slot=FAKE, pool_header=FAKE)
+    assert attn(lib, c) == -1
+    c = desc(pool_capacity=128, pool=FAKE + 4, pool_slot=FAKE, pool_header=FAKE)
+    assert attn(lib, c) == -3                                   # pool must be 16-byte aligned
+    ok = dict(pool=FAKE, pool_slot=FAKE, pool_header=FAKE)
+    # a refresh whose budget can keep more than the pool holds: max_ctx 1024 -> 880 INT4 positions
+    c = desc(pool_capacity=128, **ok)
+    r = lib.kvc_score_topk_mask(ctypes.byref(c), None, None, None, 0, 0, None, 500, None, 0, None)
+    assert r == -2 and "pool_capacity" in kvc.kvc_last_error()
+    c = desc(pool_capacity=448, **ok)                           # 500 per mille of 880 = 440 fits
+    assert lib.kvc_score_topk_mask(ctypes.byref(c), None, None, None, 0, 0, None, 500, FAKE, 16,
+                                   None) == -4                  # passes the pool check
+    # the block policy does not maintain a pool
+    assert lib.kvc_score_block_mask(ctypes.byref(c), None, None, None, 0, 0, None, 500, 16, 0,
+                                    None, 0, None) == -3
+    # pool sizes and the rebuild entry point
+    assert lib.kvc_pool_bytes(ctypes.byref(c)) == 2 * 8 * (448 // 32) * 40 * 128
+    assert lib.kvc_pool_bytes(ctypes.byref(desc())) == 0
+    assert lib.kvc_pool_build(ctypes.byref(desc()), None) == -3  # no pool
+    assert lib.kvc_pool_build(None, None) == -1
+    # attention over a pool needs room for the pool-mode partials too
+    need = lib.kvc_attention_workspace_bytes(ctypes.byref(c), 32)
+    assert need >= lib.kvc_attention_workspace_bytes(ctypes.byref(desc()), 32)
+    assert attn(lib, c, ws_bytes=need - 16) == -4
 
 
 def test_append_and_topk_argument_errors(lib):

@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import workloads as W
-from kvc_testlib import (assert_attention_close, check_codes, keep4_from_mask, mask_bits,
-                         oracle_heads, prot, source_np, to_f32)
+from kvc_testlib import (assert_attention_close, check_codes, check_pool, keep4_from_mask,
+                         mask_bits, oracle_heads, prot, source_np, to_f32)
 from oracle import policy, regions
 
 pytestmark = pytest.mark.gpu
@@ -48,6 +48,9 @@ def cpu_buffers(lc):
         "keep_mask": c.keep_mask.cpu().numpy(),
         "scores": c.scores.cpu().numpy(),
         "table": lc.table_np,
+        "pool": c.pool.cpu().numpy() if c.pool is not None else None,
+        "pool_slot": c.pool_slot.cpu().numpy() if c.pool is not None else None,
+        "pool_header": c.pool_header.cpu().numpy() if c.pool is not None else None,
     }
 
 
@@ -123,6 +126,8 @@ def check_pair(w, lc, cpu, qn, out, lse, b, kvh):
     keep4 = keep4_from_mask(cpu["keep_mask"][b, kvh], L, *prot(w))
     np.testing.assert_array_equal(keep4, expected_keep4(w, lc, cpu, b, kvh, L),
                                   err_msg=f"keep mask b={b} h={kvh}")
+    if cpu.get("pool") is not None:
+        check_pool(cpu, b, kvh, L, keep4, w.head_dim, prot(w)[0])
     if w.mask == "mlp" and L > 0:
         k = source_np(w, lc.layer, "K", b, L, kvh)
         v = source_np(w, lc.layer, "V", b, L, kvh)
@@ -142,8 +147,8 @@ def check_pair(w, lc, cpu, qn, out, lse, b, kvh):
     print(f"    {w.name} b={b} kvh={kvh} L={L}: max-abs {err:.2e} rel-L2 {rel:.2e} lse {lerr:.2e}", flush=True)
 
 
-def check_workload(w, pairs=None):
-    lc = LayerCache(w)
+def check_workload(w, pairs=None, pool=False):
+    lc = LayerCache(w, pool=pool)
     cpu = cpu_buffers(lc)
     qn, out, lse = run_attention(lc)
     if pairs is None:

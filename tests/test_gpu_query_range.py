@@ -1,0 +1,111 @@
+"""GPU parity of decode attention over the range of query magnitudes.
+
+The INT4 logits run on fp16 matrix instructions, so the query's path into
+them is checked at scales that make the softmax peaked (x8, x32, x64 of a
+unit-normal query), for bfloat16 and full-mantissa float32 queries, and for
+bfloat16 queries whose largest entries sit near and beyond the fp16 range
+(~3e4 and ~4e5) or far below it (2^-20). K and V carry outlier channels (x8)
+so that one quantisation group has a wide scale. Outputs must meet max-abs
+2e-3 and rel-L2 1e-3 against the float64 oracle. The LSE must be within
+2e-3 + D u S, u = 2^-24, S = the largest sum_i |q_i k_i| * scale over the
+attended tokens: the first-order bound on a float32 dot product of D terms
+(|fl(q.k) - q.k| <= D u sum|q_i k_i|), which is what a float32 logit can
+promise; an absolute 2e-3 alone is out of reach of float32 once logits
+reach ~1e3-1e4 (at unit-size queries S is a few units and the bound is
+2e-3 plus ~1e-4).
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from kvc_testlib import keep4_from_mask, oracle_heads, prot, source_np
+from oracle import reference
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SCALES = [1.0, 8.0, 32.0, 64.0, 2.0 ** 13, 2.0 ** 17, 2.0 ** -20]
+
+CASES = {
+    "bf16_d128": W.Workload("qrange_bf16", 4, 8, 2, 128, ctx_list=(145, 1000, 3000, 4500),
+                            mask="mlp", budget_permille=500, outlier_channels=4),
+    "f32_d128": W.Workload("qrange_f32", 3, 8, 2, 128, ctx_list=(200, 1500, 4000),
+                           mask="mlp", budget_permille=300, src_dtype="f32", outlier_channels=4),
+    "bf16_d64_g2": W.Workload("qrange_d64", 2, 4, 2, 64, ctx_list=(300, 2000), mask="all"),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+_caches = {}
+
+
+def layer(name):
+    from decode_attention_compressed_quantize_amd.workload_cache import LayerCache
+
+    if name not in _caches:
+        _caches.clear()
+        _caches[name] = LayerCache(CASES[name])
+    return _caches[name]
+
+
+def lse_slack(w, b, h, L, keep4, qh):
+    """D u max_t sum_i |q_i k_t,i| * scale over the attended positions (per query head)."""
+    k = source_np(w, 0, "K", b, L, h)
+    v = source_np(w, 0, "V", b, L, h)
+    kh, _ = reference.decoded(reference.encode(k, v, *prot(w)))
+    pos = reference.kept_positions(L, keep4, *prot(w))
+    scale = 1.0 / np.sqrt(w.head_dim)
+    S = (np.abs(np.asarray(qh, np.float64)) @ np.abs(kh[pos]).T).max(axis=1) * scale
+    return w.head_dim * 2.0 ** -24 * S
+
+
+def close(out, lse, ref_out, ref_lse, what, slack):
+    out = np.asarray(out, np.float64)
+    err = np.abs(out - ref_out).max()
+    rel = np.linalg.norm(out - ref_out) / max(np.linalg.norm(ref_out), 1e-30)
+    lerr = np.abs(np.asarray(lse, np.float64) - ref_lse)
+    ltol = 2e-3 + slack
+    assert err <= 2e-3, f"{what} max-abs {err:.3e}"
+    assert rel <= 1e-3, f"{what} rel-L2 {rel:.3e}"
+    assert (lerr <= ltol).all(), f"{what} lse error {lerr.max():.3e} (tolerance {ltol.min():.3e}..)"
+    return err, rel, float(lerr.max())
+
+
+@pytest.mark.parametrize("scale", SCALES)
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_attention_query_scales(name, scale):
+    import decode_attention_compressed_quantize_amd as kvc
+
+    w = CASES[name]
+    if w.src_dtype == "f32" and scale > 64:
+        pytest.skip("the near-fp16-limit cases are bfloat16 queries")
+    lc = layer(name)
+    q0 = lc.queries(0)
+    q = (q0.float() * scale).to(q0.dtype)  # a power of two: exact in either type
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device="cuda")
+    kvc.kvc_decode_attention(lc.cache, q, out, lse, lc.workspace())
+    torch.cuda.synchronize()
+    qn = q.float().cpu().numpy()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    mask = lc.cache.keep_mask.cpu().numpy()
+    G = w.group_size
+    worst = (0.0, 0.0, 0.0)
+    for b in range(w.batch):
+        L = int(lc.lengths[b])
+        for h in range(w.kv_heads):
+            keep4 = keep4_from_mask(mask[b, h], L)
+            qh = qn[b, h * G:(h + 1) * G]
+            ro, rl = oracle_heads(w, 0, b, h, L, keep4, qh)
+            hs = slice(h * G, (h + 1) * G)
+            e = close(out[b, hs], lse[b, hs], ro, rl, f"{name} x{scale:g} b={b} h={h} L={L}",
+                      lse_slack(w, b, h, L, keep4, qh))
+            worst = tuple(max(a, c) for a, c in zip(worst, e))
+    print(f"{name} q x{scale:g}: max-abs {worst[0]:.2e} rel-L2 {worst[1]:.2e} lse {worst[2]:.2e}",
+          flush=True)
