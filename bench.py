@@ -534,16 +534,188 @@ def learner_main(args):
 
 
 # ---------------------------------------------------------------------- GPU
+def decode_run(args, workload, steps, warmup, calls, reps, pool_mode="auto", replicas_arg=0):
+    """Build one workload's caches (with replicas), run ``warmup`` + ``steps`` timed decode
+    steps, then time the attention call alone: ``reps`` repetitions of ``calls`` calls per
+    layer, rotating over the replicas as the steps do. Returns the measurements."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import decode_attention_compressed_quantize_amd as kvc
+    from decode_attention_compressed_quantize_amd.workload_cache import LayerCache
+
+    kvc.lib()
+    dev = "cuda"
+    names = WORKLOAD_LAYERS[workload]
+    total_steps = warmup + steps
+    base = [W.WORKLOADS[n].replace(decode_steps=total_steps + 1) for n in names]
+    per_replica_bytes = 0
+    layers = []
+    print(f"bench: building {workload} ({len(base)} layer caches per replica)", file=sys.stderr, flush=True)
+    tier = TIER_MODE.get(workload)
+    host_moved = 0
+
+    def pooled(w):
+        if pool_mode == "off" or tier:
+            return False
+        return w.policy == "token" and w.recency_window == 0 and w.mask in ("mlp", "scores", "all")
+
+    for li, w in enumerate(base):
+        host = W.page_table(w, li)[1] if tier else 0
+        lc = LayerCache(w, layer=li, device=dev, keep_sources=False, host_pages=host,
+                        pool=pooled(w))
+        if tier == "cold":
+            host_moved += lc.demote_cold_pages()
+        elif tier == "all":
+            host_moved += lc.stream_int4_region()
+        layers.append(lc)
+        per_replica_bytes += lc.cache.nbytes()
+    replicas = replicas_arg
+    read_per_replica = sum(algorithmic_bytes(lc.w, lc.lengths, kept_counts(lc.w, lc.lengths))
+                           for lc in layers)
+    if replicas <= 0:
+        replicas = max(1, math.ceil((1 << 30) / read_per_replica) + 1) if len(base) < 8 else 1
+    if tier == "all":
+        replicas = 1  # host-tier reads are not served by the GPU's caches
+    # replicas are device copies of the prefilled caches, within 96 GiB in all
+    replicas = max(1, min(replicas, int((96 << 30) // max(1, per_replica_bytes))))
+    reps_c = [layers]
+    for r in range(1, replicas):
+        reps_c.append([lc.replica() for lc in layers])
+    # As in a model, the layers of one batch share one lengths tensor, which the
+    # caller advances once per step.
+    for rep in reps_c:
+        for lc in rep[1:]:
+            assert np.array_equal(lc.lengths, rep[0].lengths)
+            lc.seq_lens = rep[0].seq_lens
+            lc.cache.seq_lens = rep[0].seq_lens
+            lc.cache.desc.seq_lens = rep[0].seq_lens.data_ptr()
+    print(f"bench: {replicas} replica(s), {per_replica_bytes / 2**30:.2f} GiB each", file=sys.stderr, flush=True)
+
+    # inputs for every step, resident before timing
+    inputs = []
+    for r, rep in enumerate(reps_c):
+        per = []
+        for li, lc in enumerate(rep):
+            w = lc.w
+            steps_here = (total_steps + replicas - 1) // replicas + 1
+            L0 = lc.lengths.copy()
+            ks, vs, qs = [], [], []
+            for s in range(steps_here):
+                ks.append(W.kv_rows_torch(w, li, "K", L0 + s, dev)[:, None])
+                vs.append(W.kv_rows_torch(w, li, "V", L0 + s, dev)[:, None])
+                qs.append(W.queries_torch(w, li, s + 1, dev))
+            out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+            lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev)
+            per.append({"k": ks, "v": vs, "q": qs, "out": out, "lse": lse, "ws": lc.workspace(),
+                        "state": lc.refresh_state(),
+                        "one": torch.ones(w.batch, dtype=torch.int32, device=dev),
+                        "lens": lc.lengths.astype(np.int64).copy(), "n": 0})
+        inputs.append(per)
+
+    stream = torch.cuda.current_stream()
+
+    def attend(lc, st, s):
+        w = lc.w
+        if w.recency_window > 0:
+            kvc.kvc_decode_attention_windowed(lc.cache, w.recency_window, st["q"][s], st["out"],
+                                              st["lse"], st["ws"])
+        else:
+            kvc.kvc_decode_attention(lc.cache, st["q"][s], st["out"], st["lse"], st["ws"])
+
+    def step(i):
+        r = i % replicas
+        byts = 0
+        reps_c[r][0].seq_lens.add_(1)
+        for li, lc in enumerate(reps_c[r]):
+            st = inputs[r][li]
+            s = st["n"]
+            st["n"] += 1
+            st["lens"] += 1
+            lc.append_refresh(st["k"][s], st["v"][s], st["one"], ws=st["state"])
+            attend(lc, st, s)
+            byts += algorithmic_bytes(lc.w, st["lens"], kept_counts(lc.w, st["lens"]))
+        return byts
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    step_bytes = 0
+    t0.record(stream)
+    for i in range(warmup, warmup + steps):
+        step_bytes += step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    gbs = step_bytes / steps / (ms * 1e-3) / 1e9
+
+    # the attention call alone: each call between two HIP events on the launch
+    # stream, `calls` calls per layer and repetition, replicas in rotation (the
+    # layers interleaved as in a step), caches as the last step left them
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)] for _ in names]
+    per_layer_t = {}  # layer name -> per repetition, the call times (layers of one name pooled)
+    for rep in range(reps):
+        for j in range(calls):
+            r = (rep * calls + j) % replicas
+            for li, lc in enumerate(reps_c[r]):
+                st = inputs[r][li]
+                e0, e1 = ev[li][j]
+                e0.record(stream)
+                attend(lc, st, max(0, st["n"] - 1))
+                e1.record(stream)
+        torch.cuda.synchronize()
+        times = {}
+        for li, lc in enumerate(reps_c[0]):
+            times.setdefault(lc.w.name, []).extend(e0.elapsed_time(e1) for e0, e1 in ev[li])
+        for n, t in times.items():
+            per_layer_t.setdefault(n, []).append(t)
+    call_bytes = {}
+    for li, lc in enumerate(reps_c[0]):
+        call_bytes[lc.w.name] = algorithmic_bytes(lc.w, inputs[0][li]["lens"],
+                                                  kept_counts(lc.w, inputs[0][li]["lens"]))
+    per_layer = {}
+    for n, runs in per_layer_t.items():
+        means = [statistics.fmean(x) for x in runs]
+        flat = sorted(t for x in runs for t in x)
+        med = statistics.median(means)
+        peak = HOST_LINK_PEAK_GBS if tier == "all" else HBM_PEAK_GBS
+        gb = call_bytes[n] / (med * 1e-3) / 1e9
+        per_layer[n] = {
+            "attention_ms": round(med, 5), "attention_GBs": round(gb, 1), "frac": round(gb / peak, 4),
+            "rep_mean_ms_min": round(min(means), 5), "rep_mean_ms_max": round(max(means), 5),
+            "call_ms_p10": round(flat[len(flat) // 10], 5), "call_ms_p90": round(flat[(9 * len(flat)) // 10], 5),
+            "algorithmic_bytes": int(call_bytes[n]),
+        }
+    a_ms = statistics.fmean(v["attention_ms"] for v in per_layer.values())
+    a_bytes = statistics.fmean(v["algorithmic_bytes"] for v in per_layer.values())
+    res = {
+        "names": names, "base": base, "tier": tier, "host_moved": host_moved, "layers": layers,
+        "replicas": replicas, "pooled": bool(pooled(base[0])), "ms_per_step": ms, "gbs": gbs,
+        "per_layer": per_layer, "a_ms": a_ms, "a_bytes": a_bytes,
+        "a_gbs": a_bytes / (a_ms * 1e-3) / 1e9,
+    }
+    del reps_c, inputs, layers
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="long128k",
                     choices=sorted(WORKLOAD_LAYERS) + sorted(LEARNER) + sorted(DENSE))
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >1 GiB between reuses")
+    ap.add_argument("--calls", type=int, default=50, help="attention calls per layer and repetition")
+    ap.add_argument("--reps", type=int, default=7, help="repetitions of the attention-call timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the uniform4k / longtail figures that the default run adds")
     ap.add_argument("--pool", choices=["auto", "on", "off"], default="auto",
                     help="kept-record pool (auto: on for the token top-k policy, whose refresh "
                          "maintains it; the block policy and the host tier read through the mask)")
@@ -560,149 +732,15 @@ def main():
         dense_main(args)
         return
 
-    import numpy as np
     import torch
 
-    import workloads as W
-    import decode_attention_compressed_quantize_amd as kvc
-    from decode_attention_compressed_quantize_amd.workload_cache import LayerCache
-
-    kvc.lib()
-    dev = "cuda"
-    names = WORKLOAD_LAYERS[args.workload]
-    total_steps = args.warmup + args.steps
-    base = [W.WORKLOADS[n].replace(decode_steps=total_steps + 1) for n in names]
-    per_replica_bytes = 0
-    layers = []
-    print(f"bench: building {args.workload} ({len(base)} layer caches per replica)", file=sys.stderr, flush=True)
-    tier = TIER_MODE.get(args.workload)
-    host_moved = 0
-    def pooled(w):
-        if args.pool == "off" or tier:
-            return False
-        return w.policy == "token" and w.recency_window == 0 and w.mask in ("mlp", "scores", "all")
-
-    for li, w in enumerate(base):
-        host = W.page_table(w, li)[1] if tier else 0
-        lc = LayerCache(w, layer=li, device=dev, keep_sources=False, host_pages=host,
-                        pool=pooled(w))
-        if tier == "cold":
-            host_moved += lc.demote_cold_pages()
-        elif tier == "all":
-            host_moved += lc.stream_int4_region()
-        layers.append(lc)
-        per_replica_bytes += lc.cache.nbytes()
-    replicas = args.replicas
-    read_per_replica = sum(algorithmic_bytes(lc.w, lc.lengths, kept_counts(lc.w, lc.lengths))
-                           for lc in layers)
-    if replicas <= 0:
-        replicas = max(1, math.ceil((1 << 30) / read_per_replica) + 1) if len(base) < 8 else 1
-    if tier == "all":
-        replicas = 1  # host-tier reads are not served by the GPU's caches
-    # replicas are device copies of the prefilled caches, within 96 GiB in all
-    replicas = max(1, min(replicas, int((96 << 30) // max(1, per_replica_bytes))))
-    reps = [layers]
-    for r in range(1, replicas):
-        reps.append([lc.replica() for lc in layers])
-    # As in a model, the layers of one batch share one lengths tensor, which the
-    # caller advances once per step.
-    for rep in reps:
-        for lc in rep[1:]:
-            assert np.array_equal(lc.lengths, rep[0].lengths)
-            lc.seq_lens = rep[0].seq_lens
-            lc.cache.seq_lens = rep[0].seq_lens
-            lc.cache.desc.seq_lens = rep[0].seq_lens.data_ptr()
-    print(f"bench: {replicas} replica(s), {per_replica_bytes / 2**30:.2f} GiB each", file=sys.stderr, flush=True)
-
-    # inputs for every step, resident before timing
-    inputs = []
-    for r, rep in enumerate(reps):
-        per = []
-        for li, lc in enumerate(rep):
-            w = lc.w
-            steps_here = (total_steps + replicas - 1) // replicas + 1
-            L0 = lc.lengths.copy()
-            ks, vs, qs = [], [], []
-            for s in range(steps_here):
-                ks.append(W.kv_rows_torch(w, li, "K", L0 + s, dev)[:, None])
-                vs.append(W.kv_rows_torch(w, li, "V", L0 + s, dev)[:, None])
-                qs.append(W.queries_torch(w, li, s + 1, dev))
-            out = torch.empty((w.batch, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
-            lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev)
-            mlp = getattr(lc, "mlp", None)
-            per.append({"k": ks, "v": vs, "q": qs, "out": out, "lse": lse, "ws": lc.workspace(),
-                        "state": lc.refresh_state(),
-                        "mlp": mlp, "one": torch.ones(w.batch, dtype=torch.int32, device=dev),
-                        "lens": lc.lengths.astype(np.int64).copy(), "n": 0})
-        inputs.append(per)
-
-    stream = torch.cuda.current_stream()
-    attn_events = []
-
-    def step(i, record):
-        r = i % replicas
-        byts = 0
-        reps[r][0].seq_lens.add_(1)
-        for li, lc in enumerate(reps[r]):
-            st = inputs[r][li]
-            s = st["n"]
-            st["n"] += 1
-            st["lens"] += 1
-            w = lc.w
-            lc.append_refresh(st["k"][s], st["v"][s], st["one"], ws=st["state"])
-            if record:
-                e0, e1 = events.pop()
-                e0.record(stream)
-            if w.recency_window > 0:
-                kvc.kvc_decode_attention_windowed(lc.cache, w.recency_window, st["q"][s], st["out"],
-                                                  st["lse"], st["ws"])
-            else:
-                kvc.kvc_decode_attention(lc.cache, st["q"][s], st["out"], st["lse"], st["ws"])
-            if record:
-                e1.record(stream)
-                attn_events.append((e0, e1, lc.w, st["lens"].copy()))
-            byts += algorithmic_bytes(w, st["lens"], kept_counts(w, st["lens"]))
-        return byts
-
-    # The attention calls of every TIME_EVERY-th timed step are bracketed by
-    # HIP events on the launch stream (an event record costs a few us of GPU
-    # time, so recording on every step would inflate the step time).
-    TIME_EVERY = 4
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps * len(names))]
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    step_bytes = 0
-    t0.record(stream)
-    for i in range(args.warmup, args.warmup + args.steps):
-        step_bytes += step(i, (i - args.warmup) % TIME_EVERY == 0)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    gbs = step_bytes / args.steps / (ms * 1e-3) / 1e9
-
-    attn_ms = [e0.elapsed_time(e1) for e0, e1, _, _ in attn_events]
-    print("bench: attention call times (ms): " + " ".join(f"{w.name[-3:]}:{t:.4f}" for (_, _, w, _), t in
-                                                     zip(attn_events, attn_ms)), file=sys.stderr, flush=True)
-    attn_bytes = [algorithmic_bytes(w, L, kept_counts(w, L)) for _, _, w, L in attn_events]
-    # per layer: the median call time (a rare slow call, e.g. the first timed one, does not
-    # move it) against the mean algorithmic bytes; the call figure averages the layers
-    per_budget = {}
-    for (e0, e1, w, L), t, bb in zip(attn_events, attn_ms, attn_bytes):
-        d = per_budget.setdefault(w.name, ([], []))
-        d[0].append(t)
-        d[1].append(bb)
-    med = {n: statistics.median(v[0]) for n, v in per_budget.items()}
-    mean_bytes = {n: sum(v[1]) / len(v[1]) for n, v in per_budget.items()}
-    detail = {n: {"attention_ms": round(med[n], 4),
-                  "attention_GBs": round(mean_bytes[n] / (med[n] * 1e-3) / 1e9, 1)} for n in per_budget}
-    a_ms = sum(med.values()) / len(med)
-    a_bytes = sum(mean_bytes.values()) / len(mean_bytes)
-    a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
-
+    res = decode_run(args, args.workload, args.steps, args.warmup, args.calls, args.reps, args.pool,
+                     args.replicas)
+    names, base, tier = res["names"], res["base"], res["tier"]
+    ms, gbs = res["ms_per_step"], res["gbs"]
+    a_ms, a_bytes, a_gbs = res["a_ms"], res["a_bytes"], res["a_gbs"]
+    peak = HOST_LINK_PEAK_GBS if tier == "all" else HBM_PEAK_GBS
+    print("bench: attention per layer: " + json.dumps(res["per_layer"]), file=sys.stderr, flush=True)
     line = {
         "metric": "compressed-KV decode attention: KV bytes GB/s (% HBM peak), decode steps/s",
         "value": round(gbs, 2),
@@ -721,8 +759,8 @@ def main():
             "layers": names if len(set(names)) > 1 else f"{len(names)} x {names[0]}",
             "batch": base[0].batch, "q_heads": base[0].q_heads, "kv_heads": base[0].kv_heads,
             "head_dim": base[0].head_dim, "context": int(base[0].lengths().max()),
-            "replicas": replicas,
-            "kept_record_pool": bool(pooled(base[0])),
+            "replicas": res["replicas"],
+            "kept_record_pool": res["pooled"],
             "keep_policy": [(f"{w.policy}" + (f"{w.block_tokens}" if w.policy == "block" else "")
                              + (f", recency window {w.recency_window}" if w.recency_window else "")
                              + (f", budget {w.budget_permille / 10:g}%" if w.budget_permille else ""))
@@ -731,27 +769,50 @@ def main():
         "host_tier": None if not tier else {
             "mode": {"cold": "pages with every position evicted demoted after the prefill",
                      "all": "every whole INT4-region page in the host tier"}[tier],
-            "pages_in_host_tier_per_replica": host_moved,
-            "int4_pages_per_replica": int(sum(lc.num_pages for lc in layers)),
+            "pages_in_host_tier_per_replica": res["host_moved"],
+            "int4_pages_per_replica": int(sum(lc.num_pages for lc in res["layers"])),
         },
         "decode_steps_per_s": round(1000.0 / ms, 2),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "attention": {"ms_per_call": round(a_ms, 5), "GBs": round(a_gbs, 1), "per_layer": detail,
-                      "timed_calls": len(attn_ms), "timed_every_nth_step": TIME_EVERY,
-                      "statistic": "median call time per layer, averaged over the layers"},
+        "attention": {"ms_per_call": round(a_ms, 5), "GBs": round(a_gbs, 1), "per_layer": res["per_layer"],
+                      "timed_calls_per_layer": args.calls * args.reps,
+                      "statistic": f"per layer: median over {args.reps} repetitions of the mean of "
+                                   f"{args.calls} event-timed calls (replicas in rotation); the call "
+                                   f"figure averages the layers"},
         "roofline": {
             "kernel": "kvc_decode_attention call: attention_kernel (INT4 chunks + INT8 region) "
                       "then merge_kernel, timed together with HIP events on the launch stream",
             "bound": "host-link" if tier == "all" else "hbm",
             "achieved": round(a_gbs, 1),
-            "peak": HOST_LINK_PEAK_GBS if tier == "all" else HBM_PEAK_GBS,
+            "peak": peak,
             "unit": "GB/s",
-            "frac": round(a_gbs / (HOST_LINK_PEAK_GBS if tier == "all" else HBM_PEAK_GBS), 4),
+            "frac": round(a_gbs / peak, 4),
             "traffic": measured_traffic(args.workload),
             "algorithmic_bytes_per_call": int(a_bytes),
         },
         "cpu_baseline": None,
     }
+    del res
+    torch.cuda.empty_cache()
+    if args.workload == "long128k" and not args.no_others:
+        # the other two single-GPU workloads: attention per call and the decode step
+        others = {}
+        for wl in ("uniform4k", "longtail"):
+            o = decode_run(args, wl, 100, 5, args.calls, 3)
+            pl = next(iter(o["per_layer"].values()))
+            others[wl] = {
+                "attention_us": round(1000 * pl["attention_ms"], 2), "attention_GBs": pl["attention_GBs"],
+                "frac": pl["frac"], "rep_mean_us_range": [round(1000 * pl["rep_mean_ms_min"], 2),
+                                                          round(1000 * pl["rep_mean_ms_max"], 2)],
+                "algorithmic_bytes_per_call": pl["algorithmic_bytes"],
+                "ms_per_step": round(o["ms_per_step"], 5), "step_GBs": round(o["gbs"], 1),
+                "kept_record_pool": o["pooled"], "batch": o["base"][0].batch,
+                "context": int(o["base"][0].lengths().max()), "replicas": o["replicas"],
+                "timing": f"100 decode steps; attention: median over 3 repetitions of {args.calls} calls",
+            }
+            del o
+            torch.cuda.empty_cache()
+        line["other_workloads"] = others
     if tier != "all":
         add_read_ceiling(line)
     if not args.no_cpu:

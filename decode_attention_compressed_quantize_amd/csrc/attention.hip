@@ -53,6 +53,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRing = 4;      // INT4 steps in flight per wave (the one in use plus three prefetched)
 constexpr float kLoScale = 2048.0f;  // the second fp16 part of P, scaled up by 2^11
+#ifndef KVC_POOL_LOAD_AUX
+#define KVC_POOL_LOAD_AUX 2
+#endif
+// cache policy of the pool's direct-to-LDS loads: 2 marks them non-temporal (each
+// record is read once per call, so it should not displace reused lines)
+constexpr int kLoadAux = KVC_POOL_LOAD_AUX;
 static_assert(kRing % 2 == 0, "ring slots alternate between K and V steps");
 static_assert(kMaxChunk / kWaves <= 64 * 32, "the compaction gives each lane one mask word of a wave's range");
 
@@ -857,12 +863,12 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
 #pragma unroll
       for (int i = 0; i < NL16; ++i)
         __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
-                                         (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, kLoadAux);
 #pragma unroll
       for (int i = 0; i < NL4; ++i)
         __builtin_amdgcn_global_load_lds(src + NL16 * 1024 + i * 256 + lane * 4,
                                          (__attribute__((address_space(3))) void*)(dst + NL16 * 1024 + i * 256),
-                                         4, 0, 0);
+                                         4, 0, kLoadAux);
     };
 #pragma unroll
     for (int k = 0; k < NB; ++k) issue(k, k);

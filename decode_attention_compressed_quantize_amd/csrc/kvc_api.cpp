@@ -282,9 +282,10 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
     }
   }
   // The incremental update relies on every score below the previous length
-  // being unchanged, which holds when this call writes the new scores itself.
+  // being unchanged, which holds when this call writes the new scores itself
+  // or when the caller declares it by passing n_new.
   return launched(kvc::launch_topk(*c, budget_permille, static_cast<kvc::TopkState*>(ws),
-                                   mlp != nullptr, stream));
+                                   mlp != nullptr || n_new != nullptr, stream));
 }
 
 KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* mlp,

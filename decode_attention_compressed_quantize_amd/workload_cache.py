@@ -167,7 +167,9 @@ class LayerCache:
             return
         mlp = getattr(self, "mlp", None) if k_new is not None and w.mask == "mlp" else None
         if mlp is None:
-            k_new = v_new = n_new = None
+            # given scores: a decode step wrote none below the previous lengths, which
+            # passing n_new declares (the refresh state may then update in place)
+            k_new = v_new = None
         budget = 1000 if w.mask == "all" else w.budget_permille
         if self.block_policy:
             kvc_score_block_mask(self.cache, mlp, k_new, v_new, n_new, budget, w.recency_window,

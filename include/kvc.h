@@ -220,7 +220,12 @@ KVC_API kvc_status kvc_quantize_append(const kvc_cache* c, const void* k_new, co
  *                  or NULL when the caller already wrote `scores`.
  *   k_new, v_new, src, n_new_max, n_new : as for kvc_quantize_append; used
  *                  only when mlp != NULL (scores for the appended positions
- *                  are w2 . relu(W1 [k||v] + b1) + b2 in float32).
+ *                  are w2 . relu(W1 [k||v] + b1) + b2 in float32). With
+ *                  mlp == NULL, k_new, v_new, src and n_new_max are ignored and
+ *                  n_new may be NULL; a non-NULL n_new declares that the scores
+ *                  of positions below the previous call's lengths are unchanged
+ *                  (the caller wrote only those of appended positions), which
+ *                  allows the in-place update described under ws.
  *   budget_permille : 0..1000. For each (sequence, kv head), with
  *                  n4 = max(0, L-144) and k = floor(budget*n4/1000), keeps the k
  *                  INT4-region positions with the highest score; ties keep the
@@ -229,7 +234,8 @@ KVC_API kvc_status kvc_quantize_append(const kvc_cache* c, const void* k_new, co
  *                  bytes that the caller keeps for this cache from call to call
  *                  (zero-filled before the first call). With NULL every call
  *                  refreshes the mask from all scores. With a state, a call that
- *                  computes the scores itself (mlp != NULL) after exactly one
+ *                  computes the scores itself (mlp != NULL), or whose n_new
+ *                  declares the older scores unchanged, after exactly one
  *                  appended position since the previous call with the same
  *                  budget updates the mask in place; otherwise it refreshes
  *                  fully and rebuilds the state. Either way the mask is the one
@@ -535,7 +541,7 @@ KVC_API size_t kvc_dense_attention_workspace_bytes(const kvc_dense_cache* c, int
 
 /*
  * kvc_stream_read_probe - a measurement aid, not a step of the method: read a
- * device buffer once with plain 16-byte loads and XOR every 32-bit word into
+ * device buffer once with 16-byte non-temporal loads and XOR every 32-bit word into
  * *out (which the caller zeroes first), so that the attention kernels'
  * bandwidth can also be stated against the read rate this part reaches on a
  * streaming pattern, next to the vendor peak.

@@ -148,7 +148,17 @@ def _pool_decode_run(w, steps, budgets, stall=(), shrink=None, attend_every=25, 
         lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
         lc.lengths = lens.copy()
         nn = torch.from_numpy(n_new).cuda()
-        if step % 2 and w.protect:
+        if w.mask != "mlp":
+            # caller-written scores: write those of the appended positions, then
+            # refresh with n_new (the older scores are declared unchanged)
+            m.kvc_quantize_append(lc.cache, k_new, v_new, nn)
+            if w.mask == "scores":
+                for b in range(w.batch):
+                    if n_new[b]:
+                        L = int(lens[b])
+                        lc.cache.scores[b, :, L - 1] = W.given_scores_torch(w, 0, b, L, "cuda")[:, L - 1]
+            m.kvc_score_topk_mask(lc.cache, None, None, None, nn, budget, ws=state)
+        elif step % 2 and w.protect:
             m.kvc_append_score_topk_mask(lc.cache, lc.mlp, k_new, v_new, nn, budget, ws=state)
         else:
             m.kvc_quantize_append(lc.cache, k_new, v_new, nn)
@@ -191,6 +201,24 @@ def test_pool_pure_kv4_incremental():
                                                 ctx=None, ctx_list=(3, 1200), decode_steps=120,
                                                 budget_permille=400)
     _pool_decode_run(w, 120, lambda s: 400)
+
+
+def test_pool_given_scores_incremental():
+    """Caller-written scores (the long-tail workload's kind) with n_new declaring
+    the older scores unchanged: the refresh state's in-place update runs without
+    an MLP; mask and pool checked every step across the recent window's edge."""
+    w = W.WORKLOADS["longtail"].replace(name="given_inc", batch=4, kv_heads=2, q_heads=8,
+                                        ctx_range=None, ctx_list=(150, 400, 1500, 3000),
+                                        decode_steps=200)
+    _pool_decode_run(w, 160, lambda s: 500 if s < 100 else 400, stall=[(30, 2)], attend_every=40)
+
+
+def test_pool_keep_all_incremental():
+    """Every position kept (budget 1000, the uniform workload's mask) refreshed in
+    place each step: each record entering the INT4 region joins the pool."""
+    w = W.WORKLOADS["uniform4k"].replace(name="all_inc", batch=3, kv_heads=2, q_heads=8,
+                                         ctx=None, ctx_list=(100, 700, 2000), decode_steps=160)
+    _pool_decode_run(w, 150, lambda s: 1000, attend_every=50)
 
 
 def test_rollback_reappend_restores_parity():
