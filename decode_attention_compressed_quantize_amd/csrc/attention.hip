@@ -98,7 +98,7 @@ struct AttnParams {
   int host_pages;
   // pool mode
   const uint8_t* pool;
-  const int32_t* pool_header;
+  int32_t* pool_header;  // word 3 of a pair's header: its finished workgroups (pool mode)
   int pool_cap;
   uint32_t* errors;
 };
@@ -237,8 +237,17 @@ struct Smem {
   float vm[kWaves][16];
 };
 
-// Combine the four waves' (m, l, o) held in LDS into one partial and store it.
-template <int D, int G, typename OF>
+// A store that is performed at device scope (written through this XCD's L2),
+// or a plain store.
+template <bool COHERENT>
+__device__ inline void put_f32(float* a, float v) {
+  if constexpr (COHERENT) __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *a = v;
+}
+
+// Combine the four waves' (m, l, o) held in LDS into one partial and store it
+// (COHERENT: with device-scope stores, for a merge inside the same launch).
+template <int D, int G, bool COHERENT, typename OF>
 __device__ inline void store_partial(Smem<D, G>& sm, OF o_of, float* dst) {
   const int tid = threadIdx.x;
   for (int i = tid; i < G * D; i += kThreads) {
@@ -258,8 +267,11 @@ __device__ inline void store_partial(Smem<D, G>& sm, OF o_of, float* dst) {
       }
     }
     float* row = dst + (size_t)h * (2 + D);
-    row[2 + ch] = o;
-    if (ch == 0) { row[0] = M; row[1] = l; }
+    put_f32<COHERENT>(row + 2 + ch, o);
+    if (ch == 0) {
+      put_f32<COHERENT>(row, M);
+      put_f32<COHERENT>(row + 1, l);
+    }
   }
 }
 
@@ -1004,20 +1016,42 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
 }
 
 // ------------------------------------------------------------------ merge
-// One wave per (query head, kv head, sequence) merges the nsplit + 1 partials
-// of its (sequence, kv head) in a fixed order (outputs summed in index
-// order): M = max_j m_j, w_j = 2^(m_j - M) (0 for empty partials),
+// One wave merges the nsplit + 1 partials of one (sequence, kv head) for one
+// query head in a fixed order (outputs summed in index order):
+// M = max_j m_j, w_j = 2^(m_j - M) (0 for empty partials),
 // out = sum_j w_j o_j / sum_j w_j l_j, lse = ln 2 * (M + log2 sum_j w_j l_j).
 // Lane l owns output channels [l*CPL, l*CPL + CPL); the (m, l) pairs and the
 // lane's slices of the first kPre partials are loaded together up front.
-template <int D, int G>
-__global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
+// wts: kMaxParts floats of LDS that only this wave uses. COHERENT: the
+// partials were written in the same launch with device-scope stores, so they
+// are read with device-scope loads (past this XCD's L2).
+template <int D, int G, bool COHERENT>
+__device__ void merge_head(const AttnParams& p, int b, int kvh, int h, int lane, float* wts) {
   constexpr int CPL = D / 64;  // channels per lane
   constexpr int kPre = 32;     // partials whose slices are loaded up front
   typedef float fcpl __attribute__((ext_vector_type(CPL)));
-  __shared__ float wts[kMaxParts];
-  const int h = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  // CPL (1 or 2) consecutive floats, as one load
+  auto ld = [](const float* a) -> fcpl {
+    if constexpr (!COHERENT) {
+      return *reinterpret_cast<const fcpl*>(a);
+    } else if constexpr (CPL == 2) {
+      const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      return __builtin_bit_cast(fcpl, u);
+    } else {
+      const float v = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return __builtin_bit_cast(fcpl, v);
+    }
+  };
+  auto ld2 = [](const float* a) -> float2v {
+    if constexpr (!COHERENT) {
+      return *reinterpret_cast<const float2v*>(a);
+    } else {
+      const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      return __builtin_bit_cast(float2v, u);
+    }
+  };
   const int np = p.nsplit + 1;
   const size_t pstride = (size_t)G * (2 + D);
   const float* run = p.parts + ((size_t)b * p.hkv + kvh) * np * pstride + (size_t)h * (2 + D);
@@ -1026,7 +1060,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
 #pragma unroll
   for (int j = 0; j < kPre; ++j) {
     const int jj = j < np ? j : np - 1;
-    pre[j] = *reinterpret_cast<const fcpl*>(part(jj) + 2 + CPL * lane);
+    pre[j] = ld(part(jj) + 2 + CPL * lane);
   }
   // (m, l) of partials lane, lane + 64, ...: at most kMaxParts / 64 per lane
   constexpr int kML = kMaxParts / 64;
@@ -1037,7 +1071,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
     mj[r] = -INFINITY;
     lj[r] = 0.0f;
     if (j < np) {
-      const float2v ml = *reinterpret_cast<const float2v*>(part(j));
+      const float2v ml = ld2(part(j));
       mj[r] = ml[0];
       lj[r] = ml[1];
     }
@@ -1061,11 +1095,18 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
   for (int j = 0; j < kPre; ++j)
     if (j < np) acc += wts[j] * pre[j];
   // every partial is written by the attention kernel, so no load is skipped
-  for (int j = kPre; j < np; ++j) acc += wts[j] * *reinterpret_cast<const fcpl*>(part(j) + 2 + CPL * lane);
+  for (int j = kPre; j < np; ++j) acc += wts[j] * ld(part(j) + 2 + CPL * lane);
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   const size_t oq = (size_t)b * p.hkv * G + kvh * G + h;
   *reinterpret_cast<fcpl*>(p.out + oq * D + CPL * lane) = acc * inv;
   if (lane == 0 && p.lse) p.lse[oq] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+}
+
+// One wave per (query head, kv head, sequence).
+template <int D, int G>
+__global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
+  __shared__ float wts[kMaxParts];
+  merge_head<D, G, false>(p, blockIdx.z, blockIdx.y, blockIdx.x, threadIdx.x, wts);
 }
 
 // TIER: some pages live in the host tier (a separate pool in pinned host memory).
@@ -1100,16 +1141,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if constexpr (POOL) {
       int4_pool_chunk<D, G, QBF16>(p, sm, b, kvh, split);
       __syncthreads();
-      store_partial<D, G>(sm, [&](int w) { return reinterpret_cast<float*>(&sm.u.stage[w][0][0]); }, dst);
+      store_partial<D, G, POOL>(sm, [&](int w) { return reinterpret_cast<float*>(&sm.u.stage[w][0][0]); }, dst);
     } else {
       int4_mask_chunk<D, G, QBF16, TIER>(p, sm, b, kvh, split);
       __syncthreads();
-      store_partial<D, G>(sm, [&](int w) { return &sm.u.w4[w].ro.o[0][0]; }, dst);
+      store_partial<D, G, false>(sm, [&](int w) { return &sm.u.w4[w].ro.o[0][0]; }, dst);
     }
   } else {
     int8_region<D, G, QBF16>(p, sm, b, kvh);
     __syncthreads();
-    store_partial<D, G>(sm, [&](int w) { return &sm.u.i8.o[w][0][0]; }, dst);
+    store_partial<D, G, POOL>(sm, [&](int w) { return &sm.u.i8.o[w][0][0]; }, dst);
+  }
+  if constexpr (POOL) {
+    // The last of the pair's np workgroups to finish merges the partials, so
+    // no second launch is needed. Word 3 of the pair's header counts finished
+    // workgroups: the refresh leaves it 0, and the last workgroup resets it.
+    // The partials were stored at device scope (through this XCD's L2) and
+    // every wave waits for its stores to complete before the count, so a
+    // workgroup that sees the final count reads complete partials with
+    // device-scope loads; no L2 writeback or invalidation is needed.
+    static_assert(sizeof(sm.u) >= kWaves * kMaxParts * sizeof(float), "merge weights fit the staging area");
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int32_t* ctr = p.pool_header + 4 * (size_t)pair + 3;
+      const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == np - 1;
+      // a count at or past the last (a header the refresh did not write) is
+      // cleared too, so the next call starts from 0
+      if (old >= np - 1) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (s_last) {
+      const int wave = threadIdx.x >> 6;
+      if (wave < G)
+        merge_head<D, G, true>(p, b, kvh, wave, threadIdx.x & 63,
+                         reinterpret_cast<float*>(&sm.u) + wave * kMaxParts);
+    }
   }
 }
 
@@ -1126,7 +1195,8 @@ hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, bool p
     if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false, false>), grid, dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((attention_kernel<D, G, false, false, false>), grid, dim3(kThreads), 0, s, p);
   }
-  hipLaunchKernelGGL((merge_kernel<D, G>), dim3(G, c.num_kv_heads, c.batch), dim3(64), 0, s, p);
+  // pool mode merges inside the attention kernel
+  if (!pool) hipLaunchKernelGGL((merge_kernel<D, G>), dim3(G, c.num_kv_heads, c.batch), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

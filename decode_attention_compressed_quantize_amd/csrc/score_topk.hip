@@ -240,7 +240,12 @@ __device__ __attribute__((always_inline)) bool topk_step(const TopkParams& p, To
     const int xpos = p.sink + n4p;
     const uint64_t x = comp_key(order_key(sc[n4p]), xpos);
     const long long out_before = n4p - kp;  // candidates not kept
-    if (k == kp) {
+    if (k == n4) {
+      // every INT4-region position kept (budget 1000): x joins the kept set;
+      // the lists stay empty, as nothing is ever ranked against them
+      ins_slot = (int)kp;
+      ins_pos = xpos;
+    } else if (k == kp) {
       if (k == 0) {
         clear_pos = xpos;
         B = list_insert<false>(B, nb, x, nb == out_before, lane);
@@ -531,7 +536,7 @@ __device__ __attribute__((always_inline)) void topk_pair(const TopkParams& p, in
   const bool all = k >= n4;
   long long rank[3];
   rank[0] = (k > 0 && !all) ? k : 0;
-  rank[1] = (st && k > 0) ? (k - kTopkBuf + 1 > 1 ? k - kTopkBuf + 1 : 1) : 0;
+  rank[1] = (st && k > 0 && !all) ? (k - kTopkBuf + 1 > 1 ? k - kTopkBuf + 1 : 1) : 0;
   rank[2] = (st && k < n4) ? (k + kTopkBuf < n4 ? k + kTopkBuf : n4) : 0;
   uint32_t prefix[3] = {0, 0, 0};
   long long remaining[3] = {rank[0], rank[1], rank[2]};
@@ -637,7 +642,7 @@ __device__ __attribute__((always_inline)) void topk_pair(const TopkParams& p, in
           const uint32_t key = order_key(v[i]);
           if (key > T) gt |= 1u << i;
           else if (key == T) eq |= 1u << i;
-          if (st && key >= lo && key <= hi) {
+          if (st && !all && key >= lo && key <= hi) {
             const uint32_t slot = atomicAdd(&ncand, 1u);
             if (slot < kCandCap) cand[slot] = comp_key(key, t);
           }
@@ -755,10 +760,12 @@ __device__ __attribute__((always_inline)) void topk_pair(const TopkParams& p, in
     }
   }
   // global rank (1-based) of cand[i] is above_hi + i + 1
-  const int na = (int)(k < kTopkBuf ? k : kTopkBuf);
-  const int nb = (int)(n4 - k < kTopkBuf ? n4 - k : kTopkBuf);
+  // with every position kept the lists stay empty (the in-place update never
+  // consults them while the budget stays 1000)
+  const int na = all ? 0 : (int)(k < kTopkBuf ? k : kTopkBuf);
+  const int nb = all ? 0 : (int)(n4 - k < kTopkBuf ? n4 - k : kTopkBuf);
   if (wid == 0) {
-    bool ok = fits;
+    bool ok = fits || all;
     if (ok && lane < na) {
       const long long i = k - lane - above_hi - 1;
       if (i >= 0 && i < nc) st->a[lane] = cand[i];

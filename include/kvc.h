@@ -75,8 +75,14 @@
  *               pos < max_ctx holds the slot of kept INT4-region position
  *               pos, entry max_ctx + s the position whose record is in slot
  *               s < count (other entries unspecified).
- *   pool_header int32 [B][Hkv][4]  (count, length, magic, 0): the kept count,
- *               the sequence length the pool describes and a validity word.
+ *   pool_header int32 [B][Hkv][4]  (count, length, magic, n): the kept count,
+ *               the sequence length the pool describes, a validity word, and
+ *               a counter that kvc_decode_attention uses during a call (the
+ *               workgroups of a (sequence, kv head) that have finished; the
+ *               last one merges the partial results and sets it back to 0).
+ *               The calls that write the pool set it to 0. Because of that
+ *               counter, attention calls on one cache with a pool must not
+ *               overlap in time (issue them on one stream, or order them).
  * kvc_score_topk_mask / kvc_append_score_topk_mask update the pool with the
  * mask: a decode step copies at most one record per (sequence, kv head); a
  * full refresh copies the records that enter the kept set, into the slots of
@@ -336,7 +342,10 @@ KVC_API kvc_status kvc_append_score_block_mask(const kvc_cache* c, const float* 
  *   ws, ws_bytes : device scratch of at least
  *                  kvc_attention_workspace_bytes(c, num_q_heads) bytes for the
  *                  per-chunk partials; its contents on entry do not matter.
- *                  Calls sharing one workspace must not overlap.
+ *                  Calls sharing one workspace must not overlap; with a pool,
+ *                  neither may calls on one cache (see pool_header).
+ *   One launch with a pool (the last workgroup of each (sequence, kv head)
+ *   merges its partials); two without (chunks, then the merge).
  *   Attends to the INT8 positions and to the INT4-region positions whose
  *   keep_mask bit is set (with a pool: to the pool's records, which are those
  *   positions when the pool describes the current length). A sequence with

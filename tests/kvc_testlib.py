@@ -152,6 +152,7 @@ def check_pool(cpu, b, kvh, L, keep4, D, n_sink=regions.N_SINK):
     assert int(hdr[2]) & 0xFFFFFFFF == POOL_MAGIC, f"pool b={b} h={kvh}: not valid"
     assert int(hdr[1]) == L, f"pool b={b} h={kvh}: length {int(hdr[1])}, expected {L}"
     assert int(hdr[0]) == n, f"pool b={b} h={kvh}: {int(hdr[0])} records, mask keeps {n}"
+    assert int(hdr[3]) == 0, f"pool b={b} h={kvh}: workgroup counter left at {int(hdr[3])}"
     if n == 0:
         return 0
     maps = cpu["pool_slot"][b, kvh]

@@ -747,3 +747,25 @@ def test_full_decode_step_layer_sampled():
     for b, h in [(0, 0), (77, 5), (127, 7)]:
         print(f"  check fullstep b={b} kvh={h}", flush=True)
         check_pair(w, lc, cpu, qn, out, lse, b, h)
+
+
+@pytest.mark.parametrize("pool", [False, True])
+def test_stale_nonfinite_int8_scales_in_unused_slots(pool):
+    """INT8 ring slots past a short sequence's length may hold anything - an
+    un-zeroed allocation, or the scale of an inf row left behind by a rollback.
+    Those slots get weight exactly 0, so inf / NaN scales there change nothing:
+    outputs stay finite and match the oracle."""
+    w = W.WORKLOADS["long128k_b10"].replace(name="stale8", batch=4, ctx=None,
+                                            ctx_list=(5, 40, 143, 1000), budget_permille=500)
+    lc = LayerCache(w, pool=pool)
+    c = lc.cache
+    for b, L in enumerate(lc.lengths):
+        if L < 144:
+            c.int8_scales[b, :, int(L):, 0] = float("inf")
+            c.int8_scales[b, :, int(L):, 1] = float("nan")
+    cpu = cpu_buffers(lc)
+    qn, out, lse = run_attention(lc)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    for b in range(w.batch):
+        for h in range(w.kv_heads):
+            check_pair(w, lc, cpu, qn, out, lse, b, h)
