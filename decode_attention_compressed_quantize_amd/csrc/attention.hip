@@ -820,6 +820,20 @@ __device__ inline void read_staged(uint32_t lds, uint32_t o_kc, uint32_t o_km, u
   }
 }
 
+// read_staged with the wait for `after` tiles of NL loads each still in
+// flight behind the one read (at most N; the count is an immediate, so the
+// few tail cases are separate instantiations).
+template <int D, int NL, int N>
+__device__ inline void read_staged_after(int after, uint32_t lds, uint32_t o_kc, uint32_t o_km, uint32_t o_vc,
+                                         uint32_t o_vm, u32x4 (&r)[8]) {
+  if constexpr (N == 0) {
+    read_staged<D, 0>(lds, o_kc, o_km, o_vc, o_vm, r);
+  } else {
+    if (after >= N) read_staged<D, NL * N>(lds, o_kc, o_km, o_vc, o_vm, r);
+    else read_staged_after<D, NL, N - 1>(after, lds, o_kc, o_km, o_vc, o_vm, r);
+  }
+}
+
 // Chunk `split` of the pool of (b, kvh): records [r0, r1), the split-th of
 // nsplit equal shares (whole 32-record tiles) of the pool's count. Tile
 // t0 + wave + 4j goes to wave `wave` (the four waves read neighbouring tiles
@@ -868,9 +882,9 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
     const uint32_t o_vm = VM + (s * NG + core.gc) * 16;
     uint8_t* ring = &sm.u.stage[wave][0][0];
     const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
-    // direct-to-LDS loads of tile jt of this wave (past its last tile: the last again)
+    // direct-to-LDS loads of tile jt < ntw of this wave into ring slot k
     auto issue = [&](int jt, int k) {
-      const uint8_t* src = base + (size_t)(t0 + wave + kWaves * (jt < ntw ? jt : ntw - 1)) * TILE;
+      const uint8_t* src = base + (size_t)(t0 + wave + kWaves * jt) * TILE;
       uint8_t* dst = ring + k * TILE;
 #pragma unroll
       for (int i = 0; i < NL16; ++i)
@@ -883,7 +897,8 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
                                          4, 0, kLoadAux);
     };
 #pragma unroll
-    for (int k = 0; k < NB; ++k) issue(k, k);
+    for (int k = 0; k < NB; ++k)
+      if (k < ntw) issue(k, k);
     float pr[8];
     for (int jt0 = 0; jt0 < ntw; jt0 += NB) {
 #pragma unroll
@@ -891,8 +906,10 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
         const int jt = jt0 + k;
         if (jt >= ntw) break;
         u32x4 r[8];
-        read_staged<D, NL * (NB - 1)>(ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
-        issue(jt + NB, k);
+        // tiles in flight behind this one: NB - 1, fewer at the end (no tile
+        // is loaded twice)
+        read_staged_after<D, NL, NB - 1>(ntw - 1 - jt, ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
+        if (jt + NB < ntw) issue(jt + NB, k);
         const int lim = r1 - 32 * (t0 + wave + kWaves * jt);
         uint32_t kc0[NG], kc1[NG], km[8], vc[8], vm[8];
 #pragma unroll

@@ -78,7 +78,7 @@ class LayerCache:
         dt = torch.bfloat16 if w.src_dtype == "bf16" else torch.float32
         # prefill in sequence batches so the staging tensor stays small
         lmax = int(self.lengths.max())
-        per = max(1, int(2 ** 31 // max(1, lmax * w.kv_heads * w.head_dim * 2)))
+        per = max(1, int(2 ** 29 // max(1, lmax * w.kv_heads * w.head_dim * 2)))
         for b0 in range(0, w.batch, per):
             b1 = min(w.batch, b0 + per)
             k_new = torch.zeros((b1 - b0, lmax, w.kv_heads, w.head_dim), dtype=dt, device=self.device)
@@ -350,7 +350,7 @@ class DenseLayerCache:
         lmax = int(self.lengths.max())
         if lmax == 0:
             return
-        per = max(1, int(2 ** 31 // max(1, lmax * w.kv_heads * w.head_dim * 2)))
+        per = max(1, int(2 ** 29 // max(1, lmax * w.kv_heads * w.head_dim * 2)))
         for b0 in range(0, w.batch, per):
             b1 = min(w.batch, b0 + per)
             k_new = torch.zeros((b1 - b0, lmax, w.kv_heads, w.head_dim), dtype=dt, device=self.device)
