@@ -297,8 +297,31 @@ struct Int4Core {
   // Query operands of column (gc, hc): entries s*D/4 + 8m + perm[r] of the
   // head (only the slot of group gc is non-zero), scaled by 2^e with e chosen
   // per head so that the largest |q| lands in [2^14, 2^15).
+  // The lane's raw query words (bf16 pairs or floats): D/4 entries of its
+  // column's head, loaded by load_q so that the loads can be issued early.
+  static constexpr int NE = D / 4;
+  template <bool QBF16>
+  using QRaw = u32x4[QBF16 ? NE / 8 : NE / 4];
+
+  template <bool QBF16>
+  __device__ void load_q(const AttnParams& p, int b, int kvh, QRaw<QBF16>& raw) const {
+    const int ln = threadIdx.x & 63;
+    const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + (ln & 15) % G) * D + (ln >> 4) * NE;
+    const u32x4* qp = QBF16 ? reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + qoff)
+                            : reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(p.q) + qoff);
+#pragma unroll
+    for (int i = 0; i < (QBF16 ? NE / 8 : NE / 4); ++i) raw[i] = qp[i];
+  }
+
   template <bool QBF16>
   __device__ void setup(const AttnParams& p, int b, int kvh) {
+    QRaw<QBF16> raw;
+    load_q<QBF16>(p, b, kvh, raw);
+    setup_from<QBF16>(p, raw);
+  }
+
+  template <bool QBF16>
+  __device__ void setup_from(const AttnParams& p, const QRaw<QBF16>& raw) {
     lane = threadIdx.x & 63;
     s = lane >> 4;
     n = lane & 15;
@@ -309,14 +332,11 @@ struct Int4Core {
     l_col = vm1 = 0.0f;
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[m] = accl[m] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-    constexpr int NE = D / 4;
-    const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + hc) * D + s * NE;
     float qe[NE];
     if constexpr (QBF16) {
-      const u32x4* qp = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) + qoff);
 #pragma unroll
       for (int i = 0; i < NE / 8; ++i) {
-        const u32x4 x = qp[i];
+        const u32x4 x = raw[i];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           qe[8 * i + 2 * k] = __uint_as_float(x[k] << 16);
@@ -324,12 +344,11 @@ struct Int4Core {
         }
       }
     } else {
-      const float4v* qp = reinterpret_cast<const float4v*>(reinterpret_cast<const float*>(p.q) + qoff);
 #pragma unroll
       for (int i = 0; i < NE / 4; ++i) {
-        const float4v x = qp[i];
+        const u32x4 x = raw[i];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) qe[4 * i + k] = x[k];
+        for (int k = 0; k < 4; ++k) qe[4 * i + k] = __uint_as_float(x[k]);
       }
     }
     // the head's largest magnitude (its D entries are spread over the four rows)
@@ -841,8 +860,9 @@ __device__ inline void read_staged_after(int after, uint32_t lds, uint32_t o_kc,
 // buffers filled by direct-to-LDS loads (one 16-byte piece per lane per
 // instruction, whole contiguous tiles), so kStage tiles are in flight per
 // wave without holding registers; a tile's pieces then come out of LDS in
-// the order the core consumes them. The pool header load is issued before
-// the query's, so both are in flight together.
+// the order the core consumes them. The pool header and the query are loaded
+// together; the first tiles' loads are issued as soon as the header is in,
+// and the query is converted while they are in flight.
 template <int D, int G, bool QBF16>
 __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, int split) {
   using S = Shape<D, G>;
@@ -858,7 +878,10 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   const int pair = b * p.hkv + kvh;
   const u32x4 hdr = *reinterpret_cast<const u32x4*>(p.pool_header + 4 * (size_t)pair);
   const int L = p.seq_lens[b];
-  core.template setup<QBF16>(p, b, kvh);
+  // the query is loaded now and converted after the first tiles' loads are
+  // issued, so that its conversion overlaps their latency
+  typename Int4Core<D, G, !QBF16>::template QRaw<QBF16> qraw;
+  core.template load_q<QBF16>(p, b, kvh, qraw);
   int cnt = 0;
   if (hdr[2] == kPoolMagic) {
     cnt = (int)hdr[0];
@@ -873,32 +896,33 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   const int t0 = r0 / kPoolTile;
   const int ntiles = r1 > r0 ? (r1 - r0 + kPoolTile - 1) / kPoolTile : 0;
   const int ntw = __builtin_amdgcn_readfirstlane(ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0);
+  const uint8_t* base = p.pool + (size_t)pair * pool_pair_bytes(D, p.pool_cap);
+  uint8_t* ring = &sm.u.stage[wave][0][0];
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+  // direct-to-LDS loads of tile jt < ntw of this wave into ring slot k
+  auto issue = [&](int jt, int k) {
+    const uint8_t* src = base + (size_t)(t0 + wave + kWaves * jt) * TILE;
+    uint8_t* dst = ring + k * TILE;
+#pragma unroll
+    for (int i = 0; i < NL16; ++i)
+      __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, kLoadAux);
+#pragma unroll
+    for (int i = 0; i < NL4; ++i)
+      __builtin_amdgcn_global_load_lds(src + NL16 * 1024 + i * 256 + lane * 4,
+                                       (__attribute__((address_space(3))) void*)(dst + NL16 * 1024 + i * 256),
+                                       4, 0, kLoadAux);
+  };
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+    if (k < ntw) issue(k, k);
+  core.template setup_from<QBF16>(p, qraw);
   if (ntw > 0) {
-    const uint8_t* base = p.pool + (size_t)pair * pool_pair_bytes(D, p.pool_cap);
     const int s = lane >> 4;
     const uint32_t o_kc = (uint32_t)lane * S::SB;
     const uint32_t o_km = KM + (s * NG + core.gc) * 16;
     const uint32_t o_vc = VC + (s * VD + core.vdw) * 16;
     const uint32_t o_vm = VM + (s * NG + core.gc) * 16;
-    uint8_t* ring = &sm.u.stage[wave][0][0];
-    const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
-    // direct-to-LDS loads of tile jt < ntw of this wave into ring slot k
-    auto issue = [&](int jt, int k) {
-      const uint8_t* src = base + (size_t)(t0 + wave + kWaves * jt) * TILE;
-      uint8_t* dst = ring + k * TILE;
-#pragma unroll
-      for (int i = 0; i < NL16; ++i)
-        __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
-                                         (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, kLoadAux);
-#pragma unroll
-      for (int i = 0; i < NL4; ++i)
-        __builtin_amdgcn_global_load_lds(src + NL16 * 1024 + i * 256 + lane * 4,
-                                         (__attribute__((address_space(3))) void*)(dst + NL16 * 1024 + i * 256),
-                                         4, 0, kLoadAux);
-    };
-#pragma unroll
-    for (int k = 0; k < NB; ++k)
-      if (k < ntw) issue(k, k);
     float pr[8];
     for (int jt0 = 0; jt0 < ntw; jt0 += NB) {
 #pragma unroll
@@ -1133,11 +1157,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ Smem<D, G> sm;
   // One-dimensional grid, dispatched in index order and spread round-robin
   // over the 8 XCDs. The INT8 regions take `pairs` consecutive items, before
-  // (int8_first) or after the INT4 chunks; INT4 item j is chunk j / pairs of
-  // pair j % pairs (chunk-major: the first, fullest chunks of every sequence
-  // go first, and each XCD gets every 8th pair of every chunk index, i.e. the
-  // same mix of sequence lengths). Pair = b * Hkv + kvh. Partial index: INT4
-  // chunk j at j, the INT8 region at nsplit.
+  // (int8_first = 1) or after (0) the INT4 chunks; INT4 item j is chunk
+  // j / pairs of pair j % pairs (chunk-major: the first, fullest chunks of
+  // every sequence go first, and each XCD gets every 8th pair of every chunk
+  // index, i.e. the same mix of sequence lengths). Pair = b * Hkv + kvh.
+  // Partial index: INT4 chunk j at j, the INT8 region at nsplit.
   const int pairs = p.hkv * p.batch;
   const int n4 = pairs * p.nsplit;
   const int item = blockIdx.x;

@@ -140,7 +140,11 @@ AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window, bool po
     p.pool = 1;
     p.nsplit = (int)j;
     p.chunk = 0;
-    p.int8_first = pairs <= 768 ? 1 : 0;
+    // INT8 regions first when each pair has many chunks (they overlap the
+    // chunks' streaming); after the chunks with one chunk per pair (a first
+    // round of INT8 workgroups would hold every CU for their latency, and
+    // alternating them with chunks halves the streaming workgroups)
+    p.int8_first = j == 1 ? 0 : 1;
     return p;
   }
   constexpr long long kResident = 768;  // 3 workgroups per CU x 256 CUs
