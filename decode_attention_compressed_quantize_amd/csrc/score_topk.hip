@@ -220,25 +220,54 @@ __device__ inline uint64_t list_pop_front(uint64_t v, int& n) {
 // length L - 1 under this budget or a list it needs has run out.
 __device__ __attribute__((always_inline)) bool topk_step(const TopkParams& p, TopkState* st, int L, int n4, long long k,
                           const float* sc, uint32_t* mrow, int lane, int b, int h) {
-  if (L < 1 || st->magic != kTopkMagic || st->budget != p.budget || st->len != L - 1) return false;
+  if (L < 1) return false;
   const int slots = p.sink + p.recent;
   const int n4p = L - 1 > slots ? L - 1 - slots : 0;
   const long long kp = ((long long)p.budget * n4p) / 1000;
-  if (st->k != kp) return false;
   const int pair = b * p.hkv + h;
   int32_t* phdr = p.pool.cap > 0 ? p.pool.header + 4 * (size_t)pair : nullptr;
-  // the pool must hold exactly the kept records of length L - 1
-  if (phdr && (phdr[2] != (int32_t)kPoolMagic || phdr[1] != L - 1 || phdr[0] != kp)) return false;
-  int ins_pos = -1, ins_slot = -1;  // pool: the record of ins_pos goes to ins_slot
+  // Every load the step may need is issued before any decision, so that the
+  // step costs about one memory round trip: the state and its lists, the pool
+  // header, the entering position's score, and - speculatively - the record
+  // of the entering position (the one the pool takes in most steps; its page
+  // comes from the table first) and the slot of the smallest kept key (the
+  // one an entering key displaces).
+  const bool entering = n4 != n4p;
+  const int xpos = p.sink + n4p;  // leaves the recent window (or, unprotected, is appended)
+  const float sx = entering ? sc[n4p] : 0.0f;
+  const uint32_t s_magic = st->magic;
+  const int32_t s_len = st->len, s_k = st->k, s_budget = st->budget;
   int na = st->na, nb = st->nb;
+  uint64_t A = lane < na ? st->a[lane] : 0, B = lane < nb ? st->b[lane] : 0;  // lane < 64 = kTopkBuf
+  int32_t h0 = 0, h1 = 0, h2 = 0;
+  if (phdr) {
+    h0 = phdr[0];
+    h1 = phdr[1];
+    h2 = phdr[2];
+  }
+  int xpage = -1;
+  uint4 xrec = make_uint4(0u, 0u, 0u, 0u);
+  if (phdr && entering) {
+    const int pg = p.pool.block_table[(size_t)b * p.pool.max_pages + (xpos >> 4)];
+    if (pg >= 0 && pg < p.pool.num_pages + p.pool.host_pages) {
+      xpage = pg;
+      if (lane < pool_chunks(p.pool.D))
+        xrec = *reinterpret_cast<const uint4*>(pool_src_chunk(p.pool, pg, h, xpos, lane));
+    }
+  }
+  int a0slot = -1;
+  if (phdr && na > 0) {
+    const int a0pos = (int)comp_pos(wave_at(A, 0));
+    if (a0pos >= 0 && a0pos < p.max_ctx) a0slot = pool_slot_of(p.pool, pair)[a0pos];
+  }
+  if (s_magic != kTopkMagic || s_budget != p.budget || s_len != L - 1 || s_k != kp) return false;
+  // the pool must hold exactly the kept records of length L - 1
+  if (phdr && (h2 != (int32_t)kPoolMagic || h1 != L - 1 || h0 != kp)) return false;
+  int ins_pos = -1, ins_slot = -1;  // pool: the record of ins_pos goes to ins_slot
   if (na < 0 || na > kTopkBuf || nb < 0 || nb > kTopkBuf) return false;
-  uint64_t A = lane < na ? st->a[lane] : 0, B = lane < nb ? st->b[lane] : 0;
   int clear_pos = -1, set_pos = -1;
-  if (n4 != n4p) {
-    // position sink + n4p leaves the recent window (or, without INT8
-    // protection, is the one appended) and becomes a candidate
-    const int xpos = p.sink + n4p;
-    const uint64_t x = comp_key(order_key(sc[n4p]), xpos);
+  if (entering) {
+    const uint64_t x = comp_key(order_key(sx), xpos);
     const long long out_before = n4p - kp;  // candidates not kept
     if (k == n4) {
       // every INT4-region position kept (budget 1000): x joins the kept set;
@@ -255,7 +284,7 @@ __device__ __attribute__((always_inline)) bool topk_step(const TopkParams& p, To
         if (x > a0) {  // x displaces the smallest kept key
           clear_pos = comp_pos(a0);
           ins_pos = xpos;
-          if (phdr) ins_slot = pool_slot_of(p.pool, pair)[clear_pos];
+          if (phdr) ins_slot = a0slot;
           const bool whole = na == k;
           A = list_pop_front(A, na);
           B = list_push_front(B, nb, a0, lane);
@@ -287,7 +316,7 @@ __device__ __attribute__((always_inline)) bool topk_step(const TopkParams& p, To
     // a slot outside the kept records or a page outside the pools: rebuild instead
     if (ins_slot < 0 || ins_slot > kp || (ins_slot == kp && k == kp) || ins_slot >= p.pool.cap)
       return false;
-    ins_page = pool_page(p.pool, b, ins_pos);
+    ins_page = ins_pos == xpos && xpage >= 0 ? xpage : pool_page(p.pool, b, ins_pos);
     if (ins_page < 0) return false;
   }
   if (lane == 0) {
@@ -310,7 +339,12 @@ __device__ __attribute__((always_inline)) bool topk_step(const TopkParams& p, To
   if (lane < nb) st->b[lane] = B;
   if (phdr) {
     if (ins_pos >= 0) {
-      pool_copy_wave(p.pool, pair, h, ins_page, ins_pos, ins_slot, lane);
+      if (ins_pos == xpos && xpage >= 0) {  // the record fetched ahead
+        if (lane < pool_chunks(p.pool.D))
+          pool_put_chunk(pool_tile(p.pool, pair, ins_slot), p.pool.D, ins_slot % kPoolTile, lane, xrec);
+      } else {
+        pool_copy_wave(p.pool, pair, h, ins_page, ins_pos, ins_slot, lane);
+      }
       if (lane == 0) {
         pool_slot_of(p.pool, pair)[ins_pos] = ins_slot;
         pool_pos_of(p.pool, pair)[ins_slot] = ins_pos;

@@ -187,13 +187,13 @@ def _pool_decode_run(w, steps, budgets, stall=(), shrink=None, attend_every=25, 
 
 
 def test_pool_incremental_every_step():
-    """300 steps: lists drain and rebuild (full refreshes update the pool from the
-    changed mask bits), a budget change at step 200, stalled sequences; pool checked
+    """400 steps: lists drain and rebuild (full refreshes update the pool from the
+    changed mask bits), a budget change at step 300, stalled sequences; pool checked
     every step."""
     w = W.WORKLOADS["fullstep"].replace(name="pinc", batch=3, kv_heads=2, q_heads=8, layers=1,
-                                        ctx=2000, ctx_list=(140, 700, 2000), decode_steps=300,
+                                        ctx=2000, ctx_list=(140, 700, 2000), decode_steps=400,
                                         budget_permille=500)  # the pool holds the larger budget
-    _pool_decode_run(w, 300, lambda s: 500 if s < 200 else 300, stall=[(50, 1), (51, 1), (120, 2)])
+    _pool_decode_run(w, 400, lambda s: 500 if s < 300 else 300, stall=[(50, 1), (51, 1), (120, 2)])
 
 
 def test_pool_pure_kv4_incremental():
