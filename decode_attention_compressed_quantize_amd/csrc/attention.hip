@@ -218,10 +218,13 @@ struct Smem {
     uint32_t vbuf[32][kVStride];          // V codes of the current 32 tokens
     uint32_t mbuf[32][D / 32];            // K or V (scale | min << 16) of the current 32 tokens
   };
+  // INT8 region: the 144 slots' rows (K codes then V codes) at a padded
+  // stride, so that 16 rows read at one offset fall in distinct banks
+  static constexpr int kRow8 = 2 * D + 16;
   struct Int8 {
-    float q[G][D];
-    int8_t vcode[kWaves][36][D];
-    float p[kWaves][36][G];
+    uint8_t rows[144][kRow8];
+    float scales[144][2];
+    float p[kWaves][48][G];  // p * V scale of the wave's slots
     float o[kWaves][G][D];
   };
   // pool mode: each wave's ring of kStage tiles filled by direct-to-LDS loads;
@@ -956,104 +959,173 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
 }
 
 // ------------------------------------------------------------------ INT8 region
-// The <= 144 protected positions of one (sequence, kv head) in float32: each
-// wave takes 36 slots, lane = slot for the logits, lane = channels for P.V.
+// The <= 144 protected positions of one (sequence, kv head): high-fidelity
+// attention over INT8 codes (KV4-RL review, section 1 and 3).
 // Which slots hold attended positions follows from L alone: all 144 when
 // L >= 144, else exactly slots [0, L) (slot = position below 144). So every
-// slot's codes and scales are loaded at once, together with the query and the
-// length, and masked afterwards; the region's sums do not depend on order.
+// slot's codes and scales are loaded at once and masked afterwards.
+//  - Loads: each slot's K and V rows (2D bytes) and the scales go straight to
+//    LDS with 4-byte direct-to-LDS loads, one row per instruction, coalesced.
+//  - Logits on v_mfma_f32_16x16x32_f16: rows are 16 slots, columns the G
+//    heads. A code c enters as the exact fp16 subnormal (c + 128) * 2^-24 (a
+//    byte XOR and a byte permute); the query is scaled per head by a power of
+//    two into [2^14, 2^15) and split into two fp16 parts (one for a bf16
+//    query), so q.(c + 128) is float32-accurate, and 128 * sum(q) is taken off
+//    in float32. Wave w owns the row blocks w, w + 4, w + 8 of the 9.
+//  - Softmax per head over the wave's slots, then P.V in float32 on the VALU
+//    (lane = channels, p * V_scale from LDS, codes read from the rows).
+// The wave's (m, l, o) per head go to LDS for store_partial.
 template <int D, int G, bool QBF16>
 __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh) {
   constexpr int CPL = D / 64;
-  constexpr int NW = D / 16;  // 16-byte words per K (or V) row
+  constexpr int NK = D / 32;  // MFMA k-steps over the head dimension
+  constexpr int RB = 9;       // 16-slot row blocks of the 144 slots
+  constexpr int kRow = Smem<D, G>::kRow8;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int slot = wave * 36 + lane;
+  const int s4 = lane >> 4, n = lane & 15;
   const int slots = p.sink + p.recent;  // 144, or 0 without INT8 protection
-  const bool inr = lane < 36 && slot < slots;
-  const size_t base = ((size_t)b * p.hkv + kvh) * slots;
-  u32x4 kw[NW];
-  float2v sc = {0.0f, 0.0f};
-  if (inr) {
-    const u32x4* row = reinterpret_cast<const u32x4*>(p.codes8 + (base + slot) * 2 * D);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) kw[i] = row[i];
-    u32x4 vw[NW];
-#pragma unroll
-    for (int i = 0; i < NW; ++i) vw[i] = row[NW + i];
-    sc = *reinterpret_cast<const float2v*>(p.scales8 + (base + slot) * 2);
-#pragma unroll
-    for (int i = 0; i < NW; ++i) *reinterpret_cast<u32x4*>(&sm.u.i8.vcode[wave][lane][16 * i]) = vw[i];
-  }
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int h = i / D, d = i % D;
-    sm.u.i8.q[h][d] = load_q<QBF16>(p.q, ((size_t)b * p.hkv * G + kvh * G + h) * D + d) * p.alpha;
-  }
+  auto& i8 = sm.u.i8;
   int L = p.seq_lens[b];
   if ((L < 0 || L > p.max_ctx) && threadIdx.x == 0) flag(p, KVC_ERR_LENGTH);
   L = clamp_len(p, L);
   const int nvalid = L < slots ? L : slots;
-  const int cntw = nvalid - wave * 36 < 0 ? 0 : (nvalid - wave * 36 > 36 ? 36 : nvalid - wave * 36);
-  const bool valid = lane < cntw;
+  // ---- rows and scales into LDS (only the slots that can be valid)
+  const size_t base = ((size_t)b * p.hkv + kvh) * slots;
+  if (nvalid > 0) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(p.codes8) + base * 2 * D;
+    for (int r = wave; r < nvalid; r += kWaves)
+      if (lane < 2 * D / 4)
+        __builtin_amdgcn_global_load_lds(src + (size_t)r * 2 * D + lane * 4,
+                                         (__attribute__((address_space(3))) void*)&i8.rows[r][0], 4, 0, 0);
+    const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(p.scales8 + base * 2);
+    const int sbytes = nvalid * 8;
+    for (int o = 256 * wave; o < sbytes; o += 256 * kWaves)
+      if (o + lane * 4 < sbytes)
+        __builtin_amdgcn_global_load_lds(ssrc + o + lane * 4,
+                                         (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(&i8.scales[0][0]) + o),
+                                         4, 0, 0);
+  }
+  // ---- query operands of column n (head n < G): 2^e_h * q, hi and lo fp16
+  float qe[NK][8];
+  const int hq = n < G ? n : 0;
+  const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + hq) * D;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qe[kk][t] = load_q<QBF16>(p.q, qoff + 32 * kk + 8 * s4 + t);
+  float mx = 0.0f, qsum = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      mx = fmaxf(mx, fabsf(qe[kk][t]));
+      qsum += qe[kk][t];
+    }
+  mx = rows_max(mx);      // over the head's D entries (four lanes n, n + 16, ...)
+  qsum = rows_sum(qsum);
+  int e = 0;
+  if (mx > 0.0f) {
+    const int ex = (int)((__float_as_uint(mx) >> 23) & 255u) - 127;
+    e = 14 - ex;
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+  }
+  const float qsc = exp2i(e);
+  half8 bh[NK], bl[QBF16 ? 1 : NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float v = n < G ? qe[kk][t] * qsc : 0.0f;
+      const _Float16 hi = (_Float16)v;
+      bh[kk][t] = hi;
+      if constexpr (!QBF16) bl[kk][t] = (_Float16)(v - (float)hi);
+    }
+  // logit of code sum: (acc * 2^(24 - e) - 128 * sum(q)) * K_scale * alpha
+  const float unscale = exp2i(24 - e);
+  const float off = 128.0f * qsum;
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  float s[G];
+  // ---- logits of the wave's row blocks
+  constexpr int kMaxRB = (RB + kWaves - 1) / kWaves;  // 3
+  float sl[kMaxRB][4];
+  float m = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h) s[h] = -INFINITY;
-  if (valid) {
-    float dot[G];
+  for (int i = 0; i < kMaxRB; ++i) {
+    const int rb = wave + kWaves * i;
 #pragma unroll
-    for (int h = 0; h < G; ++h) dot[h] = 0.0f;
+    for (int j = 0; j < 4; ++j) sl[i][j] = -INFINITY;
+    if (rb >= RB || 16 * rb >= nvalid) continue;
+    float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t* row = &i8.rows[16 * rb + n][0];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
+    for (int kk = 0; kk < NK; ++kk) {
+      const uint2 x = *reinterpret_cast<const uint2*>(row + 32 * kk + 8 * s4);
+      const uint32_t x0 = x.x ^ 0x80808080u, x1 = x.y ^ 0x80808080u;
+      const half8 a = as_half8(__builtin_amdgcn_perm(0u, x0, 0x0c010c00u), __builtin_amdgcn_perm(0u, x0, 0x0c030c02u),
+                               __builtin_amdgcn_perm(0u, x1, 0x0c010c00u), __builtin_amdgcn_perm(0u, x1, 0x0c030c02u));
+      acc = mfma16x16x32(a, bh[kk], acc);
+      if constexpr (!QBF16) acc = mfma16x16x32(a, bl[kk], acc);
+    }
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float c = (float)(int8_t)(kw[i][k / 4] >> (8 * (k % 4)));
-#pragma unroll
-        for (int h = 0; h < G; ++h) dot[h] = fmaf(sm.u.i8.q[h][16 * i + k], c, dot[h]);
+    for (int j = 0; j < 4; ++j) {
+      const int slot = 16 * rb + 4 * s4 + j;
+      if (slot < nvalid) {
+        sl[i][j] = (acc[j] * unscale - off) * i8.scales[slot][0] * p.alpha;
+        m = fmaxf(m, sl[i][j]);
       }
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = sc[0] * dot[h];
   }
-  // p of slot j for the G heads, side by side, so the P.V loop reads them at once
-  float m[G], l[G], o[G][CPL];
+  m = rows_max(m);  // over the wave's slots, per head (column n)
+  float l = 0.0f;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mx = wave_max(s[h]);
-    m[h] = mx;
-    const float pr = valid ? __builtin_amdgcn_exp2f(s[h] - mx) : 0.0f;
-    l[h] = wave_sum(pr);
-    // slots past cntw hold whatever the buffer holds: their weight is exactly 0
-    if (lane < 36) sm.u.i8.p[wave][lane][h] = valid ? pr * sc[1] : 0.0f;
+  for (int i = 0; i < kMaxRB; ++i) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  // P.V over all 36 slots of the wave: slots past cntw have weight 0 and
-  // codes that are finite integers whatever the buffer holds, so the loop has
-  // a fixed trip count and its LDS reads can be issued together
-#pragma unroll 12
-  for (int j = 0; j < 36; ++j) {
-    float pj[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) pj[h] = sm.u.i8.p[wave][j][h];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const float v = (float)sm.u.i8.vcode[wave][j][lane * CPL + c];
-#pragma unroll
-      for (int h = 0; h < G; ++h) o[h][c] = fmaf(pj[h], v, o[h][c]);
+    for (int j = 0; j < 4; ++j) {
+      const int slot = 16 * (wave + kWaves * i) + 4 * s4 + j;
+      const bool valid = slot < nvalid && wave + kWaves * i < RB;
+      const float pr = valid ? __builtin_amdgcn_exp2f(sl[i][j] - m) : 0.0f;
+      l += pr;
+      // slots past the length may hold anything: their weight is exactly 0
+      if (n < G) i8.p[wave][16 * i + 4 * s4 + j][n] = valid ? pr * i8.scales[slot][1] : 0.0f;
     }
   }
-  if (lane < G) {
+  l = rows_sum(l);
+  const bool any = m != -INFINITY;
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  // ---- P.V over the wave's slots (16 per row block), lane = CPL channels
+  float o[G][CPL];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      if (lane == h) { sm.m[wave][h] = cntw > 0 ? m[h] : -INFINITY; sm.l[wave][h] = cntw > 0 ? l[h] : 0.0f; }
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxRB; ++i) {
+    const int rb = wave + kWaves * i;
+    if (rb >= RB || 16 * rb >= nvalid) continue;
+#pragma unroll 4
+    for (int t = 0; t < 16; ++t) {
+      float pj[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pj[h] = i8.p[wave][16 * i + t][h];
+      const uint8_t* vrow = &i8.rows[16 * rb + t][D];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float v = (float)(int8_t)vrow[lane * CPL + c];
+#pragma unroll
+        for (int h = 0; h < G; ++h) o[h][c] = fmaf(pj[h], v, o[h][c]);
+      }
+    }
+  }
+  if (lane < G) {  // lane h holds column h
+    sm.m[wave][lane] = any ? m : -INFINITY;
+    sm.l[wave][lane] = any ? l : 0.0f;
   }
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) sm.u.i8.o[wave][h][lane * CPL + c] = o[h][c];
+    for (int c = 0; c < CPL; ++c) i8.o[wave][h][lane * CPL + c] = o[h][c];
 }
 
 // ------------------------------------------------------------------ merge
