@@ -111,6 +111,24 @@ __device__ inline int clamp_len(const AttnParams& p, int L) {
   return L < 0 ? 0 : (L > p.max_ctx ? p.max_ctx : L);
 }
 
+// Words at a workgroup-uniform address read through the scalar cache and
+// waited for in the same block: the wait counts only scalar and LDS
+// operations, so the vector loads already in flight are not waited for (as
+// they would be for a vector load issued after them). The words must not
+// change during the launch.
+__device__ inline uint32_t scalar_load1(const void* ptr) {
+  uint32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+// four words at a and one at b, both in flight together
+__device__ inline void scalar_load4_1(const void* a, const void* b, u32x4& va, uint32_t& vb) {
+  asm volatile("s_load_dwordx4 %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(va), "=&s"(vb)
+               : "s"(a), "s"(b)
+               : "memory");
+}
+
 __device__ inline float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
@@ -863,9 +881,9 @@ __device__ inline void read_staged_after(int after, uint32_t lds, uint32_t o_kc,
 // buffers filled by direct-to-LDS loads (one 16-byte piece per lane per
 // instruction, whole contiguous tiles), so kStage tiles are in flight per
 // wave without holding registers; a tile's pieces then come out of LDS in
-// the order the core consumes them. The pool header and the query are loaded
-// together; the first tiles' loads are issued as soon as the header is in,
-// and the query is converted while they are in flight.
+// the order the core consumes them. The pool header, the query and the first
+// tiles (guessed from the capacity, checked against the count) are all
+// requested at once, and the query is converted while they are in flight.
 template <int D, int G, bool QBF16>
 __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, int split) {
   using S = Shape<D, G>;
@@ -879,32 +897,24 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int pair = b * p.hkv + kvh;
-  const u32x4 hdr = *reinterpret_cast<const u32x4*>(p.pool_header + 4 * (size_t)pair);
-  const int L = p.seq_lens[b];
-  // the query is loaded now and converted after the first tiles' loads are
-  // issued, so that its conversion overlaps their latency
+  // the query is loaded first and converted while the first tiles are in flight
   typename Int4Core<D, G, !QBF16>::template QRaw<QBF16> qraw;
   core.template load_q<QBF16>(p, b, kvh, qraw);
-  int cnt = 0;
-  if (hdr[2] == kPoolMagic) {
-    cnt = (int)hdr[0];
-    cnt = cnt < 0 ? 0 : (cnt > p.pool_cap ? p.pool_cap : cnt);
-  }
-  // the pool must describe the current length (reported once per pair)
-  if (split == 0 && threadIdx.x == 0 && (hdr[2] != kPoolMagic || (int)hdr[1] != clamp_len(p, L)))
-    flag(p, KVC_ERR_POOL);
-  const int share = ((cnt + p.nsplit - 1) / p.nsplit + kPoolTile - 1) / kPoolTile * kPoolTile;
-  const int r0 = split * share;
-  const int r1 = r0 + share < cnt ? r0 + share : cnt;
-  const int t0 = r0 / kPoolTile;
-  const int ntiles = r1 > r0 ? (r1 - r0 + kPoolTile - 1) / kPoolTile : 0;
-  const int ntw = __builtin_amdgcn_readfirstlane(ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0);
+  // this wave's first tile and tile count for a pool of c records (records [r0, r1))
+  auto range = [&](int c, int& t0, int& ntw, int& r1) {
+    const int share = ((c + p.nsplit - 1) / p.nsplit + kPoolTile - 1) / kPoolTile * kPoolTile;
+    const int r0 = split * share;
+    r1 = r0 + share < c ? r0 + share : c;
+    const int ntiles = r1 > r0 ? (r1 - r0 + kPoolTile - 1) / kPoolTile : 0;
+    t0 = __builtin_amdgcn_readfirstlane(r0 / kPoolTile);
+    ntw = __builtin_amdgcn_readfirstlane(ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0);
+  };
   const uint8_t* base = p.pool + (size_t)pair * pool_pair_bytes(D, p.pool_cap);
   uint8_t* ring = &sm.u.stage[wave][0][0];
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
-  // direct-to-LDS loads of tile jt < ntw of this wave into ring slot k
-  auto issue = [&](int jt, int k) {
-    const uint8_t* src = base + (size_t)(t0 + wave + kWaves * jt) * TILE;
+  // direct-to-LDS loads of pool tile `tile` of the pair into ring slot k
+  auto issue_tile = [&](int tile, int k) {
+    const uint8_t* src = base + (size_t)tile * TILE;
     uint8_t* dst = ring + k * TILE;
 #pragma unroll
     for (int i = 0; i < NL16; ++i)
@@ -916,10 +926,52 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
                                        (__attribute__((address_space(3))) void*)(dst + NL16 * 1024 + i * 256),
                                        4, 0, kLoadAux);
   };
+  int t0, ntw, r1;
+  // tile jt of this wave into ring slot k
+  auto issue = [&](int jt, int k) { issue_tile(t0 + wave + kWaves * jt, k); };
+  // The first NB tiles are requested before the header is in, for the chunk
+  // a full pool (count = capacity) would give; a count that rounds to the
+  // same 32-record shares (always with one chunk per pair, and for a budget
+  // near the capacity) keeps them. Exactly NB tiles are requested (a wave
+  // with fewer re-reads its first one, or the pair's tile 0), so that the
+  // wait for the query loaded before them is exact; every tile lies inside
+  // the pool's capacity (64 records or more).
+  range(p.pool_cap, t0, ntw, r1);
+  const int t0_guess = t0, ntw_guess = ntw;
 #pragma unroll
   for (int k = 0; k < NB; ++k)
-    if (k < ntw) issue(k, k);
+    issue_tile(k < ntw_guess ? t0 + wave + kWaves * k : (ntw_guess > 0 ? t0 + wave : 0), k);
+  // header and length through the scalar cache (word 3, which this launch
+  // changes, is not used here)
+  u32x4 hdr;
+  uint32_t Lw;
+  scalar_load4_1(p.pool_header + 4 * (size_t)pair, p.seq_lens + b, hdr, Lw);
+  const int L = (int)Lw;
+  // the query's conversion (which waits for every load in flight: the tiles'
+  // direct-to-LDS loads leave the compiler no exact count) stays behind the
+  // header's load
+#pragma unroll
+  for (auto& x : qraw) asm volatile("" : "+v"(x));
   core.template setup_from<QBF16>(p, qraw);
+  int cnt = 0;
+  if (hdr[2] == kPoolMagic) {
+    cnt = (int)hdr[0];
+    cnt = cnt < 0 ? 0 : (cnt > p.pool_cap ? p.pool_cap : cnt);
+  }
+  // the pool must describe the current length (reported once per pair)
+  if (split == 0 && threadIdx.x == 0 && (hdr[2] != kPoolMagic || (int)hdr[1] != clamp_len(p, L)))
+    flag(p, KVC_ERR_POOL);
+  range(cnt, t0, ntw, r1);
+  if (t0 != t0_guess || ntw > ntw_guess) {
+    // other tiles: the guessed loads land first, then the ring is refilled
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+      if (k < ntw) issue(k, k);
+  }
+  // else: the same tiles. Slots past ntw hold tiles that are never read: the
+  // per-tile waits below count only the tiles < ntw issued after a tile, at
+  // most what is in flight behind it, so they only wait longer.
   if (ntw > 0) {
     const int s = lane >> 4;
     const uint32_t o_kc = (uint32_t)lane * S::SB;
@@ -965,7 +1017,8 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
 // L >= 144, else exactly slots [0, L) (slot = position below 144). So every
 // slot's codes and scales are loaded at once and masked afterwards.
 //  - Loads: each slot's K and V rows (2D bytes) and the scales go straight to
-//    LDS with 4-byte direct-to-LDS loads, one row per instruction, coalesced.
+//    LDS with 4-byte direct-to-LDS loads, one row per instruction, coalesced,
+//    all 144 slots at once (not waiting for L).
 //  - Logits on v_mfma_f32_16x16x32_f16: rows are 16 slots, columns the G
 //    heads. A code c enters as the exact fp16 subnormal (c + 128) * 2^-24 (a
 //    byte XOR and a byte permute); the query is scaled per head by a power of
@@ -985,21 +1038,24 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
   const int lane = threadIdx.x & 63;
   const int s4 = lane >> 4, n = lane & 15;
   const int slots = p.sink + p.recent;  // 144, or 0 without INT8 protection
+  static_assert(kSink + kRecent == 144 && (kSink + kRecent) % kWaves == 0, "INT8 slots");
   auto& i8 = sm.u.i8;
-  int L = p.seq_lens[b];
-  if ((L < 0 || L > p.max_ctx) && threadIdx.x == 0) flag(p, KVC_ERR_LENGTH);
-  L = clamp_len(p, L);
-  const int nvalid = L < slots ? L : slots;
-  // ---- rows and scales into LDS (only the slots that can be valid)
+  // ---- rows and scales of every slot into LDS, requested without waiting for
+  // the length (slots past it are masked below, whatever they hold)
   const size_t base = ((size_t)b * p.hkv + kvh) * slots;
-  if (nvalid > 0) {
+  if (slots > 0) {
     const uint8_t* src = reinterpret_cast<const uint8_t*>(p.codes8) + base * 2 * D;
-    for (int r = wave; r < nvalid; r += kWaves)
+    constexpr int kSlots = kSink + kRecent;  // slots is kSlots here
+#pragma unroll
+    for (int i = 0; i < kSlots / kWaves; ++i) {
+      const int r = wave + kWaves * i;
       if (lane < 2 * D / 4)
         __builtin_amdgcn_global_load_lds(src + (size_t)r * 2 * D + lane * 4,
                                          (__attribute__((address_space(3))) void*)&i8.rows[r][0], 4, 0, 0);
+    }
     const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(p.scales8 + base * 2);
-    const int sbytes = nvalid * 8;
+    constexpr int sbytes = kSlots * 8;
+#pragma unroll
     for (int o = 256 * wave; o < sbytes; o += 256 * kWaves)
       if (o + lane * 4 < sbytes)
         __builtin_amdgcn_global_load_lds(ssrc + o + lane * 4,
@@ -1014,6 +1070,11 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
   for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
     for (int t = 0; t < 8; ++t) qe[kk][t] = load_q<QBF16>(p.q, qoff + 32 * kk + 8 * s4 + t);
+  // the length, read after the loads above are issued
+  int L = (int)scalar_load1(p.seq_lens + b);
+  if ((L < 0 || L > p.max_ctx) && threadIdx.x == 0) flag(p, KVC_ERR_LENGTH);
+  L = clamp_len(p, L);
+  const int nvalid = L < slots ? L : slots;
   float mx = 0.0f, qsum = 0.0f;
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
