@@ -256,6 +256,8 @@ struct Smem {
   float m[kWaves][G];
   float l[kWaves][G];
   float vm[kWaves][16];
+  float m8[kWaves][G];  // the INT8 part of a chunk workgroup that does both regions
+  float l8[kWaves][G];
 };
 
 // A store that is performed at device scope (written through this XCD's L2),
@@ -293,6 +295,43 @@ __device__ inline void store_partial(Smem<D, G>& sm, OF o_of, float* dst) {
       put_f32<COHERENT>(row, M);
       put_f32<COHERENT>(row + 1, l);
     }
+  }
+}
+
+// The output of a workgroup that did a pair's whole attention (one chunk per
+// pair, INT8 region included): the four waves' INT4 and INT8 (m, l, o)
+// combined as in the merge, normalised and stored, with the natural-log lse.
+template <int D, int G, typename OF4, typename OF8>
+__device__ inline void store_final(const AttnParams& p, Smem<D, G>& sm, OF4 o4_of, OF8 o8_of, int b, int kvh) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int h = i / D, ch = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, fmaxf(sm.m[w][h], sm.m8[w][h]));
+    float o = 0.0f, l = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.m[w][h];
+        if (mw == -INFINITY) continue;
+        const float a = __builtin_amdgcn_exp2f(mw - M);
+        o += a * o4_of(w)[h * D + ch];
+        l += a * sm.l[w][h];
+      }
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.m8[w][h];
+        if (mw == -INFINITY) continue;
+        const float a = __builtin_amdgcn_exp2f(mw - M);
+        o += a * o8_of(w)[h * D + ch];
+        l += a * sm.l8[w][h];
+      }
+    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const size_t oq = (size_t)b * p.hkv * G + kvh * G + h;
+    p.out[oq * D + ch] = o * inv;
+    if (ch == 0 && p.lse) p.lse[oq] = l > 0.0f ? (M + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -807,6 +846,201 @@ __device__ void int4_mask_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   core.finish(sm.m[wave], sm.l[wave], sm.vm[wave], &wv.ro.o[0][0], cnt > 0);
 }
 
+// ------------------------------------------------------------------ INT8 region
+// The <= 144 protected positions of one (sequence, kv head): high-fidelity
+// attention over INT8 codes (KV4-RL review, sections 1 and 3).
+// Which slots hold attended positions follows from L alone: all 144 when
+// L >= 144, else exactly slots [0, L) (slot = position below 144). So every
+// slot's codes and scales are loaded and masked afterwards.
+// The 144 slots form 9 blocks of 16; wave w takes blocks w, w + 4, w + 8
+// (those below 9). Where a wave keeps its blocks in LDS is the caller's: a
+// workgroup of the INT8 region alone loads them into its Int8 area; a chunk
+// workgroup that also does the INT8 region (one chunk per pair) loads them
+// into the wave's ring as its last tiles free it.
+//  - Loads: each slot's K and V rows (2D bytes, at a padded stride so that the
+//    16 rows read at one offset fall in distinct banks) and the block's scales
+//    go straight to LDS with 4-byte direct-to-LDS loads, one row per
+//    instruction, coalesced: kLoads8 instructions per block.
+//  - Logits on v_mfma_f32_16x16x32_f16: rows are 16 slots, columns the G
+//    heads. A code c enters as the exact fp16 subnormal (c + 128) * 2^-24 (a
+//    byte XOR and a byte permute); the query is scaled per head by a power of
+//    two into [2^14, 2^15) and split into two fp16 parts (one for a bf16
+//    query), so q.(c + 128) is float32-accurate, and 128 * sum(q) is taken off
+//    in float32.
+//  - Softmax per head over the wave's slots, then P.V in float32 on the VALU
+//    (lane = channels, p * V_scale from LDS, codes read from the rows).
+constexpr int kSlots8 = kSink + kRecent;
+constexpr int kBlocks8 = kSlots8 / 16;                      // 9
+constexpr int kWaveBlocks8 = (kBlocks8 + kWaves - 1) / kWaves;  // 3
+constexpr int kLoads8 = 16 + 1;                             // direct-to-LDS loads per block
+static_assert(kSlots8 == 144 && kSlots8 % 16 == 0, "INT8 slots");
+
+template <int D>
+constexpr int row8_stride() { return 2 * D + 16; }
+
+// Block rb (< 9) of the INT8 slots starting at slot `base` (pair * 144):
+// rows to `rows` (16 x row8_stride bytes), scales to `sc` ([16][2] floats).
+template <int D>
+__device__ inline void int8_issue_block(const AttnParams& p, size_t base, int rb, uint8_t* rows, float* sc) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(p.codes8) + (base + 16 * (size_t)rb) * 2 * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (lane < 2 * D / 4)
+      __builtin_amdgcn_global_load_lds(src + r * 2 * D + lane * 4,
+                                       (__attribute__((address_space(3))) void*)(rows + r * row8_stride<D>()), 4,
+                                       0, 0);
+  const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(p.scales8 + (base + 16 * (size_t)rb) * 2);
+  if (lane < 32)
+    __builtin_amdgcn_global_load_lds(ssrc + lane * 4, (__attribute__((address_space(3))) void*)sc, 4, 0, 0);
+}
+
+// The query entries lane (s4, n) needs: head n (< G) at dims 32 kk + 8 s4 + t.
+template <int D, int G, bool QBF16>
+__device__ inline void int8_load_q(const AttnParams& p, int b, int kvh, float (&qe)[D / 32][8]) {
+  const int lane = threadIdx.x & 63;
+  const int s4 = lane >> 4, n = lane & 15;
+  const int hq = n < G ? n : 0;
+  const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + hq) * D;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qe[kk][t] = load_q<QBF16>(p.q, qoff + 32 * kk + 8 * s4 + t);
+}
+
+// The wave's blocks, already in LDS: blk(i, rows, sc, pp) gives block i's rows
+// and scales and a [16][G] float scratch for p * V_scale. Out: m and l of
+// column n (lane n < G: head n; base-2 logits), and o[h][c] = channel
+// lane * CPL + c of head h (unnormalised); m = -inf, l = 0, o = 0 when the
+// wave has no valid slot.
+template <int D, int G, typename BLK>
+__device__ inline void int8_wave(const AttnParams& p, int nvalid, const float (&qe)[D / 32][8], BLK blk,
+                                 float& m_out, float& l_out, float (&o)[G][D / 64]) {
+  constexpr int CPL = D / 64;
+  constexpr int NK = D / 32;  // MFMA k-steps over the head dimension
+  constexpr int kRow = row8_stride<D>();
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int s4 = lane >> 4, n = lane & 15;
+  // ---- query operands of column n (head n < G): 2^e_h * q, hi and lo fp16
+  float mx = 0.0f, qsum = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      mx = fmaxf(mx, fabsf(qe[kk][t]));
+      qsum += qe[kk][t];
+    }
+  mx = rows_max(mx);  // over the head's D entries (four lanes n, n + 16, ...)
+  qsum = rows_sum(qsum);
+  int e = 0;
+  if (mx > 0.0f) {
+    const int ex = (int)((__float_as_uint(mx) >> 23) & 255u) - 127;
+    e = 14 - ex;
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+  }
+  const float qsc = exp2i(e);
+  half8 bh[NK], bl[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float v = n < G ? qe[kk][t] * qsc : 0.0f;
+      const _Float16 hi = (_Float16)v;
+      bh[kk][t] = hi;
+      bl[kk][t] = (_Float16)(v - (float)hi);
+    }
+  // logit of code sum: (acc * 2^(24 - e) - 128 * sum(q)) * K_scale * alpha
+  const float unscale = exp2i(24 - e);
+  const float off = 128.0f * qsum;
+  // ---- logits of the wave's blocks
+  float sl[kWaveBlocks8][4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kWaveBlocks8; ++i) {
+    const int rb = wave + kWaves * i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sl[i][j] = -INFINITY;
+    if (rb >= kBlocks8 || 16 * rb >= nvalid) continue;
+    const uint8_t* rows;
+    const float* sc;
+    float* pp;
+    blk(i, rows, sc, pp);
+    float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t* row = rows + n * kRow;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const uint2 x = *reinterpret_cast<const uint2*>(row + 32 * kk + 8 * s4);
+      const uint32_t x0 = x.x ^ 0x80808080u, x1 = x.y ^ 0x80808080u;
+      const half8 a = as_half8(__builtin_amdgcn_perm(0u, x0, 0x0c010c00u), __builtin_amdgcn_perm(0u, x0, 0x0c030c02u),
+                               __builtin_amdgcn_perm(0u, x1, 0x0c010c00u), __builtin_amdgcn_perm(0u, x1, 0x0c030c02u));
+      acc = mfma16x16x32(a, bh[kk], acc);
+      acc = mfma16x16x32(a, bl[kk], acc);  // zero for a bf16 query: exact either way
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * s4 + j;
+      if (16 * rb + t < nvalid) {
+        sl[i][j] = (acc[j] * unscale - off) * sc[2 * t] * p.alpha;
+        m = fmaxf(m, sl[i][j]);
+      }
+    }
+  }
+  m = rows_max(m);  // over the wave's slots, per head (column n)
+  float l = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kWaveBlocks8; ++i) {
+    const int rb = wave + kWaves * i;
+    if (rb >= kBlocks8 || 16 * rb >= nvalid) continue;
+    const uint8_t* rows;
+    const float* sc;
+    float* pp;
+    blk(i, rows, sc, pp);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * s4 + j;
+      const bool valid = 16 * rb + t < nvalid;
+      const float pr = valid ? __builtin_amdgcn_exp2f(sl[i][j] - m) : 0.0f;
+      l += pr;
+      // slots past the length may hold anything: their weight is exactly 0
+      if (n < G) pp[t * G + n] = valid ? pr * sc[2 * t + 1] : 0.0f;
+    }
+  }
+  l = rows_sum(l);
+  const bool any = m != -INFINITY;
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  // ---- P.V over the wave's slots (16 per block), lane = CPL channels
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kWaveBlocks8; ++i) {
+    const int rb = wave + kWaves * i;
+    if (rb >= kBlocks8 || 16 * rb >= nvalid) continue;
+    const uint8_t* rows;
+    const float* sc;
+    float* pp;
+    blk(i, rows, sc, pp);
+#pragma unroll 4
+    for (int t = 0; t < 16; ++t) {
+      float pj[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pj[h] = pp[t * G + h];
+      const uint8_t* vrow = rows + t * kRow + D;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float v = (float)(int8_t)vrow[lane * CPL + c];
+#pragma unroll
+        for (int h = 0; h < G; ++h) o[h][c] = fmaf(pj[h], v, o[h][c]);
+      }
+    }
+  }
+  m_out = any ? m : -INFINITY;
+  l_out = any ? l : 0.0f;
+}
+
 // ------------------------------------------------------------------ INT4, pool mode
 // Reads one staged tile of the lane's pieces from LDS: K codes of tokens n and
 // 16 + n (slot s), then for each half h of the lane's eight tokens the K meta
@@ -874,6 +1108,23 @@ __device__ inline void read_staged_after(int after, uint32_t lds, uint32_t o_kc,
   }
 }
 
+// read_staged for a wave that also loads its INT8 blocks into its ring: once
+// its last INT4 tiles are issued, each freed slot takes one INT8 block
+// (kLoads8 loads), so behind a tile with `after` tiles still to come
+// N - after blocks (counted as at most 2, which every wave has) are in flight
+// too.
+template <int D, int NL, int N, int A = N>
+__device__ inline void read_staged_tail(int after, uint32_t lds, uint32_t o_kc, uint32_t o_km, uint32_t o_vc,
+                                        uint32_t o_vm, u32x4 (&r)[8]) {
+  constexpr int B = N - A < 2 ? N - A : 2;
+  if constexpr (A == 0) {
+    read_staged<D, kLoads8 * B>(lds, o_kc, o_km, o_vc, o_vm, r);
+  } else {
+    if (after >= A) read_staged<D, NL * A + kLoads8 * B>(lds, o_kc, o_km, o_vc, o_vm, r);
+    else read_staged_tail<D, NL, N, A - 1>(after, lds, o_kc, o_km, o_vc, o_vm, r);
+  }
+}
+
 // Chunk `split` of the pool of (b, kvh): records [r0, r1), the split-th of
 // nsplit equal shares (whole 32-record tiles) of the pool's count. Tile
 // t0 + wave + 4j goes to wave `wave` (the four waves read neighbouring tiles
@@ -884,7 +1135,7 @@ __device__ inline void read_staged_after(int after, uint32_t lds, uint32_t o_kc,
 // the order the core consumes them. The pool header, the query and the first
 // tiles (guessed from the capacity, checked against the count) are all
 // requested at once, and the query is converted while they are in flight.
-template <int D, int G, bool QBF16>
+template <int D, int G, bool QBF16, bool FUSE8>
 __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, int split) {
   using S = Shape<D, G>;
   constexpr int NG = S::NG, VD = S::VD;
@@ -972,6 +1223,26 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   // else: the same tiles. Slots past ntw hold tiles that are never read: the
   // per-tile waits below count only the tiles < ntw issued after a tile, at
   // most what is in flight behind it, so they only wait longer.
+  // FUSE8 (one chunk per pair): the workgroup does the INT8 region too. Wave
+  // block i goes into ring slot (ntw + i) % NB, the i-th slot that the last
+  // NB tiles free (or, with fewer than NB tiles, after the loop), followed by
+  // its scales and, where it fits, its [16][G] p scratch (else in slot
+  // (ntw + 3 + i) % NB).
+  constexpr int kRow8 = Smem<D, G>::kRow8;
+  constexpr bool kPInSlot = 16 * kRow8 + 128 + 16 * G * 4 <= TILE;
+  static_assert(!FUSE8 || (16 * kRow8 + 128 <= TILE && NB >= kWaveBlocks8 &&
+                           (kPInSlot || NB >= 2 * kWaveBlocks8) && G * D * 4 <= TILE && NB >= 2),
+                "INT8 blocks, their scratch and the two outputs fit the ring");
+  const int slots8 = FUSE8 ? p.sink + p.recent : 0;
+  const size_t base8 = ((size_t)b * p.hkv + kvh) * slots8;
+  const bool inloop8 = FUSE8 && slots8 > 0 && ntw >= NB;
+  auto slot8 = [&](int i) { return (ntw + i) % NB; };
+  auto issue8 = [&](int i) {
+    const int rb = wave + kWaves * i;
+    uint8_t* r = ring + slot8(i) * TILE;
+    if (rb < kBlocks8) int8_issue_block<D>(p, base8, rb, r, reinterpret_cast<float*>(r + 16 * kRow8));
+  };
+  if (FUSE8 && threadIdx.x == 0 && (L < 0 || L > p.max_ctx)) flag(p, KVC_ERR_LENGTH);
   if (ntw > 0) {
     const int s = lane >> 4;
     const uint32_t o_kc = (uint32_t)lane * S::SB;
@@ -987,8 +1258,16 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
         u32x4 r[8];
         // tiles in flight behind this one: NB - 1, fewer at the end (no tile
         // is loaded twice)
-        read_staged_after<D, NL, NB - 1>(ntw - 1 - jt, ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
-        if (jt + NB < ntw) issue(jt + NB, k);
+        if (FUSE8 && inloop8)
+          read_staged_tail<D, NL, NB - 1>(ntw - 1 - jt, ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
+        else
+          read_staged_after<D, NL, NB - 1>(ntw - 1 - jt, ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
+        if (jt + NB < ntw) {
+          issue(jt + NB, k);
+        } else if (FUSE8 && inloop8) {
+          const int i = jt + NB - ntw;  // slot k = slot8(i) is free for good
+          if (i < kWaveBlocks8) issue8(i);
+        }
         const int lim = r1 - 32 * (t0 + wave + kWaves * jt);
         uint32_t kc0[NG], kc1[NG], km[8], vc[8], vm[8];
 #pragma unroll
@@ -1004,184 +1283,97 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
       }
     }
   }
+  constexpr int CPL = D / 64;
+  float m8 = -INFINITY, l8 = 0.0f, o8[G][CPL];
+  if constexpr (FUSE8) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o8[h][c] = 0.0f;
+    if (slots8 > 0) {
+      if (!inloop8) {
+        __builtin_amdgcn_s_waitcnt(0);  // guessed tiles may still be landing in the ring
+#pragma unroll
+        for (int i = 0; i < kWaveBlocks8; ++i) issue8(i);
+      }
+      float qe[D / 32][8];
+      int8_load_q<D, G, QBF16>(p, b, kvh, qe);
+      const int Lc = clamp_len(p, L);
+      const int nvalid = Lc < slots8 ? Lc : slots8;
+      __builtin_amdgcn_s_waitcnt(0);  // the wave's blocks are in
+      int8_wave<D, G>(
+          p, nvalid, qe,
+          [&](int i, const uint8_t*& rows, const float*& sc, float*& pp) {
+            uint8_t* r = ring + slot8(i) * TILE;
+            rows = r;
+            sc = reinterpret_cast<const float*>(r + 16 * kRow8);
+            pp = reinterpret_cast<float*>(kPInSlot ? r + 16 * kRow8 + 128
+                                                   : ring + ((ntw + kWaveBlocks8 + i) % NB) * TILE);
+          },
+          m8, l8, o8);
+    }
+  }
   // the wave's output goes to the start of its own ring (its loads are done first)
   __builtin_amdgcn_s_waitcnt(0);
   core.finish(sm.m[wave], sm.l[wave], sm.vm[wave], reinterpret_cast<float*>(&sm.u.stage[wave][0][0]),
               ntw > 0);
+  if constexpr (FUSE8) {
+    // the INT8 part: (m, l) beside the INT4 ones, o in the ring's next slot
+    if (lane < G) {  // lane h holds column h
+      sm.m8[wave][lane] = m8;
+      sm.l8[wave][lane] = l8;
+    }
+    float* o8d = reinterpret_cast<float*>(ring + TILE);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o8d[h * D + lane * CPL + c] = o8[h][c];
+  }
 }
 
-// ------------------------------------------------------------------ INT8 region
-// The <= 144 protected positions of one (sequence, kv head): high-fidelity
-// attention over INT8 codes (KV4-RL review, section 1 and 3).
-// Which slots hold attended positions follows from L alone: all 144 when
-// L >= 144, else exactly slots [0, L) (slot = position below 144). So every
-// slot's codes and scales are loaded at once and masked afterwards.
-//  - Loads: each slot's K and V rows (2D bytes) and the scales go straight to
-//    LDS with 4-byte direct-to-LDS loads, one row per instruction, coalesced,
-//    all 144 slots at once (not waiting for L).
-//  - Logits on v_mfma_f32_16x16x32_f16: rows are 16 slots, columns the G
-//    heads. A code c enters as the exact fp16 subnormal (c + 128) * 2^-24 (a
-//    byte XOR and a byte permute); the query is scaled per head by a power of
-//    two into [2^14, 2^15) and split into two fp16 parts (one for a bf16
-//    query), so q.(c + 128) is float32-accurate, and 128 * sum(q) is taken off
-//    in float32. Wave w owns the row blocks w, w + 4, w + 8 of the 9.
-//  - Softmax per head over the wave's slots, then P.V in float32 on the VALU
-//    (lane = channels, p * V_scale from LDS, codes read from the rows).
+// ------------------------------------------------------------------ INT8 region workgroup
+// The INT8 region of one (sequence, kv head) in a workgroup of its own: each
+// wave loads its blocks into the Int8 area, then does its part (int8_wave).
 // The wave's (m, l, o) per head go to LDS for store_partial.
 template <int D, int G, bool QBF16>
 __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh) {
   constexpr int CPL = D / 64;
-  constexpr int NK = D / 32;  // MFMA k-steps over the head dimension
-  constexpr int RB = 9;       // 16-slot row blocks of the 144 slots
-  constexpr int kRow = Smem<D, G>::kRow8;
+  static_assert(Smem<D, G>::kRow8 == row8_stride<D>(), "INT8 row stride");
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int s4 = lane >> 4, n = lane & 15;
   const int slots = p.sink + p.recent;  // 144, or 0 without INT8 protection
-  static_assert(kSink + kRecent == 144 && (kSink + kRecent) % kWaves == 0, "INT8 slots");
   auto& i8 = sm.u.i8;
-  // ---- rows and scales of every slot into LDS, requested without waiting for
-  // the length (slots past it are masked below, whatever they hold)
+  // rows and scales of every slot, requested without waiting for the length
+  // (slots past it are masked, whatever they hold)
   const size_t base = ((size_t)b * p.hkv + kvh) * slots;
   if (slots > 0) {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(p.codes8) + base * 2 * D;
-    constexpr int kSlots = kSink + kRecent;  // slots is kSlots here
 #pragma unroll
-    for (int i = 0; i < kSlots / kWaves; ++i) {
-      const int r = wave + kWaves * i;
-      if (lane < 2 * D / 4)
-        __builtin_amdgcn_global_load_lds(src + (size_t)r * 2 * D + lane * 4,
-                                         (__attribute__((address_space(3))) void*)&i8.rows[r][0], 4, 0, 0);
+    for (int i = 0; i < kWaveBlocks8; ++i) {
+      const int rb = wave + kWaves * i;
+      if (rb < kBlocks8) int8_issue_block<D>(p, base, rb, &i8.rows[16 * rb][0], &i8.scales[16 * rb][0]);
     }
-    const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(p.scales8 + base * 2);
-    constexpr int sbytes = kSlots * 8;
-#pragma unroll
-    for (int o = 256 * wave; o < sbytes; o += 256 * kWaves)
-      if (o + lane * 4 < sbytes)
-        __builtin_amdgcn_global_load_lds(ssrc + o + lane * 4,
-                                         (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(&i8.scales[0][0]) + o),
-                                         4, 0, 0);
   }
-  // ---- query operands of column n (head n < G): 2^e_h * q, hi and lo fp16
-  float qe[NK][8];
-  const int hq = n < G ? n : 0;
-  const size_t qoff = ((size_t)b * p.hkv * G + kvh * G + hq) * D;
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qe[kk][t] = load_q<QBF16>(p.q, qoff + 32 * kk + 8 * s4 + t);
+  float qe[D / 32][8];
+  int8_load_q<D, G, QBF16>(p, b, kvh, qe);
   // the length, read after the loads above are issued
   int L = (int)scalar_load1(p.seq_lens + b);
   if ((L < 0 || L > p.max_ctx) && threadIdx.x == 0) flag(p, KVC_ERR_LENGTH);
   L = clamp_len(p, L);
   const int nvalid = L < slots ? L : slots;
-  float mx = 0.0f, qsum = 0.0f;
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      mx = fmaxf(mx, fabsf(qe[kk][t]));
-      qsum += qe[kk][t];
-    }
-  mx = rows_max(mx);      // over the head's D entries (four lanes n, n + 16, ...)
-  qsum = rows_sum(qsum);
-  int e = 0;
-  if (mx > 0.0f) {
-    const int ex = (int)((__float_as_uint(mx) >> 23) & 255u) - 127;
-    e = 14 - ex;
-    e = e < -100 ? -100 : (e > 100 ? 100 : e);
-  }
-  const float qsc = exp2i(e);
-  half8 bh[NK], bl[QBF16 ? 1 : NK];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float v = n < G ? qe[kk][t] * qsc : 0.0f;
-      const _Float16 hi = (_Float16)v;
-      bh[kk][t] = hi;
-      if constexpr (!QBF16) bl[kk][t] = (_Float16)(v - (float)hi);
-    }
-  // logit of code sum: (acc * 2^(24 - e) - 128 * sum(q)) * K_scale * alpha
-  const float unscale = exp2i(24 - e);
-  const float off = 128.0f * qsum;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // ---- logits of the wave's row blocks
-  constexpr int kMaxRB = (RB + kWaves - 1) / kWaves;  // 3
-  float sl[kMaxRB][4];
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kMaxRB; ++i) {
-    const int rb = wave + kWaves * i;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sl[i][j] = -INFINITY;
-    if (rb >= RB || 16 * rb >= nvalid) continue;
-    float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint8_t* row = &i8.rows[16 * rb + n][0];
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const uint2 x = *reinterpret_cast<const uint2*>(row + 32 * kk + 8 * s4);
-      const uint32_t x0 = x.x ^ 0x80808080u, x1 = x.y ^ 0x80808080u;
-      const half8 a = as_half8(__builtin_amdgcn_perm(0u, x0, 0x0c010c00u), __builtin_amdgcn_perm(0u, x0, 0x0c030c02u),
-                               __builtin_amdgcn_perm(0u, x1, 0x0c010c00u), __builtin_amdgcn_perm(0u, x1, 0x0c030c02u));
-      acc = mfma16x16x32(a, bh[kk], acc);
-      if constexpr (!QBF16) acc = mfma16x16x32(a, bl[kk], acc);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int slot = 16 * rb + 4 * s4 + j;
-      if (slot < nvalid) {
-        sl[i][j] = (acc[j] * unscale - off) * i8.scales[slot][0] * p.alpha;
-        m = fmaxf(m, sl[i][j]);
-      }
-    }
-  }
-  m = rows_max(m);  // over the wave's slots, per head (column n)
-  float l = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kMaxRB; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int slot = 16 * (wave + kWaves * i) + 4 * s4 + j;
-      const bool valid = slot < nvalid && wave + kWaves * i < RB;
-      const float pr = valid ? __builtin_amdgcn_exp2f(sl[i][j] - m) : 0.0f;
-      l += pr;
-      // slots past the length may hold anything: their weight is exactly 0
-      if (n < G) i8.p[wave][16 * i + 4 * s4 + j][n] = valid ? pr * i8.scales[slot][1] : 0.0f;
-    }
-  }
-  l = rows_sum(l);
-  const bool any = m != -INFINITY;
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  // ---- P.V over the wave's slots (16 per row block), lane = CPL channels
-  float o[G][CPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kMaxRB; ++i) {
-    const int rb = wave + kWaves * i;
-    if (rb >= RB || 16 * rb >= nvalid) continue;
-#pragma unroll 4
-    for (int t = 0; t < 16; ++t) {
-      float pj[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pj[h] = i8.p[wave][16 * i + t][h];
-      const uint8_t* vrow = &i8.rows[16 * rb + t][D];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float v = (float)(int8_t)vrow[lane * CPL + c];
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h][c] = fmaf(pj[h], v, o[h][c]);
-      }
-    }
-  }
+  __builtin_amdgcn_s_waitcnt(0);  // the wave's own blocks are in
+  float m, l, o[G][CPL];
+  int8_wave<D, G>(
+      p, nvalid, qe,
+      [&](int i, const uint8_t*& rows, const float*& sc, float*& pp) {
+        const int rb = wave + kWaves * i;
+        rows = &i8.rows[16 * rb][0];
+        sc = &i8.scales[16 * rb][0];
+        pp = &i8.p[wave][16 * i][0];
+      },
+      m, l, o);
   if (lane < G) {  // lane h holds column h
-    sm.m[wave][lane] = any ? m : -INFINITY;
-    sm.l[wave][lane] = any ? l : 0.0f;
+    sm.m[wave][lane] = m;
+    sm.l[wave][lane] = l;
   }
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -1285,9 +1477,22 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
 
 // TIER: some pages live in the host tier (a separate pool in pinned host memory).
 // POOL: the INT4 records come from the kept-record pool.
-template <int D, int G, bool QBF16, bool TIER, bool POOL>
+// FUSE8 (pool mode, one chunk per pair): workgroup = pair, which does the
+// INT8 region too and writes the output itself (no partials, no merge).
+template <int D, int G, bool QBF16, bool TIER, bool POOL, bool FUSE8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(AttnParams p) {
   __shared__ Smem<D, G> sm;
+  if constexpr (FUSE8) {
+    static_assert(POOL, "FUSE8 is a pool mode");
+    const int pair = blockIdx.x;
+    const int kvh = pair % p.hkv, b = pair / p.hkv;
+    int4_pool_chunk<D, G, QBF16, true>(p, sm, b, kvh, 0);
+    __syncthreads();
+    store_final<D, G>(
+        p, sm, [&](int w) { return reinterpret_cast<const float*>(&sm.u.stage[w][0][0]); },
+        [&](int w) { return reinterpret_cast<const float*>(&sm.u.stage[w][1][0]); }, b, kvh);
+    return;
+  }
   // One-dimensional grid, dispatched in index order and spread round-robin
   // over the 8 XCDs. The INT8 regions take `pairs` consecutive items, before
   // (int8_first = 1) or after (0) the INT4 chunks; INT4 item j is chunk
@@ -1313,7 +1518,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float* dst = p.parts + (((size_t)b * p.hkv + kvh) * np + split) * G * (2 + D);
   if (split < p.nsplit) {
     if constexpr (POOL) {
-      int4_pool_chunk<D, G, QBF16>(p, sm, b, kvh, split);
+      int4_pool_chunk<D, G, QBF16, false>(p, sm, b, kvh, split);
       __syncthreads();
       store_partial<D, G, POOL>(sm, [&](int w) { return reinterpret_cast<float*>(&sm.u.stage[w][0][0]); }, dst);
     } else {
@@ -1357,17 +1562,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 template <int D, int G>
-hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, bool pool, hipStream_t s) {
+hipError_t launch_dq(const kvc_cache& c, const AttnParams& p, bool qbf16, bool pool, bool fuse8, hipStream_t s) {
   const dim3 grid((unsigned)(p.nsplit + 1) * c.num_kv_heads * c.batch);
-  if (pool) {
-    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((attention_kernel<D, G, false, false, true>), grid, dim3(kThreads), 0, s, p);
+  if (pool && fuse8 && p.nsplit == 1) {  // one workgroup per pair does both regions
+    const dim3 g1((unsigned)c.num_kv_heads * c.batch);
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false, true, true>), g1, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, false, true, true>), g1, dim3(kThreads), 0, s, p);
+  } else if (pool) {
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false, true, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, false, true, false>), grid, dim3(kThreads), 0, s, p);
   } else if (p.host_pages > 0) {
-    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, true, false>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((attention_kernel<D, G, false, true, false>), grid, dim3(kThreads), 0, s, p);
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, true, false, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, true, false, false>), grid, dim3(kThreads), 0, s, p);
   } else {
-    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false, false>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((attention_kernel<D, G, false, false, false>), grid, dim3(kThreads), 0, s, p);
+    if (qbf16) hipLaunchKernelGGL((attention_kernel<D, G, true, false, false, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((attention_kernel<D, G, false, false, false, false>), grid, dim3(kThreads), 0, s, p);
   }
   // pool mode merges inside the attention kernel
   if (!pool) hipLaunchKernelGGL((merge_kernel<D, G>), dim3(G, c.num_kv_heads, c.batch), dim3(64), 0, s, p);
@@ -1444,17 +1653,18 @@ hipError_t launch_attention(const kvc_cache& c, const void* q, kvc_dtype q_dtype
   }
   const bool bf = q_dtype == KVC_BF16;
   const bool pool = plan.pool != 0;
+  const bool fuse8 = plan.fuse8 != 0;
   if (c.head_dim == 128) {
     switch (G) {
-      case 1: return launch_dq<128, 1>(c, p, bf, pool, s);
-      case 2: return launch_dq<128, 2>(c, p, bf, pool, s);
-      case 4: return launch_dq<128, 4>(c, p, bf, pool, s);
+      case 1: return launch_dq<128, 1>(c, p, bf, pool, fuse8, s);
+      case 2: return launch_dq<128, 2>(c, p, bf, pool, fuse8, s);
+      case 4: return launch_dq<128, 4>(c, p, bf, pool, fuse8, s);
     }
   } else {
     switch (G) {
-      case 1: return launch_dq<64, 1>(c, p, bf, pool, s);
-      case 2: return launch_dq<64, 2>(c, p, bf, pool, s);
-      case 4: return launch_dq<64, 4>(c, p, bf, pool, s);
+      case 1: return launch_dq<64, 1>(c, p, bf, pool, fuse8, s);
+      case 2: return launch_dq<64, 2>(c, p, bf, pool, fuse8, s);
+      case 4: return launch_dq<64, 4>(c, p, bf, pool, fuse8, s);
     }
   }
   return hipErrorInvalidValue;

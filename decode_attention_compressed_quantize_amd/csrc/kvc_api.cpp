@@ -140,11 +140,15 @@ AttnPlan plan_attention(const kvc_cache& c, int num_q_heads, int window, bool po
     p.pool = 1;
     p.nsplit = (int)j;
     p.chunk = 0;
-    // INT8 regions first when each pair has many chunks (they overlap the
-    // chunks' streaming); after the chunks with one chunk per pair (a first
-    // round of INT8 workgroups would hold every CU for their latency, and
-    // alternating them with chunks halves the streaming workgroups)
+    // INT8 regions first when each pair has several chunks (they overlap the
+    // chunks' streaming). With one chunk per pair: when all chunks are
+    // resident at once, INT8 workgroups could only follow them, so the chunk's
+    // workgroup does the INT8 region itself and writes the output (fuse8);
+    // with more pairs than that, separate INT8 workgroups after the chunks
+    // fill the CUs that short sequences free (measured faster on mixed
+    // lengths than fusing).
     p.int8_first = j == 1 ? 0 : 1;
+    p.fuse8 = j == 1 && pairs <= kPoolSlots ? 1 : 0;
     return p;
   }
   constexpr long long kResident = 768;  // 3 workgroups per CU x 256 CUs

@@ -33,6 +33,10 @@ struct AttnPlan {
   // chunk j of a (sequence, kv head) is the j-th of nsplit equal shares of its
   // pool's record count (the workspace layout is the same as mask mode's).
   int pool;
+  // Pool mode with one chunk per pair: the chunk's workgroup also does the
+  // INT8 region and writes the output itself (no INT8 workgroups, partials or
+  // merge).
+  int fuse8;
 };
 
 // window > 0: chunks cover only the last `window` INT4-region positions.

@@ -33,6 +33,13 @@ CASES = {
     "f32_d128": W.Workload("qrange_f32", 3, 8, 2, 128, ctx_list=(200, 1500, 4000),
                            mask="mlp", budget_permille=300, src_dtype="f32", outlier_channels=4),
     "bf16_d64_g2": W.Workload("qrange_d64", 2, 4, 2, 64, ctx_list=(300, 2000), mask="all"),
+    # kept-record pools of one chunk per pair: the chunk's workgroup does the
+    # INT8 region too (its blocks in the chunk's LDS ring) and writes the output;
+    # L = 100 has no INT4 record, L = 150 a handful
+    "bf16_d128_fused": W.Workload("qrange_fused", 3, 8, 2, 128, ctx_list=(100, 700, 1100),
+                                  mask="mlp", budget_permille=500, outlier_channels=4),
+    "f32_d64_g4_fused": W.Workload("qrange_fused64", 2, 8, 2, 64, ctx_list=(150, 900), mask="all",
+                                   src_dtype="f32", outlier_channels=4),
 }
 
 
@@ -50,7 +57,7 @@ def layer(name):
 
     if name not in _caches:
         _caches.clear()
-        _caches[name] = LayerCache(CASES[name])
+        _caches[name] = LayerCache(CASES[name], pool=name.endswith("_fused"))
     return _caches[name]
 
 
