@@ -242,7 +242,6 @@ struct Smem {
   struct Int8 {
     uint8_t rows[144][kRow8];
     float scales[144][2];
-    float p[kWaves][48][G];  // p * V scale of the wave's slots
     float o[kWaves][G][D];
   };
   // pool mode: each wave's ring of kStage tiles filled by direct-to-LDS loads;
@@ -908,17 +907,27 @@ __device__ inline void int8_load_q(const AttnParams& p, int b, int kvh, float (&
     for (int t = 0; t < 8; ++t) qe[kk][t] = load_q<QBF16>(p.q, qoff + 32 * kk + 8 * s4 + t);
 }
 
-// The wave's blocks, already in LDS: blk(i, rows, sc, pp) gives block i's rows
-// and scales and a [16][G] float scratch for p * V_scale. Out: m and l of
-// column n (lane n < G: head n; base-2 logits), and o[h][c] = channel
-// lane * CPL + c of head h (unnormalised); m = -inf, l = 0, o = 0 when the
-// wave has no valid slot.
-template <int D, int G, typename BLK>
+// The wave's blocks, already in LDS: blk(i, rows, sc) gives block i's rows
+// and scales. Out: m and l of column n (lane n < G: head n; base-2 logits),
+// and the wave's unnormalised output of head h at o_dst[h * D + channel]
+// (LDS; 0 when the wave has no valid slot, and then m = -inf, l = 0).
+// Both contractions run on MFMA with the lane layout of a 16 x 16 tile
+// (lane (s4, n): column n, rows 4 s4 + j):
+//  - logits C[slot][head] over k = the head dimension (16x16x32): A = the
+//    slot's K codes, B = the scaled query, hi and lo parts in two
+//    accumulators; every block's chain is issued together (a block past the
+//    wave's valid ones reads the wave's first block and is masked);
+//  - P.V C[channel][head] over k = the block's 16 slots (16x16x16): A = the
+//    V codes (code c enters as (c + 128) 2^-24), B = p * V_scale of the
+//    lane's own four slots, split into fp16 hi and lo parts accumulated
+//    together (float32-accurate), then o = 2^24 C - 128 sum(p * V_scale).
+template <int D, int G, bool QBF16, typename BLK>
 __device__ inline void int8_wave(const AttnParams& p, int nvalid, const float (&qe)[D / 32][8], BLK blk,
-                                 float& m_out, float& l_out, float (&o)[G][D / 64]) {
-  constexpr int CPL = D / 64;
-  constexpr int NK = D / 32;  // MFMA k-steps over the head dimension
+                                 float& m_out, float& l_out, float* o_dst) {
+  constexpr int NK = D / 32;  // logit k-steps over the head dimension
+  constexpr int NT = D / 16;  // P.V channel tiles
   constexpr int kRow = row8_stride<D>();
+  constexpr int NB8 = kWaveBlocks8;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int s4 = lane >> 4, n = lane & 15;
@@ -940,7 +949,7 @@ __device__ inline void int8_wave(const AttnParams& p, int nvalid, const float (&
     e = e < -100 ? -100 : (e > 100 ? 100 : e);
   }
   const float qsc = exp2i(e);
-  half8 bh[NK], bl[NK];
+  half8 bh[NK], bl[QBF16 ? 1 : NK];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
@@ -948,94 +957,97 @@ __device__ inline void int8_wave(const AttnParams& p, int nvalid, const float (&
       const float v = n < G ? qe[kk][t] * qsc : 0.0f;
       const _Float16 hi = (_Float16)v;
       bh[kk][t] = hi;
-      bl[kk][t] = (_Float16)(v - (float)hi);
+      if constexpr (!QBF16) bl[kk][t] = (_Float16)(v - (float)hi);
     }
   // logit of code sum: (acc * 2^(24 - e) - 128 * sum(q)) * K_scale * alpha
   const float unscale = exp2i(24 - e);
   const float off = 128.0f * qsum;
-  // ---- logits of the wave's blocks
-  float sl[kWaveBlocks8][4];
-  float m = -INFINITY;
+  // ---- the wave's blocks
+  bool vb[NB8];
+  int rb[NB8];
+  const uint8_t* rows[NB8];
+  const float* sc[NB8];
 #pragma unroll
-  for (int i = 0; i < kWaveBlocks8; ++i) {
-    const int rb = wave + kWaves * i;
+  for (int i = 0; i < NB8; ++i) {
+    rb[i] = wave + kWaves * i;
+    vb[i] = rb[i] < kBlocks8 && 16 * rb[i] < nvalid;
+    blk(vb[i] ? i : 0, rows[i], sc[i]);
+  }
+  // ---- logits
+  float4v ch[NB8], cl[NB8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sl[i][j] = -INFINITY;
-    if (rb >= kBlocks8 || 16 * rb >= nvalid) continue;
-    const uint8_t* rows;
-    const float* sc;
-    float* pp;
-    blk(i, rows, sc, pp);
-    float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint8_t* row = rows + n * kRow;
+  for (int i = 0; i < NB8; ++i) ch[i] = cl[i] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const uint2 x = *reinterpret_cast<const uint2*>(row + 32 * kk + 8 * s4);
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int i = 0; i < NB8; ++i) {
+      const uint2 x = *reinterpret_cast<const uint2*>(rows[i] + n * kRow + 32 * kk + 8 * s4);
       const uint32_t x0 = x.x ^ 0x80808080u, x1 = x.y ^ 0x80808080u;
       const half8 a = as_half8(__builtin_amdgcn_perm(0u, x0, 0x0c010c00u), __builtin_amdgcn_perm(0u, x0, 0x0c030c02u),
                                __builtin_amdgcn_perm(0u, x1, 0x0c010c00u), __builtin_amdgcn_perm(0u, x1, 0x0c030c02u));
-      acc = mfma16x16x32(a, bh[kk], acc);
-      acc = mfma16x16x32(a, bl[kk], acc);  // zero for a bf16 query: exact either way
+      ch[i] = mfma16x16x32(a, bh[kk], ch[i]);
+      if constexpr (!QBF16) cl[i] = mfma16x16x32(a, bl[kk], cl[i]);
     }
+  float sl[NB8][4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NB8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = 4 * s4 + j;
-      if (16 * rb + t < nvalid) {
-        sl[i][j] = (acc[j] * unscale - off) * sc[2 * t] * p.alpha;
-        m = fmaxf(m, sl[i][j]);
-      }
+      const bool valid = vb[i] && 16 * rb[i] + t < nvalid;
+      const float acc = QBF16 ? ch[i][j] : ch[i][j] + cl[i][j];
+      const float v = (acc * unscale - off) * sc[i][2 * t] * p.alpha;
+      sl[i][j] = valid ? v : -INFINITY;
+      m = fmaxf(m, sl[i][j]);
     }
-  }
   m = rows_max(m);  // over the wave's slots, per head (column n)
-  float l = 0.0f;
+  // ---- softmax weights; B operands p * V_scale (column n, slots 4 s4 + j)
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  half4 Bh[NB8], Bl[NB8];
+  float l = 0.0f, ps = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kWaveBlocks8; ++i) {
-    const int rb = wave + kWaves * i;
-    if (rb >= kBlocks8 || 16 * rb >= nvalid) continue;
-    const uint8_t* rows;
-    const float* sc;
-    float* pp;
-    blk(i, rows, sc, pp);
+  for (int i = 0; i < NB8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = 4 * s4 + j;
-      const bool valid = 16 * rb + t < nvalid;
-      const float pr = valid ? __builtin_amdgcn_exp2f(sl[i][j] - m) : 0.0f;
-      l += pr;
+      const bool valid = vb[i] && 16 * rb[i] + t < nvalid && n < G;
       // slots past the length may hold anything: their weight is exactly 0
-      if (n < G) pp[t * G + n] = valid ? pr * sc[2 * t + 1] : 0.0f;
+      const float pr = valid ? __builtin_amdgcn_exp2f(sl[i][j] - m) : 0.0f;
+      const float pv = valid ? pr * sc[i][2 * t + 1] : 0.0f;
+      l += pr;
+      ps += pv;
+      const _Float16 hi = (_Float16)pv;
+      Bh[i][j] = hi;
+      Bl[i][j] = (_Float16)(pv - (float)hi);
+    }
+  l = rows_sum(l);
+  ps = rows_sum(ps);
+  const bool any = m != -INFINITY;
+  // ---- P.V: channel tile c, rows = channels 16 c + 4 s4 + r, column = head n
+  float4v oc[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) oc[c] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < NB8; ++i) {
+    if (!vb[i]) continue;
+    const uint8_t* vr = rows[i] + D + n;  // lane reads channel 16 c + n of slots 4 s4 + j
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const uint32_t b0 = vr[(4 * s4 + 0) * kRow + 16 * c], b1 = vr[(4 * s4 + 1) * kRow + 16 * c];
+      const uint32_t b2 = vr[(4 * s4 + 2) * kRow + 16 * c], b3 = vr[(4 * s4 + 3) * kRow + 16 * c];
+      const uint32_t w0 = (b0 | (b1 << 16)) ^ 0x00800080u, w1 = (b2 | (b3 << 16)) ^ 0x00800080u;
+      const half4 A = __builtin_bit_cast(half4, (u32x2){w0, w1});
+      oc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bh[i], oc[c], 0, 0, 0);
+      oc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bl[i], oc[c], 0, 0, 0);
     }
   }
-  l = rows_sum(l);
-  const bool any = m != -INFINITY;
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  // ---- P.V over the wave's slots (16 per block), lane = CPL channels
+  if (n < G) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int c = 0; c < NT; ++c)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) o[h][c] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kWaveBlocks8; ++i) {
-    const int rb = wave + kWaves * i;
-    if (rb >= kBlocks8 || 16 * rb >= nvalid) continue;
-    const uint8_t* rows;
-    const float* sc;
-    float* pp;
-    blk(i, rows, sc, pp);
-#pragma unroll 4
-    for (int t = 0; t < 16; ++t) {
-      float pj[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pj[h] = pp[t * G + h];
-      const uint8_t* vrow = rows + t * kRow + D;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float v = (float)(int8_t)vrow[lane * CPL + c];
-#pragma unroll
-        for (int h = 0; h < G; ++h) o[h][c] = fmaf(pj[h], v, o[h][c]);
-      }
-    }
+      for (int r = 0; r < 4; ++r)
+        o_dst[n * D + 16 * c + 4 * s4 + r] = any ? fmaf(oc[c][r], 16777216.0f, -128.0f * ps) : 0.0f;
   }
   m_out = any ? m : -INFINITY;
   l_out = any ? l : 0.0f;
@@ -1226,13 +1238,10 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   // FUSE8 (one chunk per pair): the workgroup does the INT8 region too. Wave
   // block i goes into ring slot (ntw + i) % NB, the i-th slot that the last
   // NB tiles free (or, with fewer than NB tiles, after the loop), followed by
-  // its scales and, where it fits, its [16][G] p scratch (else in slot
-  // (ntw + 3 + i) % NB).
+  // its scales; the INT8 output goes to slot 1 and the INT4 one to slot 0.
   constexpr int kRow8 = Smem<D, G>::kRow8;
-  constexpr bool kPInSlot = 16 * kRow8 + 128 + 16 * G * 4 <= TILE;
-  static_assert(!FUSE8 || (16 * kRow8 + 128 <= TILE && NB >= kWaveBlocks8 &&
-                           (kPInSlot || NB >= 2 * kWaveBlocks8) && G * D * 4 <= TILE && NB >= 2),
-                "INT8 blocks, their scratch and the two outputs fit the ring");
+  static_assert(!FUSE8 || (16 * kRow8 + 128 <= TILE && NB >= kWaveBlocks8 && G * D * 4 <= TILE && NB >= 2),
+                "INT8 blocks and the two outputs fit the ring");
   const int slots8 = FUSE8 ? p.sink + p.recent : 0;
   const size_t base8 = ((size_t)b * p.hkv + kvh) * slots8;
   const bool inloop8 = FUSE8 && slots8 > 0 && ntw >= NB;
@@ -1283,13 +1292,9 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
       }
     }
   }
-  constexpr int CPL = D / 64;
-  float m8 = -INFINITY, l8 = 0.0f, o8[G][CPL];
+  float m8 = -INFINITY, l8 = 0.0f;
+  float* o8d = reinterpret_cast<float*>(ring + TILE);
   if constexpr (FUSE8) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) o8[h][c] = 0.0f;
     if (slots8 > 0) {
       if (!inloop8) {
         __builtin_amdgcn_s_waitcnt(0);  // guessed tiles may still be landing in the ring
@@ -1301,33 +1306,29 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
       const int Lc = clamp_len(p, L);
       const int nvalid = Lc < slots8 ? Lc : slots8;
       __builtin_amdgcn_s_waitcnt(0);  // the wave's blocks are in
-      int8_wave<D, G>(
+      int8_wave<D, G, QBF16>(
           p, nvalid, qe,
-          [&](int i, const uint8_t*& rows, const float*& sc, float*& pp) {
-            uint8_t* r = ring + slot8(i) * TILE;
+          [&](int i, const uint8_t*& rows, const float*& sc) {
+            const uint8_t* r = ring + slot8(i) * TILE;
             rows = r;
             sc = reinterpret_cast<const float*>(r + 16 * kRow8);
-            pp = reinterpret_cast<float*>(kPInSlot ? r + 16 * kRow8 + 128
-                                                   : ring + ((ntw + kWaveBlocks8 + i) % NB) * TILE);
           },
-          m8, l8, o8);
+          m8, l8, o8d);
+    } else {
+      for (int i = lane; i < G * D; i += 64) o8d[i] = 0.0f;
     }
   }
-  // the wave's output goes to the start of its own ring (its loads are done first)
+  // the wave's output goes to the start of its own ring (its loads are done
+  // first; with FUSE8 the INT8 part has read its blocks)
   __builtin_amdgcn_s_waitcnt(0);
   core.finish(sm.m[wave], sm.l[wave], sm.vm[wave], reinterpret_cast<float*>(&sm.u.stage[wave][0][0]),
               ntw > 0);
   if constexpr (FUSE8) {
-    // the INT8 part: (m, l) beside the INT4 ones, o in the ring's next slot
+    // the INT8 part's (m, l) beside the INT4 ones (its o is in slot 1)
     if (lane < G) {  // lane h holds column h
       sm.m8[wave][lane] = m8;
       sm.l8[wave][lane] = l8;
     }
-    float* o8d = reinterpret_cast<float*>(ring + TILE);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) o8d[h * D + lane * CPL + c] = o8[h][c];
   }
 }
 
@@ -1337,7 +1338,6 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
 // The wave's (m, l, o) per head go to LDS for store_partial.
 template <int D, int G, bool QBF16>
 __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh) {
-  constexpr int CPL = D / 64;
   static_assert(Smem<D, G>::kRow8 == row8_stride<D>(), "INT8 row stride");
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -1361,24 +1361,19 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
   L = clamp_len(p, L);
   const int nvalid = L < slots ? L : slots;
   __builtin_amdgcn_s_waitcnt(0);  // the wave's own blocks are in
-  float m, l, o[G][CPL];
-  int8_wave<D, G>(
+  float m, l;
+  int8_wave<D, G, QBF16>(
       p, nvalid, qe,
-      [&](int i, const uint8_t*& rows, const float*& sc, float*& pp) {
+      [&](int i, const uint8_t*& rows, const float*& sc) {
         const int rb = wave + kWaves * i;
         rows = &i8.rows[16 * rb][0];
         sc = &i8.scales[16 * rb][0];
-        pp = &i8.p[wave][16 * i][0];
       },
-      m, l, o);
+      m, l, &i8.o[wave][0][0]);
   if (lane < G) {  // lane h holds column h
     sm.m[wave][lane] = m;
     sm.l[wave][lane] = l;
   }
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) i8.o[wave][h][lane * CPL + c] = o[h][c];
 }
 
 // ------------------------------------------------------------------ merge
