@@ -269,25 +269,33 @@ __device__ inline void put_f32(float* a, float v) {
 
 // Combine the four waves' (m, l, o) held in LDS into one partial and store it
 // (COHERENT: with device-scope stores, for a merge inside the same launch).
+// One element (head h, channel ch) of the four waves' combined (M, o, l).
+template <int D, int G, typename OF>
+__device__ inline void combine_waves(const Smem<D, G>& sm, OF o_of, int h, int ch, float& M, float& o, float& l) {
+  M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][h]);
+  o = 0.0f;
+  l = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm.m[w][h];
+      if (mw == -INFINITY) continue;
+      const float a = __builtin_amdgcn_exp2f(mw - M);
+      o = __builtin_fmaf(a, o_of(w)[h * D + ch], o);
+      l = __builtin_fmaf(a, sm.l[w][h], l);
+    }
+  }
+}
+
 template <int D, int G, bool COHERENT, typename OF>
 __device__ inline void store_partial(Smem<D, G>& sm, OF o_of, float* dst) {
   const int tid = threadIdx.x;
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, ch = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][h]);
-    float o = 0.0f, l = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm.m[w][h];
-        if (mw == -INFINITY) continue;
-        const float a = __builtin_amdgcn_exp2f(mw - M);
-        o += a * o_of(w)[h * D + ch];
-        l += a * sm.l[w][h];
-      }
-    }
+    float M, o, l;
+    combine_waves<D, G>(sm, o_of, h, ch, M, o, l);
     float* row = dst + (size_t)h * (2 + D);
     put_f32<COHERENT>(row + 2 + ch, o);
     if (ch == 0) {
@@ -1336,8 +1344,10 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
 // The INT8 region of one (sequence, kv head) in a workgroup of its own: each
 // wave loads its blocks into the Int8 area, then does its part (int8_wave).
 // The wave's (m, l, o) per head go to LDS for store_partial.
-template <int D, int G, bool QBF16>
-__device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh) {
+// after_loads() runs in every thread once the wave's blocks are in (it may
+// synchronise the workgroup).
+template <int D, int G, bool QBF16, typename AL>
+__device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh, AL after_loads) {
   static_assert(Smem<D, G>::kRow8 == row8_stride<D>(), "INT8 row stride");
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -1361,6 +1371,7 @@ __device__ void int8_region(const AttnParams& p, Smem<D, G>& sm, int b, int kvh)
   L = clamp_len(p, L);
   const int nvalid = L < slots ? L : slots;
   __builtin_amdgcn_s_waitcnt(0);  // the wave's own blocks are in
+  after_loads();
   float m, l;
   int8_wave<D, G, QBF16>(
       p, nvalid, qe,
@@ -1446,17 +1457,23 @@ __device__ void merge_head(const AttnParams& p, int b, int kvh, int h, int lane,
   for (int r = 0; r < kML; ++r) {
     const int j = lane + 64 * r;
     const float w = (mj[r] == -INFINITY || M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj[r] - M);
-    den += w * lj[r];
+    den = __builtin_fmaf(w, lj[r], den);
     if (j < np) wts[j] = w;
   }
   den = wave_sum(den);
   __builtin_amdgcn_wave_barrier();  // one wave: its LDS writes are seen by its later reads
+  // acc = sum_j w_j o_j as fused multiply-adds in index order (the two-partial
+  // shortcut of the INT8 workgroup repeats exactly these operations)
   fcpl acc = {};
+  auto fma_acc = [&](float w, fcpl v) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = __builtin_fmaf(w, v[c], acc[c]);
+  };
 #pragma unroll
   for (int j = 0; j < kPre; ++j)
-    if (j < np) acc += wts[j] * pre[j];
+    if (j < np) fma_acc(wts[j], pre[j]);
   // every partial is written by the attention kernel, so no load is skipped
-  for (int j = kPre; j < np; ++j) acc += wts[j] * ld(part(j) + 2 + CPL * lane);
+  for (int j = kPre; j < np; ++j) fma_acc(wts[j], ld(part(j) + 2 + CPL * lane));
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   const size_t oq = (size_t)b * p.hkv * G + kvh * G + h;
   *reinterpret_cast<fcpl*>(p.out + oq * D + CPL * lane) = acc * inv;
@@ -1522,8 +1539,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       store_partial<D, G, false>(sm, [&](int w) { return &sm.u.w4[w].ro.o[0][0]; }, dst);
     }
   } else {
-    int8_region<D, G, QBF16>(p, sm, b, kvh);
+    // Pool mode, one chunk per pair: the INT8 workgroup usually runs after its
+    // chunk has finished (INT8 workgroups are dispatched after the chunks). It
+    // reads the pair's count at its start; if the chunk has already counted
+    // itself, this workgroup is the last: it loads the chunk's partial while
+    // it computes, and merges with its own partial straight from LDS (no
+    // partial store, no count), with the merge's exact operations, so the
+    // output is the same bits either way.
+    const bool peek = POOL && p.nsplit == 1;
+    int32_t* ctr = p.pool_header + 4 * (size_t)pair + 3;
+    __shared__ int s_fast;
+    int seen = -1;
+    if (peek && threadIdx.x == 0) seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    constexpr int kE = (G * D + kThreads - 1) / kThreads;  // output elements per thread
+    float c_m[kE], c_l[kE], c_o[kE];
+    bool fast = false;
+    const float* run = p.parts + ((size_t)b * p.hkv + kvh) * np * G * (2 + D);  // the chunk's partial
+    int8_region<D, G, QBF16>(p, sm, b, kvh, [&] {
+      if (!peek) return;
+      if (threadIdx.x == 0) s_fast = seen == np - 1;
+      __syncthreads();
+      fast = s_fast != 0;
+      if (fast) {
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+          const int i = threadIdx.x + kThreads * e;
+          const int h = (i < G * D ? i : 0) / D, ch = (i < G * D ? i : 0) % D;
+          const float* row = run + (size_t)h * (2 + D);
+          c_m[e] = __hip_atomic_load(row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          c_l[e] = __hip_atomic_load(row + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          c_o[e] = __hip_atomic_load(row + 2 + ch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    });
     __syncthreads();
+    if (POOL && fast) {
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        const int i = threadIdx.x + kThreads * e;
+        if (i >= G * D) break;
+        const int h = i / D, ch = i % D;
+        float M8, o8, l8;
+        combine_waves<D, G>(sm, [&](int w) { return &sm.u.i8.o[w][0][0]; }, h, ch, M8, o8, l8);
+        // merge_head over the partials (chunk, INT8), operation for operation
+        const float M = fmaxf(c_m[e], M8);
+        const float w0 = (c_m[e] == -INFINITY || M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(c_m[e] - M);
+        const float w1 = (M8 == -INFINITY || M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M8 - M);
+        const float den = __builtin_fmaf(w0, c_l[e], 0.0f) + __builtin_fmaf(w1, l8, 0.0f);
+        const float acc = __builtin_fmaf(w1, o8, __builtin_fmaf(w0, c_o[e], 0.0f));
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        const size_t oq = (size_t)b * p.hkv * G + kvh * G + h;
+        p.out[oq * D + ch] = acc * inv;
+        if (ch == 0 && p.lse) p.lse[oq] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+      }
+      // the count reached np - 1 without this workgroup: it ends at 0
+      if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
     store_partial<D, G, POOL>(sm, [&](int w) { return &sm.u.i8.o[w][0][0]; }, dst);
   }
   if constexpr (POOL) {

@@ -352,6 +352,25 @@ def test_pool_and_mask_modes_agree_and_rerun_is_bit_identical():
     assert np.abs(lse.cpu().numpy() - l_pool).max() < 1e-4
 
 
+def test_pool_one_chunk_per_pair_many_pairs_rerun_is_bit_identical():
+    """More pairs than the 512 resident chunk workgroups, one chunk per pair:
+    separate INT8 workgroups run after the chunks, and one that finds its
+    chunk already counted merges from LDS without storing its own partial
+    (else it stores it and the last of the two merges). Either way the output
+    is the same bits: five calls are bit-identical, and sampled pairs (the
+    shortest, the longest and others) match the oracle."""
+    lens = tuple(int(x) for x in np.linspace(145, 1000, 72).round()[::-1])
+    w = W.WORKLOADS["longtail"].replace(name="many_pairs", batch=len(lens), ctx_range=None,
+                                        ctx_list=lens)
+    lc = check_workload(w, [(0, 0), (71, 7), (35, 3), (10, 5), (60, 1)], pool=True)
+    q = lc.queries(0)
+    _, o0, l0 = run_attention(lc, q=q)
+    for _ in range(4):
+        _, o1, l1 = run_attention(lc, q=q)
+        np.testing.assert_array_equal(o0, o1)
+        np.testing.assert_array_equal(l0, l1)
+
+
 def test_error_word():
     """Lengths beyond max_ctx, table entries outside the pools and a pool that no
     longer describes the length set their bits; a clean run sets none."""
