@@ -486,7 +486,7 @@ struct Int4Core {
       if constexpr (NC >= 4 * G) sv[i] += row_ror<2 * G>(sv[i]);
       if constexpr (NC >= 2 * G) sv[i] += row_ror<G>(sv[i]);
     }
-    if (lim < 32) {
+    if (__builtin_expect(lim < 32, 0)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (tok(i) >= lim) sv[i] = -INFINITY;
@@ -495,7 +495,7 @@ struct Int4Core {
 #pragma unroll
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
     const float mnew = fmaxf(m_col, alpha_h * rows_max(tmax));
-    if (__ballot(mnew > m_col) != 0) {
+    if (__builtin_expect(__ballot(mnew > m_col) != 0, 0)) {
       const float f = __builtin_amdgcn_exp2f(m_col - mnew);  // 0 on the first tile
       l_col *= f;
       vm1 *= f;
@@ -534,7 +534,7 @@ struct Int4Core {
     uint32_t vm[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) vm[i] = vmi[i];
-    if (lim < 32) {
+    if (__builtin_expect(lim < 32, 0)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (tok(i) >= lim) vm[i] = 0u;
@@ -1268,7 +1268,7 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
     const uint32_t o_vm = VM + (s * NG + core.gc) * 16;
     float pr[8];
     for (int jt0 = 0; jt0 < ntw; jt0 += NB) {
-#pragma unroll
+#pragma unroll 1
       for (int k = 0; k < NB; ++k) {
         const int jt = jt0 + k;
         if (jt >= ntw) break;
