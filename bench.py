@@ -784,8 +784,11 @@ def main():
                                    f"{args.calls} event-timed calls (replicas in rotation); the call "
                                    f"figure averages the layers"},
         "roofline": {
-            "kernel": "kvc_decode_attention call: attention_kernel (INT4 chunks + INT8 region) "
-                      "then merge_kernel, timed together with HIP events on the launch stream",
+            "kernel": ("kvc_decode_attention call: one attention_kernel launch (INT4 chunks over the "
+                       "kept-record pool and the INT8 region, merged in-kernel), timed with HIP events "
+                       "on the launch stream" if res["pooled"] else
+                       "kvc_decode_attention call: attention_kernel (INT4 chunks + INT8 region) "
+                       "then merge_kernel, timed together with HIP events on the launch stream"),
             "bound": "host-link" if tier == "all" else "hbm",
             "achieved": round(a_gbs, 1),
             "peak": peak,

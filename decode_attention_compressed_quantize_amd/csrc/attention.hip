@@ -244,13 +244,23 @@ struct Smem {
     float scales[144][2];
     float o[kWaves][G][D];
   };
-  // pool mode: each wave's ring of kStage tiles filled by direct-to-LDS loads;
-  // after its last tile the wave's output o[G][D] goes to the start of its ring
-  static constexpr int kStage = 15360 / (40 * D);
+  // pool mode: each wave's ring of kStage tiles (5 KB: with two workgroups per
+  // CU about 10 MB are in flight, where HBM streams fastest; deeper rings read
+  // slower) filled by direct-to-LDS loads; after its last tile the wave's
+  // output o[G][D] goes to the start of its ring
+  static constexpr int kStage = 5120 / (40 * D);
+  // a chunk workgroup that also does the INT8 region: the ring, then each
+  // wave's (up to) three INT8 blocks of 16 rows and their scales
+  static constexpr int kBlk8 = (16 * kRow8 + 128 + 15) / 16 * 16;
+  struct Fused8 {
+    uint8_t stage[kWaves][kStage][40 * D];
+    uint8_t blk[kWaves][3][kBlk8];
+  };
   union {
     Wave4 w4[kWaves];
     Int8 i8;
     uint8_t stage[kWaves][kStage][40 * D];
+    Fused8 f8;
   } u;
   float m[kWaves][G];
   float l[kWaves][G];
@@ -863,11 +873,11 @@ __device__ void int4_mask_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
 // (those below 9). Where a wave keeps its blocks in LDS is the caller's: a
 // workgroup of the INT8 region alone loads them into its Int8 area; a chunk
 // workgroup that also does the INT8 region (one chunk per pair) loads them
-// into the wave's ring as its last tiles free it.
+// into an area of each wave's own beside its ring.
 //  - Loads: each slot's K and V rows (2D bytes, at a padded stride so that the
 //    16 rows read at one offset fall in distinct banks) and the block's scales
 //    go straight to LDS with 4-byte direct-to-LDS loads, one row per
-//    instruction, coalesced: kLoads8 instructions per block.
+//    instruction, coalesced, and one more for the block's scales.
 //  - Logits on v_mfma_f32_16x16x32_f16: rows are 16 slots, columns the G
 //    heads. A code c enters as the exact fp16 subnormal (c + 128) * 2^-24 (a
 //    byte XOR and a byte permute); the query is scaled per head by a power of
@@ -879,7 +889,6 @@ __device__ void int4_mask_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
 constexpr int kSlots8 = kSink + kRecent;
 constexpr int kBlocks8 = kSlots8 / 16;                      // 9
 constexpr int kWaveBlocks8 = (kBlocks8 + kWaves - 1) / kWaves;  // 3
-constexpr int kLoads8 = 16 + 1;                             // direct-to-LDS loads per block
 static_assert(kSlots8 == 144 && kSlots8 % 16 == 0, "INT8 slots");
 
 template <int D>
@@ -1128,23 +1137,6 @@ __device__ inline void read_staged_after(int after, uint32_t lds, uint32_t o_kc,
   }
 }
 
-// read_staged for a wave that also loads its INT8 blocks into its ring: once
-// its last INT4 tiles are issued, each freed slot takes one INT8 block
-// (kLoads8 loads), so behind a tile with `after` tiles still to come
-// N - after blocks (counted as at most 2, which every wave has) are in flight
-// too.
-template <int D, int NL, int N, int A = N>
-__device__ inline void read_staged_tail(int after, uint32_t lds, uint32_t o_kc, uint32_t o_km, uint32_t o_vc,
-                                        uint32_t o_vm, u32x4 (&r)[8]) {
-  constexpr int B = N - A < 2 ? N - A : 2;
-  if constexpr (A == 0) {
-    read_staged<D, kLoads8 * B>(lds, o_kc, o_km, o_vc, o_vm, r);
-  } else {
-    if (after >= A) read_staged<D, NL * A + kLoads8 * B>(lds, o_kc, o_km, o_vc, o_vm, r);
-    else read_staged_tail<D, NL, N, A - 1>(after, lds, o_kc, o_km, o_vc, o_vm, r);
-  }
-}
-
 // Chunk `split` of the pool of (b, kvh): records [r0, r1), the split-th of
 // nsplit equal shares (whole 32-record tiles) of the pool's count. Tile
 // t0 + wave + 4j goes to wave `wave` (the four waves read neighbouring tiles
@@ -1171,6 +1163,25 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   // the query is loaded first and converted while the first tiles are in flight
   typename Int4Core<D, G, !QBF16>::template QRaw<QBF16> qraw;
   core.template load_q<QBF16>(p, b, kvh, qraw);
+  // FUSE8 (one chunk per pair): the workgroup does the INT8 region too. Each
+  // wave's blocks are requested now, into LDS of their own beside the ring
+  // (before the tiles, so the tiles' waits need not count them), and used
+  // after the INT4 loop.
+  constexpr int kRow8 = Smem<D, G>::kRow8;
+  static_assert(kWaveBlocks8 == 3 && 16 * kRow8 + 128 <= Smem<D, G>::kBlk8 && G * D * 4 <= 3 * Smem<D, G>::kBlk8,
+                "INT8 blocks and their output fit the wave's block area");
+  const int slots8 = FUSE8 ? p.sink + p.recent : 0;
+  if constexpr (FUSE8) {
+    if (slots8 > 0) {
+      const size_t base8 = ((size_t)b * p.hkv + kvh) * slots8;
+#pragma unroll
+      for (int i = 0; i < kWaveBlocks8; ++i) {
+        const int rb = wave + kWaves * i;
+        uint8_t* r = &sm.u.f8.blk[wave][i][0];
+        if (rb < kBlocks8) int8_issue_block<D>(p, base8, rb, r, reinterpret_cast<float*>(r + 16 * kRow8));
+      }
+    }
+  }
   // this wave's first tile and tile count for a pool of c records (records [r0, r1))
   auto range = [&](int c, int& t0, int& ntw, int& r1) {
     const int share = ((c + p.nsplit - 1) / p.nsplit + kPoolTile - 1) / kPoolTile * kPoolTile;
@@ -1243,22 +1254,6 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   // else: the same tiles. Slots past ntw hold tiles that are never read: the
   // per-tile waits below count only the tiles < ntw issued after a tile, at
   // most what is in flight behind it, so they only wait longer.
-  // FUSE8 (one chunk per pair): the workgroup does the INT8 region too. Wave
-  // block i goes into ring slot (ntw + i) % NB, the i-th slot that the last
-  // NB tiles free (or, with fewer than NB tiles, after the loop), followed by
-  // its scales; the INT8 output goes to slot 1 and the INT4 one to slot 0.
-  constexpr int kRow8 = Smem<D, G>::kRow8;
-  static_assert(!FUSE8 || (16 * kRow8 + 128 <= TILE && NB >= kWaveBlocks8 && G * D * 4 <= TILE && NB >= 2),
-                "INT8 blocks and the two outputs fit the ring");
-  const int slots8 = FUSE8 ? p.sink + p.recent : 0;
-  const size_t base8 = ((size_t)b * p.hkv + kvh) * slots8;
-  const bool inloop8 = FUSE8 && slots8 > 0 && ntw >= NB;
-  auto slot8 = [&](int i) { return (ntw + i) % NB; };
-  auto issue8 = [&](int i) {
-    const int rb = wave + kWaves * i;
-    uint8_t* r = ring + slot8(i) * TILE;
-    if (rb < kBlocks8) int8_issue_block<D>(p, base8, rb, r, reinterpret_cast<float*>(r + 16 * kRow8));
-  };
   if (FUSE8 && threadIdx.x == 0 && (L < 0 || L > p.max_ctx)) flag(p, KVC_ERR_LENGTH);
   if (ntw > 0) {
     const int s = lane >> 4;
@@ -1275,16 +1270,8 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
         u32x4 r[8];
         // tiles in flight behind this one: NB - 1, fewer at the end (no tile
         // is loaded twice)
-        if (FUSE8 && inloop8)
-          read_staged_tail<D, NL, NB - 1>(ntw - 1 - jt, ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
-        else
-          read_staged_after<D, NL, NB - 1>(ntw - 1 - jt, ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
-        if (jt + NB < ntw) {
-          issue(jt + NB, k);
-        } else if (FUSE8 && inloop8) {
-          const int i = jt + NB - ntw;  // slot k = slot8(i) is free for good
-          if (i < kWaveBlocks8) issue8(i);
-        }
+        read_staged_after<D, NL, NB - 1>(ntw - 1 - jt, ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
+        if (jt + NB < ntw) issue(jt + NB, k);
         const int lim = r1 - 32 * (t0 + wave + kWaves * jt);
         uint32_t kc0[NG], kc1[NG], km[8], vc[8], vm[8];
 #pragma unroll
@@ -1301,14 +1288,9 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
     }
   }
   float m8 = -INFINITY, l8 = 0.0f;
-  float* o8d = reinterpret_cast<float*>(ring + TILE);
+  float* o8d = reinterpret_cast<float*>(&sm.u.f8.blk[wave][0][0]);  // after the blocks are read
   if constexpr (FUSE8) {
     if (slots8 > 0) {
-      if (!inloop8) {
-        __builtin_amdgcn_s_waitcnt(0);  // guessed tiles may still be landing in the ring
-#pragma unroll
-        for (int i = 0; i < kWaveBlocks8; ++i) issue8(i);
-      }
       float qe[D / 32][8];
       int8_load_q<D, G, QBF16>(p, b, kvh, qe);
       const int Lc = clamp_len(p, L);
@@ -1317,9 +1299,8 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
       int8_wave<D, G, QBF16>(
           p, nvalid, qe,
           [&](int i, const uint8_t*& rows, const float*& sc) {
-            const uint8_t* r = ring + slot8(i) * TILE;
-            rows = r;
-            sc = reinterpret_cast<const float*>(r + 16 * kRow8);
+            rows = &sm.u.f8.blk[wave][i][0];
+            sc = reinterpret_cast<const float*>(rows + 16 * kRow8);
           },
           m8, l8, o8d);
     } else {
@@ -1332,7 +1313,7 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   core.finish(sm.m[wave], sm.l[wave], sm.vm[wave], reinterpret_cast<float*>(&sm.u.stage[wave][0][0]),
               ntw > 0);
   if constexpr (FUSE8) {
-    // the INT8 part's (m, l) beside the INT4 ones (its o is in slot 1)
+    // the INT8 part's (m, l) beside the INT4 ones (its o is in the block area)
     if (lane < G) {  // lane h holds column h
       sm.m8[wave][lane] = m8;
       sm.l8[wave][lane] = l8;
@@ -1502,7 +1483,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __syncthreads();
     store_final<D, G>(
         p, sm, [&](int w) { return reinterpret_cast<const float*>(&sm.u.stage[w][0][0]); },
-        [&](int w) { return reinterpret_cast<const float*>(&sm.u.stage[w][1][0]); }, b, kvh);
+        [&](int w) { return reinterpret_cast<const float*>(&sm.u.f8.blk[w][0][0]); }, b, kvh);
     return;
   }
   // One-dimensional grid, dispatched in index order and spread round-robin
