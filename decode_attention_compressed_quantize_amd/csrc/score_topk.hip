@@ -162,6 +162,8 @@ struct TopkParams {
   int budget;
   int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
   PoolRef pool;      // kept-record pool maintained with the mask (pool.cap = 0: none)
+  int group;         // pairs per workgroup: 1, or kTopkGroup for a decode step (topk_group)
+  int pairs;         // batch * hkv
 };
 
 // Order-preserving key: larger score -> larger key; NaN -> 0 (below -inf); -0 == +0.
@@ -179,6 +181,7 @@ __device__ inline uint64_t comp_key(uint32_t key, int pos) {
 __device__ inline int comp_pos(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
 
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkGroup = kTopkThreads / 64;  // pairs per workgroup in a decode step
 constexpr int kCandCap = 512;  // keys around the threshold a refresh can sort into the lists
 
 // ---- one decode step on the lists, one wave, lane i holding a[i] and b[i]
@@ -520,13 +523,14 @@ __device__ __attribute__((always_inline)) int pool_apply(const TopkParams& p, Po
 // key above the threshold and the lowest positions equal to it (the unique
 // answer under "score descending, then position ascending"), and collects the
 // keys between the two outer ranks; sorted, they give the lists.
+// The full refresh of one (sequence, kv head) by the whole workgroup (the
+// incremental step, when there is a state, has been tried by topk_group).
 __device__ __attribute__((always_inline)) void topk_pair(const TopkParams& p, int h, int b) {
   __shared__ uint32_t hist[3][256];
   __shared__ uint32_t scan[kTopkThreads / 64];
   __shared__ uint32_t sel_digit[3], sel_above[3];
   __shared__ uint64_t cand[kCandCap];
   __shared__ uint32_t ncand;
-  __shared__ int done;
   __shared__ PoolLds ps;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -542,14 +546,11 @@ __device__ __attribute__((always_inline)) void topk_pair(const TopkParams& p, in
   uint32_t* mrow = p.mask + ((size_t)b * p.hkv + h) * p.words;
   TopkState* st = p.state ? p.state + (size_t)b * p.hkv + h : nullptr;
 
-  if (wid == 0) {
-    const bool ok = st && p.incremental && topk_step(p, st, L, n4, k, sc, mrow, lane, b, h);
-    if (lane == 0) done = ok ? 1 : 0;
-    if (lane == 0) ncand = 0;
-    if (lane == 0) ps.oldpop = 0;
+  if (tid == 0) {
+    ncand = 0;
+    ps.oldpop = 0;
   }
   __syncthreads();
-  if (done) return;
   // a pool that holds exactly the kept records of an earlier length is
   // updated by the records that change; anything else is rebuilt
   const bool pooled = p.pool.cap > 0;
@@ -1001,6 +1002,47 @@ __device__ inline uint32_t block_mask_word(int w, int L, int sink, int rec0, int
   return bits;
 }
 
+// The refresh of p.group pairs in one workgroup (1, or kTopkGroup in a decode
+// step with a state): wave w applies the incremental step (topk_step, one
+// wave's work) to pair p.group * g + w, so that a step over thousands of
+// pairs is one resident round of workgroups instead of one 1024-thread
+// workgroup per pair; the pairs whose step does not apply (no state, a list
+// ran out, a new budget, a stale state) are then refreshed in full one after
+// another by the whole workgroup (topk_pair). Each pair gets the same result
+// whatever the grouping.
+__device__ __attribute__((always_inline)) void topk_group(const TopkParams& p, int g) {
+  __shared__ uint32_t need;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  if (tid == 0) need = 0;
+  __syncthreads();
+  const int pair = g * p.group + wid;
+  if (wid < p.group && pair < p.pairs) {
+    const int b = pair / p.hkv, h = pair % p.hkv;
+    int L = p.seq_lens[b];
+    bool ok = false;
+    if (L >= 0 && L <= p.max_ctx && p.state && p.incremental) {
+      const int n4 = L > p.sink + p.recent ? L - p.sink - p.recent : 0;
+      const long long k = ((long long)p.budget * n4) / 1000;
+      const float* sc = p.scores + ((size_t)b * p.hkv + h) * p.max_ctx + p.sink;
+      uint32_t* mrow = p.mask + ((size_t)b * p.hkv + h) * p.words;
+      ok = topk_step(p, p.state + (size_t)b * p.hkv + h, L, n4, k, sc, mrow, lane, b, h);
+    }
+    if (!ok && lane == 0) atomicOr(&need, 1u << wid);
+  }
+  __syncthreads();
+  uint32_t nd = need;
+  while (nd) {
+    const int w = __builtin_ctz(nd);
+    nd &= nd - 1;
+    const int q = g * p.group + w;
+    topk_pair(p, q % p.hkv, q / p.hkv);
+    __syncthreads();
+  }
+}
+
+
 template <int B>
 __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, int b) {
   static_assert(B == 16 || B == 32 || B == 64, "block size");
@@ -1383,22 +1425,24 @@ __global__ __launch_bounds__(kTopkThreads) void block_topk_kernel(BlockTopkParam
   block_topk_pair<B>(p, sm, blockIdx.x % p.hkv, blockIdx.x / p.hkv);
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-  topk_pair(p, blockIdx.x, blockIdx.y);
-}
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) { topk_group(p, blockIdx.x); }
+
+// workgroups the refresh of a call takes
+inline int topk_groups(const TopkParams& p) { return (p.pairs + p.group - 1) / p.group; }
 
 // Scoring and the keep-mask refresh in one launch, for calls that append at
 // most 128 positions: the refresh only reads scores of INT4-region positions,
 // which lie below L - 128 and so were written by earlier calls. Workgroups
-// [0, pairs) refresh one (sequence, kv head) each; the rest score 4 appended
-// rows each (one per 256-thread quarter) for one kv head.
+// [0, pairs) refresh one (sequence, kv head) each, or kTopkGroup of them with
+// a refresh state (topk_group); the rest score 4 appended rows each (one per
+// 256-thread quarter) for one kv head.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(ScoreParams sp, TopkParams tp) {
   __shared__ float xs[kTopkThreads / kScoreThreads][2 * D];
   __shared__ float wsum[kTopkThreads / kScoreThreads][kScoreThreads / 64];
-  const int pairs = tp.hkv * sp.batch;
+  const int pairs = (tp.pairs + tp.group - 1) / tp.group;  // refresh workgroups
   if ((int)blockIdx.x < pairs) {
-    topk_pair(tp, blockIdx.x % tp.hkv, blockIdx.x / tp.hkv);
+    topk_group(tp, blockIdx.x);
     return;
   }
   const int g = blockIdx.x - pairs;
@@ -1419,9 +1463,9 @@ __global__ __launch_bounds__(kTopkThreads) void append_score_topk_kernel(QuantPa
                                                                          TopkParams tp, int nq) {
   __shared__ float xs[kTopkThreads / kScoreThreads][2 * D];
   __shared__ float wsum[kTopkThreads / kScoreThreads][kScoreThreads / 64];
-  const int pairs = tp.hkv * sp.batch;
+  const int pairs = (tp.pairs + tp.group - 1) / tp.group;  // refresh workgroups
   if ((int)blockIdx.x < pairs) {
-    topk_pair(tp, blockIdx.x % tp.hkv, blockIdx.x / tp.hkv);
+    topk_group(tp, blockIdx.x);
     return;
   }
   if ((int)blockIdx.x < pairs + nq) {
@@ -1478,6 +1522,9 @@ TopkParams topk_params(const kvc_cache& c, int budget_permille, TopkState* state
   p.sink = c.n_sink;
   p.recent = c.n_recent;
   p.pool = pool_ref(c);
+  p.pairs = c.batch * c.num_kv_heads;
+  // a decode step with a state: kTopkGroup pairs per workgroup (one wave each)
+  p.group = incremental && state ? kTopkGroup : 1;
   return p;
 }
 
@@ -1501,7 +1548,7 @@ hipError_t launch_score(const kvc_cache& c, const float* mlp, const void* k_new,
 hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state, bool incremental,
                        hipStream_t s) {
   const TopkParams p = topk_params(c, budget_permille, state, incremental);
-  hipLaunchKernelGGL(topk_kernel, dim3(c.num_kv_heads, c.batch), dim3(kTopkThreads), 0, s, p);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)topk_groups(p)), dim3(kTopkThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1603,7 +1650,7 @@ hipError_t launch_score_topk(const kvc_cache& c, const float* mlp, const void* k
   const TopkParams tp = topk_params(c, budget_permille, state, true);
   const long long rows = (long long)c.batch * n_new_max;
   const long long quads = (rows + 3) / 4;
-  const dim3 grid((unsigned)((long long)c.batch * c.num_kv_heads + quads * c.num_kv_heads));
+  const dim3 grid((unsigned)(topk_groups(tp) + quads * c.num_kv_heads));
   const bool bf = src == KVC_BF16;
   if (c.head_dim == 128) {
     if (bf) hipLaunchKernelGGL((score_topk_kernel<128, true>), grid, dim3(kTopkThreads), 0, s, sp, tp);
@@ -1625,7 +1672,7 @@ hipError_t launch_append_score_topk(const kvc_cache& c, const float* mlp, const 
   const long long rows = (long long)c.batch * n_new_max;
   const long long quads = (rows + 3) / 4;
   const int nq = (int)((qp.items + kTopkThreads / 64 - 1) / (kTopkThreads / 64));
-  const dim3 grid((unsigned)((long long)c.batch * c.num_kv_heads + nq + quads * c.num_kv_heads));
+  const dim3 grid((unsigned)(topk_groups(tp) + nq + quads * c.num_kv_heads));
   const bool bf = src == KVC_BF16;
   if (c.head_dim == 128) {
     if (bf) hipLaunchKernelGGL((append_score_topk_kernel<128, true>), grid, dim3(kTopkThreads), 0, s, qp, sp, tp, nq);
