@@ -316,8 +316,10 @@ KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* m
   }
   // rows appended in this call sit in the protected recent window: the
   // refresh reads neither their codes nor their scores, so all three run in
-  // one launch; otherwise the two calls run in order
-  if (mlp && n_new_max > 0 && n_new_max <= c->n_recent)
+  // one launch (the refresh is the incremental kind when this call scores the
+  // rows or n_new declares the caller's older scores unchanged); otherwise the
+  // two calls run in order
+  if ((mlp || n_new) && n_new_max > 0 && n_new_max <= c->n_recent)
     return launched(kvc::launch_append_score_topk(*c, mlp, k_new, v_new, src, n_new_max, n_new,
                                                   budget_permille, static_cast<kvc::TopkState*>(ws),
                                                   stream));

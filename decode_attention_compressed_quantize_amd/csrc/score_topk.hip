@@ -1670,7 +1670,7 @@ hipError_t launch_append_score_topk(const kvc_cache& c, const float* mlp, const 
   const ScoreParams sp = score_params(c, mlp, k_new, v_new, n_new_max, n_new);
   const TopkParams tp = topk_params(c, budget_permille, state, true);
   const long long rows = (long long)c.batch * n_new_max;
-  const long long quads = (rows + 3) / 4;
+  const long long quads = mlp ? (rows + 3) / 4 : 0;  // no scoring with the caller's scores
   const int nq = (int)((qp.items + kTopkThreads / 64 - 1) / (kTopkThreads / 64));
   const dim3 grid((unsigned)(topk_groups(tp) + nq + quads * c.num_kv_heads));
   const bool bf = src == KVC_BF16;

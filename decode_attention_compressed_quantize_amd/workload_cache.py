@@ -181,6 +181,13 @@ class LayerCache:
         """One decode-step update: append the rows, score them and refresh the
         keep mask (one launch for the token policy with MLP scores)."""
         w = self.w
+        if w.mask in ("scores", "all") and not self.block_policy:
+            # the caller's scores (or keep-all): n_new declares the older ones
+            # unchanged, so the encoding and the refresh run as one launch
+            budget = 1000 if w.mask == "all" else w.budget_permille
+            kvc_append_score_topk_mask(self.cache, None, k_new, v_new, n_new, budget, ws=ws,
+                                       stream=stream)
+            return
         if w.mask == "mlp" and getattr(self, "mlp", None) is not None:
             if self.block_policy:
                 kvc_append_score_block_mask(self.cache, self.mlp, k_new, v_new, n_new,

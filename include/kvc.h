@@ -260,11 +260,14 @@ KVC_API kvc_status kvc_score_topk_mask(const kvc_cache* c, const float* mlp, con
  * Source: KV4-RL review, section 3 (quantize-on-append into the INT4 store and
  * the INT8 side cache) and KVP promo page, section "Core mechanism" (score the
  * new tokens, rank, truncate), steps that one decode step performs in order.
- *   Arguments, ownership and errors as for the two calls. When mlp != NULL and
+ *   Arguments, ownership and errors as for the two calls. When
  *   1 <= n_new_max <= n_recent, every appended position lies in the protected
  *   recent window, whose codes and scores the refresh does not read, so the
- *   encoding, the scoring and the refresh run as one launch; otherwise the two
- *   calls run in order on the stream.
+ *   encoding, the scoring (mlp != NULL) and the refresh run as one launch,
+ *   provided the refresh may be incremental: mlp != NULL, or mlp == NULL with
+ *   n_new != NULL (the caller's scores, those below the previous lengths
+ *   unchanged, as for kvc_score_topk_mask); otherwise the two calls run in
+ *   order on the stream.
  */
 KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* mlp,
                                               const void* k_new, const void* v_new, kvc_dtype src,

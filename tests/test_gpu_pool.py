@@ -151,13 +151,18 @@ def _pool_decode_run(w, steps, budgets, stall=(), shrink=None, attend_every=25, 
         if w.mask != "mlp":
             # caller-written scores: write those of the appended positions, then
             # refresh with n_new (the older scores are declared unchanged)
-            m.kvc_quantize_append(lc.cache, k_new, v_new, nn)
+            # (odd steps: the two in one call, which runs as one launch)
+            if not (step % 2 and w.protect):
+                m.kvc_quantize_append(lc.cache, k_new, v_new, nn)
             if w.mask == "scores":
                 for b in range(w.batch):
                     if n_new[b]:
                         L = int(lens[b])
                         lc.cache.scores[b, :, L - 1] = W.given_scores_torch(w, 0, b, L, "cuda")[:, L - 1]
-            m.kvc_score_topk_mask(lc.cache, None, None, None, nn, budget, ws=state)
+            if step % 2 and w.protect:
+                m.kvc_append_score_topk_mask(lc.cache, None, k_new, v_new, nn, budget, ws=state)
+            else:
+                m.kvc_score_topk_mask(lc.cache, None, None, None, nn, budget, ws=state)
         elif step % 2 and w.protect:
             m.kvc_append_score_topk_mask(lc.cache, lc.mlp, k_new, v_new, nn, budget, ws=state)
         else:
