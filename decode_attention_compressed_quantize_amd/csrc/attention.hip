@@ -1,5 +1,8 @@
 // Split-region decode attention over the compressed cache, with the exact
-// log-sum-exp merge of the per-chunk partials in a second, small launch.
+// log-sum-exp merge of the per-chunk partials: in a second, small launch
+// (mask mode), in the same launch by the last workgroup of each (sequence,
+// kv head) (pool mode), or, with one chunk per pair, by the chunk's own
+// workgroup, which then also does the INT8 region (pool mode, fuse8).
 //
 // Source: KV4-RL review, section 3 - the INT4 region and the protected INT8
 // region are processed independently and their outputs are combined by an
@@ -11,8 +14,8 @@
 // (sequence, kv head) for the INT8 region. Every workgroup writes one
 // unnormalised partial (m, l, o[D]) per query head: m is the max logit in log2
 // units (logit * log2 e), l = sum 2^(s - m), o = sum 2^(s - m) * v. The merge
-// kernel combines the partials of each (sequence, kv head) in a fixed order,
-// so results do not depend on scheduling. The INT4 records come either from
+// combines the partials of each (sequence, kv head) in a fixed order, so
+// results do not depend on scheduling. The INT4 records come either from
 // the paged store through the keep mask (mask mode: chunk j of a (sequence,
 // kv head) is a range of positions whose kept records are gathered), or from
 // the kept-record pool (pool mode: chunk j is the j-th of nsplit equal shares
