@@ -181,7 +181,8 @@ __device__ inline uint64_t comp_key(uint32_t key, int pos) {
 __device__ inline int comp_pos(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
 
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkGroup = kTopkThreads / 64;  // pairs per workgroup in a decode step
+constexpr int kTopkGroup = kTopkThreads / 64;  // at most this many pairs per workgroup in a decode step
+constexpr int kTopkResident = 2 * 256;         // 1024-thread workgroups resident at once (2 per CU)
 constexpr int kCandCap = 512;  // keys around the threshold a refresh can sort into the lists
 
 // ---- one decode step on the lists, one wave, lane i holding a[i] and b[i]
@@ -1002,14 +1003,14 @@ __device__ inline uint32_t block_mask_word(int w, int L, int sink, int rec0, int
   return bits;
 }
 
-// The refresh of p.group pairs in one workgroup (1, or kTopkGroup in a decode
-// step with a state): wave w applies the incremental step (topk_step, one
-// wave's work) to pair p.group * g + w, so that a step over thousands of
-// pairs is one resident round of workgroups instead of one 1024-thread
-// workgroup per pair; the pairs whose step does not apply (no state, a list
-// ran out, a new budget, a stale state) are then refreshed in full one after
-// another by the whole workgroup (topk_pair). Each pair gets the same result
-// whatever the grouping.
+// The refresh of p.group pairs in one workgroup (1, or up to kTopkGroup in a
+// decode step with a state): wave w applies the incremental step (topk_step,
+// one wave's work) to pair p.group * g + w, so that a step over thousands of
+// pairs is one resident round of workgroups instead of several rounds of one
+// 1024-thread workgroup per pair; the pairs whose step does not apply (no
+// state, a list ran out, a new budget, a stale state) are then refreshed in
+// full one after another by the whole workgroup (topk_pair). Each pair gets
+// the same result whatever the grouping.
 __device__ __attribute__((always_inline)) void topk_group(const TopkParams& p, int g) {
   __shared__ uint32_t need;
   const int tid = threadIdx.x;
@@ -1523,8 +1524,16 @@ TopkParams topk_params(const kvc_cache& c, int budget_permille, TopkState* state
   p.recent = c.n_recent;
   p.pool = pool_ref(c);
   p.pairs = c.batch * c.num_kv_heads;
-  // a decode step with a state: kTopkGroup pairs per workgroup (one wave each)
-  p.group = incremental && state ? kTopkGroup : 1;
+  // A decode step with a state packs pairs (one wave each) until the launch
+  // fits one resident round (two 1024-thread workgroups per CU); no more, as
+  // the pairs of a workgroup that need a full refresh take turns.
+  p.group = 1;
+  if (incremental && state) {
+    const int round = kTopkResident;
+    p.group = (p.pairs + round - 1) / round;
+    if (p.group > kTopkGroup) p.group = kTopkGroup;
+    if (p.group < 1) p.group = 1;
+  }
   return p;
 }
 

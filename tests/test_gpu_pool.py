@@ -218,6 +218,18 @@ def test_pool_given_scores_incremental():
     _pool_decode_run(w, 160, lambda s: 500 if s < 100 else 400, stall=[(30, 2)], attend_every=40)
 
 
+def test_pool_decode_steps_many_pairs():
+    """More pairs (600) than one round of 1024-thread refresh workgroups: a decode
+    step packs two pairs per workgroup (one wave each), and the budget change at
+    step 5 makes every pair's step fall back to the full refresh, the two pairs
+    of a workgroup taking turns. Masks and pools match the oracle after every
+    step."""
+    lens = tuple(int(x) for x in np.linspace(150, 600, 150).round())
+    w = W.WORKLOADS["longtail"].replace(name="many_steps", batch=len(lens), kv_heads=4, q_heads=16,
+                                        ctx_range=None, ctx_list=lens, decode_steps=12)
+    _pool_decode_run(w, 10, lambda s: 500 if s < 5 else 400, attend_every=100)
+
+
 def test_pool_keep_all_incremental():
     """Every position kept (budget 1000, the uniform workload's mask) refreshed in
     place each step: each record entering the INT4 region joins the pool."""
