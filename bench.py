@@ -24,6 +24,7 @@ import json
 import statistics
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -715,6 +716,8 @@ def main():
     ap.add_argument("--reps", type=int, default=7, help="repetitions of the attention-call timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling (a child measuring another workload)")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the uniform4k / longtail figures that the default run adds")
     ap.add_argument("--pool", choices=["auto", "on", "off"], default="auto",
@@ -736,7 +739,7 @@ def main():
     import torch
 
     # the streaming-read ceiling, measured before the caches take the memory
-    ceil = read_ceiling_gbs() if TIER_MODE.get(args.workload) != "all" else None
+    ceil = read_ceiling_gbs() if TIER_MODE.get(args.workload) != "all" and not args.no_ceiling else None
     torch.cuda.empty_cache()
     res = decode_run(args, args.workload, args.steps, args.warmup, args.calls, args.reps, args.pool,
                      args.replicas)
@@ -802,25 +805,34 @@ def main():
     del res
     torch.cuda.empty_cache()
     if args.workload == "long128k" and not args.no_others:
-        # the other two single-GPU workloads: attention per call and the decode step
+        # The other two single-GPU workloads: attention per call and the decode
+        # step, each measured in a child process of its own (a fresh address
+        # space, as when the workload runs alone: measured in this process after
+        # the 128K caches were freed, the uniform call read ~6% slower). This
+        # process holds no caches meanwhile and does no GPU work.
         others = {}
         for wl in ("uniform4k", "longtail"):
-            o = decode_run(args, wl, 100, 5, args.calls, 3)
-            pl = next(iter(o["per_layer"].values()))
+            cmd = [sys.executable, "-u", os.path.abspath(__file__), "--workload", wl, "--steps", "100",
+                   "--warmup", "5", "--calls", str(args.calls), "--reps", "3", "--no-cpu", "--no-ceiling"]
+            print(f"bench: measuring {wl} in a child process", file=sys.stderr, flush=True)
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+            if r.returncode != 0:
+                raise SystemExit(f"bench: {wl} child failed with status {r.returncode}")
+            o = json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1])
+            pl = next(iter(o["attention"]["per_layer"].values()))
             others[wl] = {
                 "attention_us": round(1000 * pl["attention_ms"], 2), "attention_GBs": pl["attention_GBs"],
                 "frac": pl["frac"], "rep_mean_us_range": [round(1000 * pl["rep_mean_ms_min"], 2),
                                                           round(1000 * pl["rep_mean_ms_max"], 2)],
                 "algorithmic_bytes_per_call": pl["algorithmic_bytes"],
-                "ms_per_step": round(o["ms_per_step"], 5), "step_GBs": round(o["gbs"], 1),
-                "kept_record_pool": o["pooled"], "batch": o["base"][0].batch,
-                "context": int(o["base"][0].lengths().max()), "replicas": o["replicas"],
-                "timing": f"100 decode steps; attention: median over 3 repetitions of {args.calls} calls",
+                "ms_per_step": o["ms_per_step"], "step_GBs": o["value"],
+                "kept_record_pool": o["config"]["kept_record_pool"], "batch": o["config"]["batch"],
+                "context": o["config"]["context"], "replicas": o["config"]["replicas"],
+                "timing": f"100 decode steps; attention: median over 3 repetitions of {args.calls} calls; "
+                          f"own process",
             }
-            del o
-            torch.cuda.empty_cache()
         line["other_workloads"] = others
-    if tier != "all":
+    if tier != "all" and not args.no_ceiling:
         add_read_ceiling(line, ceil)
     if not args.no_cpu:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
