@@ -1258,6 +1258,34 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
   // per-tile waits below count only the tiles < ntw issued after a tile, at
   // most what is in flight behind it, so they only wait longer.
   if (FUSE8 && threadIdx.x == 0 && (L < 0 || L > p.max_ctx)) flag(p, KVC_ERR_LENGTH);
+  // FUSE8: the wave's INT8 part (its blocks are in LDS since before the first
+  // tile). It runs inside the INT4 loop, before tile s8 of the wave is read
+  // (the tiles in flight land meanwhile); s8 differs from wave to wave, so that across the chip the INT8 parts are
+  // spread over the streaming instead of all running after it, when the HBM
+  // would have nothing to do. A wave without INT4 tiles does it after the loop.
+  float m8 = -INFINITY, l8 = 0.0f;
+  float* o8d = reinterpret_cast<float*>(&sm.u.f8.blk[wave][0][0]);  // after the blocks are read
+  auto int8_part = [&] {
+    if constexpr (FUSE8) {
+      if (slots8 > 0) {
+        const int Lc = clamp_len(p, L);
+        const int nvalid = Lc < slots8 ? Lc : slots8;
+        float qe[D / 32][8];
+        int8_load_q<D, G, QBF16>(p, b, kvh, qe);
+        __builtin_amdgcn_s_waitcnt(0);  // the wave's blocks and its query are in
+        int8_wave<D, G, QBF16>(
+            p, nvalid, qe,
+            [&](int i, const uint8_t*& rows, const float*& sc) {
+              rows = &sm.u.f8.blk[wave][i][0];
+              sc = reinterpret_cast<const float*>(rows + 16 * kRow8);
+            },
+            m8, l8, o8d);
+      } else {
+        for (int i = lane; i < G * D; i += 64) o8d[i] = 0.0f;
+      }
+    }
+  };
+  const int s8 = ntw > 0 ? __builtin_amdgcn_readfirstlane((int)((blockIdx.x * kWaves + wave) % ntw)) : -1;
   if (ntw > 0) {
     const int s = lane >> 4;
     const uint32_t o_kc = (uint32_t)lane * S::SB;
@@ -1273,6 +1301,7 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
         u32x4 r[8];
         // tiles in flight behind this one: NB - 1, fewer at the end (no tile
         // is loaded twice)
+        if (FUSE8 && __builtin_expect(jt == s8, 0)) int8_part();
         read_staged_after<D, NL, NB - 1>(ntw - 1 - jt, ring_lds + k * TILE, o_kc, o_km, o_vc, o_vm, r);
         if (jt + NB < ntw) issue(jt + NB, k);
         const int lim = r1 - 32 * (t0 + wave + kWaves * jt);
@@ -1290,26 +1319,7 @@ __device__ void int4_pool_chunk(const AttnParams& p, Smem<D, G>& sm, int b, int 
       }
     }
   }
-  float m8 = -INFINITY, l8 = 0.0f;
-  float* o8d = reinterpret_cast<float*>(&sm.u.f8.blk[wave][0][0]);  // after the blocks are read
-  if constexpr (FUSE8) {
-    if (slots8 > 0) {
-      float qe[D / 32][8];
-      int8_load_q<D, G, QBF16>(p, b, kvh, qe);
-      const int Lc = clamp_len(p, L);
-      const int nvalid = Lc < slots8 ? Lc : slots8;
-      __builtin_amdgcn_s_waitcnt(0);  // the wave's blocks are in
-      int8_wave<D, G, QBF16>(
-          p, nvalid, qe,
-          [&](int i, const uint8_t*& rows, const float*& sc) {
-            rows = &sm.u.f8.blk[wave][i][0];
-            sc = reinterpret_cast<const float*>(rows + 16 * kRow8);
-          },
-          m8, l8, o8d);
-    } else {
-      for (int i = lane; i < G * D; i += 64) o8d[i] = 0.0f;
-    }
-  }
+  if (FUSE8 && ntw <= 0) int8_part();
   // the wave's output goes to the start of its own ring (its loads are done
   // first; with FUSE8 the INT8 part has read its blocks)
   __builtin_amdgcn_s_waitcnt(0);
