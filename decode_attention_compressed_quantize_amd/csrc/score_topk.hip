@@ -182,7 +182,13 @@ __device__ inline int comp_pos(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkGroup = kTopkThreads / 64;  // at most this many pairs per workgroup in a decode step
-constexpr int kTopkResident = 2 * 256;         // 1024-thread workgroups resident at once (2 per CU)
+// Top-k workgroups a decode step aims for: half of the 256 resident 1024-thread
+// workgroups (one per CU at 128 VGPRs), leaving the rest of the round to the
+// encoding and scoring workgroups of the same launch (measured: 128 against
+// 256 and 512 took the uniform step from 75.7 to 70.6 us, the long-tail step
+// from 211.8 to 205.1 us and the 36-layer step from 10.04 to 9.87 ms; 64 and
+// 32 were no faster)
+constexpr int kTopkResident = 128;
 constexpr int kCandCap = 512;  // keys around the threshold a refresh can sort into the lists
 
 // ---- one decode step on the lists, one wave, lane i holding a[i] and b[i]
@@ -1524,9 +1530,9 @@ TopkParams topk_params(const kvc_cache& c, int budget_permille, TopkState* state
   p.recent = c.n_recent;
   p.pool = pool_ref(c);
   p.pairs = c.batch * c.num_kv_heads;
-  // A decode step with a state packs pairs (one wave each) until the launch
-  // fits one resident round (two 1024-thread workgroups per CU); no more, as
-  // the pairs of a workgroup that need a full refresh take turns.
+  // A decode step with a state packs pairs (one wave each) into about
+  // kTopkResident workgroups; no more per workgroup than that needs, as the
+  // pairs of a workgroup that need a full refresh take turns.
   p.group = 1;
   if (incremental && state) {
     const int round = kTopkResident;
