@@ -117,11 +117,23 @@ __device__ inline void quantize_item(const QuantParams& p, long long item, int l
   const long long bj = item / p.hkv;
   const int j = (int)(bj % p.n_new_max);
   const int b = (int)(bj / p.n_new_max);
+  // The loads that depend on nothing else go out together (the row - every
+  // row j < n_new_max lies in the caller's buffer -, the count and the
+  // length), then the page and the pool header, so an append costs two
+  // memory round trips before its stores.
+  const bool is_v = lane >= 32;
+  const int hl = lane & 31;
+  float x[EPL];
+  const size_t src_off = (((size_t)b * p.n_new_max + j) * p.hkv + h) * D + (size_t)hl * EPL;
+  load_elems<EPL, BF16>(is_v ? p.v_new : p.k_new, src_off, x);
   const int nn = p.n_new[b];
-  if (j >= nn) return;
   const int L = p.seq_lens[b];
+  if (j >= nn) return;
   const int pos = L - nn + j;
   if (pos < 0 || pos >= p.max_ctx || L > p.max_ctx) return;
+  const int lp = pos / kPage;
+  if (lp >= p.max_pages) return;
+  const int page = p.block_table[(size_t)b * p.max_pages + lp];
   if (p.pool_header && j == 0 && lane == 0) {
     // a pool describing length H holds records of positions in [sink, H - recent);
     // rows [pos, L) that reach into that range make it stale
@@ -129,16 +141,7 @@ __device__ inline void quantize_item(const QuantParams& p, long long item, int l
     const int lo = pos > p.sink ? pos : p.sink;
     if (lo < L && lo < ph[1] - p.recent) ph[2] = 0;
   }
-  const int lp = pos / kPage;
-  if (lp >= p.max_pages) return;
-  const int page = p.block_table[(size_t)b * p.max_pages + lp];
   if (page < 0 || page >= p.num_pages + p.host_pages) return;
-
-  const bool is_v = lane >= 32;
-  const int hl = lane & 31;
-  float x[EPL];
-  const size_t src_off = (((size_t)b * p.n_new_max + j) * p.hkv + h) * D + (size_t)hl * EPL;
-  load_elems<EPL, BF16>(is_v ? p.v_new : p.k_new, src_off, x);
 
   // ---- INT4: group min / max over LPG lanes
   float mn = x[0], mx = x[0];

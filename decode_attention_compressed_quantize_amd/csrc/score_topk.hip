@@ -82,30 +82,31 @@ __device__ __attribute__((always_inline)) void score_row(const ScoreParams& p, c
   const int lane = gtid & 63;
   const int part = gtid & 7;
   const long long total = (long long)p.batch * p.n_new_max;
+  static_assert(IN <= kScoreThreads, "one input entry per thread");
   int b = 0, pos = -1;
-  size_t src = 0;
+  float v = 0.0f;
   if (f < total) {
     b = (int)(f / p.n_new_max);
     const int j = (int)(f % p.n_new_max);
+    // the row's entry (every row j < n_new_max lies in the caller's buffer),
+    // the count and the length are loaded together: one memory round trip
+    const size_t src = (((size_t)b * p.n_new_max + j) * p.hkv + h) * D;
+    if (gtid < IN) {
+      const void* base = gtid < D ? p.k_new : p.v_new;
+      const int d = gtid < D ? gtid : gtid - D;
+      if constexpr (BF16) v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[src + d] << 16);
+      else v = reinterpret_cast<const float*>(base)[src + d];
+    }
     const int nn = p.n_new[b];
+    const int L = p.seq_lens[b];
     if (j < nn) {
-      pos = p.seq_lens[b] - nn + j;
+      pos = L - nn + j;
       if (pos >= p.max_ctx) pos = -1;
-      src = (((size_t)b * p.n_new_max + j) * p.hkv + h) * D;
     }
   }
   const bool valid = pos >= 0;
   __syncthreads();  // xs and wsum of the previous row are consumed
-  if (valid) {
-    for (int i = gtid; i < IN; i += kScoreThreads) {
-      const void* base = i < D ? p.k_new : p.v_new;
-      const int d = i < D ? i : i - D;
-      float v;
-      if constexpr (BF16) v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[src + d] << 16);
-      else v = reinterpret_cast<const float*>(base)[src + d];
-      xs[i] = v;
-    }
-  }
+  if (valid && gtid < IN) xs[gtid] = v;
   __syncthreads();
   float acc = 0.0f;
   if (valid) {
