@@ -1,8 +1,9 @@
 """GPU test of kvc_decode_attention_noalloc: the allocation-free variant of
 kvc_decode_attention (its partials live in the library's per-GPU scratch).
 
-Two calls in a row through the C ABI, the second on a smaller cache (so it
-reads a scratch that still holds the first call's partials), each compared
+Calls in a row through the C ABI, the second on a smaller cache (so it
+reads a scratch that still holds the first call's partials), the third on a
+cache with a kept-record pool, each compared
 with kvc_decode_attention on the same inputs: the same kernels and the same
 split plan run, so outputs and LSE must be bit-identical; and both are
 checked against the CPU oracle on sampled (sequence, kv head) pairs.
@@ -17,10 +18,15 @@ pytestmark = pytest.mark.gpu
 
 
 def _cases():
+    """(workload, kept-record pool): mask mode twice (the second smaller), then
+    pool mode, whose last workgroup per (sequence, kv head) merges the
+    partials from the scratch in the same launch."""
     big = W.Workload("noalloc_big", 8, 32, 8, 128, ctx=6000, mask="mlp", budget_permille=500)
     small = W.Workload("noalloc_small", 3, 8, 4, 64, ctx_list=(700, 145, 1999), mask="mlp",
                        budget_permille=300, src_dtype="f32")
-    return [big, small]
+    pooled = W.Workload("noalloc_pool", 4, 32, 8, 128, ctx_list=(9000, 145, 3000, 20000), mask="mlp",
+                        budget_permille=300)
+    return [(big, False), (small, False), (pooled, True)]
 
 
 def test_noalloc_matches_workspace_entry_point_twice():
@@ -29,10 +35,10 @@ def test_noalloc_matches_workspace_entry_point_twice():
     from kvc_testlib import assert_attention_close, keep4_from_mask, oracle_heads
 
     kvc.lib()
-    for i, w in enumerate(_cases()):
+    for i, (w, pool) in enumerate(_cases()):
         print(f"noalloc call {i}: {w.name} B={w.batch} Hq={w.q_heads} Hkv={w.kv_heads} "
-              f"D={w.head_dim}", flush=True)
-        lc = LayerCache(w)
+              f"D={w.head_dim} pool={pool}", flush=True)
+        lc = LayerCache(w, pool=pool)
         q = lc.queries(0)
         need = kvc.kvc_attention_workspace_bytes(lc.cache, w.q_heads)
         assert 0 < need <= kvc.NOALLOC_SCRATCH_BYTES
