@@ -559,9 +559,13 @@ def decode_run(args, workload, steps, warmup, calls, reps, pool_mode="auto", rep
     host_moved = 0
 
     def pooled(w):
+        # auto: the token policy; the block policy maintains a pool too (--pool on),
+        # but at 128K its refresh launch then costs more than the attention saves
         if pool_mode == "off" or tier:
             return False
-        return w.policy == "token" and w.recency_window == 0 and w.mask in ("mlp", "scores", "all")
+        if w.recency_window != 0 or w.mask not in ("mlp", "scores", "all"):
+            return False
+        return w.policy == "token" or (w.policy == "block" and pool_mode == "on")
 
     for li, w in enumerate(base):
         host = W.page_table(w, li)[1] if tier else 0
@@ -721,8 +725,8 @@ def main():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the uniform4k / longtail figures that the default run adds")
     ap.add_argument("--pool", choices=["auto", "on", "off"], default="auto",
-                    help="kept-record pool (auto: on for the token top-k policy, whose refresh "
-                         "maintains it; the block policy and the host tier read through the mask)")
+                    help="kept-record pool (auto: on for the token top-k policy; on: also for the "
+                         "block policy; the host tier and recency windows read through the mask)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "

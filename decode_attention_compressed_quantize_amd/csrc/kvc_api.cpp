@@ -84,6 +84,22 @@ kvc_status check_pool_budget(const kvc_cache* c, int budget_permille) {
   return KVC_OK;
 }
 
+// The same for the block policy: whole blocks of B tokens are kept (the first
+// and the last candidate block can be short), at most floor(budget * nb / 1000)
+// of the nb candidate blocks.
+kvc_status check_pool_block_budget(const kvc_cache* c, int budget_permille, int block_tokens,
+                                   int window) {
+  if (c->pool_capacity <= 0) return KVC_OK;
+  const long long n4 = int4_capacity(c);
+  const long long span = window > 0 && window < n4 ? window : n4;
+  const long long nb = (span + block_tokens - 1) / block_tokens + (window > 0 ? 1 : 0);
+  long long keep = (long long)budget_permille * nb / 1000 * block_tokens;
+  if (keep > n4) keep = n4;
+  if (keep > c->pool_capacity)
+    return fail(KVC_E_SHAPE, "the budget can keep more records than pool_capacity holds");
+  return KVC_OK;
+}
+
 kvc_status check_append(const void* k_new, const void* v_new, kvc_dtype src, int n_new_max,
                         const int32_t* n_new) {
   if (n_new_max < 0) return fail(KVC_E_SHAPE, "n_new_max must be >= 0");
@@ -345,10 +361,8 @@ KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, co
                                         const int32_t* n_new, int32_t budget_permille,
                                         int32_t block_tokens, int32_t recency_window, void* ws,
                                         size_t ws_bytes, hipStream_t stream) {
-  kvc_status st = check_cache(c, kNeedMask | kNeedScores);
+  kvc_status st = check_cache(c, kNeedMask | kNeedScores | (c && c->pool_capacity > 0 ? kNeedInt4 : 0u));
   if (st != KVC_OK) return st;
-  if (c->pool_capacity > 0)
-    return fail(KVC_E_UNSUPPORTED, "the block policy does not maintain a kept-record pool");
   if (budget_permille < 0 || budget_permille > 1000)
     return fail(KVC_E_SHAPE, "budget_permille must be in [0, 1000]");
   if (block_tokens != 16 && block_tokens != 32 && block_tokens != 64)
@@ -356,6 +370,8 @@ KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, co
   if ((long long)c->max_ctx > (long long)kvc::kMaxBlocks * block_tokens)
     return fail(KVC_E_UNSUPPORTED, "too many blocks per sequence");
   if (recency_window < 0) return fail(KVC_E_SHAPE, "recency_window must be >= 0");
+  st = check_pool_block_budget(c, budget_permille, block_tokens, recency_window);
+  if (st != KVC_OK) return st;
   if (ws) {
     if (ws_bytes < kvc_block_workspace_bytes(c, block_tokens))
       return fail(KVC_E_WORKSPACE, "block refresh state smaller than kvc_block_workspace_bytes");
@@ -387,8 +403,6 @@ KVC_API kvc_status kvc_append_score_block_mask(const kvc_cache* c, const float* 
                                                hipStream_t stream) {
   kvc_status st = check_cache(c, kNeedInt4 | kNeedInt8 | kNeedMask | kNeedScores);
   if (st != KVC_OK) return st;
-  if (c->pool_capacity > 0)
-    return fail(KVC_E_UNSUPPORTED, "the block policy does not maintain a kept-record pool");
   st = check_append(k_new, v_new, src, n_new_max, n_new);
   if (st != KVC_OK) return st;
   if (budget_permille < 0 || budget_permille > 1000)
@@ -398,6 +412,8 @@ KVC_API kvc_status kvc_append_score_block_mask(const kvc_cache* c, const float* 
   if ((long long)c->max_ctx > (long long)kvc::kMaxBlocks * block_tokens)
     return fail(KVC_E_UNSUPPORTED, "too many blocks per sequence");
   if (recency_window < 0) return fail(KVC_E_SHAPE, "recency_window must be >= 0");
+  st = check_pool_block_budget(c, budget_permille, block_tokens, recency_window);
+  if (st != KVC_OK) return st;
   if (ws) {
     if (ws_bytes < kvc_block_workspace_bytes(c, block_tokens))
       return fail(KVC_E_WORKSPACE, "block refresh state smaller than kvc_block_workspace_bytes");

@@ -850,6 +850,7 @@ struct BlockTopkParams {
   int budget;
   int window;
   int sink, recent;  // INT8-protected sink and recent positions (16/128, or 0/0)
+  PoolRef pool;      // kept-record pool maintained with the mask (pool.cap = 0: none)
 };
 
 constexpr int kBlockWaves = kTopkThreads / 64;
@@ -1051,7 +1052,9 @@ __device__ __attribute__((always_inline)) void topk_group(const TopkParams& p, i
 }
 
 
-template <int B>
+// POOL: the kept-record pool is maintained with the mask (a separate
+// instance, so that the kernels without a pool keep their own code).
+template <int B, bool POOL>
 __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, int b) {
   static_assert(B == 16 || B == 32 || B == 64, "block size");
   constexpr int kOldWords = 5;  // previous mask words held per thread (the rest re-read)
@@ -1088,6 +1091,26 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
     thr_ok = valid && st->has_thr != 0 && st->budget == p.budget;
     thr0 = st->thr;
   }
+  // a pool that holds exactly the kept records of an earlier length is updated
+  // by the records that change (as in the token refresh); anything else, and
+  // masks longer than the words a thread keeps, is rebuilt
+  // The pool's header and the page of xpos, the position entering the INT4
+  // region at this length (the one leaving the recent window), are loaded here
+  // with the state but not looked at before the key passes, so that they add
+  // no round trip of their own; xpos's record is requested (by wave 0) after
+  // those passes and lands during the mask pass: in the usual decode step it
+  // is the only record that joins the pool.
+  const bool pooled = POOL && p.pool.cap > 0;
+  const int pair = b * p.hkv + h;
+  int32_t ph0 = 0, ph1 = -1, ph2 = 0;
+  if (pooled) {
+    const int32_t* ph = p.pool.header + 4 * (size_t)pair;
+    ph0 = ph[0];
+    ph1 = ph[1];
+    ph2 = ph[2];
+  }
+  const int xpos = pooled && n4 > 0 ? sink + n4 - 1 : -1;
+  const int xpg = xpos >= 0 ? p.pool.block_table[(size_t)b * p.pool.max_pages + (xpos >> 4)] : -1;
   // keys above / equal to thr0 as the state left them, and which old keys leave
   const int n4o = len0 > slots ? len0 - slots : 0;
   const int c0o = p.window > 0 ? (n4o - p.window > 0 ? n4o - p.window : 0) : 0;
@@ -1401,17 +1424,124 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   auto word_bits = [&](int w) -> uint32_t {
     return block_mask_word<B>(w, L, sink, rec0, lo4, hi4, kept_block);
   };
+  // a pool that holds exactly the kept records of an earlier length is updated
+  // by the records that change (as in the token refresh); anything else, and
+  // masks longer than the words a thread keeps, is rebuilt
+  int plen_old = -1, pcnt_old = 0;
+  if ((uint32_t)ph2 == kPoolMagic && ph1 >= 0 && ph1 <= p.max_ctx && ph0 >= 0 && ph0 <= p.pool.cap) {
+    plen_old = ph1;
+    pcnt_old = ph0;
+  }
+  const bool pdiff = pooled && plen_old >= 0 && p.words <= kOldWords * kTopkThreads;
+  const int pn4_old = plen_old > slots ? plen_old - slots : 0;
+  const int xpage = xpg >= 0 && xpg < p.pool.num_pages + p.pool.host_pages ? xpg : -1;
+  uint4 xrec = make_uint4(0u, 0u, 0u, 0u);
+  if (POOL && xpage >= 0 && wid == 0 && lane < pool_chunks(p.pool.D))
+    xrec = *reinterpret_cast<const uint4*>(pool_src_chunk(p.pool, xpage, h, xpos, lane));
+  // pool: per word, the kept INT4 records that leave and those that enter
+  uint32_t remw[POOL ? kOldWords : 1], addw[POOL ? kOldWords : 1], oldpop = 0;
 #pragma unroll
   for (int m = 0; m < kOldWords; ++m) {
     const int w = tid + m * kTopkThreads;
+    if constexpr (POOL) remw[m] = addw[m] = 0u;
     if (w < p.words) {
       const uint32_t bits = word_bits(w);
       if (bits != old_w[m]) mrow[w] = bits;
+      if constexpr (POOL) if (pdiff) {
+        // only entering records have their pages looked up (a record the pool
+        // holds stays valid while the caller keeps the table, as the pool
+        // contract requires), so a word without one costs no load
+        const uint32_t old_in = region_bits(w, old_w[m], sink, sink + pn4_old);
+        const uint32_t new_in = region_bits(w, bits, sink, sink + n4);
+        oldpop += (uint32_t)__popc(old_in);
+        remw[m] = old_in & ~new_in;
+        uint32_t add = new_in & ~old_in;
+        const bool only_x = xpage >= 0 && w == (xpos >> 5) && add == 1u << (xpos & 31);
+        if (add && !only_x) {
+          int pa = -1, pb = -1;
+          add = pool_word_bits(p.pool, b, w, add, sink, sink + n4, pa, pb);
+        }
+        addw[m] = add;
+      }
     }
   }
   for (int w = tid + kOldWords * kTopkThreads; w < p.words; w += kTopkThreads) {
     const uint32_t bits = word_bits(w);
     if (bits != mrow[w]) mrow[w] = bits;
+  }
+  if constexpr (POOL) if (pooled) {
+    // the keys and the kept-block bitmap are no longer read: their LDS holds
+    // the pool's lists
+    static_assert(sizeof(PoolLds) <= sizeof(sm.keys), "pool lists fit the key cache");
+    PoolLds& ps = *reinterpret_cast<PoolLds*>(sm.keys);
+    uint32_t mine = 0;
+    bool other = false;  // a change of this thread's words other than xpos entering
+#pragma unroll
+    for (int m = 0; m < kOldWords; ++m) {
+      mine |= remw[m] | addw[m];
+      const int w = tid + m * kTopkThreads;
+      other = other || remw[m] != 0u ||
+              (addw[m] != 0u && !(w == (xpos >> 5) && addw[m] == 1u << (xpos & 31)));
+    }
+    // (the barrier also ends every read of the keys, whose LDS ps reuses)
+    // most decode steps change no kept record, or only add xpos (fast)
+    const bool changes = __syncthreads_or(mine != 0) != 0;
+    const bool fast = changes && __syncthreads_or(other) == 0;
+    if (tid == 0) ps.oldpop = 0;
+    __syncthreads();
+    long long rcarry = 0, acarry = 0;
+#pragma unroll
+    for (int m = 0; m < kOldWords && changes && !fast; ++m) {
+      const int w = tid + m * kTopkThreads;
+      uint32_t both;
+      const uint32_t ex = block_excl((uint32_t)__popc(remw[m]) | ((uint32_t)__popc(addw[m]) << 16),
+                                     ps.scan, both, lane, wid);
+      long long ir = rcarry + (ex & 0xFFFFu), ia = acarry + (ex >> 16);
+      for (uint32_t r = remw[m]; r; r &= r - 1u, ++ir)
+        if (ir < kDiffCap) ps.rem[ir] = 32 * w + __builtin_ctz(r);
+      for (uint32_t a = addw[m]; a; a &= a - 1u, ++ia)
+        if (ia < kDiffCap) ps.add[ia] = 32 * w + __builtin_ctz(a);
+      rcarry += both & 0xFFFFu;
+      acarry += both >> 16;
+    }
+    if (pdiff) atomicAdd(&ps.oldpop, oldpop);
+    __syncthreads();
+    TopkParams tp{};
+    tp.pool = p.pool;
+    tp.words = p.words;
+    tp.sink = p.sink;
+    tp.max_ctx = p.max_ctx;
+    const long long cnt_new = (long long)pcnt_old - rcarry + acarry + (fast ? 1 : 0);
+    long long count = -1;
+    if (pdiff && rcarry <= kDiffCap && acarry <= kDiffCap && ps.oldpop == (uint32_t)pcnt_old &&
+        cnt_new <= p.pool.cap) {
+      if (fast) {
+        // xpos takes slot pcnt_old, from the record wave 0 loaded at the start
+        if (wid == 0) {
+          if (lane < pool_chunks(p.pool.D))
+            pool_put_chunk(pool_tile(p.pool, pair, pcnt_old), p.pool.D, pcnt_old % kPoolTile, lane, xrec);
+          if (lane == 0) {
+            pool_slot_of(p.pool, pair)[xpos] = pcnt_old;
+            pool_pos_of(p.pool, pair)[pcnt_old] = xpos;
+          }
+        }
+        count = pcnt_old + 1;
+      } else {
+        count = changes ? pool_apply(tp, ps, pair, b, h, pcnt_old, (int)rcarry, (int)acarry) : pcnt_old;
+      }
+    }
+    if (count < 0) count = pool_rebuild(tp, ps, pair, b, h, n4, mrow);
+    // count is the same in every thread; no other thread's store needs to
+    // precede the header's (the kernel's end orders them for the readers)
+    if (tid == 0) {
+      int32_t* phdr = p.pool.header + 4 * (size_t)pair;
+      const bool fits = count <= p.pool.cap;
+      if (!fits) report_error(p.pool.errors, KVC_ERR_POOL);
+      phdr[0] = (int32_t)(fits ? count : p.pool.cap);
+      phdr[1] = L;
+      phdr[2] = fits ? (int32_t)kPoolMagic : 0;
+      phdr[3] = 0;
+    }
   }
   if (st && tid == 0) {
     st->magic = kBlockMagic;
@@ -1427,10 +1557,10 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   }
 }
 
-template <int B>
+template <int B, bool POOL>
 __global__ __launch_bounds__(kTopkThreads) void block_topk_kernel(BlockTopkParams p) {
   __shared__ BlockLds sm;
-  block_topk_pair<B>(p, sm, blockIdx.x % p.hkv, blockIdx.x / p.hkv);
+  block_topk_pair<B, POOL>(p, sm, blockIdx.x % p.hkv, blockIdx.x / p.hkv);
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) { topk_group(p, blockIdx.x); }
@@ -1568,7 +1698,7 @@ hipError_t launch_topk(const kvc_cache& c, int budget_permille, TopkState* state
   return hipGetLastError();
 }
 
-template <int D, bool BF16, int B>
+template <int D, bool BF16, int B, bool POOL>
 __global__ __launch_bounds__(kTopkThreads) void score_block_kernel(ScoreParams sp, BlockTopkParams bp,
                                                                   QuantParams qp, int nq) {
   __shared__ BlockLds sm;
@@ -1576,7 +1706,7 @@ __global__ __launch_bounds__(kTopkThreads) void score_block_kernel(ScoreParams s
   __shared__ float wsum[kTopkThreads / kScoreThreads][kScoreThreads / 64];
   const int pairs = bp.hkv * sp.batch;
   if ((int)blockIdx.x < pairs) {  // the refresh never reads this call's rows: they are protected
-    block_topk_pair<B>(bp, sm, blockIdx.x % bp.hkv, blockIdx.x / bp.hkv);
+    block_topk_pair<B, POOL>(bp, sm, blockIdx.x % bp.hkv, blockIdx.x / bp.hkv);
     return;
   }
   // workgroups [pairs, pairs + nq) encode the appended rows (nq = 0: the
@@ -1610,6 +1740,7 @@ static BlockTopkParams block_params(const kvc_cache& c, int budget_permille, int
   p.window = window;
   p.sink = c.n_sink;
   p.recent = c.n_recent;
+  p.pool = pool_ref(c);
   return p;
 }
 
@@ -1617,10 +1748,14 @@ hipError_t launch_block_topk(const kvc_cache& c, int budget_permille, int block_
                              void* state, hipStream_t s) {
   const BlockTopkParams p = block_params(c, budget_permille, block_tokens, window, state);
   const dim3 grid(c.batch * c.num_kv_heads), block(kTopkThreads);
-  switch (block_tokens) {
-    case 16: hipLaunchKernelGGL(block_topk_kernel<16>, grid, block, 0, s, p); break;
-    case 32: hipLaunchKernelGGL(block_topk_kernel<32>, grid, block, 0, s, p); break;
-    case 64: hipLaunchKernelGGL(block_topk_kernel<64>, grid, block, 0, s, p); break;
+  const bool pool = p.pool.cap > 0;
+  switch (block_tokens * 2 + (pool ? 1 : 0)) {
+    case 32: hipLaunchKernelGGL((block_topk_kernel<16, false>), grid, block, 0, s, p); break;
+    case 33: hipLaunchKernelGGL((block_topk_kernel<16, true>), grid, block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((block_topk_kernel<32, false>), grid, block, 0, s, p); break;
+    case 65: hipLaunchKernelGGL((block_topk_kernel<32, true>), grid, block, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((block_topk_kernel<64, false>), grid, block, 0, s, p); break;
+    case 129: hipLaunchKernelGGL((block_topk_kernel<64, true>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1631,9 +1766,17 @@ static void launch_score_block_d(const dim3& grid, int block_tokens, const Score
                                  const BlockTopkParams& bp, const QuantParams& qp, int nq,
                                  hipStream_t s) {
   const dim3 block(kTopkThreads);
-  if (block_tokens == 16) hipLaunchKernelGGL((score_block_kernel<D, BF16, 16>), grid, block, 0, s, sp, bp, qp, nq);
-  else if (block_tokens == 32) hipLaunchKernelGGL((score_block_kernel<D, BF16, 32>), grid, block, 0, s, sp, bp, qp, nq);
-  else hipLaunchKernelGGL((score_block_kernel<D, BF16, 64>), grid, block, 0, s, sp, bp, qp, nq);
+  const bool pool = bp.pool.cap > 0;
+  if (block_tokens == 16) {
+    if (pool) hipLaunchKernelGGL((score_block_kernel<D, BF16, 16, true>), grid, block, 0, s, sp, bp, qp, nq);
+    else hipLaunchKernelGGL((score_block_kernel<D, BF16, 16, false>), grid, block, 0, s, sp, bp, qp, nq);
+  } else if (block_tokens == 32) {
+    if (pool) hipLaunchKernelGGL((score_block_kernel<D, BF16, 32, true>), grid, block, 0, s, sp, bp, qp, nq);
+    else hipLaunchKernelGGL((score_block_kernel<D, BF16, 32, false>), grid, block, 0, s, sp, bp, qp, nq);
+  } else {
+    if (pool) hipLaunchKernelGGL((score_block_kernel<D, BF16, 64, true>), grid, block, 0, s, sp, bp, qp, nq);
+    else hipLaunchKernelGGL((score_block_kernel<D, BF16, 64, false>), grid, block, 0, s, sp, bp, qp, nq);
+  }
 }
 
 hipError_t launch_score_block(const kvc_cache& c, const float* mlp, const void* k_new,

@@ -26,6 +26,12 @@ def pool_capacity_for(w: W.Workload) -> int:
     n4max = max(0, w.max_ctx() - slots)
     if w.mask in ("scores", "mlp") and w.policy == "token":
         keep = (w.budget_permille * n4max) // 1000
+    elif w.mask in ("scores", "mlp") and w.policy == "block":
+        # whole blocks; with a recency window the first candidate block can be partial
+        B = w.block_tokens
+        span = min(w.recency_window, n4max) if w.recency_window > 0 else n4max
+        nb = -(-span // B) + (1 if w.recency_window > 0 else 0)
+        keep = min(n4max, (w.budget_permille * nb) // 1000 * B)
     else:
         keep = n4max
     return max(64, (keep + 63) // 64 * 64)

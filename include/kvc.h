@@ -101,8 +101,11 @@
  * attending. pool_capacity (a multiple of 64) must hold the largest kept
  * count, floor(budget_permille * n4 / 1000) at n4 = max_ctx - 144 (- 0 without
  * INT8 protection); the refresh returns KVC_E_SHAPE when the budget could
- * exceed it. The block policy does not maintain a pool (KVC_E_UNSUPPORTED
- * with pool_capacity > 0), and kvc_decode_attention_windowed reads the mask.
+ * exceed it. The block policy (kvc_score_block_mask, kvc_append_score_block_mask)
+ * maintains the pool the same way; its largest kept count is
+ * floor(budget_permille * nb / 1000) * block_tokens over the nb candidate
+ * blocks (ceil(n4 / block_tokens), or ceil(window / block_tokens) + 1 with a
+ * recency window), at most n4. kvc_decode_attention_windowed reads the mask.
  *
  * Error word (optional; errors != NULL): kernels OR KVC_ERR_* bits into
  * errors[0] when they meet device contents they cannot use (a length outside
@@ -309,7 +312,11 @@ KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* m
  *                  above either way. The state assumes the scores below the
  *                  previous length minus 128 were not changed by anyone else.
  *   The mask it writes is a valid input for kvc_decode_attention like any other.
- *   Returns KVC_E_WORKSPACE for a state smaller than required.
+ *   With pool_capacity > 0 the kept-record pool is updated with the mask (the
+ *   records that leave and enter move in place while at most 1024 of each do
+ *   and the pool held the previous kept set; otherwise it is rebuilt).
+ *   Returns KVC_E_WORKSPACE for a state smaller than required, KVC_E_SHAPE
+ *   when the budget could keep more records than pool_capacity holds.
  */
 KVC_API kvc_status kvc_score_block_mask(const kvc_cache* c, const float* mlp, const void* k_new,
                                         const void* v_new, kvc_dtype src, int32_t n_new_max,

@@ -130,9 +130,19 @@ def test_pool_argument_errors(lib):
     c = desc(pool_capacity=448, **ok)                           # 500 per mille of 880 = 440 fits
     assert lib.kvc_score_topk_mask(ctypes.byref(c), None, None, None, 0, 0, None, 500, FAKE, 16,
                                    None) == -4                  # passes the pool check
-    # the block policy does not maintain a pool
+    # the block policy maintains a pool too: its whole blocks count against the capacity
+    c128 = desc(pool_capacity=128, **ok)
+    assert lib.kvc_score_block_mask(ctypes.byref(c128), None, None, None, 0, 0, None, 500, 16, 0,
+                                    None, 0, None) == -2
+    assert "pool_capacity" in kvc.kvc_last_error()
+    # 500 per mille of 55 blocks of 16 = 27 blocks, 432 records: fits 448
     assert lib.kvc_score_block_mask(ctypes.byref(c), None, None, None, 0, 0, None, 500, 16, 0,
-                                    None, 0, None) == -3
+                                    FAKE, 16, None) == -4       # passes the pool check
+    # a recency window of 100 positions: 7 + 1 candidate blocks, 4 kept = 64 records fit 128
+    assert lib.kvc_score_block_mask(ctypes.byref(c128), None, None, None, 0, 0, None, 500, 16, 100,
+                                    FAKE, 16, None) == -4
+    assert lib.kvc_append_score_block_mask(ctypes.byref(c128), None, FAKE, FAKE, 0, 1, FAKE, 500,
+                                           16, 0, None, 0, None) == -2
     # pool sizes and the rebuild entry point
     assert lib.kvc_pool_bytes(ctypes.byref(c)) == 2 * 8 * (448 // 32) * 40 * 128
     assert lib.kvc_pool_bytes(ctypes.byref(desc())) == 0

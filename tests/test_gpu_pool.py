@@ -424,3 +424,116 @@ def test_error_word():
     run_attention(lc)
     assert c.error_bits() & m.KVC_ERR_LENGTH
     lc.seq_lens[0] = int(lens[0])
+
+
+def _block_pool_run(w, steps, plan, stall=(), attend_every=20):
+    """Decode steps of the block policy on a pooled cache through one block
+    refresh state (even steps: append, then kvc_score_block_mask; odd steps: the
+    fused kvc_append_score_block_mask): after every step the mask equals the
+    oracle's block policy on the GPU's scores and the pool holds exactly the kept
+    records; attention over the pool is checked against the oracle every few steps."""
+    m = kvc()
+    lc = LayerCache(w, pool=True, errors=True)
+    state = m.block_workspace(lc.cache, 16)  # the largest of the three sizes
+    lens = lc.lengths.copy()
+    ns, nr = prot(w)
+    for step in range(steps):
+        budget, window, block = plan(step)
+        n_new = np.ones(w.batch, np.int32)
+        for (s_, b) in stall:
+            if s_ == step:
+                n_new[b] = 0
+        k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+        v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+        lens += n_new
+        lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+        lc.lengths = lens.copy()
+        nn = torch.from_numpy(n_new).cuda()
+        if step % 2:
+            m.kvc_append_score_block_mask(lc.cache, lc.mlp, k_new, v_new, nn, budget, window, block,
+                                          ws=state)
+        else:
+            m.kvc_quantize_append(lc.cache, k_new, v_new, nn)
+            m.kvc_score_block_mask(lc.cache, lc.mlp, k_new, v_new, nn, budget, window, block, ws=state)
+        cpu = cpu_buffers(lc)
+        for b in range(w.batch):
+            L = int(lens[b])
+            start, n4 = regions.int4_range(L, ns, nr)
+            for h in range(w.kv_heads):
+                bits = mask_bits(cpu["keep_mask"][b, h], cpu["keep_mask"].shape[-1] * 32)
+                want = policy.block_keep(cpu["scores"][b, h, start:start + n4], budget, block, window)
+                assert np.array_equal(bits[start:start + n4], want), f"step {step} b={b} h={h}"
+                check_pool(cpu, b, h, L, bits[start:start + n4], w.head_dim, ns)
+        if step % attend_every == attend_every - 1:
+            qn, out, lse = run_attention(lc, step=step)
+            G = w.group_size
+            for b in range(w.batch):
+                L = int(lens[b])
+                for h in range(w.kv_heads):
+                    keep4 = keep4_from_mask(cpu["keep_mask"][b, h], L, ns, nr)
+                    ro, rl = oracle_heads(w, 0, b, h, L, keep4, qn[b, h * G:(h + 1) * G])
+                    assert_attention_close(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ro, rl,
+                                           f"step {step} b={b} h={h}")
+    assert lc.cache.error_bits() == 0
+    return lc
+
+
+def test_block_pool_every_step():
+    """The block policy maintains the pool too: 240 steps through one state while
+    the budget changes (the threshold moves by many blocks: records move in place),
+    sequences stall, and the window and the block size change (state and, where
+    more than 1024 records change, the pool rebuilt); pool checked every step."""
+    w = W.WORKLOADS["fullstep"].replace(name="blk_pool", batch=3, kv_heads=2, q_heads=8, layers=1,
+                                        ctx=2500, ctx_list=(140, 700, 2500), decode_steps=240,
+                                        policy="block", budget_permille=400)
+
+    def plan(step):
+        budget = 300 if step < 60 else 120
+        window = 0 if step < 120 else 600
+        block = 16 if step < 160 else (32 if step < 200 else 64)
+        return budget, window, block
+
+    _block_pool_run(w, 240, plan, stall=[(40, 0), (41, 0), (100, 2)])
+
+
+def test_block_pool_full_size_sampled():
+    """The 128K block workloads with a pool: a few decode steps, then attention
+    over the pool on sampled pairs against the oracle, and against attention
+    through the mask on the same cache (reads the same records)."""
+    import decode_attention_compressed_quantize_amd as m
+
+    for name in ("long128k_blk_b10", "long128k_blk_b50"):
+        w = W.WORKLOADS[name].replace(decode_steps=8)  # room for the appended positions
+        lc = LayerCache(w, pool=True, errors=True)
+        state = m.block_workspace(lc.cache, w.block_tokens)
+        lens = lc.lengths.copy()
+        for step in range(3):
+            k_new = W.kv_rows_torch(w, 0, "K", lens, "cuda")[:, None]
+            v_new = W.kv_rows_torch(w, 0, "V", lens, "cuda")[:, None]
+            lens += 1
+            lc.seq_lens.copy_(torch.from_numpy(lens.astype(np.int32)))
+            lc.lengths = lens.copy()
+            nn = torch.ones(w.batch, dtype=torch.int32, device="cuda")
+            m.kvc_append_score_block_mask(lc.cache, lc.mlp, k_new, v_new, nn, w.budget_permille,
+                                          w.recency_window, w.block_tokens, ws=state)
+        print(f"{name}: errors {lc.cache.error_bits()} headers "
+              f"{lc.cache.pool_header[:, :, :3].cpu().numpy().reshape(-1, 3)[:8].tolist()}", flush=True)
+        cpu = cpu_buffers(lc)
+        ns, nr = prot(w)
+        for (b, h) in sample_pairs(w, 4, 7):
+            L = int(lens[b])
+            start, n4 = regions.int4_range(L, ns, nr)
+            bits = mask_bits(cpu["keep_mask"][b, h], cpu["keep_mask"].shape[-1] * 32)
+            check_pool(cpu, b, h, L, bits[start:start + n4], w.head_dim, ns)
+        qn, out, lse = run_attention(lc, step=3)
+        mask = cpu["keep_mask"]
+        G = w.group_size
+        for (b, h) in sample_pairs(w, 4, 7):
+            L = int(lens[b])
+            keep4 = keep4_from_mask(mask[b, h], L)
+            ro, rl = oracle_heads(w, 0, b, h, L, keep4, qn[b, h * G:(h + 1) * G])
+            assert_attention_close(out[b, h * G:(h + 1) * G], lse[b, h * G:(h + 1) * G], ro, rl,
+                                   f"{name} b={b} h={h}")
+        assert lc.cache.error_bits() == 0
+        print(f"{name}: pool counts {lc.cache.pool_header[:, :, 0].flatten().tolist()[:4]}...", flush=True)
+        del lc
