@@ -1094,12 +1094,8 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   // a pool that holds exactly the kept records of an earlier length is updated
   // by the records that change (as in the token refresh); anything else, and
   // masks longer than the words a thread keeps, is rebuilt
-  // The pool's header and the page of xpos, the position entering the INT4
-  // region at this length (the one leaving the recent window), are loaded here
-  // with the state but not looked at before the key passes, so that they add
-  // no round trip of their own; xpos's record is requested (by wave 0) after
-  // those passes and lands during the mask pass: in the usual decode step it
-  // is the only record that joins the pool.
+  // The pool's header is loaded here with the state but not looked at before
+  // the key passes, so that it adds no round trip of its own.
   const bool pooled = POOL && p.pool.cap > 0;
   const int pair = b * p.hkv + h;
   int32_t ph0 = 0, ph1 = -1, ph2 = 0;
@@ -1109,8 +1105,6 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
     ph1 = ph[1];
     ph2 = ph[2];
   }
-  const int xpos = pooled && n4 > 0 ? sink + n4 - 1 : -1;
-  const int xpg = xpos >= 0 ? p.pool.block_table[(size_t)b * p.pool.max_pages + (xpos >> 4)] : -1;
   // keys above / equal to thr0 as the state left them, and which old keys leave
   const int n4o = len0 > slots ? len0 - slots : 0;
   const int c0o = p.window > 0 ? (n4o - p.window > 0 ? n4o - p.window : 0) : 0;
@@ -1434,10 +1428,6 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
   }
   const bool pdiff = pooled && plen_old >= 0 && p.words <= kOldWords * kTopkThreads;
   const int pn4_old = plen_old > slots ? plen_old - slots : 0;
-  const int xpage = xpg >= 0 && xpg < p.pool.num_pages + p.pool.host_pages ? xpg : -1;
-  uint4 xrec = make_uint4(0u, 0u, 0u, 0u);
-  if (POOL && xpage >= 0 && wid == 0 && lane < pool_chunks(p.pool.D))
-    xrec = *reinterpret_cast<const uint4*>(pool_src_chunk(p.pool, xpage, h, xpos, lane));
   // pool: per word, the kept INT4 records that leave and those that enter
   uint32_t remw[POOL ? kOldWords : 1], addw[POOL ? kOldWords : 1], oldpop = 0;
 #pragma unroll
@@ -1456,8 +1446,7 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
         oldpop += (uint32_t)__popc(old_in);
         remw[m] = old_in & ~new_in;
         uint32_t add = new_in & ~old_in;
-        const bool only_x = xpage >= 0 && w == (xpos >> 5) && add == 1u << (xpos & 31);
-        if (add && !only_x) {
+        if (add) {
           int pa = -1, pb = -1;
           add = pool_word_bits(p.pool, b, w, add, sink, sink + n4, pa, pb);
         }
@@ -1475,23 +1464,15 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
     static_assert(sizeof(PoolLds) <= sizeof(sm.keys), "pool lists fit the key cache");
     PoolLds& ps = *reinterpret_cast<PoolLds*>(sm.keys);
     uint32_t mine = 0;
-    bool other = false;  // a change of this thread's words other than xpos entering
 #pragma unroll
-    for (int m = 0; m < kOldWords; ++m) {
-      mine |= remw[m] | addw[m];
-      const int w = tid + m * kTopkThreads;
-      other = other || remw[m] != 0u ||
-              (addw[m] != 0u && !(w == (xpos >> 5) && addw[m] == 1u << (xpos & 31)));
-    }
+    for (int m = 0; m < kOldWords; ++m) mine |= remw[m] | addw[m];
     // (the barrier also ends every read of the keys, whose LDS ps reuses)
-    // most decode steps change no kept record, or only add xpos (fast)
     const bool changes = __syncthreads_or(mine != 0) != 0;
-    const bool fast = changes && __syncthreads_or(other) == 0;
     if (tid == 0) ps.oldpop = 0;
     __syncthreads();
     long long rcarry = 0, acarry = 0;
 #pragma unroll
-    for (int m = 0; m < kOldWords && changes && !fast; ++m) {
+    for (int m = 0; m < kOldWords && changes; ++m) {
       const int w = tid + m * kTopkThreads;
       uint32_t both;
       const uint32_t ex = block_excl((uint32_t)__popc(remw[m]) | ((uint32_t)__popc(addw[m]) << 16),
@@ -1511,25 +1492,11 @@ __device__ void block_topk_pair(const BlockTopkParams& p, BlockLds& sm, int h, i
     tp.words = p.words;
     tp.sink = p.sink;
     tp.max_ctx = p.max_ctx;
-    const long long cnt_new = (long long)pcnt_old - rcarry + acarry + (fast ? 1 : 0);
+    const long long cnt_new = (long long)pcnt_old - rcarry + acarry;
     long long count = -1;
     if (pdiff && rcarry <= kDiffCap && acarry <= kDiffCap && ps.oldpop == (uint32_t)pcnt_old &&
-        cnt_new <= p.pool.cap) {
-      if (fast) {
-        // xpos takes slot pcnt_old, from the record wave 0 loaded at the start
-        if (wid == 0) {
-          if (lane < pool_chunks(p.pool.D))
-            pool_put_chunk(pool_tile(p.pool, pair, pcnt_old), p.pool.D, pcnt_old % kPoolTile, lane, xrec);
-          if (lane == 0) {
-            pool_slot_of(p.pool, pair)[xpos] = pcnt_old;
-            pool_pos_of(p.pool, pair)[pcnt_old] = xpos;
-          }
-        }
-        count = pcnt_old + 1;
-      } else {
-        count = changes ? pool_apply(tp, ps, pair, b, h, pcnt_old, (int)rcarry, (int)acarry) : pcnt_old;
-      }
-    }
+        cnt_new <= p.pool.cap)
+      count = changes ? pool_apply(tp, ps, pair, b, h, pcnt_old, (int)rcarry, (int)acarry) : pcnt_old;
     if (count < 0) count = pool_rebuild(tp, ps, pair, b, h, n4, mrow);
     // count is the same in every thread; no other thread's store needs to
     // precede the header's (the kernel's end orders them for the readers)
