@@ -219,15 +219,25 @@ def test_pool_given_scores_incremental():
 
 
 def test_pool_decode_steps_many_pairs():
-    """More pairs (600) than one round of 1024-thread refresh workgroups: a decode
-    step packs two pairs per workgroup (one wave each), and the budget change at
-    step 5 makes every pair's step fall back to the full refresh, the two pairs
-    of a workgroup taking turns. Masks and pools match the oracle after every
-    step."""
+    """600 pairs: a decode step packs five pairs per refresh workgroup (one wave
+    each), and the budget change at step 5 makes every pair's step fall back to
+    the full refresh, the pairs of a workgroup taking turns. Masks and pools
+    match the oracle after every step."""
     lens = tuple(int(x) for x in np.linspace(150, 600, 150).round())
     w = W.WORKLOADS["longtail"].replace(name="many_steps", batch=len(lens), kv_heads=4, q_heads=16,
                                         ctx_range=None, ctx_list=lens, decode_steps=12)
     _pool_decode_run(w, 10, lambda s: 500 if s < 5 else 400, attend_every=100)
+
+
+def test_pool_decode_steps_sixteen_pairs_per_workgroup():
+    """2,048 pairs: a decode step packs sixteen pairs per refresh workgroup (one
+    wave each), and the budget change at step 3 makes all sixteen of a
+    workgroup's pairs fall back to the full refresh in turn. Masks and pools
+    match the oracle after every step."""
+    lens = tuple(int(x) for x in np.linspace(150, 420, 256).round())
+    w = W.WORKLOADS["longtail"].replace(name="sixteen_steps", batch=len(lens), kv_heads=8, q_heads=32,
+                                        ctx_range=None, ctx_list=lens, decode_steps=8)
+    _pool_decode_run(w, 6, lambda s: 500 if s < 3 else 400, attend_every=100)
 
 
 def test_pool_keep_all_incremental():
