@@ -314,7 +314,8 @@ KVC_API kvc_status kvc_append_score_topk_mask(const kvc_cache* c, const float* m
  *   The mask it writes is a valid input for kvc_decode_attention like any other.
  *   With pool_capacity > 0 the kept-record pool is updated with the mask (the
  *   records that leave and enter move in place while at most 1024 of each do
- *   and the pool held the previous kept set; otherwise it is rebuilt).
+ *   and the pool held the previous kept set; otherwise it is rebuilt, which
+ *   copies every kept record: always so for max_ctx above 163,840 positions).
  *   Returns KVC_E_WORKSPACE for a state smaller than required, KVC_E_SHAPE
  *   when the budget could keep more records than pool_capacity holds.
  */
