@@ -506,6 +506,16 @@ def test_block_pool_every_step():
     _block_pool_run(w, 240, plan, stall=[(40, 0), (41, 0), (100, 2)])
 
 
+def test_block_pool_pure_kv4_d64():
+    """The block policy's pool without INT8 protection (every appended position
+    is a candidate at once) at D = 64 (two pool tiles per ring slot), with
+    32-token blocks: pool and mask checked every step."""
+    w = W.Workload("blk_pool_kv4", 3, 8, 2, 64, ctx_list=(40, 700, 1900), mask="mlp",
+                   budget_permille=400, policy="block", block_tokens=32, protect=False,
+                   decode_steps=80)
+    _block_pool_run(w, 70, lambda s: (300 if s < 35 else 150, 0, 32), stall=[(20, 1)], attend_every=14)
+
+
 def test_block_pool_full_size_sampled():
     """The 128K block workloads with a pool: a few decode steps, then attention
     over the pool on sampled pairs against the oracle, and against attention
